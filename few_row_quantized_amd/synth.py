@@ -1,0 +1,214 @@
+"""Seeded synthetic inputs for the few-row quantized GEMV.
+
+This module only draws random inputs in the storage formats the kernels and
+the oracle consume; it contains none of the product's arithmetic (no unpack,
+no dequantization, no dot products).  Both the HIP path's tests/bench and the
+CPU oracle's tests take their inputs from here.
+
+Workloads follow the matrix shapes the pages measure on (MLX quantized_matmul
+small-M verify kernels, Facts: the (M,5120)@(17408,5120)^T microbench and the
+4096x4096 / 4096x12288 residual shapes) with the value distributions of the
+affine group format (w = scale*q + bias, one fp16 scale and one fp16 bias per
+output row and group of `group_size` along K):
+
+* 4-bit: q ~ U{0..15}, two codes per byte, low nibble first.
+  scale ~ U[0.001, 0.01] rounded to fp16; bias = fp16(-8*scale + N(0, 1e-3)).
+* 2-bit: q ~ U{0..3}, four codes per byte, least-significant crumb first.
+  scale ~ U[0.005, 0.03]; bias = fp16(-1.5*scale + N(0, 1e-3)).
+* x ~ N(0, 1) rounded to bf16 (round to nearest even); the decoder-layer sweep
+  scales round(1% of K) channels by 20 (in fp32, before rounding) as outliers.
+
+Because the codes are i.i.d. uniform, the packed bytes are i.i.d. uniform over
+0..255 for both widths, so codes are drawn directly as bytes.
+
+Draw order per problem: codes, scales, bias noise, x, outlier channels.  The
+second parameter of N(0, 1e-3) is read as a standard deviation.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Shape:
+    """One projection: y[M,N] = x[M,K] * dequant(W[N,K])^T."""
+
+    name: str
+    K: int
+    N: int
+    bits: int
+    group_size: int
+    m_values: Tuple[int, ...]
+    seed: int
+    outliers: bool = False
+    # Problems that share `share_key` share codes and x (only scales and
+    # biases are redrawn), as in the group-size sweep.
+    share_key: Optional[str] = None
+
+
+def _layer(name: str, K: int, N: int, idx: int) -> Shape:
+    return Shape(f"layer27b_{name}", K, N, 4, 128, tuple(range(1, 17)),
+                 seed=40000 + 100 * idx, outliers=True)
+
+
+# Workloads.  Names say what they are; seeds are fixed per workload.
+WORKLOADS: Dict[str, Shape] = {s.name: s for s in [
+    Shape("tiny_k256_n512_4b_g64", 256, 512, 4, 64, (1, 2, 3, 4), seed=0),
+    Shape("square_k4096_n4096_4b_g64", 4096, 4096, 4, 64, (1, 2, 3, 4, 5, 8), seed=10000),
+    Shape("ffnup_k4096_n12288_4b_g32", 4096, 12288, 4, 32, (4, 8), seed=20000, share_key="ffnup"),
+    Shape("ffnup_k4096_n12288_4b_g64", 4096, 12288, 4, 64, (4, 8), seed=20001, share_key="ffnup"),
+    Shape("ffnup_k4096_n12288_4b_g128", 4096, 12288, 4, 128, (4, 8), seed=20002, share_key="ffnup"),
+    Shape("lowram27b_gateup_k5120_n17408_2b_g64", 5120, 17408, 2, 64, tuple(range(2, 13)), seed=30000),
+    Shape("lowram27b_down_k17408_n5120_2b_g64", 17408, 5120, 2, 64, tuple(range(2, 13)), seed=30100),
+    _layer("q", 5120, 6144, 0),
+    _layer("k", 5120, 1024, 1),
+    _layer("v", 5120, 1024, 2),
+    _layer("o", 6144, 5120, 3),
+    _layer("gate", 5120, 17408, 4),
+    _layer("up", 5120, 17408, 5),
+    _layer("down", 17408, 5120, 6),
+]}
+
+LAYER27B = [f"layer27b_{p}" for p in ("q", "k", "v", "o", "gate", "up", "down")]
+
+
+@dataclasses.dataclass
+class Problem:
+    """Inputs in device storage formats (all numpy, C-contiguous).
+
+    codes  uint8  [N, K*bits/8]
+    scales uint16 [N, K/group_size]   (fp16 bit patterns)
+    biases uint16 [N, K/group_size]   (fp16 bit patterns)
+    x      uint16 [Mmax, K]           (bf16 bit patterns)
+    """
+
+    shape: Shape
+    codes: np.ndarray
+    scales: np.ndarray
+    biases: np.ndarray
+    x: np.ndarray
+    outlier_channels: Optional[np.ndarray]
+    seed: int
+
+    @property
+    def K(self) -> int:
+        return self.shape.K
+
+    @property
+    def N(self) -> int:
+        return self.shape.N
+
+    @property
+    def bits(self) -> int:
+        return self.shape.bits
+
+    @property
+    def group_size(self) -> int:
+        return self.shape.group_size
+
+    def x_rows(self, M: int) -> np.ndarray:
+        return np.ascontiguousarray(self.x[:M])
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); returns uint16 bits.
+
+    Inputs are finite; NaN handling is not needed here.
+    """
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def f64_to_fp16_bits(a: np.ndarray) -> np.ndarray:
+    """Round to IEEE half precision (numpy's conversion, nearest-even); uint16 bits."""
+    return np.asarray(a, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def _draw_meta(rng: np.random.Generator, N: int, G: int, bits: int):
+    if bits == 4:
+        lo, hi, zero_point = 0.001, 0.01, 8.0
+    elif bits == 2:
+        lo, hi, zero_point = 0.005, 0.03, 1.5
+    else:
+        raise ValueError(f"unsupported bits {bits}")
+    s16 = rng.uniform(lo, hi, size=(N, G)).astype(np.float16)
+    noise = rng.normal(0.0, 1e-3, size=(N, G))
+    b16 = (-zero_point * s16.astype(np.float64) + noise).astype(np.float16)
+    return s16.view(np.uint16).copy(), b16.view(np.uint16).copy()
+
+
+def _draw_codes(rng: np.random.Generator, N: int, K: int, bits: int) -> np.ndarray:
+    return rng.integers(0, 256, size=(N, K * bits // 8), dtype=np.uint8)
+
+
+def _draw_x(rng: np.random.Generator, M: int, K: int, outliers: bool):
+    x32 = rng.standard_normal(size=(M, K)).astype(np.float32)
+    chans = None
+    if outliers:
+        n_out = int(round(0.01 * K))
+        chans = np.sort(rng.choice(K, size=n_out, replace=False))
+        x32[:, chans] *= np.float32(20.0)
+    return f32_to_bf16_bits(x32), chans
+
+
+def make_problem(shape: Shape, m_max: Optional[int] = None, seed: Optional[int] = None) -> Problem:
+    """Draw one problem.  x has m_max rows (default: the workload's largest M);
+    an M-row call uses the first M rows."""
+    m_max = m_max or max(shape.m_values)
+    base_seed = shape.seed if seed is None else seed
+    if shape.share_key is not None and seed is None:
+        # Shared codes and x across the group-size sweep; scales/biases per gs.
+        shared_seed = min(s.seed for s in WORKLOADS.values() if s.share_key == shape.share_key)
+        rng_shared = np.random.default_rng(shared_seed)
+        codes = _draw_codes(rng_shared, shape.N, shape.K, shape.bits)
+        rng_meta = np.random.default_rng(base_seed)
+        scales, biases = _draw_meta(rng_meta, shape.N, shape.K // shape.group_size, shape.bits)
+        x, chans = _draw_x(rng_shared, m_max, shape.K, shape.outliers)
+    else:
+        rng = np.random.default_rng(base_seed)
+        codes = _draw_codes(rng, shape.N, shape.K, shape.bits)
+        scales, biases = _draw_meta(rng, shape.N, shape.K // shape.group_size, shape.bits)
+        x, chans = _draw_x(rng, m_max, shape.K, shape.outliers)
+    return Problem(shape, codes, scales, biases, x, chans, base_seed)
+
+
+def custom_shape(K: int, N: int, bits: int, group_size: int, m_values: Sequence[int] = (1,),
+                 seed: int = 1234, outliers: bool = False, name: Optional[str] = None) -> Shape:
+    """A shape outside the named workloads (tests: ragged tails, edge cases)."""
+    return Shape(name or f"custom_k{K}_n{N}_{bits}b_g{group_size}", K, N, bits, group_size,
+                 tuple(m_values), seed, outliers)
+
+
+def special_problem(K: int, N: int, bits: int, group_size: int, M: int, kind: str,
+                    seed: int = 7) -> Problem:
+    """Structured inputs with closed-form results.
+
+    kind = "zero_codes": every code 0 (w = bias).
+    kind = "unit_scale_onehot": scale 1.0, bias 0.0, random codes, x row m = e_{k_m}
+      (one-hot at column k_m = (m * 37 + 5) % K); then y[m, n] = q[n, k_m] exactly.
+    """
+    shape = custom_shape(K, N, bits, group_size, (M,), seed=seed, name=f"{kind}_k{K}_n{N}")
+    p = make_problem(shape, m_max=M, seed=seed)
+    if kind == "zero_codes":
+        p.codes[:] = 0
+    elif kind == "unit_scale_onehot":
+        p.scales[:] = np.float16(1.0).view(np.uint16)
+        p.biases[:] = np.float16(0.0).view(np.uint16)
+        p.x[:] = 0
+        for m in range(M):
+            p.x[m, onehot_column(m, K)] = f32_to_bf16_bits(np.array([1.0], np.float32))[0]
+    else:
+        raise ValueError(kind)
+    return p
+
+
+def onehot_column(m: int, K: int) -> int:
+    return (m * 37 + 5) % K
+
+
+def list_workloads() -> List[str]:
+    return list(WORKLOADS)

@@ -1,0 +1,159 @@
+"""fp64 CPU oracle for the few-row quantized GEMV  y[M,N] = x[M,K] * dequant(W[N,K])^T.
+
+TEST INFRASTRUCTURE ONLY.  This module is the parity reference for the HIP
+path.  Only the test suite, the package smoke check and the benchmark's CPU
+baseline leg may import it; the product path never does.  It shares no code
+with the HIP path (no kernels, headers, helpers or tables) and imports nothing
+from the product package.
+
+What it computes is the plain definition of the operation, written out:
+
+* Affine group quantization (MLX quantized_matmul small-M verify kernels,
+  Facts: "group-size mechanism" -- 4 B of fp16 scale+bias per group; the
+  affine mode listed with qmv_wide): each weight is w[n,k] = s[n,g]*q[n,k] +
+  b[n,g] with g = k // group_size, one fp16 scale and one fp16 bias per output
+  row n and group g.  Read plainly as scale times code plus bias, not
+  scale*(q - zero).
+* Weights stored [out, in] and the product taken as x @ W^T (same page, Facts:
+  the (M,5120)@(17408,5120)^T microbench).
+* Codes packed little-endian along K: 4-bit codes two per byte, low nibble
+  first; 2-bit codes four per byte, lowest crumb first (the 2-bit order is not
+  stated on the pages; this is the reading that matches the 4-bit convention).
+* Every weight group is used once for all M rows (metal : few-row MMA mat-mul
+  and batched copies for speculative decoding, Overview: each weight is
+  dequantized once for all rows).  That is an evaluation-order property of the
+  fast path; the value it reaches is exactly this dequantize-then-matmul.
+
+Precision: fp16 -> fp64 and bf16 -> fp64 are exact.  s*q is exact (11-bit
+significand times a 4-bit integer).  Adding b is exact whenever s*q and b lie
+within ~38 binades of each other, which holds for every workload here (s and
+|b| are within a factor of ~100); each product x*w is then exact too (8-bit
+times <= ~45-bit significands).  So in practice only the K-term summation
+rounds, at K * 2^-53 relative at worst -- twelve orders of magnitude below the
+1e-3 tolerance.
+
+Parity of y is pinned by closed forms, invariants and exact rational brute
+force (the pages print no worked y values); see tests/test_oracle.py.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "fp16_bits_to_f64",
+    "bf16_bits_to_f64",
+    "unpack_codes",
+    "dequantize",
+    "qgemv_reference",
+    "abs_product_sum",
+    "tolerance",
+    "check_close",
+]
+
+
+def fp16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """IEEE binary16 bit patterns -> float64 (exact)."""
+    return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (the top half of a binary32) -> float64 (exact)."""
+    u32 = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u32.view(np.float32).astype(np.float64)
+
+
+def unpack_codes(codes: np.ndarray, K: int, bits: int) -> np.ndarray:
+    """Packed codes [N, K*bits/8] uint8 -> integer codes q [N, K] uint8.
+
+    For column k: byte = codes[n, (k*bits) // 8], shift = (k*bits) % 8,
+    q = (byte >> shift) & (2**bits - 1).
+    """
+    if bits not in (2, 4):
+        raise ValueError("bits must be 2 or 4")
+    codes = np.asarray(codes, dtype=np.uint8)
+    N = codes.shape[0]
+    if codes.shape[1] * 8 != K * bits:
+        raise ValueError("codes row length does not match K*bits/8")
+    k = np.arange(K)
+    byte_idx = (k * bits) // 8
+    shift = ((k * bits) % 8).astype(np.uint8)
+    mask = np.uint8((1 << bits) - 1)
+    q = (codes[:, byte_idx] >> shift[None, :]) & mask
+    assert q.shape == (N, K)
+    return q.astype(np.uint8)
+
+
+def dequantize(q: np.ndarray, scales: np.ndarray, biases: np.ndarray, group_size: int) -> np.ndarray:
+    """w[n,k] = s[n, k//gs] * q[n,k] + b[n, k//gs] in fp64.  scales/biases are fp16 bits."""
+    q = np.asarray(q)
+    N, K = q.shape
+    if K % group_size:
+        raise ValueError("K must be a multiple of group_size")
+    s = fp16_bits_to_f64(scales)
+    b = fp16_bits_to_f64(biases)
+    if s.shape != (N, K // group_size) or b.shape != s.shape:
+        raise ValueError("scales/biases must be [N, K/group_size]")
+    g = np.arange(K) // group_size
+    return s[:, g] * q.astype(np.float64) + b[:, g]
+
+
+def _row_chunks(N: int, K: int, rows: Optional[Sequence[int]], budget_elems: int = 1 << 23):
+    idx = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    step = max(1, budget_elems // max(K, 1))
+    for i in range(0, len(idx), step):
+        yield i, idx[i:i + step]
+
+
+def qgemv_reference(codes, scales, biases, x_bits, M: int, N: int, K: int, bits: int,
+                    group_size: int, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """y_ref[m, j] = sum_k x[m,k] * w[n_j, k] in fp64, n_j = rows[j] (default: all N).
+
+    x_bits: bf16 bit patterns [>=M, K]; the first M rows are used.
+    Dequantization is done in row chunks to bound memory (fp64 W of a
+    17408x5120 matrix would be 713 MB); chunking over output rows does not
+    reorder any sum.
+    """
+    x = bf16_bits_to_f64(np.asarray(x_bits)[:M])
+    if x.shape != (M, K):
+        raise ValueError("x must have at least M rows of length K")
+    n_out = N if rows is None else len(rows)
+    y = np.empty((M, n_out), dtype=np.float64)
+    for start, idx in _row_chunks(N, K, rows):
+        q = unpack_codes(codes[idx], K, bits)
+        w = dequantize(q, scales[idx], biases[idx], group_size)
+        y[:, start:start + len(idx)] = x @ w.T
+    return y
+
+
+def abs_product_sum(codes, scales, biases, x_bits, M: int, N: int, K: int, bits: int,
+                    group_size: int, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """sum_k |x[m,k] * w[n,k]| in fp64 (the scale of the tolerance)."""
+    x = np.abs(bf16_bits_to_f64(np.asarray(x_bits)[:M]))
+    n_out = N if rows is None else len(rows)
+    out = np.empty((M, n_out), dtype=np.float64)
+    for start, idx in _row_chunks(N, K, rows):
+        q = unpack_codes(codes[idx], K, bits)
+        w = np.abs(dequantize(q, scales[idx], biases[idx], group_size))
+        out[:, start:start + len(idx)] = x @ w.T
+    return out
+
+
+def tolerance(abs_sum: np.ndarray, rel: float = 1e-3, abs_floor: float = 1e-6) -> np.ndarray:
+    """Per-element bound |y - y_ref| <= rel * sum_k |x_k w_k| + abs_floor."""
+    return rel * np.asarray(abs_sum, dtype=np.float64) + abs_floor
+
+
+def check_close(y_test, y_ref, abs_sum, rel: float = 1e-3, abs_floor: float = 1e-6):
+    """Return (ok, worst_ratio, index).  worst_ratio = max |dy| / tol (<= 1 passes).
+    NaN/Inf in y_test fail."""
+    y_test = np.asarray(y_test, dtype=np.float64)
+    if not np.all(np.isfinite(y_test)):
+        bad = np.argwhere(~np.isfinite(y_test))[0]
+        return False, float("inf"), tuple(int(i) for i in bad)
+    tol = tolerance(abs_sum, rel, abs_floor)
+    ratio = np.abs(y_test - y_ref) / tol
+    idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+    worst = float(ratio[idx])
+    return worst <= 1.0, worst, tuple(int(i) for i in idx)
