@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the few-row quantized GEMV on one MI355X.
+
+Workload (default): the square projection K = N = 4096, 4-bit affine codes,
+group size 64, activation rows M in {1, 2, 3, 4, 5, 8}.  One step = one
+verify call per M (dispatcher's choice of path), each on the next weight copy
+of a rotating pool larger than every cache (>= 1 GiB, well above the 256 MB
+MALL), so every call streams its weights from HBM.
+
+Timing: the K timed steps are captured into one HIP graph (a dependent chain
+of launches on one stream, no host in the loop) and replayed between two
+events after W warm-up steps.  Per-M chains (one graph of L launches for each
+M) give time(M)/time(1) and the average launch duration of each kernel.
+
+Prints ONE JSON line (rank 0).  --gpus N with N > 1 exits with a message:
+this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from few_row_quantized_amd import accounting, synth  # noqa: E402
+
+METRIC = "effective weight GB/s (% of HBM peak) and time(M)/time(1) at M=1..16"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="square_k4096_n4096_4b_g64")
+    ap.add_argument("--m-values", default=None, help="comma list; default: the workload's")
+    ap.add_argument("--pool-mib", type=int, default=1024)
+    ap.add_argument("--chain", type=int, default=400, help="launches per per-M chain")
+    ap.add_argument("--path", default="auto", choices=["auto", "dot", "mfma"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hot", action="store_true", help="reuse one weight copy (cache-resident)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
+    return ap.parse_args()
+
+
+class Pool:
+    """P device copies of (codes, scales, biases) with identical contents."""
+
+    def __init__(self, p, copies):
+        import numpy as np
+        import torch
+        self.P = copies
+        c = torch.from_numpy(p.codes).cuda()
+        s = torch.from_numpy(p.scales.view(np.int16)).cuda()
+        b = torch.from_numpy(p.biases.view(np.int16)).cuda()
+        self.codes = torch.empty((copies,) + tuple(c.shape), dtype=c.dtype, device="cuda")
+        self.scales = torch.empty((copies,) + tuple(s.shape), dtype=s.dtype, device="cuda")
+        self.biases = torch.empty((copies,) + tuple(b.shape), dtype=b.dtype, device="cuda")
+        for i in range(copies):
+            self.codes[i].copy_(c)
+            self.scales[i].copy_(s)
+            self.biases[i].copy_(b)
+        torch.cuda.synchronize()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from few_row_quantized_amd import qgemv as q
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    q.lib()  # fail loudly if the library is missing
+
+    s = synth.WORKLOADS[args.workload]
+    ms = [int(v) for v in args.m_values.split(",")] if args.m_values else list(s.m_values)
+    p = synth.make_problem(s, m_max=max(ms))
+    W = accounting.weight_bytes(s.N, s.K, s.bits, s.group_size)
+    copies = 1 if args.hot else max(2, math.ceil(args.pool_mib * 2 ** 20 / W))
+    log(f"[bench] {s.name}: W={W} B, pool of {copies} copies ({copies * W / 2**20:.0f} MiB), M={ms}")
+    pool = Pool(p, copies)
+    x = torch.from_numpy(p.x.view(np.int16)).cuda()
+    ys = {M: torch.empty((M, s.N), dtype=torch.float32, device="cuda") for M in ms}
+    paths = {M: (args.path if args.path != "auto" else
+                 {q.PATH_DOT: "dot", q.PATH_MFMA: "mfma"}[q.qgemv_select(M, s.N, s.K, s.bits, s.group_size)])
+             for M in ms}
+
+    counter = [0]
+
+    def launch(M):
+        i = counter[0] % copies
+        counter[0] += 1
+        q.qgemv_run_path(args.path, pool.codes[i], pool.scales[i], pool.biases[i], x, ys[M], M,
+                         s.N, s.K, s.bits, s.group_size)
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    def time_graph(g, reps=1):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3  # seconds
+
+    # eager warm-up (first launches load code objects)
+    for M in ms:
+        launch(M)
+    torch.cuda.synchronize()
+
+    # main measurement: K steps in one graph, W warm-up steps in another
+    warm_g = capture(lambda: [launch(M) for _ in range(max(1, args.warmup)) for M in ms])
+    main_g = capture(lambda: [launch(M) for _ in range(args.steps) for M in ms])
+    log("[bench] graphs captured; warm-up")
+    time_graph(warm_g)
+    log(f"[bench] timing {args.steps} steps")
+    t_main = time_graph(main_g)
+    ms_per_step = t_main / args.steps * 1e3
+    value = (W * len(ms) * args.steps) / t_main / 1e9
+
+    # per-M chains: average launch duration of each configuration
+    per_m = {}
+    for M in ms:
+        g = capture(lambda: [launch(M) for _ in range(args.chain)])
+        time_graph(g)  # warm
+        t = time_graph(g, reps=2) / (2 * args.chain)
+        per_m[M] = t
+        log(f"[bench] M={M:2d} path={paths[M]:4s} {t * 1e6:8.3f} us/launch  "
+            f"{W / t / 1e9:8.1f} GB/s")
+    t1 = per_m.get(1, per_m[min(ms)])
+    per_m_json = {str(M): {"path": paths[M], "us": round(per_m[M] * 1e6, 4),
+                           "weight_GBps": round(W / per_m[M] / 1e9, 1),
+                           "pct_hbm_peak": round(100 * W / per_m[M] / 1e9 / HBM_PEAK_GBS, 2),
+                           "t_over_t1": round(per_m[M] / t1, 4)} for M in ms}
+
+    # dominant kernel = the (path, M) configuration with the largest time per step
+    Mdom = max(ms, key=lambda M: per_m[M])
+    alg = accounting.algorithmic_bytes(Mdom, s.N, s.K, s.bits, s.group_size)
+    achieved = alg / per_m[Mdom] / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": f"qgemv_{paths[Mdom]}_kernel M={Mdom}",
+                "bytes_per_launch": alg, "avg_launch_us": round(per_m[Mdom] * 1e6, 4)}
+
+    ceiling = None if args.no_ceiling else measure_ceiling(W, copies, args.chain, capture, time_graph)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(p, ms, W, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": s.name, "K": s.K, "N": s.N, "bits": s.bits,
+                   "group_size": s.group_size, "m_values": ms, "path": args.path,
+                   "weight_bytes": W, "pool_copies": copies,
+                   "timing": "one HIP graph of K steps; each call on the next pool copy"},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "t8_over_t1": per_m_json.get("8", {}).get("t_over_t1"),
+        "per_m": per_m_json,
+        "roofline": roofline,
+        "ceiling": ceiling,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def measure_ceiling(W, copies, chain, capture, time_graph):
+    """Pure streaming read of W bytes per launch (qgemv_stream_probe) over the
+    same rotating-pool protocol, and the same probe on a tiny buffer (the
+    per-launch floor of a graph chain)."""
+    import torch
+    from few_row_quantized_amd import qgemv as q
+    nbytes = (W + 15) // 16 * 16
+    buf = torch.randint(0, 255, (copies, nbytes), dtype=torch.uint8, device="cuda")
+    out = torch.empty(q.qgemv_stream_probe_blocks(nbytes), dtype=torch.int32, device="cuda")
+    small = 64 * 1024
+    sout = torch.empty(q.qgemv_stream_probe_blocks(small), dtype=torch.int32, device="cuda")
+    ctr = [0]
+
+    def one():
+        i = ctr[0] % copies
+        ctr[0] += 1
+        q.qgemv_stream_probe(buf[i], nbytes, out)
+
+    one()
+    g = capture(lambda: [one() for _ in range(chain)])
+    time_graph(g)
+    t = time_graph(g, reps=2) / (2 * chain)
+    gs = capture(lambda: [q.qgemv_stream_probe(buf[0], small, sout) for _ in range(chain)])
+    time_graph(gs)
+    tf = time_graph(gs, reps=2) / (2 * chain)
+    log(f"[bench] stream probe {nbytes} B: {t * 1e6:.3f} us/launch = {nbytes / t / 1e9:.1f} GB/s; "
+        f"64 KiB floor {tf * 1e6:.3f} us")
+    del buf
+    return {"stream_probe_bytes": nbytes, "stream_probe_us": round(t * 1e6, 4),
+            "stream_probe_GBps": round(nbytes / t / 1e9, 1),
+            "launch_floor_us_64KiB": round(tf * 1e6, 4)}
+
+
+def cpu_baseline(p, ms, W, budget_s):
+    """The fp64 oracle (as it stands) on the host cores: repeated verify steps
+    over the same workload until ~budget_s of CPU time is spent."""
+    sys.path.insert(0, ROOT)
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    s = p.shape
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        for M in ms:
+            oracle.qgemv_reference(p.codes, p.scales, p.biases, p.x, M, s.N, s.K, s.bits, s.group_size)
+            calls += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(W * calls / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{calls} oracle calls ({calls // len(ms)} verify steps over M={ms}) of "
+                      f"{s.name} in {dt:.1f} s; numpy fp64 dequantize + BLAS matmul"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,119 @@
+// C ABI of libqgemv: argument validation, path selection, launch.
+// The library holds no mutable state, allocates nothing and never
+// synchronizes; every entry point only validates and enqueues.
+
+#include <stdint.h>
+
+#include "qgemv_internal.h"
+#include "qgemv_select_table.h"
+
+using qgemv::QgemvArgs;
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int validate_shape(int M, int N, int K, int bits, int group_size) {
+  if (bits != 2 && bits != 4) return QGEMV_EINVAL;
+  if (group_size != 32 && group_size != 64 && group_size != 128) return QGEMV_EINVAL;
+  if (M < 1 || M > QGEMV_MAX_M) return QGEMV_EINVAL;
+  if (N < 1 || N > QGEMV_MAX_N) return QGEMV_EINVAL;
+  if (K < 64 || K > QGEMV_MAX_K || K % 64 != 0 || K % group_size != 0) return QGEMV_EINVAL;
+  return QGEMV_OK;
+}
+
+int validate(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
+             const uint16_t *x, const float *y, int M, int N, int K, int bits, int group_size) {
+  const int s = validate_shape(M, N, K, bits, group_size);
+  if (s != QGEMV_OK) return s;
+  if (!codes || !scales || !biases || !x || !y) return QGEMV_EINVAL;
+  if (!aligned(codes, 16) || !aligned(x, 16) || !aligned(scales, 16) || !aligned(biases, 16) ||
+      !aligned(y, 16))
+    return QGEMV_EALIGN;
+  return QGEMV_OK;
+}
+
+bool path_supported(int path, int K, int bits, int group_size) {
+  if (path == QGEMV_PATH_DOT || path == QGEMV_PATH_AUTO) return true;
+  if (path == QGEMV_PATH_MFMA) return qgemv::mfma_supports(K, bits, group_size);
+  return false;
+}
+
+int select_path(int M, int N, int K, int bits, int group_size) {
+  if (!qgemv::mfma_supports(K, bits, group_size)) return QGEMV_PATH_DOT;
+  return M >= qgemv::mfma_start_row(N, K, bits, group_size) ? QGEMV_PATH_MFMA : QGEMV_PATH_DOT;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qgemv_select(int M, int N, int K, int bits, int group_size) {
+  const int s = validate_shape(M, N, K, bits, group_size);
+  if (s != QGEMV_OK) return s;
+  return select_path(M, N, K, bits, group_size);
+}
+
+int qgemv_path_supported(int path, int M, int N, int K, int bits, int group_size) {
+  const int s = validate_shape(M, N, K, bits, group_size);
+  if (s != QGEMV_OK) return s;
+  if (path != QGEMV_PATH_AUTO && path != QGEMV_PATH_DOT && path != QGEMV_PATH_MFMA)
+    return QGEMV_EINVAL;
+  return path_supported(path, K, bits, group_size) ? 1 : 0;
+}
+
+int qgemv_run_path(int path, const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
+                   const uint16_t *x, float *y, int M, int N, int K, int bits, int group_size,
+                   void *stream) {
+  if (path != QGEMV_PATH_AUTO && path != QGEMV_PATH_DOT && path != QGEMV_PATH_MFMA)
+    return QGEMV_EINVAL;
+  const int s = validate(codes, scales, biases, x, y, M, N, K, bits, group_size);
+  if (s != QGEMV_OK) return s;
+  if (path == QGEMV_PATH_AUTO) path = select_path(M, N, K, bits, group_size);
+  if (!path_supported(path, K, bits, group_size)) return QGEMV_EUNSUPPORTED;
+  const QgemvArgs a{codes, scales, biases, x, y, M, N, K, bits, group_size};
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return path == QGEMV_PATH_MFMA ? qgemv::launch_mfma(a, st) : qgemv::launch_dot(a, st);
+}
+
+int qgemv_small(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
+                const uint16_t *x, float *y, int M, int N, int K, int bits, int group_size,
+                void *stream) {
+  return qgemv_run_path(QGEMV_PATH_AUTO, codes, scales, biases, x, y, M, N, K, bits, group_size,
+                        stream);
+}
+
+int qgemv_unpack_probe(int path, const uint8_t *codes, uint8_t *q_out, int N, int K, int bits,
+                       int group_size, void *stream) {
+  const int s = validate_shape(1, N, K, bits, group_size);
+  if (s != QGEMV_OK) return s;
+  if (path != QGEMV_PATH_DOT && path != QGEMV_PATH_MFMA) return QGEMV_EINVAL;
+  if (!codes || !q_out) return QGEMV_EINVAL;
+  if (!aligned(codes, 16)) return QGEMV_EALIGN;
+  if (!path_supported(path, K, bits, group_size)) return QGEMV_EUNSUPPORTED;
+  return qgemv::launch_unpack_probe(path, codes, q_out, N, K, bits,
+                                    reinterpret_cast<hipStream_t>(stream));
+}
+
+int qgemv_stream_probe_blocks(size_t nbytes) { return qgemv::stream_probe_blocks(nbytes); }
+
+int qgemv_stream_probe(const uint8_t *buf, size_t nbytes, uint32_t *out, void *stream) {
+  if (!buf || !out || nbytes == 0 || nbytes % 16 != 0) return QGEMV_EINVAL;
+  if (!aligned(buf, 16) || !aligned(out, 4)) return QGEMV_EALIGN;
+  return qgemv::launch_stream_probe(buf, nbytes, out, reinterpret_cast<hipStream_t>(stream));
+}
+
+const char *qgemv_strerror(int status) {
+  switch (status) {
+    case QGEMV_OK: return "ok";
+    case QGEMV_EINVAL: return "invalid argument (shape, bits, group size, path or null pointer)";
+    case QGEMV_EUNSUPPORTED: return "the requested path does not support this shape";
+    case QGEMV_EALIGN: return "buffer not 16-byte aligned";
+    case QGEMV_EHIP: return "HIP runtime rejected the kernel launch";
+    default: return "unknown status";
+  }
+}
+
+int qgemv_version(void) { return 100; }
+
+}  // extern "C"

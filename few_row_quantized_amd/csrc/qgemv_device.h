@@ -1,0 +1,185 @@
+// Device helpers for the few-row quantized GEMV kernels (gfx950, wave64).
+//
+// Codes become bf16 values 128+q: for 0 <= q < 128 the bf16 bit pattern of
+// 128+q is 0x4300 | q (exponent of 2^7, q in the 7 mantissa bits), so one
+// AND-OR places two codes into the two halves of a dword as an exact bf16
+// pair.  Dot products of these pairs with bf16 activations are exact per
+// product in fp32; the 128 offset is removed once per group through the
+// group's activation sum (128 * sum x), folded together with the bias.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qgemv {
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kOffsetPair = 0x43004300u;  // bf16(128) in both halves
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b16) {
+  return __builtin_bit_cast(float, b16 << 16);
+}
+
+// a.lo*b.lo + a.hi*b.hi + c, bf16 pairs, fp32 accumulate (v_dot2c_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// v_perm_b32: bytes of {hi_src, lo_src} selected by `sel` (0-3: lo_src, 4-7: hi_src, 0x0c: zero).
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi_src, lo_src, sel);
+}
+
+// A value the compiler cannot see through, kept in a VGPR.  Used for the
+// OR operand of the unpack so that AND+OR fuse into one v_and_or_b32 (a VOP3
+// instruction on gfx9 takes at most one literal/SGPR operand).
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t v) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+  return r;
+}
+
+// ---------------------------------------------------------------- code unpack
+//
+// 4-bit "offset" pairing (dot path): dword w holds codes j = 0..7 (nibble j).
+// Pair p (p = 0..3) = codes (p, p+4).
+// `off` holds kOffsetPair (pass opaque_u32(kOffsetPair) for a fused AND-OR).
+__device__ __forceinline__ void unpack4_split_pairs(uint32_t w, uint32_t (&o)[4],
+                                                    uint32_t off = kOffsetPair) {
+  o[0] = (w & 0x000F000Fu) | off;
+  o[1] = ((w >> 4) & 0x000F000Fu) | off;
+  o[2] = ((w >> 8) & 0x000F000Fu) | off;
+  o[3] = ((w >> 12) & 0x000F000Fu) | off;
+}
+
+// 4-bit "natural" pairing (MFMA path): pair p = codes (2p, 2p+1), i.e. the two
+// nibbles of byte p, so the activation operand keeps its memory order.
+__device__ __forceinline__ void unpack4_natural_pairs(uint32_t w, uint32_t (&o)[4]) {
+  const uint32_t h = w >> 4;
+  // byte p of w -> byte 0, byte p of (w >> 4) -> byte 2, zeros elsewhere.
+  o[0] = (perm_b32(h, w, 0x0c040c00u) & 0x000F000Fu) | kOffsetPair;
+  o[1] = (perm_b32(h, w, 0x0c050c01u) & 0x000F000Fu) | kOffsetPair;
+  o[2] = (perm_b32(h, w, 0x0c060c02u) & 0x000F000Fu) | kOffsetPair;
+  o[3] = (perm_b32(h, w, 0x0c070c03u) & 0x000F000Fu) | kOffsetPair;
+}
+
+// Same, as the 4-dword MFMA operand; `off` holds kOffsetPair (opaque_u32).
+__device__ __forceinline__ u32x4_t unpack4_natural_quad(uint32_t w, uint32_t off) {
+  const uint32_t h = w >> 4;
+  u32x4_t o;
+  o[0] = (perm_b32(h, w, 0x0c040c00u) & 0x000F000Fu) | off;
+  o[1] = (perm_b32(h, w, 0x0c050c01u) & 0x000F000Fu) | off;
+  o[2] = (perm_b32(h, w, 0x0c060c02u) & 0x000F000Fu) | off;
+  o[3] = (perm_b32(h, w, 0x0c070c03u) & 0x000F000Fu) | off;
+  return o;
+}
+
+// 2-bit pairing (both paths): dword w holds codes j = 0..15 (crumb j).
+// Pair j (j = 0..7) = codes (j, j+8).
+__device__ __forceinline__ void unpack2_split_pairs(uint32_t w, uint32_t (&o)[8],
+                                                    uint32_t off = kOffsetPair) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = ((w >> (2 * j)) & 0x00030003u) | off;
+}
+
+// Half h (h = 0, 1) of the 2-bit pairing as an MFMA operand: pairs 4h..4h+3.
+__device__ __forceinline__ u32x4_t unpack2_split_quad(uint32_t w, int h, uint32_t off) {
+  u32x4_t o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = ((w >> (2 * (4 * h + e))) & 0x00030003u) | off;
+  return o;
+}
+
+// ---------------------------------------------------------------- activation pairing
+//
+// Activations are re-paired to match the code pairing.  X[i] holds bf16
+// elements (2i, 2i+1) of a run of consecutive activations.
+//
+// pair of elements (e, e+4) from X[0..3] (4-bit offset pairing), e = 0..3
+__device__ __forceinline__ uint32_t xpair_stride4(const uint32_t (&X)[4], int e) {
+  return (e & 1) ? perm_b32(X[(e >> 1) + 2], X[e >> 1], 0x07060302u)
+                 : perm_b32(X[(e >> 1) + 2], X[e >> 1], 0x05040100u);
+}
+
+// pair of elements (e, e+8) from X[0..7] (2-bit pairing), e = 0..7
+__device__ __forceinline__ uint32_t xpair_stride8(const uint32_t (&X)[8], int e) {
+  return (e & 1) ? perm_b32(X[(e >> 1) + 4], X[e >> 1], 0x07060302u)
+                 : perm_b32(X[(e >> 1) + 4], X[e >> 1], 0x05040100u);
+}
+
+// ---------------------------------------------------------------- lane exchange
+//
+// 4x4 transpose of dwords between the four 16-lane rows of a wave:
+// on entry row g holds r[c] = T[g][c]; on exit row g holds r[c] = T[c][g].
+// Uses v_permlane32_swap (upper 32 lanes of the first operand <-> lower 32
+// lanes of the second) and v_permlane16_swap (odd rows of the first operand
+// <-> even rows of the second).
+__device__ __forceinline__ void transpose_rows4(uint32_t (&r)[4]) {
+  {
+    auto a = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);
+    r[0] = a[0];
+    r[2] = a[1];
+    auto b = __builtin_amdgcn_permlane32_swap(r[1], r[3], false, false);
+    r[1] = b[0];
+    r[3] = b[1];
+  }
+  {
+    auto a = __builtin_amdgcn_permlane16_swap(r[0], r[1], false, false);
+    r[0] = a[0];
+    r[1] = a[1];
+    auto b = __builtin_amdgcn_permlane16_swap(r[2], r[3], false, false);
+    r[2] = b[0];
+    r[3] = b[1];
+  }
+}
+
+__device__ __forceinline__ float dpp_row_sum16(float v) {
+  // butterfly inside each 16-lane row: mirror, half-mirror, quad swaps
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  return v;
+}
+
+// Sum V per-lane values over all 64 lanes (V % 4 == 0).  On exit out[j]
+// holds, in every lane of row rho (lanes 16*rho .. 16*rho+15), the total of
+// value index 4*j + kRowValue[rho], kRowValue = {0, 2, 1, 3}.
+// Each swap stage halves the number of live registers, so the cost is
+// ~2.5 instructions per value instead of ~6-12 for independent reductions.
+template <int V>
+__device__ __forceinline__ void wave_reduce_multi(const float (&v)[V], float (&out)[V / 4]) {
+  static_assert(V % 4 == 0, "pad to a multiple of 4");
+  float h[V / 2];
+#pragma unroll
+  for (int i = 0; i < V / 2; ++i) {
+    auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v[2 * i]),
+                                              __builtin_bit_cast(uint32_t, v[2 * i + 1]), false,
+                                              false);
+    h[i] = __builtin_bit_cast(float, (uint32_t)p[0]) + __builtin_bit_cast(float, (uint32_t)p[1]);
+  }
+#pragma unroll
+  for (int j = 0; j < V / 4; ++j) {
+    auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, h[2 * j]),
+                                              __builtin_bit_cast(uint32_t, h[2 * j + 1]), false,
+                                              false);
+    out[j] = dpp_row_sum16(__builtin_bit_cast(float, (uint32_t)p[0]) +
+                           __builtin_bit_cast(float, (uint32_t)p[1]));
+  }
+}
+
+__device__ __forceinline__ int row_value_index(int rho) {
+  // {0, 2, 1, 3}
+  return ((rho & 1) << 1) | (rho >> 1);
+}
+
+}  // namespace qgemv

@@ -1,0 +1,39 @@
+// Internal interface between the C ABI (qgemv_api.cpp) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/qgemv.h"
+
+namespace qgemv {
+
+struct QgemvArgs {
+  const uint8_t *codes;
+  const uint16_t *scales;
+  const uint16_t *biases;
+  const uint16_t *x;
+  float *y;
+  int M, N, K, bits, group_size;
+};
+
+// LDS of one workgroup: hardware limit on gfx950, and the dot path's
+// preferred x-staging budget (two workgroups per CU).
+constexpr size_t kLdsMax = 160 * 1024;
+constexpr size_t kDotLdsBudget = 80 * 1024;
+
+// Launchers: enqueue on `stream`, return QGEMV_OK / QGEMV_EUNSUPPORTED / QGEMV_EHIP.
+int launch_dot(const QgemvArgs &a, hipStream_t stream);
+int launch_mfma(const QgemvArgs &a, hipStream_t stream);
+
+// Shape support of the MFMA path (host check).
+bool mfma_supports(int K, int bits, int group_size);
+
+// Probes.
+int launch_unpack_probe(int path, const uint8_t *codes, uint8_t *q_out, int N, int K, int bits,
+                        hipStream_t stream);
+int launch_stream_probe(const uint8_t *buf, size_t nbytes, uint32_t *out, hipStream_t stream);
+int stream_probe_blocks(size_t nbytes);
+
+}  // namespace qgemv

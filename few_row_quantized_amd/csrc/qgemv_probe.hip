@@ -1,0 +1,173 @@
+// Probe kernels: decoded-code readback (bit-exactness of the unpack stage)
+// and a pure streaming read (bandwidth ceiling at a given byte count).
+
+#include "qgemv_device.h"
+#include "qgemv_internal.h"
+
+namespace qgemv {
+
+namespace {
+
+// Extract q from a bf16 pair half 0x4300|q; anything else marks an encoding error.
+__device__ __forceinline__ uint8_t code_of(uint32_t half16) {
+  return ((half16 & 0xFF80u) == 0x4300u) ? (uint8_t)(half16 & 0x7Fu) : (uint8_t)0xFF;
+}
+
+// Dot-path decoding: one thread per (row n, 16-byte chunk c), same unpack
+// routines and pair-to-column mapping as qgemv_dot_kernel.
+template <int BITS>
+__global__ __launch_bounds__(256) void unpack_probe_dot(const uint8_t *__restrict__ codes,
+                                                        uint8_t *__restrict__ q, int N, int K) {
+  constexpr int CW = 128 / BITS;
+  const int NC = K / CW;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)N * NC) return;
+  const int n = (int)(idx / NC);
+  const int c = (int)(idx % NC);
+  const size_t RB = (size_t)K * BITS / 8;
+  const uint4 v = *reinterpret_cast<const uint4 *>(codes + (size_t)n * RB + (size_t)c * 16);
+  const uint32_t cd[4] = {v.x, v.y, v.z, v.w};
+  uint8_t *qr = q + (size_t)n * K + (size_t)c * CW;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    if constexpr (BITS == 4) {
+      uint32_t p[4];
+      unpack4_split_pairs(cd[d], p);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qr[8 * d + e] = code_of(p[e] & 0xFFFFu);
+        qr[8 * d + e + 4] = code_of(p[e] >> 16);
+      }
+    } else {
+      uint32_t p[8];
+      unpack2_split_pairs(cd[d], p);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qr[16 * d + e] = code_of(p[e] & 0xFFFFu);
+        qr[16 * d + e + 8] = code_of(p[e] >> 16);
+      }
+    }
+  }
+}
+
+// MFMA-path decoding: one wave per (16-row tile, 64-byte super-chunk), same
+// lane-to-address mapping, row transpose and unpack as qgemv_mfma_kernel; each
+// B-operand slot is written to the column it stands for.
+template <int BITS>
+__global__ __launch_bounds__(64) void unpack_probe_mfma(const uint8_t *__restrict__ codes,
+                                                        uint8_t *__restrict__ q, int N, int K) {
+  constexpr int CW = 128 / BITS;
+  constexpr int SCW = 4 * CW;
+  const int lane = threadIdx.x;
+  const int col = lane & 15, kb = lane >> 4;
+  const int nsc = K / SCW;
+  const int tile = blockIdx.x / nsc;
+  const int sc = blockIdx.x % nsc;
+  const int n = tile * 16 + col;
+  const bool ok = n < N;
+  const size_t RB = (size_t)K * BITS / 8;
+  uint4 v = ok ? *reinterpret_cast<const uint4 *>(codes + (size_t)n * RB + (size_t)sc * 64 + kb * 16)
+               : make_uint4(0, 0, 0, 0);
+  uint32_t r[4] = {v.x, v.y, v.z, v.w};
+  transpose_rows4(r);  // all lanes take part, also those past row N
+  if (!ok) return;
+  uint8_t *qr = q + (size_t)n * K + (size_t)sc * SCW;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if constexpr (BITS == 4) {
+      uint32_t p[4];
+      unpack4_natural_pairs(r[c], p);
+      const int k0 = 32 * c + 8 * kb;  // B slots 2e, 2e+1 stand for k0+2e, k0+2e+1
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qr[k0 + 2 * e] = code_of(p[e] & 0xFFFFu);
+        qr[k0 + 2 * e + 1] = code_of(p[e] >> 16);
+      }
+    } else {
+      uint32_t p[8];
+      unpack2_split_pairs(r[c], p);
+      const int k0 = 64 * c + 16 * kb;  // pair e stands for k0+e and k0+e+8
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qr[k0 + e] = code_of(p[e] & 0xFFFFu);
+        qr[k0 + e + 8] = code_of(p[e] >> 16);
+      }
+    }
+  }
+}
+
+constexpr int kStreamThreads = 256;
+constexpr int kStreamUnroll = 4;
+constexpr int kStreamMaxBlocks = 2048;
+
+__global__ __launch_bounds__(kStreamThreads) void stream_probe_kernel(const uint4 *__restrict__ buf,
+                                                                      size_t n16,
+                                                                      uint32_t *__restrict__ out) {
+  __shared__ uint32_t part[kStreamThreads / 64];
+  const size_t stride = (size_t)gridDim.x * kStreamThreads;
+  size_t i = (size_t)blockIdx.x * kStreamThreads + threadIdx.x;
+  uint32_t h = 0;
+  for (; i + (kStreamUnroll - 1) * stride < n16; i += kStreamUnroll * stride) {
+    uint4 v[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) v[u] = buf[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) h ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 v = buf[i];
+    h ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  // xor over the wave, then over the block
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) h ^= __shfl_xor(h, off, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = h;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int w = 0; w < kStreamThreads / 64; ++w) t ^= part[w];
+    out[blockIdx.x] = t;
+  }
+}
+
+}  // namespace
+
+int launch_unpack_probe(int path, const uint8_t *codes, uint8_t *q_out, int N, int K, int bits,
+                        hipStream_t stream) {
+  if (path == QGEMV_PATH_DOT) {
+    const int CW = 128 / bits;
+    const size_t threads = (size_t)N * (K / CW);
+    const int blocks = (int)((threads + 255) / 256);
+    if (bits == 4)
+      hipLaunchKernelGGL(unpack_probe_dot<4>, dim3(blocks), dim3(256), 0, stream, codes, q_out, N, K);
+    else
+      hipLaunchKernelGGL(unpack_probe_dot<2>, dim3(blocks), dim3(256), 0, stream, codes, q_out, N, K);
+  } else if (path == QGEMV_PATH_MFMA) {
+    const int SCW = 4 * (128 / bits);
+    const int blocks = ((N + 15) / 16) * (K / SCW);
+    if (bits == 4)
+      hipLaunchKernelGGL(unpack_probe_mfma<4>, dim3(blocks), dim3(64), 0, stream, codes, q_out, N, K);
+    else
+      hipLaunchKernelGGL(unpack_probe_mfma<2>, dim3(blocks), dim3(64), 0, stream, codes, q_out, N, K);
+  } else {
+    return QGEMV_EINVAL;
+  }
+  return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}
+
+int stream_probe_blocks(size_t nbytes) {
+  const size_t n16 = nbytes / 16;
+  size_t blocks = (n16 + (size_t)kStreamThreads * kStreamUnroll - 1) / ((size_t)kStreamThreads * kStreamUnroll);
+  if (blocks < 1) blocks = 1;
+  if (blocks > (size_t)kStreamMaxBlocks) blocks = kStreamMaxBlocks;
+  return (int)blocks;
+}
+
+int launch_stream_probe(const uint8_t *buf, size_t nbytes, uint32_t *out, hipStream_t stream) {
+  const int blocks = stream_probe_blocks(nbytes);
+  hipLaunchKernelGGL(stream_probe_kernel, dim3(blocks), dim3(kStreamThreads), 0, stream,
+                     reinterpret_cast<const uint4 *>(buf), nbytes / 16, out);
+  return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}
+
+}  // namespace qgemv

@@ -1,0 +1,155 @@
+/*
+ * qgemv.h -- few-row quantized GEMV for AMD Instinct MI355X (gfx950).
+ *
+ *   y[M,N] = x[M,K] . dequant(W[N,K])^T,   1 <= M <= 16
+ *
+ * The verify step of speculative / multi-token-prediction decoding runs a
+ * weight matrix against a handful of activation rows ("metal : few-row MMA
+ * mat-mul and batched copies for speculative decoding", Overview: 2..16 src1
+ * rows; "MLX quantized_matmul small-M verify kernels", Facts: the M=2..12
+ * window between qmv and qmm).  This library reads and dequantizes every
+ * weight group once per call and reuses it for all M rows, instead of
+ * streaming the weights once per row.
+ *
+ * Weight format (affine group quantization, the "affine" mode of the MLX
+ * page's Facts on qmv_wide; 4 B of fp16 scale+bias per group, Facts: the
+ * group-size mechanism):
+ *   w[n,k] = s[n, k/gs] * q[n,k] + b[n, k/gs]
+ *   codes   uint8 [N][K*bits/8], row-major, no padding between rows.
+ *           bits = 4: two codes per byte, column k in bits 4*(k%2).. (low
+ *           nibble first).  bits = 2: four codes per byte, column k in bits
+ *           2*(k%4).. (lowest crumb first).
+ *   scales  IEEE fp16 bit patterns [N][K/gs], row-major.
+ *   biases  IEEE fp16 bit patterns [N][K/gs], row-major.
+ * Activations x: bfloat16 bit patterns [M][K], row-major (weights are stored
+ * [out,in], so the product is x @ W^T; MLX page, Facts: (M,5120)@(17408,5120)^T).
+ * Output y: fp32 [M][N], row-major, overwritten (no accumulate).
+ *
+ * Conventions for every entry point:
+ *   - All buffer pointers are DEVICE pointers on the current HIP device.  The
+ *     caller owns every buffer; the library allocates no device memory,
+ *     keeps no mutable state between calls and never synchronizes the host.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *     Work is enqueued asynchronously on it.
+ *   - Arguments are validated on the host before anything is launched; on
+ *     failure a negative status is returned and nothing is enqueued.
+ *   - A kernel launch error reported by the HIP runtime returns QGEMV_EHIP.
+ *   - Errors inside a running kernel cannot happen for validated arguments
+ *     (all accesses are bounded by M, N, K).
+ *   - Calls are reentrant and may run concurrently on different streams.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define QGEMV_OK 0
+#define QGEMV_EINVAL (-1)       /* bad shape / bits / group size / null pointer   */
+#define QGEMV_EUNSUPPORTED (-2) /* valid format, but the requested path cannot run it */
+#define QGEMV_EALIGN (-3)       /* a buffer pointer is not 16-byte aligned            */
+#define QGEMV_EHIP (-4)         /* the HIP runtime rejected a launch                  */
+
+/* Kernel paths. */
+#define QGEMV_PATH_AUTO 0 /* let qgemv_select choose                                 */
+#define QGEMV_PATH_DOT 1  /* multi-row dot path: one wave per row tile, lanes split K */
+#define QGEMV_PATH_MFMA 2 /* split-K bf16 MFMA path: waves split K, LDS reduction    */
+
+/* Limits checked by validation. */
+#define QGEMV_MAX_M 16
+#define QGEMV_MAX_K 131072
+#define QGEMV_MAX_N 4194304
+
+/*
+ * qgemv_small -- y = x . dequant(W)^T for 1 <= M <= 16, path chosen by
+ * qgemv_select.
+ *
+ * Requirements (else QGEMV_EINVAL / QGEMV_EALIGN):
+ *   bits in {2, 4}; group_size in {32, 64, 128}; 1 <= M <= 16;
+ *   1 <= N <= QGEMV_MAX_N; 64 <= K <= QGEMV_MAX_K; K % 64 == 0;
+ *   K % group_size == 0; codes, scales, biases, x, y non-NULL and each
+ *   16-byte aligned (every device allocation is).
+ * Numerics: products of bf16 activations with exact integer codes are
+ * accumulated in fp32 per group; the per-group scale is applied once to the
+ * group's partial dot product and the bias once to the group's activation sum
+ * (scale hoisted out of the inner loop, MLX page, Facts: the qmv_wide tuning
+ * bullet).  Result within 1e-3 * sum_k |x_k w_k| + 1e-6 of the exact value.
+ * Within one path, row m of an M-row call equals (bitwise) the M=1 call on
+ * x[m]: per-row accumulation order does not depend on M and no atomics are
+ * used, so results are deterministic.
+ */
+int qgemv_small(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
+                const uint16_t *x, float *y, int M, int N, int K, int bits, int group_size,
+                void *stream);
+
+/*
+ * qgemv_select -- the path qgemv_small takes for this shape: QGEMV_PATH_DOT or
+ * QGEMV_PATH_MFMA, or a negative status if the shape is invalid.  The choice
+ * comes from a crossover table measured on MI355X (which rows of a shape
+ * family favour the MFMA path), in the spirit of the per-type start rows of
+ * the few-row MMA PR (Overview) and MLX's per-shape qmv batch limit (MLX page,
+ * Facts: get_qmv_batch_limit), but calibrated on CDNA4.  Pure host function;
+ * touches no device.
+ */
+int qgemv_select(int M, int N, int K, int bits, int group_size);
+
+/*
+ * qgemv_run_path -- qgemv_small with an explicit path (QGEMV_PATH_AUTO,
+ * QGEMV_PATH_DOT or QGEMV_PATH_MFMA), for forced-path sweeps and tests (the
+ * pages' A/B knobs: the specgate-metal README's GGML_METAL_NO_MV_EXT /
+ * GGML_METAL_MM_MIN; MLX page, Facts: forced qmv vs qmm sweeps).
+ * Returns QGEMV_EUNSUPPORTED if the path cannot run the shape (the MFMA path
+ * needs K to be a multiple of 4*group_size and of 128 (4-bit) / 256 (2-bit),
+ * and group_size >= 64 for 2-bit codes).  Other arguments as qgemv_small.
+ */
+int qgemv_run_path(int path, const uint8_t *codes, const uint16_t *scales,
+                   const uint16_t *biases, const uint16_t *x, float *y, int M, int N, int K,
+                   int bits, int group_size, void *stream);
+
+/*
+ * qgemv_path_supported -- 1 if `path` can run this shape, 0 if not, negative
+ * status if the shape itself is invalid.  Host only.
+ */
+int qgemv_path_supported(int path, int M, int N, int K, int bits, int group_size);
+
+/*
+ * qgemv_unpack_probe -- writes the integer codes exactly as a path's kernels
+ * decode them: q_out[n][k] (uint8, [N][K], row-major) for every n < N, k < K.
+ * The kernels turn codes into bf16 values 128+q in registers; this probe runs
+ * the same device routines (same loads, lane exchanges and bit operations)
+ * and writes back q, so the decoded codes can be compared bit-exactly with
+ * the format's definition.  path: QGEMV_PATH_DOT or QGEMV_PATH_MFMA (the two
+ * paths pair codes differently).  Requirements as qgemv_run_path for that
+ * path (group_size only selects the MFMA layout, pass the one you will use);
+ * q_out non-NULL.
+ */
+int qgemv_unpack_probe(int path, const uint8_t *codes, uint8_t *q_out, int N, int K, int bits,
+                       int group_size, void *stream);
+
+/*
+ * qgemv_stream_probe -- read-only streaming kernel over `nbytes` bytes of
+ * `buf` (16-byte aligned, nbytes a multiple of 16): every byte is loaded once
+ * with 128-bit loads, folded with XOR, and one uint32 per workgroup is
+ * written to out[0 .. qgemv_stream_probe_blocks(nbytes)-1].  Its duration is
+ * the bandwidth ceiling a pure read of that many bytes reaches, measured the
+ * same way as the GEMV kernels.
+ */
+int qgemv_stream_probe(const uint8_t *buf, size_t nbytes, uint32_t *out, void *stream);
+int qgemv_stream_probe_blocks(size_t nbytes);
+
+/* qgemv_strerror -- static description of a status code. */
+const char *qgemv_strerror(int status);
+
+/* qgemv_version -- library ABI version (major*10000 + minor*100 + patch). */
+int qgemv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

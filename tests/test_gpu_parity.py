@@ -1,0 +1,229 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Bars:
+* decoded integer codes: bit-exact (unpack probe of each path, and the
+  one-hot unit-scale product y == q exactly);
+* y: |y - y_ref| <= 1e-3 * sum_k |x_k w_k| + 1e-6 per element, no NaN;
+* within one path, row m of an M-row call is bitwise equal to the M=1 call on
+  x[m], and repeated calls are bitwise identical.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from few_row_quantized_amd import qgemv as q
+from few_row_quantized_amd import synth
+
+from gpu_util import DeviceProblem, sample_columns, say
+
+pytestmark = pytest.mark.gpu
+
+PATHS = ["dot", "mfma", "auto"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu(require_gpu):
+    import torch
+    torch.cuda.init()
+    yield
+
+
+def check_y(p, y, M, cols=None, label=""):
+    ref = oracle.qgemv_reference(p.codes, p.scales, p.biases, p.x, M, p.N, p.K, p.bits,
+                                 p.group_size, rows=cols)
+    absum = oracle.abs_product_sum(p.codes, p.scales, p.biases, p.x, M, p.N, p.K, p.bits,
+                                   p.group_size, rows=cols)
+    yy = y if cols is None else y[:, cols]
+    ok, worst, idx = oracle.check_close(yy, ref, absum)
+    assert ok, f"{label}: worst |dy|/tol = {worst:.3g} at {idx}"
+    return worst
+
+
+def supported(path, p, M=1):
+    return q.qgemv_path_supported(path, M, p.N, p.K, p.bits, p.group_size)
+
+
+# ---------------------------------------------------------------- codes: bit-exact
+
+UNPACK_SHAPES = [
+    (256, 512, 4, 64), (512, 40, 4, 32), (1024, 17, 4, 128),
+    (512, 40, 2, 64), (1024, 33, 2, 128), (512, 24, 2, 32),
+]
+
+
+@pytest.mark.parametrize("K,N,bits,gs", UNPACK_SHAPES)
+@pytest.mark.parametrize("path", ["dot", "mfma"])
+def test_unpack_probe_is_bit_exact(path, K, N, bits, gs):
+    import torch
+    p = synth.make_problem(synth.custom_shape(K, N, bits, gs, seed=K + N), m_max=1)
+    if not q.qgemv_path_supported(path, 1, N, K, bits, gs):
+        pytest.skip("path does not support this shape")
+    say(f"unpack probe {path} K={K} N={N} bits={bits} gs={gs}")
+    d = DeviceProblem(p)
+    out = torch.full((N, K), 0xEE, dtype=torch.uint8, device="cuda:0")
+    q.qgemv_unpack_probe(path, d.codes, out, N, K, bits, gs)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    want = oracle.unpack_codes(p.codes, K, bits)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+@pytest.mark.parametrize("path", ["dot", "mfma"])
+def test_unpack_probe_full_size(path, name):
+    import torch
+    s = synth.WORKLOADS[name]
+    if not q.qgemv_path_supported(path, 1, s.N, s.K, s.bits, s.group_size):
+        pytest.skip("path does not support this shape")
+    p = synth.make_problem(s, m_max=1)
+    say(f"unpack probe {path} {name}")
+    d = DeviceProblem(p)
+    out = torch.empty((s.N, s.K), dtype=torch.uint8, device="cuda:0")
+    q.qgemv_unpack_probe(path, d.codes, out, s.N, s.K, s.bits, s.group_size)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), oracle.unpack_codes(p.codes, s.K, s.bits))
+
+
+@pytest.mark.parametrize("bits,gs", [(4, 64), (4, 32), (4, 128), (2, 64), (2, 128), (2, 32)])
+@pytest.mark.parametrize("path", ["dot", "mfma"])
+def test_unit_scale_onehot_gives_codes_exactly(path, bits, gs):
+    K, N, M = 1024, 48, 16
+    p = synth.special_problem(K, N, bits, gs, M, "unit_scale_onehot")
+    if not supported(path, p, M):
+        pytest.skip("path does not support this shape")
+    say(f"onehot {path} bits={bits} gs={gs}")
+    y = DeviceProblem(p).run_host(M, path)
+    codes = oracle.unpack_codes(p.codes, K, bits)
+    for m in range(M):
+        k = synth.onehot_column(m, K)
+        assert np.array_equal(y[m], codes[:, k].astype(np.float32)), f"row {m}"
+
+
+# ---------------------------------------------------------------- small shapes, every element
+
+@pytest.mark.parametrize("path", PATHS)
+def test_tiny_workload_all_m(path):
+    s = synth.WORKLOADS["tiny_k256_n512_4b_g64"]
+    p = synth.make_problem(s)
+    d = DeviceProblem(p)
+    for M in s.m_values:
+        say(f"tiny {path} M={M}")
+        check_y(p, d.run_host(M, path), M, label=f"tiny {path} M={M}")
+
+
+RAGGED = [
+    # K, N, bits, gs : N not a multiple of the tile sizes, several K stages
+    (640, 40, 4, 32), (1024, 300, 4, 64), (2048, 97, 4, 128), (8192, 33, 4, 64),
+    (512, 72, 2, 32), (1280, 300, 2, 64), (2048, 129, 2, 128), (17408, 23, 2, 64),
+    (64, 16, 4, 32), (64, 5, 2, 64),
+]
+
+
+@pytest.mark.parametrize("K,N,bits,gs", RAGGED)
+@pytest.mark.parametrize("path", PATHS)
+def test_ragged_shapes_every_element(path, K, N, bits, gs):
+    p = synth.make_problem(synth.custom_shape(K, N, bits, gs, seed=3 * K + N, outliers=True), m_max=16)
+    if not supported(path, p):
+        pytest.skip("path does not support this shape")
+    d = DeviceProblem(p)
+    for M in (1, 2, 5, 8, 13, 16):
+        say(f"ragged {path} K={K} N={N} bits={bits} gs={gs} M={M}")
+        check_y(p, d.run_host(M, path), M, label=f"{path} K={K} N={N} M={M}")
+
+
+@pytest.mark.parametrize("path", ["dot", "mfma"])
+def test_zero_codes(path):
+    K, N, M = 2048, 64, 8
+    p = synth.special_problem(K, N, 4, 64, M, "zero_codes")
+    say(f"zero codes {path}")
+    check_y(p, DeviceProblem(p).run_host(M, path), M, label="zero codes")
+
+
+# ---------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("bits,gs", [(4, 64), (2, 64), (4, 128)])
+@pytest.mark.parametrize("path", ["dot", "mfma"])
+def test_row_of_m_row_call_equals_single_row_call_bitwise(path, bits, gs):
+    import torch
+    K, N = 2048, 200
+    p = synth.make_problem(synth.custom_shape(K, N, bits, gs, seed=77), m_max=16)
+    d = DeviceProblem(p)
+    say(f"row invariance {path} bits={bits} gs={gs}")
+    singles = []
+    for m in range(16):
+        xm = d.x[m:m + 1].clone()
+        y1 = torch.empty((1, N), dtype=torch.float32, device="cuda:0")
+        q.qgemv_run_path(path, d.codes, d.scales, d.biases, xm, y1, 1, N, K, bits, gs)
+        singles.append(y1)
+    torch.cuda.synchronize()
+    singles = torch.cat(singles).cpu().numpy()
+    for M in (2, 3, 4, 5, 8, 12, 16):
+        y = d.run_host(M, path)
+        assert np.array_equal(y, singles[:M]), f"M={M}"
+
+
+@pytest.mark.parametrize("path", ["dot", "mfma"])
+def test_repeated_calls_are_bitwise_identical(path):
+    s = synth.WORKLOADS["square_k4096_n4096_4b_g64"]
+    p = synth.make_problem(s)
+    d = DeviceProblem(p)
+    say(f"determinism {path}")
+    a = d.run_host(8, path)
+    b = d.run_host(8, path)
+    assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------- full sizes, sampled columns
+
+FULL_CASES = []
+for _name, _s in synth.WORKLOADS.items():
+    if _name.startswith("tiny"):
+        continue
+    ms = list(_s.m_values)
+    if len(ms) > 6:
+        ms = sorted(set([ms[0], ms[1], 4, 5, 8, ms[-1]]) & set(ms))
+    FULL_CASES.append((_name, tuple(ms)))
+
+
+@pytest.mark.parametrize("name,ms", FULL_CASES)
+def test_full_size_sampled_columns(name, ms):
+    s = synth.WORKLOADS[name]
+    p = synth.make_problem(s)
+    d = DeviceProblem(p)
+    cols = sample_columns(s.N, 96, seed=s.seed)
+    for path in PATHS:
+        if not supported(path, p):
+            continue
+        for M in ms:
+            say(f"full {name} {path} M={M}")
+            y = d.run_host(M, path)
+            assert np.all(np.isfinite(y)), "non-finite output"
+            check_y(p, y, M, cols=cols, label=f"{name} {path} M={M}")
+
+
+def test_auto_path_matches_select():
+    # the dispatcher's choice is what qgemv_small runs: compare bitwise
+    s = synth.WORKLOADS["square_k4096_n4096_4b_g64"]
+    p = synth.make_problem(s)
+    d = DeviceProblem(p)
+    for M in s.m_values:
+        chosen = q.qgemv_select(M, s.N, s.K, s.bits, s.group_size)
+        name = {q.PATH_DOT: "dot", q.PATH_MFMA: "mfma"}[chosen]
+        say(f"auto vs {name} M={M}")
+        assert np.array_equal(d.run_host(M, "auto"), d.run_host(M, name))
+
+
+# ---------------------------------------------------------------- stream probe
+
+def test_stream_probe_reads_every_byte():
+    import torch
+    nbytes = 9 * 1024 * 1024 + 4096
+    rng = np.random.default_rng(9)
+    host = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.uint8)).to("cuda:0")
+    nb = q.qgemv_stream_probe_blocks(nbytes)
+    out = torch.zeros(nb, dtype=torch.int32, device="cuda:0")
+    q.qgemv_stream_probe(buf, nbytes, out)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(host)

@@ -1,0 +1,137 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/qgemv.h declares, and rejects invalid arguments with
+the documented status before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from few_row_quantized_amd import qgemv as q
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qgemv.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(qgemv_[a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("qgemv_small", "qgemv_select", "qgemv_run_path", "qgemv_unpack_probe",
+                 "qgemv_stream_probe", "qgemv_strerror"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(q.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+# Fake, never-dereferenced addresses: every call below fails validation first.
+A = 1 << 20  # 16-byte aligned
+MIS = A + 4   # not 16-byte aligned
+
+
+@pytest.mark.parametrize("M,N,K,bits,gs,want", [
+    (0, 64, 256, 4, 64, q.EINVAL),        # M < 1
+    (17, 64, 256, 4, 64, q.EINVAL),       # M > 16
+    (1, 0, 256, 4, 64, q.EINVAL),         # N < 1
+    (1, 64, 0, 4, 64, q.EINVAL),          # K < 64
+    (1, 64, 96, 4, 32, q.EINVAL),         # K % 64 != 0
+    (1, 64, 192, 4, 128, q.EINVAL),       # K % gs != 0
+    (1, 64, 256, 3, 64, q.EINVAL),        # bits
+    (1, 64, 256, 8, 64, q.EINVAL),        # bits
+    (1, 64, 256, 4, 16, q.EINVAL),        # group size
+    (1, 64, 256, 4, 256, q.EINVAL),       # group size
+    (1, 64, 262144, 4, 64, q.EINVAL),     # K above the limit
+])
+def test_invalid_shapes_rejected(M, N, K, bits, gs, want):
+    L = q.lib()
+    assert L.qgemv_small(A, A, A, A, A, M, N, K, bits, gs, None) == want
+    assert L.qgemv_select(M, N, K, bits, gs) == want
+    for path in (q.PATH_AUTO, q.PATH_DOT, q.PATH_MFMA):
+        assert L.qgemv_run_path(path, A, A, A, A, A, M, N, K, bits, gs, None) == want
+
+
+@pytest.mark.parametrize("which", range(5))
+def test_null_pointers_rejected(which):
+    ptrs = [A] * 5
+    ptrs[which] = None
+    assert q.lib().qgemv_small(*ptrs, 4, 64, 256, 4, 64, None) == q.EINVAL
+
+
+@pytest.mark.parametrize("which", range(5))
+def test_misaligned_pointers_rejected(which):
+    ptrs = [A] * 5
+    ptrs[which] = MIS
+    assert q.lib().qgemv_small(*ptrs, 4, 64, 256, 4, 64, None) == q.EALIGN
+
+
+def test_unknown_path_rejected():
+    L = q.lib()
+    assert L.qgemv_run_path(3, A, A, A, A, A, 1, 64, 256, 4, 64, None) == q.EINVAL
+    assert L.qgemv_run_path(-1, A, A, A, A, A, 1, 64, 256, 4, 64, None) == q.EINVAL
+    assert L.qgemv_path_supported(7, 1, 64, 256, 4, 64) == q.EINVAL
+    assert L.qgemv_unpack_probe(q.PATH_AUTO, A, A, 64, 256, 4, 64, None) == q.EINVAL
+
+
+def test_mfma_path_shape_support():
+    sup = q.qgemv_path_supported
+    assert sup("mfma", 4, 4096, 4096, 4, 64)
+    assert sup("mfma", 4, 4096, 4096, 2, 64)
+    assert not sup("mfma", 4, 4096, 4096, 2, 32)   # 2-bit gs32: dot path only
+    assert not sup("mfma", 4, 4096, 192, 4, 32)     # K not a multiple of 128
+    assert not sup("mfma", 4, 4096, 640, 4, 128)    # K not a multiple of 4*gs
+    assert sup("dot", 4, 4096, 192, 4, 32)
+    # a forced path that cannot run the shape is refused before launch
+    assert q.lib().qgemv_run_path(q.PATH_MFMA, A, A, A, A, A, 4, 64, 192, 4, 32, None) == q.EUNSUPPORTED
+
+
+def test_select_returns_a_supported_path_everywhere():
+    for bits in (2, 4):
+        for gs in (32, 64, 128):
+            for K in (256, 640, 4096, 5120, 17408):
+                if K % gs:
+                    continue
+                for M in range(1, 17):
+                    p = q.qgemv_select(M, 4096, K, bits, gs)
+                    assert p in (q.PATH_DOT, q.PATH_MFMA)
+                    assert q.qgemv_path_supported(p, M, 4096, K, bits, gs)
+
+
+def test_stream_probe_validation():
+    L = q.lib()
+    assert L.qgemv_stream_probe(None, 1024, A, None) == q.EINVAL
+    assert L.qgemv_stream_probe(A, 1000, A, None) == q.EINVAL
+    assert L.qgemv_stream_probe(A, 0, A, None) == q.EINVAL
+    assert L.qgemv_stream_probe(MIS, 1024, A, None) == q.EALIGN
+    assert 1 <= q.qgemv_stream_probe_blocks(16) <= q.qgemv_stream_probe_blocks(1 << 30)
+
+
+def test_strerror_and_version():
+    for s in (q.OK, q.EINVAL, q.EUNSUPPORTED, q.EALIGN, q.EHIP, -99):
+        assert isinstance(q.qgemv_strerror(s), str) and q.qgemv_strerror(s)
+    assert q.qgemv_version() >= 100
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(q, "_lib", None)
+    monkeypatch.setattr(q, "LIB_PATH", "/nonexistent/libqgemv.so")
+    with pytest.raises(RuntimeError):
+        q.qgemv_version()
+
+
+def test_product_path_does_not_import_oracle():
+    import ast
+    pkg = os.path.dirname(q.__file__)
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            tree = ast.parse(open(os.path.join(pkg, fn)).read())
+            for node in ast.walk(tree):
+                if isinstance(node, (ast.Import, ast.ImportFrom)):
+                    mods = [a.name for a in node.names] if isinstance(node, ast.Import) else [node.module or ""]
+                    assert not any(m.split(".")[0] == "oracle" for m in mods), fn
