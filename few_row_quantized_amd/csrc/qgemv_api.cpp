@@ -39,9 +39,26 @@ bool path_supported(int path, int K, int bits, int group_size) {
   return false;
 }
 
+// Table lookup: the measured entry of the same format whose shape class is
+// nearest (N class weighs more than K class); formats absent from the table
+// take the nearest group size of the same bit width.
 int select_path(int M, int N, int K, int bits, int group_size) {
   if (!qgemv::mfma_supports(K, bits, group_size)) return QGEMV_PATH_DOT;
-  return M >= qgemv::mfma_start_row(N, K, bits, group_size) ? QGEMV_PATH_MFMA : QGEMV_PATH_DOT;
+  const int nc = qgemv::select_n_class(N), kc = qgemv::select_k_class(K);
+  const qgemv::SelectEntry *best = nullptr;
+  int best_d = 1 << 30;
+  for (const auto &e : qgemv::kSelectTable) {
+    if (e.bits != bits) continue;
+    const int dg = e.group_size == group_size ? 0 : (e.group_size > group_size ? e.group_size / group_size : group_size / e.group_size);
+    const int d = 100 * dg + 4 * (e.n_class > nc ? e.n_class - nc : nc - e.n_class) +
+                  (e.k_class > kc ? e.k_class - kc : kc - e.k_class);
+    if (d < best_d) {
+      best_d = d;
+      best = &e;
+    }
+  }
+  if (!best) return M >= 3 ? QGEMV_PATH_MFMA : QGEMV_PATH_DOT;
+  return ((best->mfma_mask >> (M - 1)) & 1u) ? QGEMV_PATH_MFMA : QGEMV_PATH_DOT;
 }
 
 }  // namespace

@@ -39,6 +39,13 @@ __device__ __forceinline__ uint32_t perm_b32(uint32_t hi_src, uint32_t lo_src, u
   return __builtin_amdgcn_perm(hi_src, lo_src, sel);
 }
 
+// 16-byte load of data read exactly once per call (the weight codes):
+// non-temporal, so the stream does not push the activations (reused by every
+// workgroup) out of the caches.
+__device__ __forceinline__ u32x4_t load_stream_u32x4(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+}
+
 // A value the compiler cannot see through, kept in a VGPR.  Used for the
 // OR operand of the unpack so that AND+OR fuse into one v_and_or_b32 (a VOP3
 // instruction on gfx9 takes at most one literal/SGPR operand).

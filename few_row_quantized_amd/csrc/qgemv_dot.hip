@@ -76,10 +76,15 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
     const int units = M * nc;
     const int npass = (nc + 63) >> 6;  // uniform
     if (c0 != 0) __syncthreads();      // previous stage fully consumed
+    // Units are visited in an order rotated per workgroup (by blockIdx/8:
+    // workgroups are dealt round-robin over the 8 XCDs) so that the CUs sharing
+    // an L2 do not all read the same activation lines at the same moment.
+    const int rot = (int)(((blockIdx.x >> 3) * 64u) % (unsigned)units);
+    auto unit_of = [&](int uu) { return uu + rot < units ? uu + rot : uu + rot - units; };
     uint4 xa[2][CW / 8];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int u = min((int)threadIdx.x + kDotThreads * j, units - 1);
+      const int u = unit_of(min((int)threadIdx.x + kDotThreads * j, units - 1));
       const int m = u / nc;
       const int cl = u - m * nc;
 #pragma unroll
@@ -97,7 +102,8 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const int n = min(row0 + r, N - 1);
-          cw[t][r] = *reinterpret_cast<const uint4 *>(codes + (size_t)n * RB + (size_t)(c0 + c) * 16);
+          const u32x4_t v = load_stream_u32x4(codes + (size_t)n * RB + (size_t)(c0 + c) * 16);
+          cw[t][r] = make_uint4(v[0], v[1], v[2], v[3]);
 #pragma unroll
           for (int s = 0; s < NSUB; ++s) {
             const int g = ((c0 + c) * CW + s * SUBW) / gs;
@@ -163,10 +169,11 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
     };
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int u = threadIdx.x + kDotThreads * j;
-      if (u < units) stage_unit(u, xa[j]);
+      const int uu = threadIdx.x + kDotThreads * j;
+      if (uu < units) stage_unit(unit_of(uu), xa[j]);
     }
-    for (int u = threadIdx.x + 2 * kDotThreads; u < units; u += kDotThreads) {
+    for (int uu = threadIdx.x + 2 * kDotThreads; uu < units; uu += kDotThreads) {
+      const int u = unit_of(uu);
       const int m = u / nc;
       const int cl = u - m * nc;
       uint4 xv[CW / 8];
