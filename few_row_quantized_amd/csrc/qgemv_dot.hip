@@ -114,6 +114,9 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
       }
     }
 
+    // all loads of the stage stay ahead of the staging and compute
+    __builtin_amdgcn_sched_barrier(0);
+
     // 3. stage x: paired layout + per-sub-chunk sums (units beyond the first
     //    two per thread are loaded here, which only happens for large M)
     auto stage_unit = [&](int u, const uint4 (&xv)[CW / 8]) {

@@ -36,18 +36,12 @@ namespace qgemv {
 
 namespace {
 
-// activation units (16 bytes) staged per thread by the LDS variant
-constexpr int kMfmaLdsUnitsPerThread = 8;
-// The LDS-staged variant measured slower than direct fragment loads on the
-// square 4096x4096 shapes (its staging barrier serializes the waves); it is
-// kept for shapes where that may change but not selected.
-constexpr bool kMfmaUseLdsStaging = false;
 
-template <int BITS, int GS, int NT, int MAXT, int SPI>
+template <int BITS, int GS, int NT, int MAXT, int SPI, bool PERSIST>
 __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *__restrict__ y,
-    int M, int N, int K) {
+    int M, int N, int K, int ngroups) {
   constexpr int CW = 128 / BITS;       // weights per 16-byte chunk
   constexpr int SCW = 4 * CW;          // weights per 64-byte super-chunk
   constexpr int BLKW = 4 * GS;         // weights per bias block (4 groups)
@@ -70,14 +64,27 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   const int waves = blockDim.x >> 6;
   const int col = lane & 15;
   const int kb = lane >> 4;
-  const int n_base = blockIdx.x * 16 * NT;
   const int NBLK = K / BLKW;
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t offset_pair = opaque_u32(kOffsetPair);
+
+  // indicator operands: A row r = col is all ones iff r/4 == j
+  u32x4_t ind[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t v = ((col >> 2) == j) ? 0x3F803F80u : 0u;
+    ind[j] = u32x4_t{v, v, v, v};
+  }
+
+  // One tile group (16*NT output columns over all of K) per call of `group`.
+  auto group = [&](const int tg) {
+  const int n_base = tg * 16 * NT;
   // K-slice of this wave.  The slice order is rotated per workgroup (by
   // blockIdx/8: workgroups are dealt round-robin over the 8 XCDs) so that the
   // CUs sharing an L2 do not all read the same activation lines at the same
   // moment.  Partials are reduced in slice order, so results do not depend
   // on the rotation.
-  const int slice = (wave + (int)(blockIdx.x >> 3)) % waves;
+  const int slice = (wave + (tg >> 3)) % waves;
   const int b_begin = (slice * NBLK) / waves;
   const int b_end = ((slice + 1) * NBLK) / waves;
   const size_t RB = (size_t)K * BITS / 8;
@@ -96,20 +103,10 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     srow[t] = scales + (size_t)n * G;
     brow[t] = biases + (size_t)n * G;
   }
-  const uint32_t offset_pair = opaque_u32(kOffsetPair);
-
-  // indicator operands: A row r = col is all ones iff r/4 == j
-  u32x4_t ind[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t v = ((col >> 2) == j) ? 0x3F803F80u : 0u;
-    ind[j] = u32x4_t{v, v, v, v};
-  }
 
   f32x4_t acc[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NT; ++t) acc[t] = zero4;
 
   for (int blk0 = b_begin; blk0 < b_end; blk0 += BPB) {
     const int nb = min(BPB, b_end - blk0);  // blocks in this batch (uniform)
@@ -139,6 +136,10 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
         }
       }
     }
+
+    // keep the whole batch of loads ahead of the compute: without this the
+    // scheduler may sink later loads below the first waits and serialize them
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- compute, super-chunk by super-chunk in load order
     f32x4_t xsacc = zero4;
@@ -230,236 +231,19 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     const int n = n_base + 16 * t + (l & 15);
     if (m < M && n < N) y[(size_t)m * N + n] = s;
   }
-}
-
-// Same path with the activations staged once per workgroup in LDS.
-//
-// Every workgroup needs all M*K activations (its 16*NT output columns span
-// the whole of K), so with one tile per CU the activation reads through L2
-// grow with M and overtake the weight stream at M ~ 8.  Staging them once per
-// workgroup with full-line 16-byte loads (issued before the code loads, so
-// the staging never waits for HBM) halves the L2 requests of the per-lane
-// fragment loads and lets lanes of rows m >= M skip memory entirely.  The
-// per-group activation sums are formed during the staging (8-element partial
-// sums reduced over the gs/8 lanes that hold one group), which replaces the
-// indicator MFMAs of the direct kernel.
-//
-// LDS: x rows at a pitch of 2K+16 bytes (the 16-byte pad puts the 16 rows of
-// an A fragment on distinct bank groups), the group sums [M][K/gs] fp32 and
-// the split-K reduction buffer.
-template <int BITS, int GS, int NT, int MAXT, int SPI>
-__global__ __launch_bounds__(MAXT) void qgemv_mfma_lds_kernel(
-    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
-    const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *__restrict__ y,
-    int M, int N, int K) {
-  constexpr int CW = 128 / BITS;
-  constexpr int SCW = 4 * CW;
-  constexpr int BLKW = 4 * GS;
-  constexpr int BSC = BLKW / SCW;
-  constexpr int STEPS_SC = SCW / 32;
-  constexpr int STEPS_G = GS / 32;
-  constexpr int UNR = SPI > BSC ? SPI : BSC;
-  constexpr int BPB = UNR / BSC;
-  constexpr int UPG = GS / 8;          // 16-byte activation units per group
-  constexpr int XUNITS = kMfmaLdsUnitsPerThread;
-  static_assert(BSC >= 1 && BLKW % SCW == 0 && UNR % BSC == 0, "block layout");
-
-  extern __shared__ uint4 lds_u4[];
-  uint8_t *lds = reinterpret_cast<uint8_t *>(lds_u4);
-  const int XP = 2 * K + 16;  // bytes per staged row
-  const int G = K / GS;
-  float *xsl = reinterpret_cast<float *>(lds + (size_t)M * XP);  // [M][G]
-  float *red = xsl + (size_t)M * G;                              // [waves][NT][4][64]
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int waves = blockDim.x >> 6;
-  const int col = lane & 15;
-  const int kb = lane >> 4;
-  const int n_base = blockIdx.x * 16 * NT;
-  const int NBLK = K / BLKW;
-  const int slice = (wave + (int)(blockIdx.x >> 3)) % waves;  // rotated as in the direct kernel
-  const int b_begin = (slice * NBLK) / waves;
-  const int b_end = ((slice + 1) * NBLK) / waves;
-  const size_t RB = (size_t)K * BITS / 8;
-
-  // ---- 1. activation staging loads: 16-byte units, row after row
-  const int upr = K / 8;
-  const int units = M * upr;
-  uint4 xu[XUNITS];
-#pragma unroll
-  for (int i = 0; i < XUNITS; ++i) {
-    if (i * (int)blockDim.x < units) {  // uniform
-      const int u = min((int)threadIdx.x + i * (int)blockDim.x, units - 1);
-      xu[i] = reinterpret_cast<const uint4 *>(x)[u];  // row-major [M][K]: unit u = row u/upr
-    }
-  }
-
-  // ---- 2. codes and metadata of the first batch
-  const uint8_t *crow[NT];
-  const uint16_t *srow[NT];
-  const uint16_t *brow[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int n = min(n_base + 16 * t + col, N - 1);
-    crow[t] = codes + (size_t)n * RB + kb * 16;
-    srow[t] = scales + (size_t)n * G;
-    brow[t] = biases + (size_t)n * G;
-  }
-  u32x4_t cv[UNR][NT];
-  uint2 s4[BPB][NT], b4[BPB][NT];
-  auto issue_batch = [&](int blk0, int nb) {
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      if (u / BSC < nb) {
-        const int gsc = blk0 * BSC + u;
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-          cv[u][t] = load_stream_u32x4(crow[t] + (size_t)gsc * 64);
-        if (u % BSC == 0) {
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            s4[u / BSC][t] = *reinterpret_cast<const uint2 *>(srow[t] + (size_t)(gsc / BSC) * 4);
-            b4[u / BSC][t] = *reinterpret_cast<const uint2 *>(brow[t] + (size_t)(gsc / BSC) * 4);
-          }
-        }
-      }
-    }
   };
-  if (b_begin < b_end) issue_batch(b_begin, min(BPB, b_end - b_begin));
 
-  // ---- 3. write the staged activations and their group sums to LDS
-#pragma unroll
-  for (int i = 0; i < XUNITS; ++i) {
-    if (i * (int)blockDim.x < units) {  // uniform
-      const int u = (int)threadIdx.x + i * (int)blockDim.x;
-      const int m = u / upr;
-      const int jj = u - m * upr;
-      const uint4 v = xu[i];
-      float part = dot2_bf16(v.x, 0x3F803F80u, 0.f);
-      part = dot2_bf16(v.y, 0x3F803F80u, part);
-      part = dot2_bf16(v.z, 0x3F803F80u, part);
-      part = dot2_bf16(v.w, 0x3F803F80u, part);
-      // the UPG lanes of one group are consecutive and aligned
-#pragma unroll
-      for (int off = 1; off < UPG; off <<= 1) part += __shfl_xor(part, off, 64);
-      if (u < units) {
-        *reinterpret_cast<uint4 *>(lds + (size_t)m * XP + (size_t)jj * 16) = v;
-        if (jj % UPG == 0) xsl[m * G + jj / UPG] = part;
-      }
+  if constexpr (PERSIST) {
+    // Persistent workgroups: the grid holds as many workgroups as the device
+    // runs at once, and each walks tile groups tg, tg + gridDim.x, ... so that
+    // no partial last round of workgroups is left for a few CUs.
+    for (int tg = blockIdx.x; tg < ngroups; tg += gridDim.x) {
+      if (tg != (int)blockIdx.x) __syncthreads();  // reduction buffer drained
+      group(tg);
     }
-  }
-  __syncthreads();
-
-  // ---- 4. split-K MFMA over this wave's blocks
-  const int mrow = col < M ? col : M - 1;  // rows >= M repeat a real row; never stored
-  const uint8_t *xrow = lds + (size_t)mrow * XP + kb * (CW / 4) * 2;
-  const float *xsrow = xsl + (size_t)mrow * G;
-  const uint32_t offset_pair = opaque_u32(kOffsetPair);
-  f32x4_t acc[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-
-  for (int blk0 = b_begin; blk0 < b_end; blk0 += BPB) {
-    const int nb = min(BPB, b_end - blk0);
-    if (blk0 != b_begin) issue_batch(blk0, nb);
-    f32x4_t accg[NT];
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      if (u / BSC >= nb) break;
-      const int gsc = blk0 * BSC + u;
-      const int scb = u % BSC;
-      // A fragments of this super-chunk from LDS
-      u32x4_t xa4[BITS == 4 ? 4 : 8];
-#pragma unroll
-      for (int i = 0; i < (BITS == 4 ? 4 : 8); ++i) {
-        const int c = BITS == 4 ? i : (i >> 1);
-        const int k0 = gsc * SCW + c * CW + (BITS == 4 ? 0 : 8 * (i & 1));
-        xa4[i] = *reinterpret_cast<const u32x4_t *>(xrow + (size_t)k0 * 2);
-      }
-      uint32_t cur[NT][4];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        cur[t][0] = cv[u][t][0];
-        cur[t][1] = cv[u][t][1];
-        cur[t][2] = cv[u][t][2];
-        cur[t][3] = cv[u][t][3];
-        transpose_rows4(cur[t]);
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-#pragma unroll
-        for (int h = 0; h < (BITS == 4 ? 1 : 2); ++h) {
-          const int st = scb * STEPS_SC + (BITS == 4 ? c : 2 * c + h);
-          const int j = st / STEPS_G;
-          const bool gfirst = (st % STEPS_G) == 0;
-          const bool glast = (st % STEPS_G) == STEPS_G - 1;
-          u32x4_t xa;
-          if constexpr (BITS == 4) {
-            xa = xa4[c];
-          } else {
-            const uint32_t X[8] = {xa4[2 * c][0],     xa4[2 * c][1],     xa4[2 * c][2],
-                                   xa4[2 * c][3],     xa4[2 * c + 1][0], xa4[2 * c + 1][1],
-                                   xa4[2 * c + 1][2], xa4[2 * c + 1][3]};
-            xa = u32x4_t{xpair_stride8(X, 4 * h + 0), xpair_stride8(X, 4 * h + 1),
-                         xpair_stride8(X, 4 * h + 2), xpair_stride8(X, 4 * h + 3)};
-          }
-          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xa);
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            u32x4_t bw;
-            if constexpr (BITS == 4) {
-              bw = unpack4_natural_quad(cur[t][c], offset_pair);
-            } else {
-              bw = unpack2_split_quad(cur[t][c], h, offset_pair);
-            }
-            accg[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                a, __builtin_bit_cast(bf16x8_t, bw), gfirst ? zero4 : accg[t], 0, 0, 0);
-          }
-          if (glast) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-              const uint32_t sw = (j < 2) ? s4[u / BSC][t].x : s4[u / BSC][t].y;
-              const float s = half_bits_to_float((j & 1) ? (sw >> 16) : (sw & 0xFFFFu));
-#pragma unroll
-              for (int i = 0; i < 4; ++i) acc[t][i] = fmaf(s, accg[t][i], acc[t][i]);
-            }
-          }
-        }
-      }
-      if (scb == BSC - 1) {
-        // bias with the 128 offset: acc += xsum[m][g0+kb] * (b - 128 s)[n][g0+kb]
-        const int blk = gsc / BSC;
-        const float xsv = xsrow[blk * 4 + kb];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const uint32_t sw = (kb < 2) ? s4[u / BSC][t].x : s4[u / BSC][t].y;
-          const uint32_t bw = (kb < 2) ? b4[u / BSC][t].x : b4[u / BSC][t].y;
-          const float s = half_bits_to_float((kb & 1) ? (sw >> 16) : (sw & 0xFFFFu));
-          const float b = half_bits_to_float((kb & 1) ? (bw >> 16) : (bw & 0xFFFFu));
-          const float bo = fmaf(-128.f, s, b);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsv, bo, acc[t], 0, 0, 0);
-        }
-      }
-    }
-  }
-
-  // ---- 5. split-K reduction over the waves, fixed order
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[((slice * NT + t) * 4 + i) * 64 + lane] = acc[t][i];
-  __syncthreads();
-  for (int o = threadIdx.x; o < NT * 256; o += blockDim.x) {
-    const int t = o >> 8;
-    const int i = (o >> 6) & 3;
-    const int l = o & 63;
-    float sum = 0.f;
-    for (int w = 0; w < waves; ++w) sum += red[((w * NT + t) * 4 + i) * 64 + l];
-    const int m = 4 * (l >> 4) + i;
-    const int n = n_base + 16 * t + (l & 15);
-    if (m < M && n < N) y[(size_t)m * N + n] = sum;
+  } else {
+    // one tile group per workgroup (all groups resident at once)
+    group(blockIdx.x);
   }
 }
 
@@ -484,45 +268,61 @@ int pick_waves(int nblk, int max_waves) {
 // register budget of its thread cap without spills.
 template <int BITS, int GS, int NT>
 struct MfmaShape {
-  static constexpr int SPI = (BITS == 4 && GS == 128) ? 4 : 2;
+  static constexpr int SPI = (BITS == 4 && GS == 128 && NT == 1) ? 4 : 2;
   static constexpr int MAXT = (BITS == 4 && NT == 1 && GS <= 64) ? 1024 : 512;
 };
 
-size_t mfma_lds_bytes(int M, int K, int group_size, int waves, int nt) {
-  return (size_t)M * (2 * (size_t)K + 16) + (size_t)M * (K / group_size) * 4 +
-         (size_t)waves * nt * 4 * 64 * 4;
+// Device CU count (per device id, cached).
+int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 template <int BITS, int GS, int NT>
 int launch_mfma_t(const QgemvArgs &a, hipStream_t stream) {
   constexpr int MAXT = MfmaShape<BITS, GS, NT>::MAXT;
   constexpr int SPI = MfmaShape<BITS, GS, NT>::SPI;
+  const auto kern = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, true>;
+  const auto kern1 = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, false>;
   const int nblk = a.K / (4 * GS);
   const int waves = pick_waves(nblk, MAXT / 64);
   const int tiles = (a.N + 15) / 16;
-  const int blocks = (tiles + NT - 1) / NT;
-  const size_t lds = mfma_lds_bytes(a.M, a.K, GS, waves, NT);
-  const bool staged = kMfmaUseLdsStaging && lds <= kLdsMax &&
-                      (size_t)a.M * a.K / 8 <= (size_t)kMfmaLdsUnitsPerThread * 64 * waves;
-  if (staged) {
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&qgemv_mfma_lds_kernel<BITS, GS, NT, MAXT, SPI>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
-    if (attr != hipSuccess) return QGEMV_EHIP;
-    hipLaunchKernelGGL((qgemv_mfma_lds_kernel<BITS, GS, NT, MAXT, SPI>), dim3(blocks),
-                       dim3(64 * waves), lds, stream, a.codes, a.scales, a.biases, a.x, a.y, a.M,
-                       a.N, a.K);
-  } else {
-    hipLaunchKernelGGL((qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI>), dim3(blocks), dim3(64 * waves),
-                       0, stream, a.codes, a.scales, a.biases, a.x, a.y, a.M, a.N, a.K);
+  const int groups = (tiles + NT - 1) / NT;
+  // workgroups resident at once for this block size (cached per wave count)
+  static int occ_cache[MAXT / 64 + 1] = {0};
+  int occ = occ_cache[waves];
+  if (occ == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void *>(kern),
+                                                     64 * waves, 0) != hipSuccess ||
+        occ <= 0)
+      occ = 1;
+    occ_cache[waves] = occ;
   }
+  const int slots = occ * cu_count();
+  if (groups <= slots)
+    hipLaunchKernelGGL(kern1, dim3(groups), dim3(64 * waves), 0, stream, a.codes, a.scales,
+                       a.biases, a.x, a.y, a.M, a.N, a.K, groups);
+  else
+    hipLaunchKernelGGL(kern, dim3(slots), dim3(64 * waves), 0, stream, a.codes, a.scales, a.biases,
+                       a.x, a.y, a.M, a.N, a.K, groups);
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
 }
 
 template <int BITS, int GS>
 int launch_mfma_gs(const QgemvArgs &a, hipStream_t stream) {
+  // more output columns per workgroup on wide matrices: every workgroup reads
+  // all M*K activations, so wider groups cut that traffic per weight byte
   const int tiles = (a.N + 15) / 16;
-  if (tiles >= 512) return launch_mfma_t<BITS, GS, 2>(a, stream);
+  const int cus = cu_count();
+  if (tiles >= 2 * cus) return launch_mfma_t<BITS, GS, 2>(a, stream);
   return launch_mfma_t<BITS, GS, 1>(a, stream);
 }
 
