@@ -162,7 +162,7 @@ def main():
     alg = accounting.algorithmic_bytes(Mdom, s.N, s.K, s.bits, s.group_size)
     achieved = alg / per_m[Mdom] / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(s.name, Mdom),
                 "kernel": f"qgemv_{paths[Mdom]}_kernel M={Mdom}",
                 "bytes_per_launch": alg, "avg_launch_us": round(per_m[Mdom] * 1e6, 4)}
 
@@ -189,6 +189,25 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def measured_traffic(workload, M):
+    """HBM bytes per launch (read + write) from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE passes for this workload, scaled by the counters'
+    reading of kernels of known size.  None when no such profile exists or
+    when the kernel sources changed since it was taken."""
+    import glob
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    srcs = sorted(glob.glob(os.path.join(ROOT, "few_row_quantized_amd", "csrc", "*")))
+    sha = hashlib.sha256(b"".join(open(f, "rb").read() for f in srcs)).hexdigest()
+    t = rec.get("per_m", {}).get(str(M))
+    if rec.get("csrc_sha256") != sha or t is None:
+        return None
+    return t["read_bytes"] + t["write_bytes"]
 
 
 def measure_ceiling(W, copies, chain, capture, time_graph):

@@ -386,3 +386,16 @@ def test_bf16_rounding_is_nearest_even():
     v = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 1.0 + 2 ** -8 + 2 ** -20], np.float32)
     got = synth.f32_to_bf16_bits(v).tolist()
     assert got == [0x3F80, 0x3F80, 0x3F82, 0xC020, 0x3F81]
+
+
+@pytest.mark.parametrize("bits,gs,K,N,M", [(4, 64, 128, 6, 2), (2, 32, 128, 5, 3)])
+def test_abs_product_sum_matches_exact_rational(bits, gs, K, N, M):
+    p = synth.make_problem(synth.custom_shape(K, N, bits, gs, seed=7 + K + N), m_max=M)
+    got = oracle.abs_product_sum(p.codes, p.scales, p.biases, p.x, M, N, K, bits, gs)
+    for n in range(N):
+        q = bitstream_codes(p.codes[n], K, bits)
+        w = [frac_fp16(int(p.scales[n, k // gs])) * q[k] + frac_fp16(int(p.biases[n, k // gs]))
+             for k in range(K)]
+        for m in range(M):
+            want = sum(abs(frac_bf16(int(p.x[m, k])) * w[k]) for k in range(K))
+            assert abs(Fraction(got[m, n]) - want) <= Fraction(K) * Fraction(2) ** -52 * want
