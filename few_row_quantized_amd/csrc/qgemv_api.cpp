@@ -108,7 +108,7 @@ int qgemv_unpack_probe(int path, const uint8_t *codes, uint8_t *q_out, int N, in
   if (!codes || !q_out) return QGEMV_EINVAL;
   if (!aligned(codes, 16)) return QGEMV_EALIGN;
   if (!path_supported(path, K, bits, group_size)) return QGEMV_EUNSUPPORTED;
-  return qgemv::launch_unpack_probe(path, codes, q_out, N, K, bits,
+  return qgemv::launch_unpack_probe(path, codes, q_out, N, K, bits, group_size,
                                     reinterpret_cast<hipStream_t>(stream));
 }
 

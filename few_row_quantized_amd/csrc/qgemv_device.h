@@ -98,6 +98,16 @@ __device__ __forceinline__ void unpack2_split_pairs(uint32_t w, uint32_t (&o)[8]
   for (int j = 0; j < 8; ++j) o[j] = ((w >> (2 * j)) & 0x00030003u) | off;
 }
 
+// 4-bit split pairing as the 4-dword MFMA operand (pairs (p, p+4)).
+__device__ __forceinline__ u32x4_t unpack4_split_quad(uint32_t w, uint32_t off) {
+  u32x4_t o;
+  o[0] = (w & 0x000F000Fu) | off;
+  o[1] = ((w >> 4) & 0x000F000Fu) | off;
+  o[2] = ((w >> 8) & 0x000F000Fu) | off;
+  o[3] = ((w >> 12) & 0x000F000Fu) | off;
+  return o;
+}
+
 // Half h (h = 0, 1) of the 2-bit pairing as an MFMA operand: pairs 4h..4h+3.
 __device__ __forceinline__ u32x4_t unpack2_split_quad(uint32_t w, int h, uint32_t off) {
   u32x4_t o;
@@ -147,6 +157,50 @@ __device__ __forceinline__ void transpose_rows4(uint32_t (&r)[4]) {
     r[2] = b[0];
     r[3] = b[1];
   }
+}
+
+// Partial transpose for the MFMA path.  On entry row g (lanes 16g..16g+15)
+// holds the 4 dwords of chunk g of a 64-byte super-chunk in r[0..3].  LVL
+// selects how far the dwords are exchanged so that each register holds codes
+// of one quantization group:
+//   LVL 0 (no exchange):  r[i] in row g = dword i of chunk g
+//   LVL 1 (permlane32):   r[i] in row g = dword (i&1) + 2(g>>1) of chunk (g&1) + 2(i>>1)
+//   LVL 2 (full 4x4):     r[i] in row g = dword g of chunk i
+template <int LVL>
+__device__ __forceinline__ void transpose_rows_lvl(uint32_t (&r)[4]) {
+  if constexpr (LVL == 1) {
+    auto a = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);
+    r[0] = a[0];
+    r[2] = a[1];
+    auto b = __builtin_amdgcn_permlane32_swap(r[1], r[3], false, false);
+    r[1] = b[0];
+    r[3] = b[1];
+  } else if constexpr (LVL == 2) {
+    transpose_rows4(r);
+  }
+}
+template <int LVL>
+__device__ __forceinline__ int lvl_chunk(int i, int g) {
+  return LVL == 0 ? g : (LVL == 1 ? (g & 1) + 2 * (i >> 1) : i);
+}
+template <int LVL>
+__device__ __forceinline__ int lvl_dword(int i, int g) {
+  return LVL == 0 ? i : (LVL == 1 ? (i & 1) + 2 * (g >> 1) : g);
+}
+
+// P[j] is a per-lane partial for value j (j = 0..3) that must be summed over
+// the four 16-lane rows.  Returns, in row j, the total of value j (lane
+// positions within a row are kept).  Two swap stages, three adds.
+__device__ __forceinline__ float rows_transpose_reduce4(const float (&P)[4]) {
+  auto a = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, P[0]),
+                                            __builtin_bit_cast(uint32_t, P[2]), false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, P[1]),
+                                            __builtin_bit_cast(uint32_t, P[3]), false, false);
+  const float u02 = __builtin_bit_cast(float, (uint32_t)a[0]) + __builtin_bit_cast(float, (uint32_t)a[1]);
+  const float u13 = __builtin_bit_cast(float, (uint32_t)b[0]) + __builtin_bit_cast(float, (uint32_t)b[1]);
+  auto c = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, u02),
+                                            __builtin_bit_cast(uint32_t, u13), false, false);
+  return __builtin_bit_cast(float, (uint32_t)c[0]) + __builtin_bit_cast(float, (uint32_t)c[1]);
 }
 
 __device__ __forceinline__ float dpp_row_sum16(float v) {

@@ -32,7 +32,7 @@ bool mfma_supports(int K, int bits, int group_size);
 
 // Probes.
 int launch_unpack_probe(int path, const uint8_t *codes, uint8_t *q_out, int N, int K, int bits,
-                        hipStream_t stream);
+                        int group_size, hipStream_t stream);
 int launch_stream_probe(const uint8_t *buf, size_t nbytes, uint32_t *out, hipStream_t stream);
 int stream_probe_blocks(size_t nbytes);
 

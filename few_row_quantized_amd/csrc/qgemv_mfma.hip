@@ -42,20 +42,25 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *__restrict__ y,
     int M, int N, int K, int ngroups) {
-  constexpr int CW = 128 / BITS;       // weights per 16-byte chunk
-  constexpr int SCW = 4 * CW;          // weights per 64-byte super-chunk
-  constexpr int BLKW = 4 * GS;         // weights per bias block (4 groups)
+  constexpr int CW = 128 / BITS;       // codes per 16-byte chunk
+  constexpr int SCW = 4 * CW;          // codes per 64-byte super-chunk
+  constexpr int DW = CW / 4;           // codes per dword
+  constexpr int HS = BITS == 4 ? 1 : 2;  // MFMA steps per code dword
+  constexpr int BLKW = 4 * GS;         // codes per bias block (4 groups)
   constexpr int BSC = BLKW / SCW;      // super-chunks per block
-  constexpr int STEPS_SC = SCW / 32;   // MFMA steps per super-chunk
-  constexpr int STEPS_G = GS / 32;     // MFMA steps per group
-  constexpr int XW = BITS == 4 ? 4 : 8;  // 16-byte activation loads per lane per super-chunk
+  constexpr int CPG = GS / CW;         // chunks per group (1, 2 or 4)
+  constexpr int GPS = 4 / CPG;         // groups per super-chunk
+  // how far the four chunk rows are exchanged so that a register holds one group
+  constexpr int LVL = CPG >= 4 ? 0 : (CPG == 2 ? 1 : 2);
+  constexpr int REGS_G = CPG;          // registers (of one super-chunk) per group
   // A wave walks its K-slice in batches of UNR super-chunks (whole blocks):
-  // all loads of a batch are issued together, in the order they are
-  // consumed, then the batch is computed.  UNR is compile-time so positions
-  // within a block and register slots are static.
+  // activations, codes and metadata of a batch are issued together, then the
+  // activation work is done while the codes are in flight, then the codes
+  // are consumed in load order.  UNR is compile-time so positions within a
+  // block and register slots are static.
   constexpr int UNR = SPI > BSC ? SPI : BSC;
   constexpr int BPB = UNR / BSC;       // blocks per batch
-  static_assert(BSC >= 1 && BLKW % SCW == 0 && UNR % BSC == 0, "block layout");
+  static_assert(BSC >= 1 && BLKW % SCW == 0 && UNR % BSC == 0 && CPG >= 1, "block layout");
 
   __shared__ float red[MAXT / 64][NT][4][64];
 
@@ -67,14 +72,11 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   const int NBLK = K / BLKW;
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   const uint32_t offset_pair = opaque_u32(kOffsetPair);
-
-  // indicator operands: A row r = col is all ones iff r/4 == j
-  u32x4_t ind[4];
+  // element offset, within a super-chunk, of the codes register i holds in
+  // this lane's row after the partial transpose
+  int xoff[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t v = ((col >> 2) == j) ? 0x3F803F80u : 0u;
-    ind[j] = u32x4_t{v, v, v, v};
-  }
+  for (int i = 0; i < 4; ++i) xoff[i] = lvl_chunk<LVL>(i, kb) * CW + lvl_dword<LVL>(i, kb) * DW;
 
   // One tile group (16*NT output columns over all of K) per call of `group`.
   auto group = [&](const int tg) {
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   // Rows m >= M and columns n >= N only feed outputs that are never stored,
   // so their lanes read valid clamped addresses instead of branching around
   // the loads (a branch would force a wait on every load).
-  const uint16_t *xr = x + (size_t)(col < M ? col : M - 1) * K + kb * (CW / 4);
+  const uint16_t *xr = x + (size_t)(col < M ? col : M - 1) * K;
   const uint8_t *crow[NT];
   const uint16_t *srow[NT];
   const uint16_t *brow[NT];
@@ -110,39 +112,79 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
 
   for (int blk0 = b_begin; blk0 < b_end; blk0 += BPB) {
     const int nb = min(BPB, b_end - blk0);  // blocks in this batch (uniform)
-    // ---- issue: activations, codes and metadata of the batch
-    u32x4_t xv[UNR][XW];
+    // ---- issue: activations first (L2), then codes (HBM), then metadata
+    u32x4_t xv[UNR][4][HS];
     u32x4_t cv[UNR][NT];
     uint2 s4[BPB][NT], b4[BPB][NT];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       if (u / BSC < nb) {
+        const int k0 = (blk0 * BSC + u) * SCW;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int l = 0; l < HS; ++l)
+            xv[u][i][l] = *reinterpret_cast<const u32x4_t *>(xr + k0 + xoff[i] + 8 * l);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      if (u / BSC < nb) {
         const int gsc = blk0 * BSC + u;
 #pragma unroll
-        for (int i = 0; i < XW; ++i) {
-          const int c = BITS == 4 ? i : (i >> 1);
-          const int k0 = gsc * SCW + c * CW + (BITS == 4 ? 0 : 8 * (i & 1));
-          xv[u][i] = *reinterpret_cast<const u32x4_t *>(xr + k0);
-        }
+        for (int t = 0; t < NT; ++t) cv[u][t] = load_stream_u32x4(crow[t] + (size_t)gsc * 64);
+      }
+    }
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-          cv[u][t] = load_stream_u32x4(crow[t] + (size_t)gsc * 64);
-        if (u % BSC == 0) {
+    for (int bb = 0; bb < BPB; ++bb) {
+      if (bb < nb) {
 #pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            s4[u / BSC][t] = *reinterpret_cast<const uint2 *>(srow[t] + (size_t)(gsc / BSC) * 4);
-            b4[u / BSC][t] = *reinterpret_cast<const uint2 *>(brow[t] + (size_t)(gsc / BSC) * 4);
-          }
+        for (int t = 0; t < NT; ++t) {
+          s4[bb][t] = *reinterpret_cast<const uint2 *>(srow[t] + (size_t)(blk0 + bb) * 4);
+          b4[bb][t] = *reinterpret_cast<const uint2 *>(brow[t] + (size_t)(blk0 + bb) * 4);
         }
       }
     }
-
     // keep the whole batch of loads ahead of the compute: without this the
     // scheduler may sink later loads below the first waits and serialize them
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- compute, super-chunk by super-chunk in load order
-    f32x4_t xsacc = zero4;
+    // ---- activation work, overlapping the code loads: re-pair x to the
+    // code pairing and form the per-group activation sums.  xsum of group
+    // g0 + j ends up in row j of this lane's column, i.e. in the A layout of
+    // v_mfma_f32_16x16x4_f32 for the bias product.
+    float xsum[BPB];
+#pragma unroll
+    for (int bb = 0; bb < BPB; ++bb) {
+      float P[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int uu = 0; uu < BSC; ++uu) {
+        const int u = bb * BSC + uu;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = uu * GPS + i / REGS_G;  // group within the block
+#pragma unroll
+          for (int l = 0; l < HS; ++l)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) P[j] = dot2_bf16(xv[u][i][l][e], 0x3F803F80u, P[j]);
+          if constexpr (BITS == 4) {
+            const uint32_t X[4] = {xv[u][i][0][0], xv[u][i][0][1], xv[u][i][0][2], xv[u][i][0][3]};
+            xv[u][i][0] = u32x4_t{xpair_stride4(X, 0), xpair_stride4(X, 1), xpair_stride4(X, 2),
+                                  xpair_stride4(X, 3)};
+          } else {
+            const uint32_t X[8] = {xv[u][i][0][0], xv[u][i][0][1], xv[u][i][0][2], xv[u][i][0][3],
+                                   xv[u][i][1][0], xv[u][i][1][1], xv[u][i][1][2], xv[u][i][1][3]};
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              xv[u][i][h] = u32x4_t{xpair_stride8(X, 4 * h + 0), xpair_stride8(X, 4 * h + 1),
+                                    xpair_stride8(X, 4 * h + 2), xpair_stride8(X, 4 * h + 3)};
+          }
+        }
+      }
+      xsum[bb] = rows_transpose_reduce4(P);
+    }
+
+    // ---- codes, super-chunk by super-chunk in load order
     f32x4_t accg[NT];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
@@ -155,61 +197,48 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
         cur[t][1] = cv[u][t][1];
         cur[t][2] = cv[u][t][2];
         cur[t][3] = cv[u][t][3];
-        transpose_rows4(cur[t]);
+        transpose_rows_lvl<LVL>(cur[t]);
       }
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int i = 0; i < 4; ++i) {
+        const int j = scb * GPS + i / REGS_G;  // group within the block
 #pragma unroll
-        for (int h = 0; h < (BITS == 4 ? 1 : 2); ++h) {
-          const int st = scb * STEPS_SC + (BITS == 4 ? c : 2 * c + h);  // step within block
-          const int j = st / STEPS_G;                                      // group within block
-          const bool gfirst = (st % STEPS_G) == 0;
-          const bool glast = (st % STEPS_G) == STEPS_G - 1;
-          u32x4_t xa;
-          if constexpr (BITS == 4) {
-            xa = xv[u][c];
-          } else {
-            const uint32_t X[8] = {xv[u][2 * c][0],     xv[u][2 * c][1],     xv[u][2 * c][2],
-                                   xv[u][2 * c][3],     xv[u][2 * c + 1][0], xv[u][2 * c + 1][1],
-                                   xv[u][2 * c + 1][2], xv[u][2 * c + 1][3]};
-            xa = u32x4_t{xpair_stride8(X, 4 * h + 0), xpair_stride8(X, 4 * h + 1),
-                         xpair_stride8(X, 4 * h + 2), xpair_stride8(X, 4 * h + 3)};
-          }
-          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xa);
+        for (int h = 0; h < HS; ++h) {
+          const bool gfirst = (i % REGS_G) == 0 && h == 0;
+          const bool glast = (i % REGS_G) == REGS_G - 1 && h == HS - 1;
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xv[u][i][h]);
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
             u32x4_t bw;
             if constexpr (BITS == 4) {
-              bw = unpack4_natural_quad(cur[t][c], offset_pair);
+              bw = unpack4_split_quad(cur[t][i], offset_pair);
             } else {
-              bw = unpack2_split_quad(cur[t][c], h, offset_pair);
+              bw = unpack2_split_quad(cur[t][i], h, offset_pair);
             }
             accg[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 a, __builtin_bit_cast(bf16x8_t, bw), gfirst ? zero4 : accg[t], 0, 0, 0);
           }
-          xsacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ind[j]), a,
-                                                          st == 0 ? zero4 : xsacc, 0, 0, 0);
           if (glast) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
               const uint32_t sw = (j < 2) ? s4[u / BSC][t].x : s4[u / BSC][t].y;
-              const float s = half_bits_to_float((j & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+              const float sc = half_bits_to_float((j & 1) ? (sw >> 16) : (sw & 0xFFFFu));
 #pragma unroll
-              for (int i = 0; i < 4; ++i) acc[t][i] = fmaf(s, accg[t][i], acc[t][i]);
+              for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(sc, accg[t][q], acc[t][q]);
             }
           }
         }
       }
       if (scb == BSC - 1) {
-        // bias (with the 128 offset): acc += xsum[m][g0+j] * (b - 128 s)[n][g0+j]
+        // bias with the 128 offset: acc += xsum[m][g0+kb] * (b - 128 s)[n][g0+kb]
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           const uint32_t sw = (kb < 2) ? s4[u / BSC][t].x : s4[u / BSC][t].y;
           const uint32_t bw = (kb < 2) ? b4[u / BSC][t].x : b4[u / BSC][t].y;
-          const float s = half_bits_to_float((kb & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+          const float sc = half_bits_to_float((kb & 1) ? (sw >> 16) : (sw & 0xFFFFu));
           const float b = half_bits_to_float((kb & 1) ? (bw >> 16) : (bw & 0xFFFFu));
-          const float bo = fmaf(-128.f, s, b);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsacc[0], bo, acc[t], 0, 0, 0);
+          const float bo = fmaf(-128.f, sc, b);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum[u / BSC], bo, acc[t], 0, 0, 0);
         }
       }
     }

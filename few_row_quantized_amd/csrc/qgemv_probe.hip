@@ -51,46 +51,47 @@ __global__ __launch_bounds__(256) void unpack_probe_dot(const uint8_t *__restric
 }
 
 // MFMA-path decoding: one wave per (16-row tile, 64-byte super-chunk), same
-// lane-to-address mapping, row transpose and unpack as qgemv_mfma_kernel; each
-// B-operand slot is written to the column it stands for.
-template <int BITS>
+// lane-to-address mapping, partial row transpose (level LVL, chosen by the
+// group size) and unpack as qgemv_mfma_kernel; each B-operand slot is written
+// to the column it stands for.
+template <int BITS, int LVL>
 __global__ __launch_bounds__(64) void unpack_probe_mfma(const uint8_t *__restrict__ codes,
                                                         uint8_t *__restrict__ q, int N, int K) {
   constexpr int CW = 128 / BITS;
   constexpr int SCW = 4 * CW;
+  constexpr int DW = CW / 4;
   const int lane = threadIdx.x;
   const int col = lane & 15, kb = lane >> 4;
   const int nsc = K / SCW;
   const int tile = blockIdx.x / nsc;
   const int sc = blockIdx.x % nsc;
-  const int n = tile * 16 + col;
-  const bool ok = n < N;
+  const int n = min(tile * 16 + col, N - 1);
   const size_t RB = (size_t)K * BITS / 8;
-  uint4 v = ok ? *reinterpret_cast<const uint4 *>(codes + (size_t)n * RB + (size_t)sc * 64 + kb * 16)
-               : make_uint4(0, 0, 0, 0);
+  const uint4 v = *reinterpret_cast<const uint4 *>(codes + (size_t)n * RB + (size_t)sc * 64 + kb * 16);
   uint32_t r[4] = {v.x, v.y, v.z, v.w};
-  transpose_rows4(r);  // all lanes take part, also those past row N
-  if (!ok) return;
+  transpose_rows_lvl<LVL>(r);  // all lanes take part, also those past row N
+  if (tile * 16 + col >= N) return;
   uint8_t *qr = q + (size_t)n * K + (size_t)sc * SCW;
+  const uint32_t off = kOffsetPair;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int i = 0; i < 4; ++i) {
+    const int k0 = lvl_chunk<LVL>(i, kb) * CW + lvl_dword<LVL>(i, kb) * DW;
     if constexpr (BITS == 4) {
-      uint32_t p[4];
-      unpack4_natural_pairs(r[c], p);
-      const int k0 = 32 * c + 8 * kb;  // B slots 2e, 2e+1 stand for k0+2e, k0+2e+1
+      const u32x4_t p = unpack4_split_quad(r[i], off);  // pair e: codes k0+e, k0+e+4
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        qr[k0 + 2 * e] = code_of(p[e] & 0xFFFFu);
-        qr[k0 + 2 * e + 1] = code_of(p[e] >> 16);
+        qr[k0 + e] = code_of(p[e] & 0xFFFFu);
+        qr[k0 + e + 4] = code_of(p[e] >> 16);
       }
     } else {
-      uint32_t p[8];
-      unpack2_split_pairs(r[c], p);
-      const int k0 = 64 * c + 16 * kb;  // pair e stands for k0+e and k0+e+8
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        qr[k0 + e] = code_of(p[e] & 0xFFFFu);
-        qr[k0 + e + 8] = code_of(p[e] >> 16);
+      for (int h = 0; h < 2; ++h) {
+        const u32x4_t p = unpack2_split_quad(r[i], h, off);  // pair e: codes k0+4h+e, +8
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qr[k0 + 4 * h + e] = code_of(p[e] & 0xFFFFu);
+          qr[k0 + 4 * h + e + 8] = code_of(p[e] >> 16);
+        }
       }
     }
   }
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_probe_kernel(const uint
 }  // namespace
 
 int launch_unpack_probe(int path, const uint8_t *codes, uint8_t *q_out, int N, int K, int bits,
-                        hipStream_t stream) {
+                        int group_size, hipStream_t stream) {
   if (path == QGEMV_PATH_DOT) {
     const int CW = 128 / bits;
     const size_t threads = (size_t)N * (K / CW);
@@ -143,12 +144,19 @@ int launch_unpack_probe(int path, const uint8_t *codes, uint8_t *q_out, int N, i
     else
       hipLaunchKernelGGL(unpack_probe_dot<2>, dim3(blocks), dim3(256), 0, stream, codes, q_out, N, K);
   } else if (path == QGEMV_PATH_MFMA) {
-    const int SCW = 4 * (128 / bits);
-    const int blocks = ((N + 15) / 16) * (K / SCW);
-    if (bits == 4)
-      hipLaunchKernelGGL(unpack_probe_mfma<4>, dim3(blocks), dim3(64), 0, stream, codes, q_out, N, K);
-    else
-      hipLaunchKernelGGL(unpack_probe_mfma<2>, dim3(blocks), dim3(64), 0, stream, codes, q_out, N, K);
+    const int CW = 128 / bits;
+    const int blocks = ((N + 15) / 16) * (K / (4 * CW));
+    const int cpg = group_size / CW;  // chunks per group -> exchange level
+    const int lvl = cpg >= 4 ? 0 : (cpg == 2 ? 1 : 2);
+    const dim3 g(blocks), b(64);
+    if (bits == 4) {
+      if (lvl == 0) hipLaunchKernelGGL((unpack_probe_mfma<4, 0>), g, b, 0, stream, codes, q_out, N, K);
+      else if (lvl == 1) hipLaunchKernelGGL((unpack_probe_mfma<4, 1>), g, b, 0, stream, codes, q_out, N, K);
+      else hipLaunchKernelGGL((unpack_probe_mfma<4, 2>), g, b, 0, stream, codes, q_out, N, K);
+    } else {
+      if (lvl == 1) hipLaunchKernelGGL((unpack_probe_mfma<2, 1>), g, b, 0, stream, codes, q_out, N, K);
+      else hipLaunchKernelGGL((unpack_probe_mfma<2, 2>), g, b, 0, stream, codes, q_out, N, K);
+    }
   } else {
     return QGEMV_EINVAL;
   }
