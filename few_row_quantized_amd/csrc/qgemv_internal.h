@@ -26,6 +26,9 @@ constexpr size_t kDotLdsBudget = 80 * 1024;
 // Launchers: enqueue on `stream`, return QGEMV_OK / QGEMV_EUNSUPPORTED / QGEMV_EHIP.
 int launch_dot(const QgemvArgs &a, hipStream_t stream);
 int launch_mfma(const QgemvArgs &a, hipStream_t stream);
+// Persistent MFMA kernel (QGEMV_EUNSUPPORTED when the activations of a
+// wave would not fit its registers).
+int launch_persist(const QgemvArgs &a, hipStream_t stream);
 
 // Shape support of the MFMA path (host check).
 bool mfma_supports(int K, int bits, int group_size);

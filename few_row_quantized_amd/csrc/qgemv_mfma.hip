@@ -1,4 +1,4 @@
-// Split-K bf16 MFMA path of the few-row quantized GEMV (gfx950).
+// Single-pass split-K bf16 MFMA path of the few-row quantized GEMV (gfx950).
 //
 // Prior art on the pages: the few-row MMA kernels of "metal : few-row MMA
 // mat-mul and batched copies for speculative decoding" (Overview: 8x8
@@ -10,24 +10,27 @@
 //
 // CDNA4 design:
 // * One v_mfma_f32_16x16x32_bf16 computes a 16(m) x 16(n) tile over 32 k.
-//   A = activations (rows m >= M are zero and never loaded), B = weights as
-//   exact bf16 values 128+q.  A workgroup owns NT tiles of 16 output columns
-//   over the whole of K; its waves split K into "bias blocks" of 4 groups.
+//   A = activations (rows m >= M repeat row M-1 and are never stored),
+//   B = weights as exact bf16 values 128+q.  A workgroup owns NT tiles of
+//   16 output columns over the whole of K; its waves split K into
+//   contiguous slices of "bias blocks" (4 groups).
 // * Lane (col = lane%16, kb = lane/16) loads 16 contiguous bytes of row
 //   n = col at byte 16*kb of each 64-byte super-chunk, so 16 rows x 64 B are
-//   read per load instruction.  A 4x4 transpose of dwords across the four
-//   16-lane rows (v_permlane32_swap + v_permlane16_swap) then gives every
-//   MFMA step 32 consecutive-in-K codes from one chunk, i.e. from one group.
+//   read per load instruction.  A partial exchange of dwords across the four
+//   16-lane rows (none, v_permlane32_swap, or the full 4x4 transpose with
+//   v_permlane16_swap, as the group size requires) gives every MFMA step 32
+//   codes of one quantization group.
 // * The group's partial product is accumulated by gs/32 MFMAs and folded with
 //   the group scale once: acc += s * acc_g (4 FMAs per lane per group).
-// * Bias and the 128 code offset: sum_g (b - 128 s)[n,g] * xsum[m,g] is a
-//   tiny product over groups.  xsum is produced by an extra MFMA per step
-//   with an indicator A operand (row r is all ones iff r/4 is the step's
-//   group within the block), which leaves xsum[m][g0 + lane/16] in exactly
-//   the A layout of v_mfma_f32_16x16x4_f32; one such MFMA per block and tile
-//   adds the bias term.
-// * Partial tiles of the waves are summed through LDS in a fixed wave order
+// * Bias and the 128 code offset: sum_g (b - 128 s)[n,g] * xsum[m,g] over the
+//   4 groups of a block is one v_mfma_f32_16x16x4_f32, with the per-group
+//   activation sums xsum (dot2 against ones, then a row transpose-reduce)
+//   formed while the codes are still in flight.
+// * Partial tiles of the waves are summed through LDS in slice order
 //   (deterministic, no atomics) and rows m < M are stored.
+// Shapes with more 16-column tiles than CUs go to the persistent kernel
+// (qgemv_persist.hip) unless K is too long for its register-resident
+// activations.
 
 #include "qgemv_device.h"
 #include "qgemv_internal.h"
@@ -365,6 +368,12 @@ bool mfma_supports(int K, int bits, int group_size) {
 
 int launch_mfma(const QgemvArgs &a, hipStream_t stream) {
   if (!mfma_supports(a.K, a.bits, a.group_size)) return QGEMV_EUNSUPPORTED;
+  // more tiles than CUs: the persistent kernel streams several tiles per CU;
+  // otherwise one tile group per workgroup in a single pass
+  if ((a.N + 15) / 16 > cu_count()) {
+    const int st = launch_persist(a, stream);
+    if (st != QGEMV_EUNSUPPORTED) return st;
+  }
   if (a.bits == 4) {
     switch (a.group_size) {
       case 32: return launch_mfma_gs<4, 32>(a, stream);

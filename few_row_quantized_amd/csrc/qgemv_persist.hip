@@ -1,0 +1,307 @@
+// Persistent bf16 MFMA path of the few-row quantized GEMV (gfx950), for
+// shapes whose weight stream spans many tiles per CU.
+//
+// Prior art on the pages: the few-row MMA kernels of "metal : few-row MMA
+// mat-mul and batched copies for speculative decoding" (Overview: each weight
+// dequantized once for all rows, the simdgroups of a threadgroup split K) and
+// the split-K MMA variants on the MLX quantized_matmul small-M verify kernels
+// page (Facts: dequantize per quantization group rather than per MMA tile;
+// split K across the simdgroups).
+//
+// CDNA4 design:
+// * A persistent grid of one workgroup per CU; workgroup g owns the
+//   contiguous range of 16-column tiles [g*T/G, (g+1)*T/G) over the whole of K.
+// * Its W waves split K into bias blocks (4 groups): wave w owns the blocks
+//   vw, vw+W, ... (vw = w rotated per workgroup) for every tile, so its
+//   activation operands and the per-group activation sums of the bias term
+//   are loaded, re-paired and summed once and then stay in registers while
+//   the workgroup walks its tiles.
+// * Codes and group metadata of the next tile are prefetched into a ring of
+//   S register slots while the current tile is unpacked and multiplied, so a
+//   CU keeps weight bytes in flight from its first tile to its last.
+// * Every S tiles the waves' partial 16x16 tiles are summed through LDS in
+//   block order (deterministic, no atomics) and rows m < M are stored.
+// The inner MFMA step (code layout, partial lane transpose, unpack to exact
+// bf16 128+q, per-group scale fold, bias product by v_mfma_f32_16x16x4_f32)
+// is the one of the single-pass kernel.
+
+#include "qgemv_device.h"
+#include "qgemv_internal.h"
+
+namespace qgemv {
+
+namespace {
+
+template <int BITS, int GS, int BPW, int S, int MAXW>
+__global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
+    const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *__restrict__ y,
+    int M, int N, int K) {
+  constexpr int CW = 128 / BITS;         // codes per 16-byte chunk
+  constexpr int SCW = 4 * CW;            // codes per 64-byte super-chunk
+  constexpr int DW = CW / 4;             // codes per dword
+  constexpr int HS = BITS == 4 ? 1 : 2;  // MFMA steps per code dword
+  constexpr int BLKW = 4 * GS;           // codes per bias block
+  constexpr int BSC = BLKW / SCW;        // super-chunks per block
+  constexpr int CPG = GS / CW;           // chunks per group
+  constexpr int GPS = 4 / CPG;           // groups per super-chunk
+  constexpr int LVL = CPG >= 4 ? 0 : (CPG == 2 ? 1 : 2);
+  constexpr int REGS_G = CPG;
+  static_assert(BSC >= 1 && BLKW % SCW == 0 && CPG >= 1, "block layout");
+
+  __shared__ float red[S][MAXW][4][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int W = blockDim.x >> 6;
+  const int col = lane & 15;
+  const int kb = lane >> 4;
+  // Block ownership is rotated per workgroup (workgroups are dealt
+  // round-robin over the 8 XCDs, so blockIdx/8 differs between the CUs that
+  // share an L2): without it every CU asks for the same activation lines at
+  // the same moment.  Partials are summed in block order, so results do not
+  // depend on the rotation.
+  const int rot = (int)((blockIdx.x >> 3) % (unsigned)W);
+  const int vw = wave + rot < W ? wave + rot : wave + rot - W;
+  const int nblk = K / BLKW;
+  const size_t RB = (size_t)K * BITS / 8;
+  const int NG = K / GS;
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t offset_pair = opaque_u32(kOffsetPair);
+  int xoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xoff[i] = lvl_chunk<LVL>(i, kb) * CW + lvl_dword<LVL>(i, kb) * DW;
+
+  // tile range of this workgroup (the products stay below 2^31: the grid is
+  // at most the CU count and T <= 2^18)
+  const int T = (N + 15) >> 4;
+  const int t_first = (int)(blockIdx.x * (unsigned)T / gridDim.x);
+  const int ntile = (int)((blockIdx.x + 1) * (unsigned)T / gridDim.x) - t_first;
+
+  // owned blocks; a wave past the last block loads a valid block and skips
+  // the arithmetic
+  int blk[BPW];
+  bool own[BPW];
+#pragma unroll
+  for (int k = 0; k < BPW; ++k) {
+    own[k] = vw + k * W < nblk;
+    blk[k] = own[k] ? vw + k * W : nblk - 1;
+  }
+
+  // ---- activations of the owned blocks (rows m >= M read row M-1: their
+  // outputs are never stored), later re-paired to the code pairing and
+  // summed per group into the A layout of the bias MFMA
+  const uint16_t *xr = x + (size_t)(col < M ? col : M - 1) * K;
+  u32x4_t xv[BPW][BSC][4][HS];
+  float xsum[BPW];
+#pragma unroll
+  for (int k = 0; k < BPW; ++k)
+#pragma unroll
+    for (int u = 0; u < BSC; ++u) {
+      const int k0 = (blk[k] * BSC + u) * SCW;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int l = 0; l < HS; ++l)
+          xv[k][u][i][l] = *reinterpret_cast<const u32x4_t *>(xr + k0 + xoff[i] + 8 * l);
+    }
+
+  // ---- prefetch ring of codes and metadata.  Issues past the last tile are
+  // still made (a branch around loads would make the compiler wait for every
+  // load in flight), but all lanes of the wave then read the first line of
+  // the wave's own first-tile data: one cached line per instruction, and a
+  // different line for every wave of the device.
+  u32x4_t cv[S][BPW][BSC];
+  uint2 s4[S][BPW], b4[S][BPW];
+  const uint64_t crow_dead = (uint64_t)(16 * t_first) * RB;
+  const uint64_t mrow_dead = (uint64_t)(16 * t_first) * NG;
+  int it = 0;  // tile step of the next issue
+  auto issue = [&](const int slot) {
+    const uint64_t m64 = 0ull - (uint64_t)(it < ntile);  // all-ones while live
+    const int n = min(16 * (t_first + it) + col, N - 1);
+    const uint64_t crow = (((uint64_t)n * RB + kb * 16) & m64) | (crow_dead & ~m64);
+    const uint64_t mrow = (((uint64_t)n * NG) & m64) | (mrow_dead & ~m64);
+#pragma unroll
+    for (int k = 0; k < BPW; ++k) {
+#pragma unroll
+      for (int u = 0; u < BSC; ++u)
+        cv[slot][k][u] = load_stream_u32x4(codes + crow + (size_t)(blk[k] * BSC + u) * 64);
+    }
+#pragma unroll
+    for (int k = 0; k < BPW; ++k) {
+      s4[slot][k] = *reinterpret_cast<const uint2 *>(scales + mrow + blk[k] * 4);
+      b4[slot][k] = *reinterpret_cast<const uint2 *>(biases + mrow + blk[k] * 4);
+    }
+    ++it;
+  };
+
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) issue(s);
+  // keep the code loads ahead of the activation work that waits for x
+  __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+  for (int k = 0; k < BPW; ++k) {
+    float P[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < BSC; ++u) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = u * GPS + i / REGS_G;
+#pragma unroll
+        for (int l = 0; l < HS; ++l)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) P[j] = dot2_bf16(xv[k][u][i][l][e], 0x3F803F80u, P[j]);
+        if constexpr (BITS == 4) {
+          const uint32_t X[4] = {xv[k][u][i][0][0], xv[k][u][i][0][1], xv[k][u][i][0][2],
+                                 xv[k][u][i][0][3]};
+          xv[k][u][i][0] = u32x4_t{xpair_stride4(X, 0), xpair_stride4(X, 1), xpair_stride4(X, 2),
+                                   xpair_stride4(X, 3)};
+        } else {
+          const uint32_t X[8] = {xv[k][u][i][0][0], xv[k][u][i][0][1], xv[k][u][i][0][2],
+                                 xv[k][u][i][0][3], xv[k][u][i][1][0], xv[k][u][i][1][1],
+                                 xv[k][u][i][1][2], xv[k][u][i][1][3]};
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            xv[k][u][i][h] = u32x4_t{xpair_stride8(X, 4 * h + 0), xpair_stride8(X, 4 * h + 1),
+                                     xpair_stride8(X, 4 * h + 2), xpair_stride8(X, 4 * h + 3)};
+        }
+      }
+    }
+    xsum[k] = rows_transpose_reduce4(P);
+  }
+
+  // ---- groups of S tile steps (the unrolled ring); a range always has a
+  // tile (do-while: no guard branch that would let the compiler sink the
+  // prologue loads below the activation work)
+  int j0 = 0;
+  do {
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      if (j0 + s >= ntile) break;
+      issue((s + S - 1) % S);
+      __builtin_amdgcn_sched_barrier(0);
+
+      f32x4_t acc = zero4;
+#pragma unroll
+      for (int k = 0; k < BPW; ++k) {
+        if (!own[k]) continue;  // uniform per wave
+        f32x4_t accg;
+#pragma unroll
+        for (int u = 0; u < BSC; ++u) {
+          uint32_t cur[4] = {cv[s][k][u][0], cv[s][k][u][1], cv[s][k][u][2], cv[s][k][u][3]};
+          transpose_rows_lvl<LVL>(cur);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int jg = u * GPS + i / REGS_G;  // group within the block
+#pragma unroll
+            for (int h = 0; h < HS; ++h) {
+              const bool gfirst = (i % REGS_G) == 0 && h == 0;
+              const bool glast = (i % REGS_G) == REGS_G - 1 && h == HS - 1;
+              u32x4_t bw;
+              if constexpr (BITS == 4) {
+                bw = unpack4_split_quad(cur[i], offset_pair);
+              } else {
+                bw = unpack2_split_quad(cur[i], h, offset_pair);
+              }
+              accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8_t, xv[k][u][i][h]), __builtin_bit_cast(bf16x8_t, bw),
+                  gfirst ? zero4 : accg, 0, 0, 0);
+              if (glast) {
+                const uint32_t sw = (jg < 2) ? s4[s][k].x : s4[s][k].y;
+                const float scl = half_bits_to_float((jg & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[q] = fmaf(scl, accg[q], acc[q]);
+              }
+            }
+          }
+        }
+        // bias with the 128 offset: acc += xsum[m][g0+kb] * (b - 128 s)[n][g0+kb]
+        const uint32_t sw = (kb < 2) ? s4[s][k].x : s4[s][k].y;
+        const uint32_t bw = (kb < 2) ? b4[s][k].x : b4[s][k].y;
+        const float scl = half_bits_to_float((kb & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+        const float b = half_bits_to_float((kb & 1) ? (bw >> 16) : (bw & 0xFFFFu));
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum[k], fmaf(-128.f, scl, b), acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[s][wave][i][lane] = acc[i];
+    }
+
+    // ---- sum the group's partial tiles over the waves in block order
+    __syncthreads();
+    const int nj = min(S, ntile - j0);
+    for (int o = threadIdx.x; o < nj * 256; o += blockDim.x) {
+      const int s = o >> 8, i = (o >> 6) & 3, l = o & 63;
+      float v = 0.f;
+      for (int w = 0; w < W; ++w) {
+        const int pw = w >= rot ? w - rot : w - rot + W;  // wave acting as virtual wave w
+        v += red[s][pw][i][l];
+      }
+      const int m = 4 * (l >> 4) + i;
+      const int n = 16 * (t_first + j0 + s) + (l & 15);
+      if (m < M && n < N) y[(size_t)m * N + n] = v;
+    }
+    __syncthreads();  // red is rewritten by the next group
+    j0 += S;
+  } while (j0 < ntile);
+}
+
+// Per-format launch shape: blocks owned per wave (activation registers stay
+// within 64 VGPRs), the wave cap whose register budget the kernel fits, and
+// the depth S of the prefetch ring.
+template <int BITS, int GS>
+struct PersistShape {
+  static constexpr int BPW = (BITS == 4 && GS == 32) || (BITS == 2 && GS == 64) ? 2 : 1;
+  static constexpr int MAXW = (BITS == 4 && GS <= 64) ? 16 : 12;
+  static constexpr int S = 2;
+};
+
+int cu_count_persist() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+template <int BITS, int GS>
+int launch_persist_t(const QgemvArgs &a, hipStream_t stream) {
+  constexpr int BPW = PersistShape<BITS, GS>::BPW;
+  constexpr int MAXW = PersistShape<BITS, GS>::MAXW;
+  constexpr int S = PersistShape<BITS, GS>::S;
+  const int nblk = a.K / (4 * GS);
+  if (nblk > MAXW * BPW) return QGEMV_EUNSUPPORTED;  // activations would not fit the registers
+  const int waves = (nblk + BPW - 1) / BPW;
+  const int tiles = (a.N + 15) / 16;
+  const int cus = cu_count_persist();
+  const int G = tiles < cus ? tiles : cus;
+  hipLaunchKernelGGL((qgemv_persist_kernel<BITS, GS, BPW, S, MAXW>), dim3(G), dim3(64 * waves), 0,
+                     stream, a.codes, a.scales, a.biases, a.x, a.y, a.M, a.N, a.K);
+  return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}
+
+}  // namespace
+
+int launch_persist(const QgemvArgs &a, hipStream_t stream) {
+  if (!mfma_supports(a.K, a.bits, a.group_size)) return QGEMV_EUNSUPPORTED;
+  if (a.bits == 4) {
+    switch (a.group_size) {
+      case 32: return launch_persist_t<4, 32>(a, stream);
+      case 64: return launch_persist_t<4, 64>(a, stream);
+      case 128: return launch_persist_t<4, 128>(a, stream);
+    }
+  } else {
+    switch (a.group_size) {
+      case 64: return launch_persist_t<2, 64>(a, stream);
+      case 128: return launch_persist_t<2, 128>(a, stream);
+    }
+  }
+  return QGEMV_EUNSUPPORTED;
+}
+
+}  // namespace qgemv

@@ -131,6 +131,25 @@ def test_ragged_shapes_every_element(path, K, N, bits, gs):
         check_y(p, d.run_host(M, path), M, label=f"{path} K={K} N={N} M={M}")
 
 
+# More 16-column tiles than CUs: the MFMA path streams several tiles per
+# workgroup (ranges of 1 to 3 tiles, ragged last tile), or falls back to the
+# single-pass kernel when K is too long for the activations to stay in
+# registers (the last shape).
+PERSIST = [
+    (1024, 4113, 4, 32), (2048, 4500, 4, 64), (3072, 5000, 4, 128), (6144, 4200, 4, 128),
+    (1280, 4700, 2, 64), (2048, 9000, 2, 128), (8192, 4500, 4, 128),
+]
+
+
+@pytest.mark.parametrize("K,N,bits,gs", PERSIST)
+def test_many_tiles_per_cu_every_element(K, N, bits, gs):
+    p = synth.make_problem(synth.custom_shape(K, N, bits, gs, seed=5 * K + N, outliers=True), m_max=16)
+    d = DeviceProblem(p)
+    for M in (1, 3, 8, 16):
+        say(f"many tiles mfma K={K} N={N} bits={bits} gs={gs} M={M}")
+        check_y(p, d.run_host(M, "mfma"), M, label=f"mfma K={K} N={N} M={M}")
+
+
 @pytest.mark.parametrize("path", ["dot", "mfma"])
 def test_zero_codes(path):
     K, N, M = 2048, 64, 8
@@ -141,14 +160,15 @@ def test_zero_codes(path):
 
 # ---------------------------------------------------------------- invariants
 
-@pytest.mark.parametrize("bits,gs", [(4, 64), (2, 64), (4, 128)])
+@pytest.mark.parametrize("bits,gs,N", [(4, 64, 200), (2, 64, 200), (4, 128, 200), (4, 64, 4500),
+                                       (2, 128, 4500)])
 @pytest.mark.parametrize("path", ["dot", "mfma"])
-def test_row_of_m_row_call_equals_single_row_call_bitwise(path, bits, gs):
+def test_row_of_m_row_call_equals_single_row_call_bitwise(path, bits, gs, N):
     import torch
-    K, N = 2048, 200
+    K = 2048
     p = synth.make_problem(synth.custom_shape(K, N, bits, gs, seed=77), m_max=16)
     d = DeviceProblem(p)
-    say(f"row invariance {path} bits={bits} gs={gs}")
+    say(f"row invariance {path} bits={bits} gs={gs} N={N}")
     singles = []
     for m in range(16):
         xm = d.x[m:m + 1].clone()
@@ -162,12 +182,13 @@ def test_row_of_m_row_call_equals_single_row_call_bitwise(path, bits, gs):
         assert np.array_equal(y, singles[:M]), f"M={M}"
 
 
+@pytest.mark.parametrize("name", ["square_k4096_n4096_4b_g64", "layer27b_gate"])
 @pytest.mark.parametrize("path", ["dot", "mfma"])
-def test_repeated_calls_are_bitwise_identical(path):
-    s = synth.WORKLOADS["square_k4096_n4096_4b_g64"]
+def test_repeated_calls_are_bitwise_identical(path, name):
+    s = synth.WORKLOADS[name]
     p = synth.make_problem(s)
     d = DeviceProblem(p)
-    say(f"determinism {path}")
+    say(f"determinism {path} {name}")
     a = d.run_host(8, path)
     b = d.run_host(8, path)
     assert np.array_equal(a, b)
