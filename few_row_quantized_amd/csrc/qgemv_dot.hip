@@ -301,15 +301,26 @@ constexpr int dot_rows_per_wave() {
   return M <= 2 ? 2 : (M <= 4 ? 4 : (M <= 8 ? 2 : 1));
 }
 
-template <int BITS, int M>
-int launch_dot_m(const QgemvArgs &a, hipStream_t stream) {
-  constexpr int R = dot_rows_per_wave<M>();
+template <int BITS, int M, int R>
+int launch_dot_r(const QgemvArgs &a, hipStream_t stream) {
   if constexpr (BITS == 2) {
     if (a.group_size == 32) return launch_dot_t<2, M, R, 2>(a, stream);
     return launch_dot_t<2, M, R, 1>(a, stream);
   } else {
     return launch_dot_t<4, M, R, 1>(a, stream);
   }
+}
+
+template <int BITS, int M>
+int launch_dot_m(const QgemvArgs &a, hipStream_t stream) {
+  constexpr int R = dot_rows_per_wave<M>();
+  // Few rows (small N): one row per wave, so that every CU gets a workgroup.
+  // The row-to-lane arithmetic is the same for every R, so results do not
+  // depend on this choice.
+  if constexpr (R == 2 && M <= 2) {
+    if (a.N / (kDotWaves * R) < device_cu_count()) return launch_dot_r<BITS, M, 1>(a, stream);
+  }
+  return launch_dot_r<BITS, M, R>(a, stream);
 }
 
 template <int BITS>

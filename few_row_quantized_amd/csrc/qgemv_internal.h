@@ -23,6 +23,9 @@ struct QgemvArgs {
 constexpr size_t kLdsMax = 160 * 1024;
 constexpr size_t kDotLdsBudget = 80 * 1024;
 
+// Compute units of the current device (cached per device id).
+int device_cu_count();
+
 // Launchers: enqueue on `stream`, return QGEMV_OK / QGEMV_EUNSUPPORTED / QGEMV_EHIP.
 int launch_dot(const QgemvArgs &a, hipStream_t stream);
 int launch_mfma(const QgemvArgs &a, hipStream_t stream);

@@ -304,19 +304,6 @@ struct MfmaShape {
   static constexpr int MAXT = (BITS == 4 && NT == 1 && GS <= 64) ? 1024 : 512;
 };
 
-// Device CU count (per device id, cached).
-int cu_count() {
-  static int cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
 
 template <int BITS, int GS, int NT>
 int launch_mfma_t(const QgemvArgs &a, hipStream_t stream) {
@@ -338,7 +325,7 @@ int launch_mfma_t(const QgemvArgs &a, hipStream_t stream) {
       occ = 1;
     occ_cache[waves] = occ;
   }
-  const int slots = occ * cu_count();
+  const int slots = occ * device_cu_count();
   if (groups <= slots)
     hipLaunchKernelGGL(kern1, dim3(groups), dim3(64 * waves), 0, stream, a.codes, a.scales,
                        a.biases, a.x, a.y, a.M, a.N, a.K, groups);
@@ -353,7 +340,7 @@ int launch_mfma_gs(const QgemvArgs &a, hipStream_t stream) {
   // more output columns per workgroup on wide matrices: every workgroup reads
   // all M*K activations, so wider groups cut that traffic per weight byte
   const int tiles = (a.N + 15) / 16;
-  const int cus = cu_count();
+  const int cus = device_cu_count();
   if (tiles >= 2 * cus) return launch_mfma_t<BITS, GS, 2>(a, stream);
   return launch_mfma_t<BITS, GS, 1>(a, stream);
 }
@@ -370,7 +357,7 @@ int launch_mfma(const QgemvArgs &a, hipStream_t stream) {
   if (!mfma_supports(a.K, a.bits, a.group_size)) return QGEMV_EUNSUPPORTED;
   // more tiles than CUs: the persistent kernel streams several tiles per CU;
   // otherwise one tile group per workgroup in a single pass
-  if ((a.N + 15) / 16 > cu_count()) {
+  if ((a.N + 15) / 16 > device_cu_count()) {
     const int st = launch_persist(a, stream);
     if (st != QGEMV_EUNSUPPORTED) return st;
   }

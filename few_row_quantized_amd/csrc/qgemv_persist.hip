@@ -256,19 +256,6 @@ struct PersistShape {
   static constexpr int S = 2;
 };
 
-int cu_count_persist() {
-  static int cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
 template <int BITS, int GS>
 int launch_persist_t(const QgemvArgs &a, hipStream_t stream) {
   constexpr int BPW = PersistShape<BITS, GS>::BPW;
@@ -278,7 +265,7 @@ int launch_persist_t(const QgemvArgs &a, hipStream_t stream) {
   if (nblk > MAXW * BPW) return QGEMV_EUNSUPPORTED;  // activations would not fit the registers
   const int waves = (nblk + BPW - 1) / BPW;
   const int tiles = (a.N + 15) / 16;
-  const int cus = cu_count_persist();
+  const int cus = device_cu_count();
   const int G = tiles < cus ? tiles : cus;
   hipLaunchKernelGGL((qgemv_persist_kernel<BITS, GS, BPW, S, MAXW>), dim3(G), dim3(64 * waves), 0,
                      stream, a.codes, a.scales, a.biases, a.x, a.y, a.M, a.N, a.K);
