@@ -314,11 +314,17 @@ int launch_dot_r(const QgemvArgs &a, hipStream_t stream) {
 template <int BITS, int M>
 int launch_dot_m(const QgemvArgs &a, hipStream_t stream) {
   constexpr int R = dot_rows_per_wave<M>();
-  // Few rows (small N): one row per wave, so that every CU gets a workgroup.
-  // The row-to-lane arithmetic is the same for every R, so results do not
-  // depend on this choice.
-  if constexpr (R == 2 && M <= 2) {
-    if (a.N / (kDotWaves * R) < device_cu_count()) return launch_dot_r<BITS, M, 1>(a, stream);
+  // Few rows (small N): fewer rows per wave, so that every CU gets a
+  // workgroup.  The row-to-lane arithmetic is the same for every R, so
+  // results do not depend on this choice.
+  const int cus = device_cu_count();
+  if constexpr (R == 4) {
+    if (a.N / (kDotWaves * 4) < cus) {
+      if (a.N / (kDotWaves * 2) >= cus) return launch_dot_r<BITS, M, 2>(a, stream);
+      return launch_dot_r<BITS, M, 1>(a, stream);
+    }
+  } else if constexpr (R == 2) {
+    if (a.N / (kDotWaves * 2) < cus) return launch_dot_r<BITS, M, 1>(a, stream);
   }
   return launch_dot_r<BITS, M, R>(a, stream);
 }
