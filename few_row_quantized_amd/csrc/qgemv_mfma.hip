@@ -44,7 +44,7 @@ template <int BITS, int GS, int NT, int MAXT, int SPI, bool PERSIST>
 __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *__restrict__ y,
-    int M, int N, int K, int ngroups) {
+    int M, int N, int K, int ngroups, int ksplit) {
   constexpr int CW = 128 / BITS;       // codes per 16-byte chunk
   constexpr int SCW = 4 * CW;          // codes per 64-byte super-chunk
   constexpr int DW = CW / 4;           // codes per dword
@@ -83,15 +83,20 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
 
   // One tile group (16*NT output columns over all of K) per call of `group`.
   auto group = [&](const int tg) {
-  const int n_base = tg * 16 * NT;
+  // group tg = (tile group, part of K); with ksplit = 2 the two halves of K
+  // of a tile group are separate groups whose results are added into y
+  const int kpart = ksplit == 1 ? 0 : (tg & 1);
+  const int n_base = (ksplit == 1 ? tg : tg >> 1) * 16 * NT;
+  const int p_lo = kpart * NBLK / ksplit;
+  const int nbp = (kpart + 1) * NBLK / ksplit - p_lo;
   // K-slice of this wave.  The slice order is rotated per workgroup (by
   // blockIdx/8: workgroups are dealt round-robin over the 8 XCDs) so that the
   // CUs sharing an L2 do not all read the same activation lines at the same
   // moment.  Partials are reduced in slice order, so results do not depend
   // on the rotation.
   const int slice = (wave + (tg >> 3)) % waves;
-  const int b_begin = (slice * NBLK) / waves;
-  const int b_end = ((slice + 1) * NBLK) / waves;
+  const int b_begin = p_lo + (slice * nbp) / waves;
+  const int b_end = p_lo + ((slice + 1) * nbp) / waves;
   const size_t RB = (size_t)K * BITS / 8;
   const int G = K / GS;
   // Rows m >= M and columns n >= N only feed outputs that are never stored,
@@ -261,7 +266,15 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     for (int w = 0; w < waves; ++w) s += red[w][t][i][l];
     const int m = 4 * (l >> 4) + i;
     const int n = n_base + 16 * t + (l & 15);
-    if (m < M && n < N) y[(size_t)m * N + n] = s;
+    if (m < M && n < N) {
+      if (ksplit == 1) {
+        y[(size_t)m * N + n] = s;
+      } else {
+        // y was zeroed before the launch and receives exactly two addends:
+        // 0 + a + b equals 0 + b + a bit for bit, whichever half lands first
+        unsafeAtomicAdd(y + (size_t)m * N + n, s);
+      }
+    }
   }
   };
 
@@ -305,6 +318,10 @@ struct MfmaShape {
 };
 
 
+__global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ y, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) y[i] = 0.f;
+}
+
 template <int BITS, int GS, int NT>
 int launch_mfma_t(const QgemvArgs &a, hipStream_t stream) {
   constexpr int MAXT = MfmaShape<BITS, GS, NT>::MAXT;
@@ -312,9 +329,18 @@ int launch_mfma_t(const QgemvArgs &a, hipStream_t stream) {
   const auto kern = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, true>;
   const auto kern1 = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, false>;
   const int nblk = a.K / (4 * GS);
-  const int waves = pick_waves(nblk, MAXT / 64);
   const int tiles = (a.N + 15) / 16;
-  const int groups = (tiles + NT - 1) / NT;
+  const int cus = device_cu_count();
+  // Long K on few tile groups: split K in two halves across workgroups, so
+  // that the grid covers the CUs evenly (the halves are added into y).
+  const int ksplit = ((tiles + NT - 1) / NT < 2 * cus && a.K >= 8192) ? 2 : 1;
+  const int waves = pick_waves(nblk / ksplit, MAXT / 64);
+  const int groups = (tiles + NT - 1) / NT * ksplit;
+  if (ksplit == 2) {
+    const size_t n = (size_t)a.M * a.N;
+    const int fb = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(fb), dim3(256), 0, stream, a.y, n);
+  }
   // workgroups resident at once for this block size (cached per wave count)
   static int occ_cache[MAXT / 64 + 1] = {0};
   int occ = occ_cache[waves];
@@ -325,13 +351,13 @@ int launch_mfma_t(const QgemvArgs &a, hipStream_t stream) {
       occ = 1;
     occ_cache[waves] = occ;
   }
-  const int slots = occ * device_cu_count();
+  const int slots = occ * cus;
   if (groups <= slots)
     hipLaunchKernelGGL(kern1, dim3(groups), dim3(64 * waves), 0, stream, a.codes, a.scales,
-                       a.biases, a.x, a.y, a.M, a.N, a.K, groups);
+                       a.biases, a.x, a.y, a.M, a.N, a.K, groups, ksplit);
   else
     hipLaunchKernelGGL(kern, dim3(slots), dim3(64 * waves), 0, stream, a.codes, a.scales, a.biases,
-                       a.x, a.y, a.M, a.N, a.K, groups);
+                       a.x, a.y, a.M, a.N, a.K, groups, ksplit);
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
 }
 

@@ -160,15 +160,15 @@ def test_zero_codes(path):
 
 # ---------------------------------------------------------------- invariants
 
-@pytest.mark.parametrize("bits,gs,N", [(4, 64, 200), (2, 64, 200), (4, 128, 200), (4, 64, 4500),
-                                       (2, 128, 4500)])
+@pytest.mark.parametrize("bits,gs,N,K", [(4, 64, 200, 2048), (2, 64, 200, 2048), (4, 128, 200, 2048),
+                                         (4, 64, 4500, 2048), (2, 128, 4500, 2048),
+                                         (4, 128, 300, 8192), (2, 64, 150, 10240)])
 @pytest.mark.parametrize("path", ["dot", "mfma"])
-def test_row_of_m_row_call_equals_single_row_call_bitwise(path, bits, gs, N):
+def test_row_of_m_row_call_equals_single_row_call_bitwise(path, bits, gs, N, K):
     import torch
-    K = 2048
     p = synth.make_problem(synth.custom_shape(K, N, bits, gs, seed=77), m_max=16)
     d = DeviceProblem(p)
-    say(f"row invariance {path} bits={bits} gs={gs} N={N}")
+    say(f"row invariance {path} bits={bits} gs={gs} N={N} K={K}")
     singles = []
     for m in range(16):
         xm = d.x[m:m + 1].clone()
@@ -182,7 +182,7 @@ def test_row_of_m_row_call_equals_single_row_call_bitwise(path, bits, gs, N):
         assert np.array_equal(y, singles[:M]), f"M={M}"
 
 
-@pytest.mark.parametrize("name", ["square_k4096_n4096_4b_g64", "layer27b_gate"])
+@pytest.mark.parametrize("name", ["square_k4096_n4096_4b_g64", "layer27b_gate", "layer27b_down"])
 @pytest.mark.parametrize("path", ["dot", "mfma"])
 def test_repeated_calls_are_bitwise_identical(path, name):
     s = synth.WORKLOADS[name]
