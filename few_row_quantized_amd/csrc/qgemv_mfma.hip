@@ -40,11 +40,11 @@ namespace qgemv {
 namespace {
 
 
-template <int BITS, int GS, int NT, int MAXT, int SPI, bool PERSIST>
+template <int BITS, int GS, int NT, int MAXT, int SPI, int KS, bool PERSIST>
 __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *__restrict__ y,
-    int M, int N, int K, int ngroups, int ksplit) {
+    int M, int N, int K, int ngroups) {
   constexpr int CW = 128 / BITS;       // codes per 16-byte chunk
   constexpr int SCW = 4 * CW;          // codes per 64-byte super-chunk
   constexpr int DW = CW / 4;           // codes per dword
@@ -83,12 +83,12 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
 
   // One tile group (16*NT output columns over all of K) per call of `group`.
   auto group = [&](const int tg) {
-  // group tg = (tile group, part of K); with ksplit = 2 the two halves of K
-  // of a tile group are separate groups whose results are added into y
-  const int kpart = ksplit == 1 ? 0 : (tg & 1);
-  const int n_base = (ksplit == 1 ? tg : tg >> 1) * 16 * NT;
-  const int p_lo = kpart * NBLK / ksplit;
-  const int nbp = (kpart + 1) * NBLK / ksplit - p_lo;
+  // group tg = (tile group, part of K); with KS = 2 the two halves of K of a
+  // tile group are separate groups whose results are added into y
+  const int kpart = KS == 1 ? 0 : (tg & 1);
+  const int n_base = (KS == 1 ? tg : tg >> 1) * 16 * NT;
+  const int p_lo = KS == 1 ? 0 : (kpart ? NBLK >> 1 : 0);
+  const int nbp = KS == 1 ? NBLK : (kpart ? NBLK - (NBLK >> 1) : NBLK >> 1);
   // K-slice of this wave.  The slice order is rotated per workgroup (by
   // blockIdx/8: workgroups are dealt round-robin over the 8 XCDs) so that the
   // CUs sharing an L2 do not all read the same activation lines at the same
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     const int m = 4 * (l >> 4) + i;
     const int n = n_base + 16 * t + (l & 15);
     if (m < M && n < N) {
-      if (ksplit == 1) {
+      if constexpr (KS == 1) {
         y[(size_t)m * N + n] = s;
       } else {
         // y was zeroed before the launch and receives exactly two addends:
@@ -326,14 +326,19 @@ template <int BITS, int GS, int NT>
 int launch_mfma_t(const QgemvArgs &a, hipStream_t stream) {
   constexpr int MAXT = MfmaShape<BITS, GS, NT>::MAXT;
   constexpr int SPI = MfmaShape<BITS, GS, NT>::SPI;
-  const auto kern = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, true>;
-  const auto kern1 = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, false>;
+  const auto kern = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, true>;
+  const auto kern1 = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, false>;
+  const auto kern_s = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 2, true>;
+  const auto kern1_s = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 2, false>;
   const int nblk = a.K / (4 * GS);
   const int tiles = (a.N + 15) / 16;
   const int cus = device_cu_count();
-  // Long K on few tile groups: split K in two halves across workgroups, so
-  // that the grid covers the CUs evenly (the halves are added into y).
-  const int ksplit = ((tiles + NT - 1) / NT < 2 * cus && a.K >= 8192) ? 2 : 1;
+  // Few tile groups for the CUs: split K in two halves across workgroups
+  // (added into y), for long K when there are under two groups per CU, and
+  // for any K of at least 2048 when groups cover at most a quarter of the CUs.
+  const int tgroups = (tiles + NT - 1) / NT;
+  const int ksplit =
+      ((tgroups < 2 * cus && a.K >= 8192) || (4 * tgroups <= cus && a.K >= 2048)) ? 2 : 1;
   const int waves = pick_waves(nblk / ksplit, MAXT / 64);
   const int groups = (tiles + NT - 1) / NT * ksplit;
   if (ksplit == 2) {
@@ -352,12 +357,10 @@ int launch_mfma_t(const QgemvArgs &a, hipStream_t stream) {
     occ_cache[waves] = occ;
   }
   const int slots = occ * cus;
-  if (groups <= slots)
-    hipLaunchKernelGGL(kern1, dim3(groups), dim3(64 * waves), 0, stream, a.codes, a.scales,
-                       a.biases, a.x, a.y, a.M, a.N, a.K, groups, ksplit);
-  else
-    hipLaunchKernelGGL(kern, dim3(slots), dim3(64 * waves), 0, stream, a.codes, a.scales, a.biases,
-                       a.x, a.y, a.M, a.N, a.K, groups, ksplit);
+  const bool single = groups <= slots;
+  const auto k = ksplit == 1 ? (single ? kern1 : kern) : (single ? kern1_s : kern_s);
+  hipLaunchKernelGGL(k, dim3(single ? groups : slots), dim3(64 * waves), 0, stream, a.codes,
+                     a.scales, a.biases, a.x, a.y, a.M, a.N, a.K, groups);
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
 }
 
