@@ -35,9 +35,9 @@ namespace {
 
 constexpr int kDotThreads = 256;
 constexpr int kDotWaves = kDotThreads / 64;
-constexpr int kMaxPasses = 4;  // lane passes (of 64 chunks) per LDS stage
+constexpr int kMaxPasses = 3;  // lane passes (of 64 chunks) per LDS stage, at most
 
-template <int BITS, int M, int R, int NSUB>
+template <int BITS, int M, int R, int NSUB, int P>
 __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *__restrict__ y,
@@ -81,9 +81,12 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
     // an L2 do not all read the same activation lines at the same moment.
     const int rot = (int)(((blockIdx.x >> 3) * 64u) % (unsigned)units);
     auto unit_of = [&](int uu) { return uu + rot < units ? uu + rot : uu + rot - units; };
-    uint4 xa[2][CW / 8];
+    // staging units per thread loaded ahead: one at M = 1 (a stage holds at
+    // most 256 chunks), two otherwise
+    constexpr int JU = M == 1 ? 1 : 2;
+    uint4 xa[JU][CW / 8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < JU; ++j) {
       const int u = unit_of(min((int)threadIdx.x + kDotThreads * j, units - 1));
       const int m = u / nc;
       const int cl = u - m * nc;
@@ -93,10 +96,10 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
     }
 
     // 2. code and metadata loads for this stage, in the order they are consumed
-    uint4 cw[kMaxPasses][R];
-    uint32_t sr[kMaxPasses][R][NSUB], br[kMaxPasses][R][NSUB];
+    uint4 cw[P][R];
+    uint32_t sr[P][R][NSUB], br[P][R][NSUB];
 #pragma unroll
-    for (int t = 0; t < kMaxPasses; ++t) {
+    for (int t = 0; t < P; ++t) {
       if (t < npass) {
         const int c = min(lane + 64 * t, nc - 1);
 #pragma unroll
@@ -171,11 +174,11 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
       for (int s = 0; s < NSUB; ++s) xsl[(m * NSUB + s) * kch + cl] = ssum[s];
     };
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < JU; ++j) {
       const int uu = threadIdx.x + kDotThreads * j;
       if (uu < units) stage_unit(unit_of(uu), xa[j]);
     }
-    for (int uu = threadIdx.x + 2 * kDotThreads; uu < units; uu += kDotThreads) {
+    for (int uu = threadIdx.x + JU * kDotThreads; uu < units; uu += kDotThreads) {
       const int u = unit_of(uu);
       const int m = u / nc;
       const int cl = u - m * nc;
@@ -189,7 +192,7 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
 
     // 4. multi-row dot products over this stage, in load order
 #pragma unroll
-    for (int t = 0; t < kMaxPasses; ++t) {
+    for (int t = 0; t < P; ++t) {
       const int c = lane + 64 * t;
       if (t >= npass || c >= nc) continue;
 #pragma unroll
@@ -264,34 +267,45 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
   }
 }
 
-template <int BITS, int M, int R, int NSUB>
-int launch_dot_t(const QgemvArgs &a, hipStream_t stream) {
+template <int BITS, int M, int R, int NSUB, int P>
+int launch_dot_tp(const QgemvArgs &a, hipStream_t stream) {
   constexpr int CW = 128 / BITS;
   constexpr int QUADS = CW / 8;
   const int NC = a.K / CW;
   // Stages always hold whole multiples of 64 chunks, so lane l processes
   // chunks l, l+64, l+128, ... in the same order for every M (row results do
-  // not depend on M).  Up to kMaxPasses*64 chunks per stage, within the LDS
-  // budget; 64 chunks always fit (at most 139 KiB for M = 16, 2-bit codes).
+  // not depend on M).  Up to P*64 chunks per stage, within the LDS budget;
+  // 64 chunks always fit (at most 139 KiB for M = 16, 2-bit codes).
   const size_t per_chunk = (size_t)M * (QUADS * 16 + NSUB * 4);
   int kch = 64 * (int)(kDotLdsBudget / (64 * per_chunk));
   // at most two staging units per thread (loaded ahead of the codes)
   const int kch_units = 64 * ((2 * kDotThreads / M) / 64);
   if (kch > kch_units) kch = kch_units;
   if (kch < 64) kch = 64;
-  if (kch > 64 * kMaxPasses) kch = 64 * kMaxPasses;
+  if (kch > 64 * P) kch = 64 * P;
   if (kch > NC) kch = NC;  // one stage holds the whole row
   const size_t lds = per_chunk * (size_t)kch;
   if (lds > kLdsMax) return QGEMV_EUNSUPPORTED;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&qgemv_dot_kernel<BITS, M, R, NSUB>),
+      reinterpret_cast<const void *>(&qgemv_dot_kernel<BITS, M, R, NSUB, P>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
   if (attr != hipSuccess) return QGEMV_EHIP;
   const int rows_per_block = kDotWaves * R;
   const int blocks = (a.N + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL((qgemv_dot_kernel<BITS, M, R, NSUB>), dim3(blocks), dim3(kDotThreads), lds,
+  hipLaunchKernelGGL((qgemv_dot_kernel<BITS, M, R, NSUB, P>), dim3(blocks), dim3(kDotThreads), lds,
                      stream, a.codes, a.scales, a.biases, a.x, a.y, a.N, a.K, a.group_size, kch);
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}
+
+// Lane passes per stage: two when a row has at most 128 chunks (K <= 4096 at
+// 4 bits), which keeps fewer code registers live; three otherwise.  Only for
+// M <= 4, where the dot path is the one that runs.
+template <int BITS, int M, int R, int NSUB>
+int launch_dot_t(const QgemvArgs &a, hipStream_t stream) {
+  if constexpr (M <= 4) {
+    if (a.K / (128 / BITS) <= 128) return launch_dot_tp<BITS, M, R, NSUB, 2>(a, stream);
+  }
+  return launch_dot_tp<BITS, M, R, NSUB, kMaxPasses>(a, stream);
 }
 
 // rows per wave for each M: enough rows to share each x read (LDS traffic per
