@@ -81,9 +81,10 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
     // an L2 do not all read the same activation lines at the same moment.
     const int rot = (int)(((blockIdx.x >> 3) * 64u) % (unsigned)units);
     auto unit_of = [&](int uu) { return uu + rot < units ? uu + rot : uu + rot - units; };
-    // staging units per thread loaded ahead: one at M = 1 (a stage holds at
-    // most 256 chunks), two otherwise
-    constexpr int JU = M == 1 ? 1 : 2;
+    // staging units per thread loaded ahead: a stage holds at most 64*P
+    // chunks, i.e. M*64*P units, so one unit per thread while M*P <= 4, two
+    // otherwise (the launcher keeps M*kch within two units per thread)
+    constexpr int JU = M * P <= 4 ? 1 : 2;
     uint4 xa[JU][CW / 8];
 #pragma unroll
     for (int j = 0; j < JU; ++j) {
