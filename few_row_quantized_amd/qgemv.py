@@ -25,6 +25,8 @@ EALIGN = -3
 EHIP = -4
 
 MAX_M = 16
+MAX_K = 131072
+MAX_N = 4194304
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemv.so")
 

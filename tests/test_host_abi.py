@@ -25,6 +25,22 @@ def test_header_declares_the_boundary():
         assert must in names
 
 
+def test_binding_limits_match_the_header():
+    src = open(HEADER).read()
+    for name, val in (("QGEMV_MAX_M", q.MAX_M), ("QGEMV_MAX_K", q.MAX_K), ("QGEMV_MAX_N", q.MAX_N)):
+        m = re.search(r"#define\s+%s\s+(\d+)" % name, src)
+        assert m and int(m.group(1)) == val, name
+
+
+def test_shapes_at_the_limits_are_accepted_and_beyond_rejected():
+    L = q.lib()
+    # validation only (fake pointers): the limits pass shape checks, one past fails
+    assert L.qgemv_select(q.MAX_M, 64, q.MAX_K, 4, 128) in (q.PATH_DOT, q.PATH_MFMA)
+    assert L.qgemv_select(1, q.MAX_N, 128, 4, 32) in (q.PATH_DOT, q.PATH_MFMA)
+    assert L.qgemv_select(1, q.MAX_N + 1, 128, 4, 32) == q.EINVAL
+    assert L.qgemv_select(1, 64, q.MAX_K + 128, 4, 128) == q.EINVAL
+
+
 def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(q.LIB_PATH)
     for name in declared_functions():
