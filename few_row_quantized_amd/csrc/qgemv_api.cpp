@@ -1,8 +1,14 @@
 // C ABI of libqgemv: argument validation, path selection, launch.
-// The library holds no mutable state, allocates nothing and never
-// synchronizes; every entry point only validates and enqueues.
+// The library allocates no device memory and never synchronizes; every entry
+// point only validates and enqueues.  Its only host state is caches of device
+// properties (CU count, occupancy) and of the per-device LDS limit granted to
+// each kernel.
 
 #include <stdint.h>
+
+#include <mutex>
+#include <utility>
+#include <vector>
 
 #include "qgemv_internal.h"
 #include "qgemv_select_table.h"
@@ -22,6 +28,23 @@ int device_cu_count() {
     cache[dev] = n;
   }
   return cache[dev];
+}
+
+// Functions already granted the LDS limit, per device (a small table; a
+// function is added once per device it runs on).
+bool allow_max_dynamic_lds(const void *func) {
+  static std::mutex mu;
+  static std::vector<std::pair<int, const void *>> done;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto &e : done)
+    if (e.first == dev && e.second == func) return true;
+  if (hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax) !=
+      hipSuccess)
+    return false;
+  done.emplace_back(dev, func);
+  return true;
 }
 
 }  // namespace qgemv

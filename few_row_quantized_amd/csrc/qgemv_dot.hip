@@ -287,10 +287,8 @@ int launch_dot_tp(const QgemvArgs &a, hipStream_t stream) {
   if (kch > NC) kch = NC;  // one stage holds the whole row
   const size_t lds = per_chunk * (size_t)kch;
   if (lds > kLdsMax) return QGEMV_EUNSUPPORTED;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&qgemv_dot_kernel<BITS, M, R, NSUB, P>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
-  if (attr != hipSuccess) return QGEMV_EHIP;
+  if (!allow_max_dynamic_lds(reinterpret_cast<const void *>(&qgemv_dot_kernel<BITS, M, R, NSUB, P>)))
+    return QGEMV_EHIP;
   const int rows_per_block = kDotWaves * R;
   const int blocks = (a.N + rows_per_block - 1) / rows_per_block;
   hipLaunchKernelGGL((qgemv_dot_kernel<BITS, M, R, NSUB, P>), dim3(blocks), dim3(kDotThreads), lds,

@@ -26,6 +26,10 @@ constexpr size_t kDotLdsBudget = 80 * 1024;
 // Compute units of the current device (cached per device id).
 int device_cu_count();
 
+// Allow `func` up to kLdsMax bytes of dynamic LDS on the current device (set
+// once per device and function).  Returns false if the runtime refuses.
+bool allow_max_dynamic_lds(const void *func);
+
 // Launchers: enqueue on `stream`, return QGEMV_OK / QGEMV_EUNSUPPORTED / QGEMV_EHIP.
 int launch_dot(const QgemvArgs &a, hipStream_t stream);
 int launch_mfma(const QgemvArgs &a, hipStream_t stream);
