@@ -9,8 +9,10 @@ MALL), so every call streams its weights from HBM.
 
 Timing: the K timed steps are captured into one HIP graph (a dependent chain
 of launches on one stream, no host in the loop) and replayed between two
-events after W warm-up steps.  Per-M chains (one graph of L launches for each
-M) give time(M)/time(1) and the average launch duration of each kernel.
+events after W warm-up steps.  Per-cell chains (one graph of L launches for
+each M and each forced path, walked in interleaved rounds, median over the
+rounds) give time(M)/time(1) for the dispatcher's choice and for each path,
+and the average launch duration of each kernel.
 
 Prints ONE JSON line (rank 0).  --gpus N with N > 1 exits with a message:
 this build runs on one GPU.
@@ -21,6 +23,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -31,6 +34,7 @@ from few_row_quantized_amd import accounting, synth  # noqa: E402
 
 METRIC = "effective weight GB/s (% of HBM peak) and time(M)/time(1) at M=1..16"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK = 2.5e15  # dense bf16 MFMA flop/s of one MI355X
 
 
 def log(msg):
@@ -45,7 +49,8 @@ def parse():
     ap.add_argument("--workload", default="square_k4096_n4096_4b_g64")
     ap.add_argument("--m-values", default=None, help="comma list; default: the workload's")
     ap.add_argument("--pool-mib", type=int, default=1024)
-    ap.add_argument("--chain", type=int, default=400, help="launches per per-M chain")
+    ap.add_argument("--chain", type=int, default=400, help="launches per per-cell chain")
+    ap.add_argument("--rounds", type=int, default=5, help="interleaved rounds over the cells")
     ap.add_argument("--path", default="auto", choices=["auto", "dot", "mfma"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -105,10 +110,10 @@ def main():
 
     counter = [0]
 
-    def launch(M):
+    def launch(M, path=args.path):
         i = counter[0] % copies
         counter[0] += 1
-        q.qgemv_run_path(args.path, pool.codes[i], pool.scales[i], pool.biases[i], x, ys[M], M,
+        q.qgemv_run_path(path, pool.codes[i], pool.scales[i], pool.biases[i], x, ys[M], M,
                          s.N, s.K, s.bits, s.group_size)
 
     def capture(fn):
@@ -118,6 +123,7 @@ def main():
         return g
 
     def time_graph(g, reps=1):
+        # the kernels run on torch's current stream, which is where these events are recorded
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -142,20 +148,53 @@ def main():
     ms_per_step = t_main / args.steps * 1e3
     value = (W * len(ms) * args.steps) / t_main / 1e9
 
-    # per-M chains: average launch duration of each configuration
-    per_m = {}
+    # per-cell chains, one cell per (M, forced path): one graph of `chain`
+    # launches each, replayed once to warm up and then once per round, the
+    # rounds walking every cell in turn (interleaved), median over rounds
+    forced = ["dot", "mfma"] if args.path == "auto" else [args.path]
+    cells = [(M, pth) for M in ms for pth in forced
+             if q.qgemv_path_supported(pth, M, s.N, s.K, s.bits, s.group_size)]
+    graphs = {c: capture(lambda c=c: [launch(c[0], c[1]) for _ in range(args.chain)]) for c in cells}
+    for c in cells:
+        time_graph(graphs[c])
+    samples = {c: [] for c in cells}
+    for _ in range(args.rounds):
+        for c in cells:
+            samples[c].append(time_graph(graphs[c]) / args.chain)
+    t_cell = {c: statistics.median(v) for c, v in samples.items()}
+    del graphs
+
+    ceiling = None if args.no_ceiling else measure_ceiling(W, copies, args.chain, capture, time_graph)
+
+    def cell_json(M, pth, t, t1):
+        alg = accounting.algorithmic_bytes(M, s.N, s.K, s.bits, s.group_size)
+        d = {"path": pth, "us": round(t * 1e6, 4),
+             "us_min_max_over_rounds": [round(min(samples[(M, pth)]) * 1e6, 4),
+                                        round(max(samples[(M, pth)]) * 1e6, 4)],
+             "weight_GBps": round(W / t / 1e9, 1),
+             "pct_hbm_peak": round(100 * W / t / 1e9 / HBM_PEAK_GBS, 2),
+             "alg_GBps": round(alg / t / 1e9, 1),
+             "t_over_t1": round(t / t1, 4) if t1 else None,
+             "mfma_util_useful": round(accounting.useful_flops(M, s.N, s.K) / t / MFMA_BF16_PEAK, 6),
+             "mfma_util_issued": round(2 * 16 * s.N * s.K / t / MFMA_BF16_PEAK, 6)
+             if pth == "mfma" else 0.0}
+        if ceiling:
+            d["pct_stream_probe"] = round(100 * ceiling["stream_probe_us"] / (t * 1e6), 2)
+        return d
+
+    # the dispatcher's choice per M is one of the forced cells (the same launch)
+    per_m = {M: t_cell[(M, paths[M])] for M in ms}
     for M in ms:
-        g = capture(lambda: [launch(M) for _ in range(args.chain)])
-        time_graph(g)  # warm
-        t = time_graph(g, reps=2) / (2 * args.chain)
-        per_m[M] = t
-        log(f"[bench] M={M:2d} path={paths[M]:4s} {t * 1e6:8.3f} us/launch  "
-            f"{W / t / 1e9:8.1f} GB/s")
+        log(f"[bench] M={M:2d} path={paths[M]:4s} {per_m[M] * 1e6:8.3f} us/launch  "
+            f"{W / per_m[M] / 1e9:8.1f} GB/s")
     t1 = per_m.get(1, per_m[min(ms)])
-    per_m_json = {str(M): {"path": paths[M], "us": round(per_m[M] * 1e6, 4),
-                           "weight_GBps": round(W / per_m[M] / 1e9, 1),
-                           "pct_hbm_peak": round(100 * W / per_m[M] / 1e9 / HBM_PEAK_GBS, 2),
-                           "t_over_t1": round(per_m[M] / t1, 4)} for M in ms}
+    per_m_json = {str(M): cell_json(M, paths[M], per_m[M], t1) for M in ms}
+    forced_json = {}
+    for pth in forced:
+        mp = [M for M in ms if (M, pth) in t_cell]
+        if mp:
+            t1p = t_cell[(min(mp), pth)] if min(mp) == min(ms) else None
+            forced_json[pth] = {str(M): cell_json(M, pth, t_cell[(M, pth)], t1p) for M in mp}
 
     # dominant kernel = the (path, M) configuration with the largest time per step
     Mdom = max(ms, key=lambda M: per_m[M])
@@ -165,8 +204,6 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(s.name, Mdom),
                 "kernel": f"qgemv_{paths[Mdom]}_kernel M={Mdom}",
                 "bytes_per_launch": alg, "avg_launch_us": round(per_m[Mdom] * 1e6, 4)}
-
-    ceiling = None if args.no_ceiling else measure_ceiling(W, copies, args.chain, capture, time_graph)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -179,11 +216,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": s.name, "K": s.K, "N": s.N, "bits": s.bits,
                    "group_size": s.group_size, "m_values": ms, "path": args.path,
-                   "weight_bytes": W, "pool_copies": copies,
+                   "weight_bytes": W, "pool_copies": copies, "seed": p.seed,
                    "timing": "one HIP graph of K steps; each call on the next pool copy"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "t8_over_t1": per_m_json.get("8", {}).get("t_over_t1"),
         "per_m": per_m_json,
+        "forced_paths": forced_json,
+        "schedule": {"cells": [list(c) for c in cells], "rounds": args.rounds, "chain": args.chain},
         "roofline": roofline,
         "ceiling": ceiling,
         "cpu_baseline": cpu,
@@ -243,30 +282,56 @@ def measure_ceiling(W, copies, chain, capture, time_graph):
             "launch_floor_us_64KiB": round(tf * 1e6, 4)}
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(p, ms, W, budget_s):
     """The fp64 oracle (as it stands) on the host cores: repeated verify steps
-    over the same workload until ~budget_s of CPU time is spent."""
+    (one oracle call per M) until about 2/3 of budget_s is spent with the BLAS
+    pool at its default size, then at least three steps with it pinned to one
+    thread.  Per M the median call time is taken; the value is the weight
+    bytes of one step over the sum of those medians."""
     sys.path.insert(0, ROOT)
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count()
+    from threadpoolctl import threadpool_info, threadpool_limits
     s = p.shape
-    calls = 0
-    t0 = time.perf_counter()
-    while True:
-        for M in ms:
-            oracle.qgemv_reference(p.codes, p.scales, p.biases, p.x, M, s.N, s.K, s.bits, s.group_size)
-            calls += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(W * calls / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{calls} oracle calls ({calls // len(ms)} verify steps over M={ms}) of "
-                      f"{s.name} in {dt:.1f} s; numpy fp64 dequantize + BLAS matmul"}
+
+    def blas_threads():
+        return max([i.get("num_threads", 1) for i in threadpool_info()
+                    if i.get("user_api") == "blas"] or [1])
+
+    def run(budget, min_steps):
+        times = {M: [] for M in ms}
+        t0 = time.perf_counter()
+        steps = 0
+        while steps < min_steps or time.perf_counter() - t0 < budget:
+            for M in ms:
+                c0 = time.perf_counter()
+                oracle.qgemv_reference(p.codes, p.scales, p.biases, p.x, M, s.N, s.K, s.bits,
+                                       s.group_size)
+                times[M].append(time.perf_counter() - c0)
+            steps += 1
+        med = {M: statistics.median(v) for M, v in times.items()}
+        return {"GBps": round(W * len(ms) / sum(med.values()) / 1e9, 4), "steps": steps,
+                "median_ms_per_call": {str(M): round(v * 1e3, 2) for M, v in med.items()},
+                "wall_s": round(time.perf_counter() - t0, 1)}
+
+    threads = blas_threads()
+    multi = run(budget_s * 2 / 3, 3)
+    with threadpool_limits(limits=1, user_api="blas"):
+        single = run(0.0, 3)
+    return {"value": multi["GBps"], "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{multi['steps']} verify steps (one oracle call per M in {ms}) of {s.name}; "
+                      f"median call time per M; numpy fp64 unpack + dequantize + BLAS matmul",
+            "median_ms_per_call": multi["median_ms_per_call"], "wall_s": multi["wall_s"],
+            "one_thread": single, "cpu_count": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 if __name__ == "__main__":
