@@ -206,6 +206,14 @@ def special_problem(K: int, N: int, bits: int, group_size: int, M: int, kind: st
     return p
 
 
+def make_residual(M: int, N: int, seed: int) -> np.ndarray:
+    """Residual input of the fused residual sum: float32 [M, N] ~ N(0, 1), drawn
+    from its own stream (seed + 1_000_003) so the problem's other draws do not
+    change.  Its magnitude is that of y on the 4-bit workloads (|y| ~ 1-2)."""
+    rng = np.random.default_rng(seed + 1_000_003)
+    return rng.standard_normal(size=(M, N)).astype(np.float32)
+
+
 def onehot_column(m: int, K: int) -> int:
     return (m * 37 + 5) % K
 

@@ -5,7 +5,9 @@ from .qgemv_oracle import (  # noqa: F401
     check_close,
     dequantize,
     fp16_bits_to_f64,
+    qgemv_add_reference,
     qgemv_reference,
+    residual_f64,
     tolerance,
     unpack_codes,
 )

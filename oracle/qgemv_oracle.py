@@ -32,6 +32,14 @@ times <= ~45-bit significands).  So in practice only the K-term summation
 rounds, at K * 2^-53 relative at worst -- twelve orders of magnitude below the
 1e-3 tolerance.
 
+The fused residual sum ("metal : few-row MMA mat-mul and batched copies for
+speculative decoding", Overview: a fusion table entry where MUL_MAT + ADD
+writes the residual sum from the MMA store) is the same product plus an fp32
+residual tensor of the output's shape [M, N]: y[m,n] = (x W^T)[m,n] + r[m,n],
+computed here in fp64 (fp32 -> fp64 is exact).  The residual is read as
+having the output's layout, since the ADD consumes the mat-mul's result
+element by element.
+
 Parity of y is pinned by closed forms, invariants and exact rational brute
 force (the pages print no worked y values); see tests/test_oracle.py.
 """
@@ -47,6 +55,8 @@ __all__ = [
     "unpack_codes",
     "dequantize",
     "qgemv_reference",
+    "residual_f64",
+    "qgemv_add_reference",
     "abs_product_sum",
     "tolerance",
     "check_close",
@@ -127,6 +137,25 @@ def qgemv_reference(codes, scales, biases, x_bits, M: int, N: int, K: int, bits:
     return y
 
 
+def residual_f64(residual, M: int, N: int, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """fp32 residual [>=M, N] -> float64 [M, len(rows)] (exact), columns `rows` (default all N)."""
+    r = np.asarray(residual, dtype=np.float32)
+    if r.ndim != 2 or r.shape[0] < M or r.shape[1] != N:
+        raise ValueError("residual must be [>=M, N] float32")
+    r = r[:M].astype(np.float64)
+    return r if rows is None else r[:, np.asarray(rows, dtype=np.int64)]
+
+
+def qgemv_add_reference(codes, scales, biases, x_bits, residual, M: int, N: int, K: int, bits: int,
+                        group_size: int, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Fused residual sum in fp64: y_ref[m, j] = sum_k x[m,k] w[n_j,k] + r[m, n_j].
+
+    residual: float32 [>=M, N], the output's layout; the first M rows are used.
+    """
+    prod = qgemv_reference(codes, scales, biases, x_bits, M, N, K, bits, group_size, rows=rows)
+    return prod + residual_f64(residual, M, N, rows)
+
+
 def abs_product_sum(codes, scales, biases, x_bits, M: int, N: int, K: int, bits: int,
                     group_size: int, rows: Optional[Sequence[int]] = None) -> np.ndarray:
     """sum_k |x[m,k] * w[n,k]| in fp64 (the scale of the tolerance)."""
@@ -140,19 +169,32 @@ def abs_product_sum(codes, scales, biases, x_bits, M: int, N: int, K: int, bits:
     return out
 
 
-def tolerance(abs_sum: np.ndarray, rel: float = 1e-3, abs_floor: float = 1e-6) -> np.ndarray:
-    """Per-element bound |y - y_ref| <= rel * sum_k |x_k w_k| + abs_floor."""
-    return rel * np.asarray(abs_sum, dtype=np.float64) + abs_floor
+# Relative size of the rounding that adding the residual in fp32 may add: the
+# sum is rounded once or twice (half an fp32 ulp, 2^-24 relative, each time)
+# and its magnitude is at most |r| + sum_k |x_k w_k|.
+ADD_ROUNDING = 2.0 ** -23
 
 
-def check_close(y_test, y_ref, abs_sum, rel: float = 1e-3, abs_floor: float = 1e-6):
+def tolerance(abs_sum: np.ndarray, rel: float = 1e-3, abs_floor: float = 1e-6,
+              residual_abs: Optional[np.ndarray] = None) -> np.ndarray:
+    """Per-element bound |y - y_ref| <= rel * sum_k |x_k w_k| + abs_floor, plus,
+    for the fused residual sum, 2^-23 * (|r| + sum_k |x_k w_k|)."""
+    a = np.asarray(abs_sum, dtype=np.float64)
+    tol = rel * a + abs_floor
+    if residual_abs is not None:
+        tol = tol + ADD_ROUNDING * (np.abs(np.asarray(residual_abs, dtype=np.float64)) + a)
+    return tol
+
+
+def check_close(y_test, y_ref, abs_sum, rel: float = 1e-3, abs_floor: float = 1e-6,
+                residual_abs: Optional[np.ndarray] = None):
     """Return (ok, worst_ratio, index).  worst_ratio = max |dy| / tol (<= 1 passes).
-    NaN/Inf in y_test fail."""
+    NaN/Inf in y_test fail.  residual_abs: |r| for the fused residual sum."""
     y_test = np.asarray(y_test, dtype=np.float64)
     if not np.all(np.isfinite(y_test)):
         bad = np.argwhere(~np.isfinite(y_test))[0]
         return False, float("inf"), tuple(int(i) for i in bad)
-    tol = tolerance(abs_sum, rel, abs_floor)
+    tol = tolerance(abs_sum, rel, abs_floor, residual_abs)
     ratio = np.abs(y_test - y_ref) / tol
     idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
     worst = float(ratio[idx])

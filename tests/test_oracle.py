@@ -327,6 +327,118 @@ def test_pins_catch_transposed_product(monkeypatch):
     assert not _pin_suite()
 
 
+# ---------------------------------------------------------------- fused residual sum
+
+def run_add(p: synth.Problem, M: int, r, rows=None):
+    return oracle.qgemv_add_reference(p.codes, p.scales, p.biases, p.x, r, M, p.N, p.K, p.bits,
+                                      p.group_size, rows=rows)
+
+
+def distinct_residual(M: int, N: int) -> np.ndarray:
+    """Every element different and exactly representable: r[m, n] = (N*m + n)/4 - 3."""
+    return (np.arange(M * N, dtype=np.float32).reshape(M, N) * np.float32(0.25) - np.float32(3.0))
+
+
+def test_add_zero_activations_gives_the_residual():
+    # x = 0: every product vanishes and y[m, n] is r[m, n] itself, in the
+    # output's [M, N] layout
+    K, N, M = 256, 24, 3
+    p = synth.make_problem(synth.custom_shape(K, N, 4, 64, seed=21), m_max=M)
+    p.x[:] = 0
+    r = distinct_residual(M, N)
+    y = run_add(p, M, r)
+    assert y.tolist() == [[(N * m + n) / 4 - 3 for n in range(N)] for m in range(M)]
+
+
+@pytest.mark.parametrize("bits,gs", [(4, 64), (2, 32)])
+def test_add_onehot_x_gives_dequantized_weight_plus_residual(bits, gs):
+    K, N, M = 256, 16, 2
+    p = synth.make_problem(synth.custom_shape(K, N, bits, gs, seed=23), m_max=M)
+    r = distinct_residual(M, N)
+    ks = [gs - 1, K - 1]
+    p.x[:] = 0
+    for m, k in enumerate(ks):
+        p.x[m, k] = 0x3F80  # bf16 1.0
+    y = run_add(p, M, r)
+    for m, k in enumerate(ks):
+        for n in range(N):
+            qk = bitstream_codes(p.codes[n], K, bits)[k]
+            want = (frac_fp16(int(p.scales[n, k // gs])) * qk + frac_fp16(int(p.biases[n, k // gs]))
+                    + Fraction(float(r[m, n])))
+            assert y[m, n] == float(want)
+
+
+@pytest.mark.parametrize("bits,gs,K,N,M", [(4, 64, 192, 7, 3), (2, 128, 256, 5, 2)])
+def test_add_matches_exact_rational_brute_force(bits, gs, K, N, M):
+    p = synth.make_problem(synth.custom_shape(K, N, bits, gs, seed=200 + K + N), m_max=M)
+    r = synth.make_residual(M, N, seed=p.seed)
+    y = run_add(p, M, r)
+    ex = exact_y(p, M)
+    absum = oracle.abs_product_sum(p.codes, p.scales, p.biases, p.x, M, N, K, bits, gs)
+    for m in range(M):
+        for n in range(N):
+            want = ex[m][n] + Fraction(float(r[m, n]))
+            bound = Fraction(K + 1) * Fraction(2) ** -52 * (Fraction(absum[m, n]) + abs(Fraction(float(r[m, n]))))
+            assert abs(Fraction(y[m, n]) - want) <= bound
+
+
+def test_add_sampled_rows_match_full_result():
+    p = synth.make_problem(synth.WORKLOADS["tiny_k256_n512_4b_g64"])
+    r = synth.make_residual(4, p.N, seed=p.seed)
+    y = run_add(p, 4, r)
+    rows = [0, 7, 300, 511]
+    assert np.array_equal(run_add(p, 4, r, rows=rows), y[:, rows])
+
+
+def test_add_tolerance_hand_value():
+    # sum |x w| = 1, |r| = 3: 1e-3 + 1e-6 + 2^-23 * (3 + 1)
+    tol = oracle.tolerance(np.array([1.0]), residual_abs=np.array([-3.0]))[0]
+    assert tol == 1e-3 + 1e-6 + 4.0 * 2.0 ** -23
+    ok, _, _ = oracle.check_close(np.array([4.0 + 1.0005e-3]), np.array([4.0]), np.array([1.0]),
+                                  residual_abs=np.array([3.0]))
+    assert ok
+    ok, _, _ = oracle.check_close(np.array([4.0 + 1.01e-3]), np.array([4.0]), np.array([1.0]),
+                                  residual_abs=np.array([3.0]))
+    assert not ok
+
+
+def _add_pin_suite():
+    try:
+        test_add_zero_activations_gives_the_residual()
+        test_add_onehot_x_gives_dequantized_weight_plus_residual(4, 64)
+        test_add_matches_exact_rational_brute_force(4, 64, 192, 7, 3)
+    except (AssertionError, ValueError):
+        return False
+    return True
+
+
+def _res_negated(residual, M, N, rows=None):
+    return -qo._orig_residual(residual, M, N, rows)
+
+
+def _res_transposed(residual, M, N, rows=None):
+    # the [M, N] buffer read as if it were [N, M]
+    r = np.asarray(residual, dtype=np.float32)[:M].reshape(N, M).T.astype(np.float64)
+    return r if rows is None else r[:, rows]
+
+
+def _res_row0_broadcast(residual, M, N, rows=None):
+    r = qo._orig_residual(residual, M, N, rows)
+    return np.broadcast_to(r[:1], r.shape).copy()
+
+
+def _res_dropped(residual, M, N, rows=None):
+    return np.zeros_like(qo._orig_residual(residual, M, N, rows))
+
+
+@pytest.mark.parametrize("mutant", [_res_negated, _res_transposed, _res_row0_broadcast, _res_dropped])
+def test_add_pins_catch_planted_mistakes(monkeypatch, mutant):
+    assert _add_pin_suite(), "pins must pass on the unmodified oracle"
+    monkeypatch.setattr(qo, "_orig_residual", qo.residual_f64, raising=False)
+    monkeypatch.setattr(qo, "residual_f64", mutant)
+    assert not _add_pin_suite(), f"planted mistake {mutant.__name__} went unnoticed"
+
+
 # ---------------------------------------------------------------- byte model (pages' printed values)
 
 def test_byte_model_matches_pages_printed_values():
