@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--hot", action="store_true", help="reuse one weight copy (cache-resident)")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
+    ap.add_argument("--no-residual", action="store_true",
+                    help="skip the fused residual sum (MUL_MAT + ADD) comparison")
     return ap.parse_args()
 
 
@@ -165,6 +167,9 @@ def main():
     del graphs
 
     ceiling = None if args.no_ceiling else measure_ceiling(W, copies, args.chain, capture, time_graph)
+    residual = None
+    if not args.no_residual:
+        residual = measure_residual_sum(s, p, ms, paths, pool, x, copies, args, capture, time_graph)
 
     def cell_json(M, pth, t, t1):
         alg = accounting.algorithmic_bytes(M, s.N, s.K, s.bits, s.group_size)
@@ -225,9 +230,70 @@ def main():
         "schedule": {"cells": [list(c) for c in cells], "rounds": args.rounds, "chain": args.chain},
         "roofline": roofline,
         "ceiling": ceiling,
+        "residual_sum": residual,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def measure_residual_sum(s, p, ms, paths, pool, x, copies, args, capture, time_graph):
+    """The fused residual sum y = x W^T + r against the plain product and
+    against the plain product followed by a separate fp32 add (torch's
+    elementwise kernel, i.e. the unfused MUL_MAT then ADD): per M, the
+    dispatcher's path, chains of `chain` launches on the rotating pool,
+    interleaved rounds, median over rounds."""
+    import numpy as np
+    import torch
+    from few_row_quantized_amd import qgemv as q
+    r = torch.from_numpy(synth.make_residual(max(ms), s.N, seed=p.seed)).cuda()
+    rs = {M: r[:M].contiguous() for M in ms}
+    ys = {M: torch.empty((M, s.N), dtype=torch.float32, device="cuda") for M in ms}
+    ts = {M: torch.empty((M, s.N), dtype=torch.float32, device="cuda") for M in ms}
+    ctr = [0]
+
+    def one(M, kind):
+        i = ctr[0] % copies
+        ctr[0] += 1
+        if kind == "fused":
+            q.qgemv_run_path_add(paths[M], pool.codes[i], pool.scales[i], pool.biases[i], x, rs[M],
+                                 ys[M], M, s.N, s.K, s.bits, s.group_size)
+        else:
+            q.qgemv_run_path(paths[M], pool.codes[i], pool.scales[i], pool.biases[i], x, ts[M], M,
+                             s.N, s.K, s.bits, s.group_size)
+            if kind == "separate":
+                torch.add(ts[M], rs[M], out=ys[M])
+
+    kinds = ("plain", "fused", "separate")
+    cells = [(M, k) for M in ms for k in kinds]
+    for c in cells:
+        one(*c)
+    torch.cuda.synchronize()
+    graphs = {c: capture(lambda c=c: [one(*c) for _ in range(args.chain)]) for c in cells}
+    for c in cells:
+        time_graph(graphs[c])
+    samp = {c: [] for c in cells}
+    for _ in range(args.rounds):
+        for c in cells:
+            samp[c].append(time_graph(graphs[c]) / args.chain)
+    del graphs
+    out = {}
+    for M in ms:
+        t = {k: statistics.median(samp[(M, k)]) * 1e6 for k in kinds}
+        out[str(M)] = {"path": paths[M], "plain_us": round(t["plain"], 4),
+                       "fused_us": round(t["fused"], 4), "separate_add_us": round(t["separate"], 4),
+                       "saved_us": round(t["separate"] - t["fused"], 4),
+                       "fused_over_plain": round(t["fused"] / t["plain"], 4)}
+        log(f"[bench] residual sum M={M:2d} plain {t['plain']:.3f} fused {t['fused']:.3f} "
+            f"plain+add {t['separate']:.3f} us")
+    # the fused result is the plain product plus r rounded once: check it
+    for M in ms:
+        one(M, "fused")
+        one(M, "plain")
+    torch.cuda.synchronize()
+    exact = all(np.array_equal(ys[M].cpu().numpy(), (ts[M] + rs[M]).cpu().numpy()) for M in ms)
+    return {"per_m": out, "bitwise_plain_plus_add": exact,
+            "timing": "graph chains per (M, variant), interleaved rounds, median; "
+                      "separate = plain call then torch.add(y, r)"}
 
 
 def measured_traffic(workload, M):

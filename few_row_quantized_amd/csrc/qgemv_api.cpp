@@ -140,6 +140,36 @@ int qgemv_small(const uint8_t *codes, const uint16_t *scales, const uint16_t *bi
                         stream);
 }
 
+int qgemv_run_path_add(int path, const uint8_t *codes, const uint16_t *scales,
+                       const uint16_t *biases, const uint16_t *x, const float *residual, float *y,
+                       int M, int N, int K, int bits, int group_size, void *stream) {
+  if (path != QGEMV_PATH_AUTO && path != QGEMV_PATH_DOT && path != QGEMV_PATH_MFMA)
+    return QGEMV_EINVAL;
+  const int s = validate(codes, scales, biases, x, y, M, N, K, bits, group_size);
+  if (s != QGEMV_OK) return s;
+  if (!residual) return QGEMV_EINVAL;
+  if (!aligned(residual, 16)) return QGEMV_EALIGN;
+  // the residual is either y itself or disjoint from it
+  if (residual != y) {
+    const uintptr_t r0 = reinterpret_cast<uintptr_t>(residual), y0 = reinterpret_cast<uintptr_t>(y);
+    const uintptr_t len = (uintptr_t)M * (uintptr_t)N * sizeof(float);
+    if (r0 < y0 + len && y0 < r0 + len) return QGEMV_EINVAL;
+  }
+  if (path == QGEMV_PATH_AUTO) path = select_path(M, N, K, bits, group_size);
+  if (!path_supported(path, K, bits, group_size)) return QGEMV_EUNSUPPORTED;
+  QgemvArgs a{codes, scales, biases, x, y, M, N, K, bits, group_size};
+  a.res = residual;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return path == QGEMV_PATH_MFMA ? qgemv::launch_mfma(a, st) : qgemv::launch_dot(a, st);
+}
+
+int qgemv_small_add(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
+                    const uint16_t *x, const float *residual, float *y, int M, int N, int K,
+                    int bits, int group_size, void *stream) {
+  return qgemv_run_path_add(QGEMV_PATH_AUTO, codes, scales, biases, x, residual, y, M, N, K, bits,
+                            group_size, stream);
+}
+
 int qgemv_unpack_probe(int path, const uint8_t *codes, uint8_t *q_out, int N, int K, int bits,
                        int group_size, void *stream) {
   const int s = validate_shape(1, N, K, bits, group_size);
@@ -171,6 +201,6 @@ const char *qgemv_strerror(int status) {
   }
 }
 
-int qgemv_version(void) { return 100; }
+int qgemv_version(void) { return 200; }
 
 }  // extern "C"

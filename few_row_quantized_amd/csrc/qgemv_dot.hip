@@ -1,374 +1,12 @@
-// Multi-row dot path of the few-row quantized GEMV (gfx950).
-//
-// Design (MI355X-first restatement of the "dequantize once, reuse across the
-// rows" idea: specgate-metal README, the mul_mv_ext rows 2..5 kernels; MLX
-// quantized_matmul small-M verify kernels, Facts: qmv_wide dequantizes each
-// group once into registers and reuses it across the M rows of a tile):
-//
-// * A workgroup is 4 waves; each wave owns a tile of R consecutive output rows
-//   n.  The 64 lanes of a wave split K: lane l takes 16-byte code chunks
-//   l, l+64, l+128, ... of every row in its tile, so each load instruction of
-//   the wave reads 1 KiB of one row contiguously (128-bit loads, fully
-//   coalesced).  Codes are read from HBM exactly once per call.
-// * The M activation rows are staged in LDS once per workgroup, already
-//   re-paired to match the code pairing (elements (e, e+4) for 4-bit codes,
-//   (e, e+8) for 2-bit codes), together with the activation sum of every
-//   lane chunk.  K is staged in pieces when M*K does not fit the LDS budget.
-// * Each code dword is unpacked once into bf16 pairs 128+q and used for all M
-//   rows with v_dot2c_f32_bf16.  The group's scale and bias are applied once
-//   per lane chunk and row: acc += s*d + (b - 128 s)*sum(x), i.e. the scale
-//   is folded out of the inner loop (MLX page, Facts: the qmv_wide tuning
-//   bullet) and metadata is read directly per group, not cached across lanes
-//   (same page: the scale-caching patch regressed).
-// * The R*M per-lane partial sums are reduced across the wave with
-//   permlane32/permlane16 swaps and a DPP butterfly, then stored.
-//
-// Per-row accumulation order depends only on K and the lane mapping, never on
-// M, so row m of an M-row call equals the M=1 call bitwise.
-
-#include "qgemv_device.h"
-#include "qgemv_internal.h"
+// Multi-row dot path: the plain product (kernels in qgemv_dot_impl.h).  The
+// fused residual sum's instantiations are compiled in qgemv_dot_add.hip.
+#include "qgemv_dot_impl.h"
 
 namespace qgemv {
 
-namespace {
-
-constexpr int kDotThreads = 256;
-constexpr int kDotWaves = kDotThreads / 64;
-constexpr int kMaxPasses = 3;  // lane passes (of 64 chunks) per LDS stage, at most
-
-template <int BITS, int M, int R, int NSUB, int P>
-__global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
-    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
-    const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *__restrict__ y,
-    int N, int K, int gs, int kch) {
-  constexpr int CW = 128 / BITS;        // weights per 16-byte code chunk
-  constexpr int QUADS = CW / 8;         // 16-byte units of paired x per (row m, chunk)
-  constexpr int QPS = QUADS / NSUB;     // quads per metadata sub-chunk
-  constexpr int SUBW = CW / NSUB;       // weights per sub-chunk
-  constexpr int V = ((R * M + 3) / 4) * 4;
-
-  extern __shared__ uint4 lds[];
-  uint4 *xl = lds;                                              // [M][QUADS][kch]
-  float *xsl = reinterpret_cast<float *>(lds + M * QUADS * kch);  // [M][NSUB][kch]
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int row0 = (blockIdx.x * kDotWaves + wave) * R;
-  const int NC = K / CW;
-  const int G = K / gs;
-  const size_t RB = (size_t)K * BITS / 8;
-
-  const uint32_t offset_pair = opaque_u32(kOffsetPair);
-  float acc[R][M];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
-
-  for (int c0 = 0; c0 < NC; c0 += kch) {
-    const int nc = min(kch, NC - c0);
-
-    // 1. activations for staging, first units: loaded before the codes so that
-    //    writing them to LDS does not wait for HBM.  Loads never sit behind a
-    //    per-lane branch (that would force a wait right after each load):
-    //    lanes past the end read a valid clamped address and ignore the data.
-    const int units = M * nc;
-    const int npass = (nc + 63) >> 6;  // uniform
-    if (c0 != 0) __syncthreads();      // previous stage fully consumed
-    // Units are visited in an order rotated per workgroup (by blockIdx/8:
-    // workgroups are dealt round-robin over the 8 XCDs) so that the CUs sharing
-    // an L2 do not all read the same activation lines at the same moment.
-    const int rot = (int)(((blockIdx.x >> 3) * 64u) % (unsigned)units);
-    auto unit_of = [&](int uu) { return uu + rot < units ? uu + rot : uu + rot - units; };
-    // staging units per thread loaded ahead: a stage holds at most 64*P
-    // chunks, i.e. M*64*P units, so one unit per thread while M*P <= 4, two
-    // otherwise (the launcher keeps M*kch within two units per thread)
-    constexpr int JU = M * P <= 4 ? 1 : 2;
-    uint4 xa[JU][CW / 8];
-#pragma unroll
-    for (int j = 0; j < JU; ++j) {
-      const int u = unit_of(min((int)threadIdx.x + kDotThreads * j, units - 1));
-      const int m = u / nc;
-      const int cl = u - m * nc;
-#pragma unroll
-      for (int i = 0; i < CW / 8; ++i)
-        xa[j][i] = reinterpret_cast<const uint4 *>(x + (size_t)m * K + (size_t)(c0 + cl) * CW)[i];
-    }
-
-    // 2. code and metadata loads for this stage, in the order they are consumed
-    uint4 cw[P][R];
-    uint32_t sr[P][R][NSUB], br[P][R][NSUB];
-#pragma unroll
-    for (int t = 0; t < P; ++t) {
-      if (t < npass) {
-        const int c = min(lane + 64 * t, nc - 1);
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const int n = min(row0 + r, N - 1);
-          const u32x4_t v = load_stream_u32x4(codes + (size_t)n * RB + (size_t)(c0 + c) * 16);
-          cw[t][r] = make_uint4(v[0], v[1], v[2], v[3]);
-#pragma unroll
-          for (int s = 0; s < NSUB; ++s) {
-            const int g = ((c0 + c) * CW + s * SUBW) / gs;
-            sr[t][r][s] = scales[(size_t)n * G + g];
-            br[t][r][s] = biases[(size_t)n * G + g];
-          }
-        }
-      }
-    }
-
-    // all loads of the stage stay ahead of the staging and compute
-    __builtin_amdgcn_sched_barrier(0);
-
-    // 3. stage x: paired layout + per-sub-chunk sums (units beyond the first
-    //    two per thread are loaded here, which only happens for large M)
-    auto stage_unit = [&](int u, const uint4 (&xv)[CW / 8]) {
-      const int m = u / nc;
-      const int cl = u - m * nc;
-      uint32_t X[CW / 2];
-#pragma unroll
-      for (int i = 0; i < CW / 8; ++i) {
-        X[4 * i] = xv[i].x;
-        X[4 * i + 1] = xv[i].y;
-        X[4 * i + 2] = xv[i].z;
-        X[4 * i + 3] = xv[i].w;
-      }
-      float ssum[NSUB];
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) ssum[s] = 0.f;
-#pragma unroll
-      for (int i = 0; i < CW / 2; ++i)
-        ssum[(2 * i) / SUBW] = dot2_bf16(X[i], 0x3F803F80u, ssum[(2 * i) / SUBW]);
-      if constexpr (BITS == 4) {
-        // code dword d covers elements 8d..8d+7; pairs (8d+e, 8d+e+4)
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t Xd[4] = {X[4 * d], X[4 * d + 1], X[4 * d + 2], X[4 * d + 3]};
-          uint4 q;
-          q.x = xpair_stride4(Xd, 0);
-          q.y = xpair_stride4(Xd, 1);
-          q.z = xpair_stride4(Xd, 2);
-          q.w = xpair_stride4(Xd, 3);
-          xl[(m * QUADS + d) * kch + cl] = q;
-        }
-      } else {
-        // code dword d covers elements 16d..16d+15; pairs (16d+e, 16d+e+8),
-        // quads (d, h) hold e = 4h..4h+3
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          uint32_t Xd[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) Xd[i] = X[8 * d + i];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            uint4 q;
-            q.x = xpair_stride8(Xd, 4 * h + 0);
-            q.y = xpair_stride8(Xd, 4 * h + 1);
-            q.z = xpair_stride8(Xd, 4 * h + 2);
-            q.w = xpair_stride8(Xd, 4 * h + 3);
-            xl[(m * QUADS + 2 * d + h) * kch + cl] = q;
-          }
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) xsl[(m * NSUB + s) * kch + cl] = ssum[s];
-    };
-#pragma unroll
-    for (int j = 0; j < JU; ++j) {
-      const int uu = threadIdx.x + kDotThreads * j;
-      if (uu < units) stage_unit(unit_of(uu), xa[j]);
-    }
-    for (int uu = threadIdx.x + JU * kDotThreads; uu < units; uu += kDotThreads) {
-      const int u = unit_of(uu);
-      const int m = u / nc;
-      const int cl = u - m * nc;
-      uint4 xv[CW / 8];
-#pragma unroll
-      for (int i = 0; i < CW / 8; ++i)
-        xv[i] = reinterpret_cast<const uint4 *>(x + (size_t)m * K + (size_t)(c0 + cl) * CW)[i];
-      stage_unit(u, xv);
-    }
-    __syncthreads();
-
-    // 4. multi-row dot products over this stage, in load order
-#pragma unroll
-    for (int t = 0; t < P; ++t) {
-      const int c = lane + 64 * t;
-      if (t >= npass || c >= nc) continue;
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        float d[R][M];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-          for (int m = 0; m < M; ++m) d[r][m] = 0.f;
-#pragma unroll
-        for (int qq = 0; qq < QPS; ++qq) {
-          const int q = s * QPS + qq;
-          uint32_t pr[R][4];
-#pragma unroll
-          for (int r = 0; r < R; ++r) {
-            const uint32_t cd[4] = {cw[t][r].x, cw[t][r].y, cw[t][r].z, cw[t][r].w};
-            if constexpr (BITS == 4) {
-              unpack4_split_pairs(cd[q], pr[r], offset_pair);
-            } else {
-              uint32_t p8[8];
-              unpack2_split_pairs(cd[q >> 1], p8, offset_pair);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) pr[r][e] = p8[4 * (q & 1) + e];
-            }
-          }
-#pragma unroll
-          for (int m = 0; m < M; ++m) {
-            const uint4 xv = xl[(m * QUADS + q) * kch + c];
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-              float a = d[r][m];
-              a = dot2_bf16(pr[r][0], xv.x, a);
-              a = dot2_bf16(pr[r][1], xv.y, a);
-              a = dot2_bf16(pr[r][2], xv.z, a);
-              a = dot2_bf16(pr[r][3], xv.w, a);
-              d[r][m] = a;
-            }
-          }
-        }
-        // fold scale and bias (with the 128 offset) once per sub-chunk
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const float sc = half_bits_to_float(sr[t][r][s]);
-          const float bo = fmaf(-128.f, sc, half_bits_to_float(br[t][r][s]));
-#pragma unroll
-          for (int m = 0; m < M; ++m) {
-            const float xs = xsl[(m * NSUB + s) * kch + c];
-            acc[r][m] = fmaf(sc, d[r][m], fmaf(bo, xs, acc[r][m]));
-          }
-        }
-      }
-    }
-  }
-
-  // 5. reduce over the 64 lanes and store y[m][row0 + r]
-  float v[V];
-#pragma unroll
-  for (int i = 0; i < V; ++i) v[i] = (i < R * M) ? acc[i / M][i % M] : 0.f;
-  float red[V / 4];
-  wave_reduce_multi<V>(v, red);
-  const int rho = lane >> 4;
-  if ((lane & 15) == 0) {
-#pragma unroll
-    for (int j = 0; j < V / 4; ++j) {
-      const int idx = 4 * j + row_value_index(rho);
-      if (idx < R * M) {
-        const int r = idx / M, m = idx % M;
-        const int n = row0 + r;
-        if (n < N) y[(size_t)m * N + n] = red[j];
-      }
-    }
-  }
-}
-
-template <int BITS, int M, int R, int NSUB, int P>
-int launch_dot_tp(const QgemvArgs &a, hipStream_t stream) {
-  constexpr int CW = 128 / BITS;
-  constexpr int QUADS = CW / 8;
-  const int NC = a.K / CW;
-  // Stages always hold whole multiples of 64 chunks, so lane l processes
-  // chunks l, l+64, l+128, ... in the same order for every M (row results do
-  // not depend on M).  Up to P*64 chunks per stage, within the LDS budget;
-  // 64 chunks always fit (at most 139 KiB for M = 16, 2-bit codes).
-  const size_t per_chunk = (size_t)M * (QUADS * 16 + NSUB * 4);
-  int kch = 64 * (int)(kDotLdsBudget / (64 * per_chunk));
-  // at most two staging units per thread (loaded ahead of the codes)
-  const int kch_units = 64 * ((2 * kDotThreads / M) / 64);
-  if (kch > kch_units) kch = kch_units;
-  if (kch < 64) kch = 64;
-  if (kch > 64 * P) kch = 64 * P;
-  if (kch > NC) kch = NC;  // one stage holds the whole row
-  const size_t lds = per_chunk * (size_t)kch;
-  if (lds > kLdsMax) return QGEMV_EUNSUPPORTED;
-  if (!allow_max_dynamic_lds(reinterpret_cast<const void *>(&qgemv_dot_kernel<BITS, M, R, NSUB, P>)))
-    return QGEMV_EHIP;
-  const int rows_per_block = kDotWaves * R;
-  const int blocks = (a.N + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL((qgemv_dot_kernel<BITS, M, R, NSUB, P>), dim3(blocks), dim3(kDotThreads), lds,
-                     stream, a.codes, a.scales, a.biases, a.x, a.y, a.N, a.K, a.group_size, kch);
-  return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
-}
-
-// Lane passes per stage: two when a row has at most 128 chunks (K <= 4096 at
-// 4 bits), which keeps fewer code registers live; three otherwise.  Only for
-// M <= 4, where the dot path is the one that runs.
-template <int BITS, int M, int R, int NSUB>
-int launch_dot_t(const QgemvArgs &a, hipStream_t stream) {
-  if constexpr (M <= 4) {
-    if (a.K / (128 / BITS) <= 128) return launch_dot_tp<BITS, M, R, NSUB, 2>(a, stream);
-  }
-  return launch_dot_tp<BITS, M, R, NSUB, kMaxPasses>(a, stream);
-}
-
-// rows per wave for each M: enough rows to share each x read (LDS traffic per
-// code byte ~ 4M/R), few enough to keep R*M accumulators in registers.
-template <int M>
-constexpr int dot_rows_per_wave() {
-  return M <= 2 ? 2 : (M <= 4 ? 4 : (M <= 8 ? 2 : 1));
-}
-
-template <int BITS, int M, int R>
-int launch_dot_r(const QgemvArgs &a, hipStream_t stream) {
-  if constexpr (BITS == 2) {
-    if (a.group_size == 32) return launch_dot_t<2, M, R, 2>(a, stream);
-    return launch_dot_t<2, M, R, 1>(a, stream);
-  } else {
-    return launch_dot_t<4, M, R, 1>(a, stream);
-  }
-}
-
-template <int BITS, int M>
-int launch_dot_m(const QgemvArgs &a, hipStream_t stream) {
-  constexpr int R = dot_rows_per_wave<M>();
-  // Few rows (small N): fewer rows per wave, so that every CU gets a
-  // workgroup.  The row-to-lane arithmetic is the same for every R, so
-  // results do not depend on this choice.
-  const int cus = device_cu_count();
-  if constexpr (R == 4) {
-    if (a.N / (kDotWaves * 4) < cus) {
-      if (a.N / (kDotWaves * 2) >= cus) return launch_dot_r<BITS, M, 2>(a, stream);
-      return launch_dot_r<BITS, M, 1>(a, stream);
-    }
-  } else if constexpr (R == 2) {
-    if (a.N / (kDotWaves * 2) < cus) return launch_dot_r<BITS, M, 1>(a, stream);
-  }
-  return launch_dot_r<BITS, M, R>(a, stream);
-}
-
-template <int BITS>
-int launch_dot_bits(const QgemvArgs &a, hipStream_t stream) {
-  switch (a.M) {
-    case 1: return launch_dot_m<BITS, 1>(a, stream);
-    case 2: return launch_dot_m<BITS, 2>(a, stream);
-    case 3: return launch_dot_m<BITS, 3>(a, stream);
-    case 4: return launch_dot_m<BITS, 4>(a, stream);
-    case 5: return launch_dot_m<BITS, 5>(a, stream);
-    case 6: return launch_dot_m<BITS, 6>(a, stream);
-    case 7: return launch_dot_m<BITS, 7>(a, stream);
-    case 8: return launch_dot_m<BITS, 8>(a, stream);
-    case 9: return launch_dot_m<BITS, 9>(a, stream);
-    case 10: return launch_dot_m<BITS, 10>(a, stream);
-    case 11: return launch_dot_m<BITS, 11>(a, stream);
-    case 12: return launch_dot_m<BITS, 12>(a, stream);
-    case 13: return launch_dot_m<BITS, 13>(a, stream);
-    case 14: return launch_dot_m<BITS, 14>(a, stream);
-    case 15: return launch_dot_m<BITS, 15>(a, stream);
-    case 16: return launch_dot_m<BITS, 16>(a, stream);
-    default: return QGEMV_EINVAL;
-  }
-}
-
-}  // namespace
-
 int launch_dot(const QgemvArgs &a, hipStream_t stream) {
-  return a.bits == 4 ? launch_dot_bits<4>(a, stream) : launch_dot_bits<2>(a, stream);
+  if (a.res) return launch_dot_add(a, stream);
+  return launch_dot_impl<false>(a, stream);
 }
 
 }  // namespace qgemv

@@ -16,6 +16,9 @@ struct QgemvArgs {
   const uint16_t *x;
   float *y;
   int M, N, K, bits, group_size;
+  // Fused residual sum: y = product + res (res [M][N] fp32, may equal y);
+  // nullptr for the plain product.
+  const float *res = nullptr;
 };
 
 // LDS of one workgroup: hardware limit on gfx950, and the dot path's
@@ -32,6 +35,7 @@ bool allow_max_dynamic_lds(const void *func);
 
 // Launchers: enqueue on `stream`, return QGEMV_OK / QGEMV_EUNSUPPORTED / QGEMV_EHIP.
 int launch_dot(const QgemvArgs &a, hipStream_t stream);
+int launch_dot_add(const QgemvArgs &a, hipStream_t stream);  // a.res != nullptr
 int launch_mfma(const QgemvArgs &a, hipStream_t stream);
 // Persistent MFMA kernel (QGEMV_EUNSUPPORTED when the activations of a
 // wave would not fit its registers).

@@ -28,6 +28,11 @@
 //   formed while the codes are still in flight.
 // * Partial tiles of the waves are summed through LDS in slice order
 //   (deterministic, no atomics) and rows m < M are stored.
+// * Fused residual sum (ADD, "metal : few-row MMA mat-mul and batched copies
+//   for speculative decoding", Overview: MUL_MAT + ADD writes the residual
+//   sum from the store): each thread loads the residual of the outputs it
+//   will store at the start of its tile group and adds it in the store, so
+//   y = fl(product + r), bit for bit the plain call and a separate fp32 add.
 // Shapes with more 16-column tiles than CUs go to the persistent kernel
 // (qgemv_persist.hip) unless K is too long for its register-resident
 // activations.
@@ -40,11 +45,20 @@ namespace qgemv {
 namespace {
 
 
-template <int BITS, int GS, int NT, int MAXT, int SPI, int KS, bool PERSIST>
+// Bit pattern that y holds, before a K-split launch with the residual sum,
+// until the first half of K lands.  A NaN payload that no partial sum can
+// carry: partials derive from bf16 and fp16 inputs, whose NaNs have zero low
+// 13 bits in fp32, and fresh NaNs are the canonical 0x7FC00000.
+constexpr uint32_t kSplitSentinel = 0x7FC0DEADu;
+
+// y and res may be the same buffer (in-place residual sum): neither is
+// declared restrict; every element is read before it is written, by the same
+// thread.
+template <int BITS, int GS, int NT, int MAXT, int SPI, int KS, bool PERSIST, bool ADD>
 __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
-    const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *__restrict__ y,
-    int M, int N, int K, int ngroups) {
+    const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *y,
+    const float *res, int M, int N, int K, int ngroups) {
   constexpr int CW = 128 / BITS;       // codes per 16-byte chunk
   constexpr int SCW = 4 * CW;          // codes per 64-byte super-chunk
   constexpr int DW = CW / 4;           // codes per dword
@@ -112,6 +126,21 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     crow[t] = codes + (size_t)n * RB + kb * 16;
     srow[t] = scales + (size_t)n * G;
     brow[t] = biases + (size_t)n * G;
+  }
+
+  // residual of the outputs this thread stores in its first NT reduction
+  // steps (all of them when the workgroup has at least 4 waves), loaded ahead
+  // of the weight stream; clamped indices read a valid element, never used
+  float rpre[NT];
+  if constexpr (ADD) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int o = min((int)threadIdx.x + j * (int)blockDim.x, NT * 256 - 1);
+      const int l = o & 63;
+      const int m = min(4 * (l >> 4) + ((o >> 6) & 3), M - 1);
+      const int n = min(n_base + 16 * (o >> 8) + (l & 15), N - 1);
+      rpre[j] = res[(size_t)m * N + n];
+    }
   }
 
   f32x4_t acc[NT];
@@ -258,7 +287,9 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[slice][t][i][lane] = acc[t][i];
   __syncthreads();
-  for (int o = threadIdx.x; o < NT * 256; o += blockDim.x) {
+  // output o of the tile group: sum over the slices, then store (pre: the
+  // residual rv was prefetched)
+  auto finish = [&](const int o, const bool pre, float rv) {
     const int t = o >> 8;
     const int i = (o >> 6) & 3;
     const int l = o & 63;
@@ -267,15 +298,32 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     const int m = 4 * (l >> 4) + i;
     const int n = n_base + 16 * t + (l & 15);
     if (m < M && n < N) {
+      float *dst = y + (size_t)m * N + n;
+      if constexpr (ADD) {
+        if (!pre) rv = res[(size_t)m * N + n];
+      }
       if constexpr (KS == 1) {
-        y[(size_t)m * N + n] = s;
-      } else {
+        *dst = ADD ? s + rv : s;
+      } else if constexpr (!ADD) {
         // y was zeroed before the launch and receives exactly two addends:
         // 0 + a + b equals 0 + b + a bit for bit, whichever half lands first
-        unsafeAtomicAdd(y + (size_t)m * N + n, s);
+        unsafeAtomicAdd(dst, s);
+      } else {
+        // y held kSplitSentinel: the first half leaves its partial there, the
+        // second finds it and stores (a + b) + r.  a + b and b + a are the same
+        // float, so the result is the plain product's plus r, whichever half
+        // lands first.
+        const float old = atomicExch(dst, s);
+        if (__builtin_bit_cast(uint32_t, old) != kSplitSentinel) *dst = (old + s) + rv;
       }
     }
+  };
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int o = threadIdx.x + j * blockDim.x;
+    if (o < NT * 256) finish(o, true, ADD ? rpre[j] : 0.f);
   }
+  for (int o = threadIdx.x + NT * blockDim.x; o < NT * 256; o += blockDim.x) finish(o, false, 0.f);
   };
 
   if constexpr (PERSIST) {
@@ -318,33 +366,40 @@ struct MfmaShape {
 };
 
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ y, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) y[i] = 0.f;
+// y[0..n) = v (bit pattern): zero before a K-split launch, kSplitSentinel
+// before one with the residual sum
+__global__ __launch_bounds__(256) void fill_kernel(uint32_t *__restrict__ y, size_t n, uint32_t v) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) y[i] = v;
 }
 
-template <int BITS, int GS, int NT>
+template <int BITS, int GS, int NT, bool ADD>
 int launch_mfma_t(const QgemvArgs &a, hipStream_t stream) {
   constexpr int MAXT = MfmaShape<BITS, GS, NT>::MAXT;
   constexpr int SPI = MfmaShape<BITS, GS, NT>::SPI;
-  const auto kern = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, true>;
-  const auto kern1 = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, false>;
-  const auto kern_s = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 2, true>;
-  const auto kern1_s = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 2, false>;
+  const auto kern = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, true, ADD>;
+  const auto kern1 = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, false, ADD>;
+  const auto kern_s = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 2, true, ADD>;
+  const auto kern1_s = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 2, false, ADD>;
   const int nblk = a.K / (4 * GS);
   const int tiles = (a.N + 15) / 16;
   const int cus = device_cu_count();
   // Few tile groups for the CUs: split K in two halves across workgroups
   // (added into y), for long K when there are under two groups per CU, and
   // for any K of at least 2048 when groups cover at most a quarter of the CUs.
+  // Not for an in-place residual sum: y must be prefilled, which would erase
+  // the residual.
   const int tgroups = (tiles + NT - 1) / NT;
+  const bool in_place = ADD && static_cast<const void *>(a.res) == static_cast<const void *>(a.y);
   const int ksplit =
-      ((tgroups < 2 * cus && a.K >= 8192) || (4 * tgroups <= cus && a.K >= 2048)) ? 2 : 1;
+      !in_place && ((tgroups < 2 * cus && a.K >= 8192) || (4 * tgroups <= cus && a.K >= 2048)) ? 2
+                                                                                                : 1;
   const int waves = pick_waves(nblk / ksplit, MAXT / 64);
   const int groups = (tiles + NT - 1) / NT * ksplit;
   if (ksplit == 2) {
     const size_t n = (size_t)a.M * a.N;
     const int fb = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(fb), dim3(256), 0, stream, a.y, n);
+    hipLaunchKernelGGL(fill_kernel, dim3(fb), dim3(256), 0, stream,
+                       reinterpret_cast<uint32_t *>(a.y), n, ADD ? kSplitSentinel : 0u);
   }
   // workgroups resident at once for this block size (cached per wave count)
   static int occ_cache[MAXT / 64 + 1] = {0};
@@ -360,7 +415,7 @@ int launch_mfma_t(const QgemvArgs &a, hipStream_t stream) {
   const bool single = groups <= slots;
   const auto k = ksplit == 1 ? (single ? kern1 : kern) : (single ? kern1_s : kern_s);
   hipLaunchKernelGGL(k, dim3(single ? groups : slots), dim3(64 * waves), 0, stream, a.codes,
-                     a.scales, a.biases, a.x, a.y, a.M, a.N, a.K, groups);
+                     a.scales, a.biases, a.x, a.y, a.res, a.M, a.N, a.K, groups);
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
 }
 
@@ -370,8 +425,12 @@ int launch_mfma_gs(const QgemvArgs &a, hipStream_t stream) {
   // all M*K activations, so wider groups cut that traffic per weight byte
   const int tiles = (a.N + 15) / 16;
   const int cus = device_cu_count();
-  if (tiles >= 2 * cus) return launch_mfma_t<BITS, GS, 2>(a, stream);
-  return launch_mfma_t<BITS, GS, 1>(a, stream);
+  if (a.res) {
+    if (tiles >= 2 * cus) return launch_mfma_t<BITS, GS, 2, true>(a, stream);
+    return launch_mfma_t<BITS, GS, 1, true>(a, stream);
+  }
+  if (tiles >= 2 * cus) return launch_mfma_t<BITS, GS, 2, false>(a, stream);
+  return launch_mfma_t<BITS, GS, 1, false>(a, stream);
 }
 
 }  // namespace

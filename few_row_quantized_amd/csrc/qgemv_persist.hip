@@ -21,6 +21,11 @@
 //   CU keeps weight bytes in flight from its first tile to its last.
 // * Every S tiles the waves' partial 16x16 tiles are summed through LDS in
 //   block order (deterministic, no atomics) and rows m < M are stored.
+// * Fused residual sum (ADD, "metal : few-row MMA mat-mul and batched copies
+//   for speculative decoding", Overview: MUL_MAT + ADD writes the residual
+//   sum from the store): the residual of the S tiles' outputs a thread stores
+//   is loaded when their first tile starts and added in the store, so
+//   y = fl(product + r), bit for bit the plain call and a separate fp32 add.
 // The inner MFMA step (code layout, partial lane transpose, unpack to exact
 // bf16 128+q, per-group scale fold, bias product by v_mfma_f32_16x16x4_f32)
 // is the one of the single-pass kernel.
@@ -32,11 +37,14 @@ namespace qgemv {
 
 namespace {
 
-template <int BITS, int GS, int BPW, int S, int MAXW>
+// y and res may be the same buffer (in-place residual sum): neither is
+// declared restrict; every element is read before it is written, by the same
+// thread.
+template <int BITS, int GS, int BPW, int S, int MAXW, bool ADD>
 __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
-    const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *__restrict__ y,
-    int M, int N, int K) {
+    const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *y,
+    const float *res, int M, int N, int K) {
   constexpr int CW = 128 / BITS;         // codes per 16-byte chunk
   constexpr int SCW = 4 * CW;            // codes per 64-byte super-chunk
   constexpr int DW = CW / 4;             // codes per dword
@@ -176,6 +184,20 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   // prologue loads below the activation work)
   int j0 = 0;
   do {
+    // residual of the outputs this thread stores for these S tiles (its first
+    // S reduction steps: all of them with at least 4 waves); clamped indices
+    // read a valid element and are never used
+    float rpre[S];
+    if constexpr (ADD) {
+#pragma unroll
+      for (int j = 0; j < S; ++j) {
+        const int o = min((int)threadIdx.x + j * (int)blockDim.x, S * 256 - 1);
+        const int l = o & 63;
+        const int m = min(4 * (l >> 4) + ((o >> 6) & 3), M - 1);
+        const int n = min(16 * (t_first + j0 + (o >> 8)) + (l & 15), N - 1);
+        rpre[j] = res[(size_t)m * N + n];
+      }
+    }
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       if (j0 + s >= ntile) break;
@@ -230,7 +252,7 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
     // ---- sum the group's partial tiles over the waves in block order
     __syncthreads();
     const int nj = min(S, ntile - j0);
-    for (int o = threadIdx.x; o < nj * 256; o += blockDim.x) {
+    auto finish = [&](const int o, const bool pre, float rv) {
       const int s = o >> 8, i = (o >> 6) & 3, l = o & 63;
       float v = 0.f;
       for (int w = 0; w < W; ++w) {
@@ -239,8 +261,20 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
       }
       const int m = 4 * (l >> 4) + i;
       const int n = 16 * (t_first + j0 + s) + (l & 15);
-      if (m < M && n < N) y[(size_t)m * N + n] = v;
+      if (m < M && n < N) {
+        if constexpr (ADD) {
+          if (!pre) rv = res[(size_t)m * N + n];
+          v += rv;
+        }
+        y[(size_t)m * N + n] = v;
+      }
+    };
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      const int o = threadIdx.x + j * blockDim.x;
+      if (o < nj * 256) finish(o, true, ADD ? rpre[j] : 0.f);
     }
+    for (int o = threadIdx.x + S * blockDim.x; o < nj * 256; o += blockDim.x) finish(o, false, 0.f);
     __syncthreads();  // red is rewritten by the next group
     j0 += S;
   } while (j0 < ntile);
@@ -256,7 +290,7 @@ struct PersistShape {
   static constexpr int S = 2;
 };
 
-template <int BITS, int GS>
+template <int BITS, int GS, bool ADD>
 int launch_persist_t(const QgemvArgs &a, hipStream_t stream) {
   constexpr int BPW = PersistShape<BITS, GS>::BPW;
   constexpr int MAXW = PersistShape<BITS, GS>::MAXW;
@@ -267,9 +301,14 @@ int launch_persist_t(const QgemvArgs &a, hipStream_t stream) {
   const int tiles = (a.N + 15) / 16;
   const int cus = device_cu_count();
   const int G = tiles < cus ? tiles : cus;
-  hipLaunchKernelGGL((qgemv_persist_kernel<BITS, GS, BPW, S, MAXW>), dim3(G), dim3(64 * waves), 0,
-                     stream, a.codes, a.scales, a.biases, a.x, a.y, a.M, a.N, a.K);
+  hipLaunchKernelGGL((qgemv_persist_kernel<BITS, GS, BPW, S, MAXW, ADD>), dim3(G), dim3(64 * waves),
+                     0, stream, a.codes, a.scales, a.biases, a.x, a.y, a.res, a.M, a.N, a.K);
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}
+
+template <int BITS, int GS>
+int launch_persist_gs(const QgemvArgs &a, hipStream_t stream) {
+  return a.res ? launch_persist_t<BITS, GS, true>(a, stream) : launch_persist_t<BITS, GS, false>(a, stream);
 }
 
 }  // namespace
@@ -278,14 +317,14 @@ int launch_persist(const QgemvArgs &a, hipStream_t stream) {
   if (!mfma_supports(a.K, a.bits, a.group_size)) return QGEMV_EUNSUPPORTED;
   if (a.bits == 4) {
     switch (a.group_size) {
-      case 32: return launch_persist_t<4, 32>(a, stream);
-      case 64: return launch_persist_t<4, 64>(a, stream);
-      case 128: return launch_persist_t<4, 128>(a, stream);
+      case 32: return launch_persist_gs<4, 32>(a, stream);
+      case 64: return launch_persist_gs<4, 64>(a, stream);
+      case 128: return launch_persist_gs<4, 128>(a, stream);
     }
   } else {
     switch (a.group_size) {
-      case 64: return launch_persist_t<2, 64>(a, stream);
-      case 128: return launch_persist_t<2, 128>(a, stream);
+      case 64: return launch_persist_gs<2, 64>(a, stream);
+      case 128: return launch_persist_gs<2, 128>(a, stream);
     }
   }
   return QGEMV_EUNSUPPORTED;

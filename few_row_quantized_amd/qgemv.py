@@ -50,6 +50,9 @@ def lib() -> ctypes.CDLL:
         gemv = [vp, vp, vp, vp, vp, i, i, i, i, i, vp]
         L.qgemv_small.argtypes = gemv
         L.qgemv_run_path.argtypes = [i] + gemv
+        gemv_add = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+        L.qgemv_small_add.argtypes = gemv_add
+        L.qgemv_run_path_add.argtypes = [i] + gemv_add
         L.qgemv_select.argtypes = [i, i, i, i, i]
         L.qgemv_path_supported.argtypes = [i, i, i, i, i, i]
         L.qgemv_unpack_probe.argtypes = [i, vp, vp, i, i, i, i, vp]
@@ -58,7 +61,8 @@ def lib() -> ctypes.CDLL:
         L.qgemv_strerror.argtypes = [i]
         L.qgemv_strerror.restype = ctypes.c_char_p
         L.qgemv_version.argtypes = []
-        for name in ("qgemv_small", "qgemv_run_path", "qgemv_select", "qgemv_path_supported",
+        for name in ("qgemv_small", "qgemv_run_path", "qgemv_small_add", "qgemv_run_path_add",
+                     "qgemv_select", "qgemv_path_supported",
                      "qgemv_unpack_probe", "qgemv_stream_probe", "qgemv_stream_probe_blocks",
                      "qgemv_version"):
             getattr(L, name).restype = ctypes.c_int
@@ -110,6 +114,20 @@ def qgemv_run_path(path, codes, scales, biases, x, y, M: int, N: int, K: int, bi
                                        _stream(stream)), "qgemv_run_path")
 
 
+def qgemv_small_add(codes, scales, biases, x, residual, y, M: int, N: int, K: int, bits: int,
+                    group_size: int, stream=None) -> int:
+    return _check(lib().qgemv_small_add(_ptr(codes), _ptr(scales), _ptr(biases), _ptr(x),
+                                        _ptr(residual), _ptr(y), M, N, K, bits, group_size,
+                                        _stream(stream)), "qgemv_small_add")
+
+
+def qgemv_run_path_add(path, codes, scales, biases, x, residual, y, M: int, N: int, K: int,
+                       bits: int, group_size: int, stream=None) -> int:
+    return _check(lib().qgemv_run_path_add(_path(path), _ptr(codes), _ptr(scales), _ptr(biases),
+                                           _ptr(x), _ptr(residual), _ptr(y), M, N, K, bits,
+                                           group_size, _stream(stream)), "qgemv_run_path_add")
+
+
 def qgemv_select(M: int, N: int, K: int, bits: int, group_size: int) -> int:
     return _check(lib().qgemv_select(M, N, K, bits, group_size), "qgemv_select")
 
@@ -145,11 +163,12 @@ def qgemv_version() -> int:
 # ---------------------------------------------------------------- torch convenience
 
 def small(codes, scales, biases, x, bits: int, group_size: int, out=None, path="auto",
-          stream=None):
-    """y = x . dequant(W)^T on torch device tensors.
+          stream=None, residual=None):
+    """y = x . dequant(W)^T (+ residual) on torch device tensors.
 
     codes uint8 [N, K*bits/8]; scales/biases float16 (or int16) [N, K/gs];
     x bfloat16 (or int16) [M, K]; returns (or fills) y float32 [M, N].
+    residual: optional float32 [M, N] added in the kernels' store (may be `out`).
     """
     import torch
 
@@ -171,5 +190,12 @@ def small(codes, scales, biases, x, bits: int, group_size: int, out=None, path="
         out = torch.empty((M, N), dtype=torch.float32, device=codes.device)
     elif out.dtype != torch.float32 or tuple(out.shape) != (M, N) or not out.is_contiguous():
         raise ValueError("out must be a contiguous float32 [M, N] tensor")
-    qgemv_run_path(path, codes, scales, biases, x, out, M, N, K, bits, group_size, stream)
+    if residual is None:
+        qgemv_run_path(path, codes, scales, biases, x, out, M, N, K, bits, group_size, stream)
+        return out
+    if (residual.dtype != torch.float32 or tuple(residual.shape) != (M, N)
+            or not residual.is_contiguous() or residual.device != codes.device):
+        raise ValueError("residual must be a contiguous float32 [M, N] tensor on the same device")
+    qgemv_run_path_add(path, codes, scales, biases, x, residual, out, M, N, K, bits, group_size,
+                       stream)
     return out

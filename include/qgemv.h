@@ -80,12 +80,45 @@ extern "C" {
  * (scale hoisted out of the inner loop, MLX page, Facts: the qmv_wide tuning
  * bullet).  Result within 1e-3 * sum_k |x_k w_k| + 1e-6 of the exact value.
  * Within one path, row m of an M-row call equals (bitwise) the M=1 call on
- * x[m]: per-row accumulation order does not depend on M and no atomics are
- * used, so results are deterministic.
+ * x[m]: per-row accumulation order does not depend on M, and results are
+ * deterministic (where the MFMA path splits K over two workgroups, y receives
+ * exactly two float additions onto zero, which commute bit for bit).
  */
 int qgemv_small(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
                 const uint16_t *x, float *y, int M, int N, int K, int bits, int group_size,
                 void *stream);
+
+/*
+ * qgemv_small_add -- the fused residual sum: y = x . dequant(W)^T + residual,
+ * for 1 <= M <= 16, path chosen by qgemv_select (the MUL_MAT + ADD fusion of
+ * "metal : few-row MMA mat-mul and batched copies for speculative decoding",
+ * Overview: the residual sum is written from the mat-mul's store, saving the
+ * separate ADD launch and its read and write of y).
+ *
+ * residual: fp32 [M][N], row-major, the output's layout; DEVICE pointer,
+ * 16-byte aligned, read only.  It may be y itself (in place: y += x W^T);
+ * otherwise it must not overlap y (QGEMV_EINVAL).  NULL -> QGEMV_EINVAL.
+ * Other arguments, requirements and errors as qgemv_small.
+ * Numerics: y[m,n] is the fp32 product that qgemv_small would store for this
+ * path, plus residual[m,n] rounded once in fp32 -- bit for bit qgemv_small
+ * followed by a separate fp32 add -- except for an in-place call on a shape
+ * where the MFMA path splits K across workgroups: that call runs the unsplit
+ * kernel (the split needs y prefilled), whose product may differ from the
+ * split one in the last bits.  Tolerance against the exact value:
+ * 1e-3 * sum_k |x_k w_k| + 1e-6 + 2^-23 * (|r| + sum_k |x_k w_k|).
+ * Row m still equals (bitwise) the M=1 call on x[m] and residual[m].
+ */
+int qgemv_small_add(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
+                    const uint16_t *x, const float *residual, float *y, int M, int N, int K,
+                    int bits, int group_size, void *stream);
+
+/*
+ * qgemv_run_path_add -- qgemv_small_add with an explicit path (as
+ * qgemv_run_path).
+ */
+int qgemv_run_path_add(int path, const uint8_t *codes, const uint16_t *scales,
+                       const uint16_t *biases, const uint16_t *x, const float *residual, float *y,
+                       int M, int N, int K, int bits, int group_size, void *stream);
 
 /*
  * qgemv_select -- the path qgemv_small takes for this shape: QGEMV_PATH_DOT or

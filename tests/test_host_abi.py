@@ -21,7 +21,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for must in ("qgemv_small", "qgemv_select", "qgemv_run_path", "qgemv_unpack_probe",
-                 "qgemv_stream_probe", "qgemv_strerror"):
+                 "qgemv_stream_probe", "qgemv_strerror", "qgemv_small_add", "qgemv_run_path_add"):
         assert must in names
 
 
@@ -85,6 +85,42 @@ def test_misaligned_pointers_rejected(which):
     ptrs = [A] * 5
     ptrs[which] = MIS
     assert q.lib().qgemv_small(*ptrs, 4, 64, 256, 4, 64, None) == q.EALIGN
+
+
+# ---------------------------------------------------------------- fused residual sum
+
+@pytest.mark.parametrize("M,N,K,bits,gs,want", [
+    (0, 64, 256, 4, 64, q.EINVAL), (17, 64, 256, 4, 64, q.EINVAL), (1, 64, 96, 4, 32, q.EINVAL),
+    (1, 64, 256, 8, 64, q.EINVAL), (1, 64, 256, 4, 16, q.EINVAL),
+])
+def test_add_invalid_shapes_rejected(M, N, K, bits, gs, want):
+    L = q.lib()
+    B = A + (1 << 24)  # residual apart from y
+    assert L.qgemv_small_add(A, A, A, A, B, A, M, N, K, bits, gs, None) == want
+    for path in (q.PATH_AUTO, q.PATH_DOT, q.PATH_MFMA):
+        assert L.qgemv_run_path_add(path, A, A, A, A, B, A, M, N, K, bits, gs, None) == want
+
+
+@pytest.mark.parametrize("which", range(6))
+def test_add_null_and_misaligned_pointers_rejected(which):
+    L = q.lib()
+    ptrs = [A, A, A, A, A + (1 << 24), A]
+    ptrs[which] = None
+    assert L.qgemv_small_add(*ptrs, 4, 64, 256, 4, 64, None) == q.EINVAL
+    ptrs = [A, A, A, A, A + (1 << 24), A]
+    ptrs[which] = ptrs[which] + 4
+    assert L.qgemv_small_add(*ptrs, 4, 64, 256, 4, 64, None) == q.EALIGN
+
+
+def test_add_partially_overlapping_residual_rejected():
+    L = q.lib()
+    M, N = 4, 64
+    row = N * 4
+    # residual one row after y, or one row before: overlap, refused
+    assert L.qgemv_small_add(A, A, A, A, A + row, A, M, N, 256, 4, 64, None) == q.EINVAL
+    assert L.qgemv_small_add(A, A, A, A, A, A + row, M, N, 256, 4, 64, None) == q.EINVAL
+    # an unknown path is refused before anything else
+    assert L.qgemv_run_path_add(5, A, A, A, A, A, A, M, N, 256, 4, 64, None) == q.EINVAL
 
 
 def test_unknown_path_rejected():
