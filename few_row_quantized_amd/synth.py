@@ -15,6 +15,9 @@ output row and group of `group_size` along K):
   scale ~ U[0.001, 0.01] rounded to fp16; bias = fp16(-8*scale + N(0, 1e-3)).
 * 2-bit: q ~ U{0..3}, four codes per byte, least-significant crumb first.
   scale ~ U[0.005, 0.03]; bias = fp16(-1.5*scale + N(0, 1e-3)).
+* 8-bit: q ~ U{0..255}, one code per byte.  scale ~ U[1e-4, 1e-3];
+  bias = fp16(-128*scale + N(0, 1e-3)): the zero point in the middle of the
+  code range as for the other widths, and weights of about the 4-bit range.
 * x ~ N(0, 1) rounded to bf16 (round to nearest even); the decoder-layer sweep
   scales round(1% of K) channels by 20 (in fp32, before rounding) as outliers.
 
@@ -70,6 +73,11 @@ WORKLOADS: Dict[str, Shape] = {s.name: s for s in [
     _layer("gate", 5120, 17408, 4),
     _layer("up", 5120, 17408, 5),
     _layer("down", 17408, 5120, 6),
+    # 8-bit affine gs64 (MLX page, Facts: int8 qmv_wide on Gemma-4-12B gate/up
+    # 15360x3840; the (M,5120)@(17408,5120)^T microbench also run at 8 bits)
+    Shape("square_k4096_n4096_8b_g64", 4096, 4096, 8, 64, (1, 2, 3, 4, 5, 8), seed=50000),
+    Shape("gemma12b_gateup_k3840_n15360_8b_g64", 3840, 15360, 8, 64, (1, 2, 4, 8), seed=50100),
+    Shape("mlxbench_k5120_n17408_8b_g64", 5120, 17408, 8, 64, tuple(range(1, 17)), seed=50200),
 ]}
 
 LAYER27B = [f"layer27b_{p}" for p in ("q", "k", "v", "o", "gate", "up", "down")]
@@ -133,6 +141,8 @@ def _draw_meta(rng: np.random.Generator, N: int, G: int, bits: int):
         lo, hi, zero_point = 0.001, 0.01, 8.0
     elif bits == 2:
         lo, hi, zero_point = 0.005, 0.03, 1.5
+    elif bits == 8:
+        lo, hi, zero_point = 1e-4, 1e-3, 128.0
     else:
         raise ValueError(f"unsupported bits {bits}")
     s16 = rng.uniform(lo, hi, size=(N, G)).astype(np.float16)

@@ -18,7 +18,9 @@ What it computes is the plain definition of the operation, written out:
   the (M,5120)@(17408,5120)^T microbench).
 * Codes packed little-endian along K: 4-bit codes two per byte, low nibble
   first; 2-bit codes four per byte, lowest crumb first (the 2-bit order is not
-  stated on the pages; this is the reading that matches the 4-bit convention).
+  stated on the pages; this is the reading that matches the 4-bit convention);
+  8-bit codes one per byte (the int8 affine mode of qmv_wide, MLX page,
+  Facts: the int8 M=8 speedup; the code is the unsigned byte).
 * Every weight group is used once for all M rows (metal : few-row MMA mat-mul
   and batched copies for speculative decoding, Overview: each weight is
   dequantized once for all rows).  That is an evaluation-order property of the
@@ -28,7 +30,7 @@ Precision: fp16 -> fp64 and bf16 -> fp64 are exact.  s*q is exact (11-bit
 significand times a 4-bit integer).  Adding b is exact whenever s*q and b lie
 within ~38 binades of each other, which holds for every workload here (s and
 |b| are within a factor of ~100); each product x*w is then exact too (8-bit
-times <= ~45-bit significands).  So in practice only the K-term summation
+times <= ~45-bit significands; 8-bit codes give an 19-bit s*q, still exact).  So in practice only the K-term summation
 rounds, at K * 2^-53 relative at worst -- twelve orders of magnitude below the
 1e-3 tolerance.
 
@@ -80,8 +82,8 @@ def unpack_codes(codes: np.ndarray, K: int, bits: int) -> np.ndarray:
     For column k: byte = codes[n, (k*bits) // 8], shift = (k*bits) % 8,
     q = (byte >> shift) & (2**bits - 1).
     """
-    if bits not in (2, 4):
-        raise ValueError("bits must be 2 or 4")
+    if bits not in (2, 4, 8):
+        raise ValueError("bits must be 2, 4 or 8")
     codes = np.asarray(codes, dtype=np.uint8)
     N = codes.shape[0]
     if codes.shape[1] * 8 != K * bits:

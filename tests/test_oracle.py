@@ -98,7 +98,14 @@ def test_unpack_2bit_closed_form_bytes():
     assert q.tolist() == [[0, 1, 2, 3, 3, 2, 1, 0]]
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+def test_unpack_8bit_closed_form_bytes():
+    # one code per byte, the byte itself (unsigned)
+    codes = np.array([[0x00, 0xFF, 0x80, 0x7F, 0x21]], np.uint8)
+    q = oracle.unpack_codes(codes, 5 * 8 // 8, 8)
+    assert q.tolist() == [[0, 255, 128, 127, 33]]
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
 def test_unpack_matches_bitstream_and_packer(bits):
     rng = np.random.default_rng(3)
     K, N = 128, 5
@@ -142,7 +149,7 @@ def test_dequant_special_cases():
 
 # ---------------------------------------------------------------- closed forms of y
 
-@pytest.mark.parametrize("bits,gs", [(4, 64), (4, 32), (2, 64), (2, 128)])
+@pytest.mark.parametrize("bits,gs", [(4, 64), (4, 32), (2, 64), (2, 128), (8, 64)])
 def test_zero_codes_gives_bias_times_group_sums(bits, gs):
     K, N, M = 256, 24, 3
     p = synth.special_problem(K, N, bits, gs, M, "zero_codes")
@@ -157,7 +164,7 @@ def test_zero_codes_gives_bias_times_group_sums(bits, gs):
             assert abs(y[m, n] - want) <= 1e-12 * (1 + abs(want))
 
 
-@pytest.mark.parametrize("bits,gs", [(4, 64), (4, 128), (2, 32), (2, 64)])
+@pytest.mark.parametrize("bits,gs", [(4, 64), (4, 128), (2, 32), (2, 64), (8, 32), (8, 128)])
 def test_onehot_x_selects_one_dequantized_column(bits, gs):
     K, N = 256, 16
     shape = synth.custom_shape(K, N, bits, gs, seed=11)
@@ -229,6 +236,7 @@ def test_sampled_rows_match_full_result():
 @pytest.mark.parametrize("bits,gs,K,N,M", [
     (4, 32, 64, 5, 2), (4, 64, 192, 7, 3), (4, 128, 256, 4, 2),
     (2, 32, 128, 6, 3), (2, 64, 256, 5, 2), (2, 128, 128, 3, 1),
+    (8, 32, 64, 5, 3), (8, 64, 192, 4, 2), (8, 128, 256, 3, 2),
 ])
 def test_matches_exact_rational_brute_force(bits, gs, K, N, M):
     shape = synth.custom_shape(K, N, bits, gs, seed=100 + K + N + bits)
@@ -265,6 +273,9 @@ def _pin_suite():
         test_onehot_x_selects_one_dequantized_column(2, 32)
         test_matches_exact_rational_brute_force(4, 64, 192, 7, 3)
         test_matches_exact_rational_brute_force(2, 64, 256, 5, 2)
+        test_unpack_8bit_closed_form_bytes()
+        test_onehot_x_selects_one_dequantized_column(8, 32)
+        test_matches_exact_rational_brute_force(8, 64, 192, 4, 2)
     except AssertionError:
         return False
     return True
@@ -276,6 +287,14 @@ def _mutant_high_nibble_first(codes, K, bits):
         q = q.reshape(q.shape[0], -1, 2)[:, :, ::-1].reshape(q.shape[0], K)
     else:
         q = q.reshape(q.shape[0], -1, 4)[:, :, ::-1].reshape(q.shape[0], K)
+    return q
+
+
+def _mutant_signed_bytes(codes, K, bits):
+    # 8-bit codes read as two's-complement int8 (q - 256 for q >= 128)
+    q = qo._orig_unpack(codes, K, bits).astype(np.int16)
+    if bits == 8:
+        q = np.where(q >= 128, q - 256, q)
     return q
 
 
@@ -301,6 +320,7 @@ def _mutant_scale_bias_swapped(q, scales, biases, gs):
 
 @pytest.mark.parametrize("target,mutant", [
     ("unpack_codes", _mutant_high_nibble_first),
+    ("unpack_codes", _mutant_signed_bytes),
     ("dequantize", _mutant_dropped_bias),
     ("dequantize", _mutant_bias_sign),
     ("dequantize", _mutant_group_index),
@@ -476,6 +496,18 @@ def test_generator_is_deterministic_and_shaped():
     q = oracle.unpack_codes(a.codes[:64], 4096, 4)
     freq = np.bincount(q.ravel(), minlength=16) / q.size
     assert np.all(np.abs(freq - 1 / 16) < 0.005)
+
+
+def test_generator_8bit_distributions():
+    s = synth.WORKLOADS["square_k4096_n4096_8b_g64"]
+    a = synth.make_problem(s)
+    assert a.codes.shape == (4096, 4096) and a.scales.shape == (4096, 64)
+    s16 = oracle.fp16_bits_to_f64(a.scales)
+    assert s16.min() >= 1e-4 - 1e-7 and s16.max() <= 1e-3 + 1e-6
+    resid = oracle.fp16_bits_to_f64(a.biases) + 128 * s16
+    assert abs(resid.mean()) < 1e-4 and 0.8e-3 < resid.std() < 1.2e-3
+    freq = np.bincount(a.codes[:64].ravel(), minlength=256) / a.codes[:64].size
+    assert np.all(np.abs(freq - 1 / 256) < 0.001)
 
 
 def test_group_size_sweep_shares_codes_and_x():
