@@ -54,7 +54,7 @@ namespace {
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int validate_shape(int M, int N, int K, int bits, int group_size) {
-  if (bits != 2 && bits != 4) return QGEMV_EINVAL;
+  if (bits != 2 && bits != 4 && bits != 8) return QGEMV_EINVAL;
   if (group_size != 32 && group_size != 64 && group_size != 128) return QGEMV_EINVAL;
   if (M < 1 || M > QGEMV_MAX_M) return QGEMV_EINVAL;
   if (N < 1 || N > QGEMV_MAX_N) return QGEMV_EINVAL;

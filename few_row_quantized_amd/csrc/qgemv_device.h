@@ -1,11 +1,13 @@
 // Device helpers for the few-row quantized GEMV kernels (gfx950, wave64).
 //
-// Codes become bf16 values 128+q: for 0 <= q < 128 the bf16 bit pattern of
-// 128+q is 0x4300 | q (exponent of 2^7, q in the 7 mantissa bits), so one
-// AND-OR places two codes into the two halves of a dword as an exact bf16
-// pair.  Dot products of these pairs with bf16 activations are exact per
+// 2- and 4-bit codes become bf16 values 128+q: for 0 <= q < 128 the bf16 bit
+// pattern of 128+q is 0x4300 | q (exponent of 2^7, q in the 7 mantissa bits),
+// so one AND-OR places two codes into the two halves of a dword as an exact
+// bf16 pair.  Dot products of these pairs with bf16 activations are exact per
 // product in fp32; the 128 offset is removed once per group through the
 // group's activation sum (128 * sum x), folded together with the bias.
+// 8-bit codes (0..255) do not fit that pattern; they are converted exactly
+// without an offset (unpack8_pairs).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -114,6 +116,29 @@ __device__ __forceinline__ u32x4_t unpack2_split_quad(uint32_t w, int h, uint32_
 #pragma unroll
   for (int e = 0; e < 4; ++e) o[e] = ((w >> (2 * (4 * h + e))) & 0x00030003u) | off;
   return o;
+}
+
+// 8-bit codes: byte j of dword w is code j (0..255).  Every code is exact in
+// bf16 (at most 8 significant bits), so no offset is needed: each byte is
+// converted to fp32 (v_cvt_f32_ubyte0..3, exact), whose upper half is the
+// bf16 pattern of the same value, and v_perm packs two such halves.  Pairs are
+// the natural ones, codes (0, 1) and (2, 3): the activations keep their memory
+// order.
+__device__ __forceinline__ uint32_t bf16_pair_of(float lo, float hi) {
+  return perm_b32(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo), 0x07060302u);
+}
+
+__device__ __forceinline__ void unpack8_pairs(uint32_t w, uint32_t (&o)[2]) {
+  o[0] = bf16_pair_of((float)(w & 0xFFu), (float)((w >> 8) & 0xFFu));
+  o[1] = bf16_pair_of((float)((w >> 16) & 0xFFu), (float)(w >> 24));
+}
+
+// Two code dwords (8 codes) as the 4-dword MFMA operand, natural order.
+__device__ __forceinline__ u32x4_t unpack8_quad(uint32_t w0, uint32_t w1) {
+  uint32_t a[2], b[2];
+  unpack8_pairs(w0, a);
+  unpack8_pairs(w1, b);
+  return u32x4_t{a[0], a[1], b[0], b[1]};
 }
 
 // ---------------------------------------------------------------- activation pairing

@@ -14,8 +14,9 @@
 //   re-paired to match the code pairing (elements (e, e+4) for 4-bit codes,
 //   (e, e+8) for 2-bit codes), together with the activation sum of every
 //   lane chunk.  K is staged in pieces when M*K does not fit the LDS budget.
-// * Each code dword is unpacked once into bf16 pairs 128+q and used for all M
-//   rows with v_dot2c_f32_bf16.  The group's scale and bias are applied once
+// * Each code dword is unpacked once into bf16 pairs 128+q (2- and 4-bit
+//   codes) or q (8-bit codes, natural pairs) and used for all M rows with
+//   v_dot2c_f32_bf16.  The group's scale and bias are applied once
 //   per lane chunk and row: acc += s*d + (b - 128 s)*sum(x), i.e. the scale
 //   is folded out of the inner loop (MLX page, Facts: the qmv_wide tuning
 //   bullet) and metadata is read directly per group, not cached across lanes
@@ -167,7 +168,12 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
 #pragma unroll
       for (int i = 0; i < CW / 2; ++i)
         ssum[(2 * i) / SUBW] = dot2_bf16(X[i], 0x3F803F80u, ssum[(2 * i) / SUBW]);
-      if constexpr (BITS == 4) {
+      if constexpr (BITS == 8) {
+        // natural pairs: quad d holds elements 8d..8d+7 in memory order
+#pragma unroll
+        for (int d = 0; d < QUADS; ++d)
+          xl[(m * QUADS + d) * kch + cl] = make_uint4(X[4 * d], X[4 * d + 1], X[4 * d + 2], X[4 * d + 3]);
+      } else if constexpr (BITS == 4) {
         // code dword d covers elements 8d..8d+7; pairs (8d+e, 8d+e+4)
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
@@ -237,7 +243,16 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             const uint32_t cd[4] = {cw[t][r].x, cw[t][r].y, cw[t][r].z, cw[t][r].w};
-            if constexpr (BITS == 4) {
+            if constexpr (BITS == 8) {
+              // quad q = code dwords 2q, 2q+1 (codes 8q..8q+7, natural pairs)
+              uint32_t lo[2], hi[2];
+              unpack8_pairs(cd[2 * q], lo);
+              unpack8_pairs(cd[2 * q + 1], hi);
+              pr[r][0] = lo[0];
+              pr[r][1] = lo[1];
+              pr[r][2] = hi[0];
+              pr[r][3] = hi[1];
+            } else if constexpr (BITS == 4) {
               unpack4_split_pairs(cd[q], pr[r], offset_pair);
             } else {
               uint32_t p8[8];
@@ -264,7 +279,9 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const float sc = half_bits_to_float(sr[t][r][s]);
-          const float bo = fmaf(-128.f, sc, half_bits_to_float(br[t][r][s]));
+          // 2/4-bit codes carry the 128 offset, removed with the bias
+          const float bo = BITS == 8 ? half_bits_to_float(br[t][r][s])
+                                     : fmaf(-128.f, sc, half_bits_to_float(br[t][r][s]));
 #pragma unroll
           for (int m = 0; m < M; ++m) {
             const float xs = xsl[(m * NSUB + s) * kch + c];
@@ -338,14 +355,19 @@ int launch_dot_t(const QgemvArgs &a, hipStream_t stream) {
 
 // rows per wave for each M: enough rows to share each x read (LDS traffic per
 // code byte ~ 4M/R), few enough to keep R*M accumulators in registers.
-template <int M>
+// 8-bit codes fill twice the code registers per row (16 codes per 16-byte
+// chunk), so they take fewer rows per wave.
+template <int BITS, int M>
 constexpr int dot_rows_per_wave() {
+  if constexpr (BITS == 8) return M <= 8 ? 2 : 1;
   return M <= 2 ? 2 : (M <= 4 ? 4 : (M <= 8 ? 2 : 1));
 }
 
 template <int BITS, int M, int R, bool ADD>
 int launch_dot_r(const QgemvArgs &a, hipStream_t stream) {
-  if constexpr (BITS == 2) {
+  if constexpr (BITS == 8) {
+    return launch_dot_t<8, M, R, 1, ADD>(a, stream);  // a 16-code chunk never spans two groups
+  } else if constexpr (BITS == 2) {
     if (a.group_size == 32) return launch_dot_t<2, M, R, 2, ADD>(a, stream);
     return launch_dot_t<2, M, R, 1, ADD>(a, stream);
   } else {
@@ -355,7 +377,7 @@ int launch_dot_r(const QgemvArgs &a, hipStream_t stream) {
 
 template <int BITS, int M, bool ADD>
 int launch_dot_m(const QgemvArgs &a, hipStream_t stream) {
-  constexpr int R = dot_rows_per_wave<M>();
+  constexpr int R = dot_rows_per_wave<BITS, M>();
   // Few rows (small N): fewer rows per wave, so that every CU gets a
   // workgroup.  The row-to-lane arithmetic is the same for every R, so
   // results do not depend on this choice.
@@ -394,8 +416,9 @@ int launch_dot_bits(const QgemvArgs &a, hipStream_t stream) {
   }
 }
 
-// Every instantiation for one value of ADD (each translation unit that includes
-// this header compiles one of them).
+// The instantiations of the 2- and 4-bit codes for one value of ADD; the
+// 8-bit ones are launch_dot_bits<8, ADD> (each translation unit that includes
+// this header compiles one set, so they build in parallel).
 template <bool ADD>
 int launch_dot_impl(const QgemvArgs &a, hipStream_t stream) {
   return a.bits == 4 ? launch_dot_bits<4, ADD>(a, stream) : launch_dot_bits<2, ADD>(a, stream);

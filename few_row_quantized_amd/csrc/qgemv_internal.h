@@ -35,7 +35,8 @@ bool allow_max_dynamic_lds(const void *func);
 
 // Launchers: enqueue on `stream`, return QGEMV_OK / QGEMV_EUNSUPPORTED / QGEMV_EHIP.
 int launch_dot(const QgemvArgs &a, hipStream_t stream);
-int launch_dot_add(const QgemvArgs &a, hipStream_t stream);  // a.res != nullptr
+int launch_dot_add(const QgemvArgs &a, hipStream_t stream);  // a.res != nullptr, 2/4-bit
+int launch_dot8(const QgemvArgs &a, hipStream_t stream);     // 8-bit codes
 int launch_mfma(const QgemvArgs &a, hipStream_t stream);
 // Persistent MFMA kernel (QGEMV_EUNSUPPORTED when the activations of a
 // wave would not fit its registers).

@@ -11,7 +11,8 @@
 // CDNA4 design:
 // * One v_mfma_f32_16x16x32_bf16 computes a 16(m) x 16(n) tile over 32 k.
 //   A = activations (rows m >= M repeat row M-1 and are never stored),
-//   B = weights as exact bf16 values 128+q.  A workgroup owns NT tiles of
+//   B = weights as exact bf16 values 128+q (2/4-bit) or q (8-bit, two code
+//   dwords per MFMA step).  A workgroup owns NT tiles of
 //   16 output columns over the whole of K; its waves split K into
 //   contiguous slices of "bias blocks" (4 groups).
 // * Lane (col = lane%16, kb = lane/16) loads 16 contiguous bytes of row
@@ -62,7 +63,10 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   constexpr int CW = 128 / BITS;       // codes per 16-byte chunk
   constexpr int SCW = 4 * CW;          // codes per 64-byte super-chunk
   constexpr int DW = CW / 4;           // codes per dword
-  constexpr int HS = BITS == 4 ? 1 : 2;  // MFMA steps per code dword
+  constexpr int HS = BITS == 2 ? 2 : 1;  // MFMA steps per code dword (8-bit: one per two dwords)
+  // activation operands per super-chunk: one per code register (2/4-bit) or
+  // per pair of code registers (8-bit)
+  constexpr int XR = BITS == 8 ? 2 : 4;
   constexpr int BLKW = 4 * GS;         // codes per bias block (4 groups)
   constexpr int BSC = BLKW / SCW;      // super-chunks per block
   constexpr int CPG = GS / CW;         // chunks per group (1, 2 or 4)
@@ -150,7 +154,7 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   for (int blk0 = b_begin; blk0 < b_end; blk0 += BPB) {
     const int nb = min(BPB, b_end - blk0);  // blocks in this batch (uniform)
     // ---- issue: activations first (L2), then codes (HBM), then metadata
-    u32x4_t xv[UNR][4][HS];
+    u32x4_t xv[UNR][XR][HS];
     u32x4_t cv[UNR][NT];
     uint2 s4[BPB][NT], b4[BPB][NT];
 #pragma unroll
@@ -158,10 +162,11 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
       if (u / BSC < nb) {
         const int k0 = (blk0 * BSC + u) * SCW;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < XR; ++i)
 #pragma unroll
           for (int l = 0; l < HS; ++l)
-            xv[u][i][l] = *reinterpret_cast<const u32x4_t *>(xr + k0 + xoff[i] + 8 * l);
+            xv[u][i][l] = *reinterpret_cast<const u32x4_t *>(
+                xr + k0 + (BITS == 8 ? xoff[2 * i] : xoff[i]) + 8 * l);
       }
     }
 #pragma unroll
@@ -197,6 +202,17 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
 #pragma unroll
       for (int uu = 0; uu < BSC; ++uu) {
         const int u = bb * BSC + uu;
+        if constexpr (BITS == 8) {
+          // natural order: only the group sums; step e of the super-chunk
+          // holds 8 codes of group (uu*SCW + 32e)/GS of the block
+#pragma unroll
+          for (int e = 0; e < XR; ++e) {
+            const int j = (uu * SCW + 32 * e) / GS;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) P[j] = dot2_bf16(xv[u][e][0][c], 0x3F803F80u, P[j]);
+          }
+          continue;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = uu * GPS + i / REGS_G;  // group within the block
@@ -236,8 +252,35 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
         cur[t][3] = cv[u][t][3];
         transpose_rows_lvl<LVL>(cur[t]);
       }
+      if constexpr (BITS == 8) {
+        // MFMA step e takes code registers 2e, 2e+1 (8 consecutive codes of
+        // this lane's row; the activations at xoff[2e]..+7)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+        for (int e = 0; e < XR; ++e) {
+          const int kk = scb * SCW + 32 * e;  // first code of the step within the block
+          const int j = kk / GS;              // its group within the block
+          const bool gfirst = kk % GS == 0;
+          const bool glast = (kk + 32) % GS == 0;
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xv[u][e][0]);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const u32x4_t bw = unpack8_quad(cur[t][2 * e], cur[t][2 * e + 1]);
+            accg[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                a, __builtin_bit_cast(bf16x8_t, bw), gfirst ? zero4 : accg[t], 0, 0, 0);
+          }
+          if (glast) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              const uint32_t sw = (j < 2) ? s4[u / BSC][t].x : s4[u / BSC][t].y;
+              const float sc = half_bits_to_float((j & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+#pragma unroll
+              for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(sc, accg[t][q], acc[t][q]);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < (BITS == 8 ? 0 : 4); ++i) {
         const int j = scb * GPS + i / REGS_G;  // group within the block
 #pragma unroll
         for (int h = 0; h < HS; ++h) {
@@ -274,7 +317,7 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
           const uint32_t bw = (kb < 2) ? b4[u / BSC][t].x : b4[u / BSC][t].y;
           const float sc = half_bits_to_float((kb & 1) ? (sw >> 16) : (sw & 0xFFFFu));
           const float b = half_bits_to_float((kb & 1) ? (bw >> 16) : (bw & 0xFFFFu));
-          const float bo = fmaf(-128.f, sc, b);
+          const float bo = BITS == 8 ? b : fmaf(-128.f, sc, b);  // 2/4-bit: remove the 128 offset
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum[u / BSC], bo, acc[t], 0, 0, 0);
         }
       }
@@ -366,6 +409,8 @@ struct MfmaShape {
 };
 
 
+
+
 // y[0..n) = v (bit pattern): zero before a K-split launch, kSplitSentinel
 // before one with the residual sum
 __global__ __launch_bounds__(256) void fill_kernel(uint32_t *__restrict__ y, size_t n, uint32_t v) {
@@ -437,7 +482,10 @@ int launch_mfma_gs(const QgemvArgs &a, hipStream_t stream) {
 
 bool mfma_supports(int K, int bits, int group_size) {
   if (bits == 2 && group_size < 64) return false;
-  const int scw = bits == 4 ? 128 : 256;
+  // 8-bit gs128: a bias block (4 groups) would be 8 super-chunks per batch,
+  // beyond the register budget
+  if (bits == 8 && group_size > 64) return false;
+  const int scw = 512 / bits;  // codes per 64-byte super-chunk
   return K % scw == 0 && K % (4 * group_size) == 0;
 }
 
@@ -449,7 +497,12 @@ int launch_mfma(const QgemvArgs &a, hipStream_t stream) {
     const int st = launch_persist(a, stream);
     if (st != QGEMV_EUNSUPPORTED) return st;
   }
-  if (a.bits == 4) {
+  if (a.bits == 8) {
+    switch (a.group_size) {
+      case 32: return launch_mfma_gs<8, 32>(a, stream);
+      case 64: return launch_mfma_gs<8, 64>(a, stream);
+    }
+  } else if (a.bits == 4) {
     switch (a.group_size) {
       case 32: return launch_mfma_gs<4, 32>(a, stream);
       case 64: return launch_mfma_gs<4, 64>(a, stream);

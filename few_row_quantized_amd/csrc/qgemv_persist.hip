@@ -315,6 +315,10 @@ int launch_persist_gs(const QgemvArgs &a, hipStream_t stream) {
 
 int launch_persist(const QgemvArgs &a, hipStream_t stream) {
   if (!mfma_supports(a.K, a.bits, a.group_size)) return QGEMV_EUNSUPPORTED;
+  // 8-bit codes take the single-pass kernel: a persistent variant (one block
+  // per wave) measured slower than it on the 15360 x 3840 shape, 31.5 vs
+  // 18.7 us at M = 1
+  if (a.bits == 8) return QGEMV_EUNSUPPORTED;
   if (a.bits == 4) {
     switch (a.group_size) {
       case 32: return launch_persist_gs<4, 32>(a, stream);

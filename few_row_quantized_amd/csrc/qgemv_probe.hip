@@ -13,6 +13,14 @@ __device__ __forceinline__ uint8_t code_of(uint32_t half16) {
   return ((half16 & 0xFF80u) == 0x4300u) ? (uint8_t)(half16 & 0x7Fu) : (uint8_t)0xFF;
 }
 
+// Extract q from a bf16 pair half that should hold the exact value q
+// (8-bit codes); anything else marks an encoding error (0xFF, which a true
+// code 255 shares: such an error shows only where the code is not 255).
+__device__ __forceinline__ uint8_t code8_of(uint32_t half16) {
+  const float f = bf16_bits_to_float(half16);
+  return (f >= 0.f && f <= 255.f && f == (float)(int)f) ? (uint8_t)(int)f : (uint8_t)0xFF;
+}
+
 // Dot-path decoding: one thread per (row n, 16-byte chunk c), same unpack
 // routines and pair-to-column mapping as qgemv_dot_kernel.
 template <int BITS>
@@ -30,7 +38,15 @@ __global__ __launch_bounds__(256) void unpack_probe_dot(const uint8_t *__restric
   uint8_t *qr = q + (size_t)n * K + (size_t)c * CW;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    if constexpr (BITS == 4) {
+    if constexpr (BITS == 8) {
+      uint32_t p[2];
+      unpack8_pairs(cd[d], p);  // pairs (4d, 4d+1), (4d+2, 4d+3)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        qr[4 * d + 2 * e] = code8_of(p[e] & 0xFFFFu);
+        qr[4 * d + 2 * e + 1] = code8_of(p[e] >> 16);
+      }
+    } else if constexpr (BITS == 4) {
       uint32_t p[4];
       unpack4_split_pairs(cd[d], p);
 #pragma unroll
@@ -73,6 +89,20 @@ __global__ __launch_bounds__(64) void unpack_probe_mfma(const uint8_t *__restric
   if (tile * 16 + col >= N) return;
   uint8_t *qr = q + (size_t)n * K + (size_t)sc * SCW;
   const uint32_t off = kOffsetPair;
+  if constexpr (BITS == 8) {
+    // MFMA step e: registers 2e, 2e+1 = 8 consecutive codes from k0(2e)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int k0 = lvl_chunk<LVL>(2 * e, kb) * CW + lvl_dword<LVL>(2 * e, kb) * DW;
+      const u32x4_t p = unpack8_quad(r[2 * e], r[2 * e + 1]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        qr[k0 + 2 * c] = code8_of(p[c] & 0xFFFFu);
+        qr[k0 + 2 * c + 1] = code8_of(p[c] >> 16);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int k0 = lvl_chunk<LVL>(i, kb) * CW + lvl_dword<LVL>(i, kb) * DW;
@@ -139,7 +169,9 @@ int launch_unpack_probe(int path, const uint8_t *codes, uint8_t *q_out, int N, i
     const int CW = 128 / bits;
     const size_t threads = (size_t)N * (K / CW);
     const int blocks = (int)((threads + 255) / 256);
-    if (bits == 4)
+    if (bits == 8)
+      hipLaunchKernelGGL(unpack_probe_dot<8>, dim3(blocks), dim3(256), 0, stream, codes, q_out, N, K);
+    else if (bits == 4)
       hipLaunchKernelGGL(unpack_probe_dot<4>, dim3(blocks), dim3(256), 0, stream, codes, q_out, N, K);
     else
       hipLaunchKernelGGL(unpack_probe_dot<2>, dim3(blocks), dim3(256), 0, stream, codes, q_out, N, K);
@@ -149,7 +181,10 @@ int launch_unpack_probe(int path, const uint8_t *codes, uint8_t *q_out, int N, i
     const int cpg = group_size / CW;  // chunks per group -> exchange level
     const int lvl = cpg >= 4 ? 0 : (cpg == 2 ? 1 : 2);
     const dim3 g(blocks), b(64);
-    if (bits == 4) {
+    if (bits == 8) {
+      if (lvl == 0) hipLaunchKernelGGL((unpack_probe_mfma<8, 0>), g, b, 0, stream, codes, q_out, N, K);
+      else hipLaunchKernelGGL((unpack_probe_mfma<8, 1>), g, b, 0, stream, codes, q_out, N, K);
+    } else if (bits == 4) {
       if (lvl == 0) hipLaunchKernelGGL((unpack_probe_mfma<4, 0>), g, b, 0, stream, codes, q_out, N, K);
       else if (lvl == 1) hipLaunchKernelGGL((unpack_probe_mfma<4, 1>), g, b, 0, stream, codes, q_out, N, K);
       else hipLaunchKernelGGL((unpack_probe_mfma<4, 2>), g, b, 0, stream, codes, q_out, N, K);

@@ -18,7 +18,9 @@
  *   codes   uint8 [N][K*bits/8], row-major, no padding between rows.
  *           bits = 4: two codes per byte, column k in bits 4*(k%2).. (low
  *           nibble first).  bits = 2: four codes per byte, column k in bits
- *           2*(k%4).. (lowest crumb first).
+ *           2*(k%4).. (lowest crumb first).  bits = 8: one code per byte,
+ *           the unsigned byte (the int8 affine mode of qmv_wide, MLX page,
+ *           Facts: the int8 M=8 speedup).
  *   scales  IEEE fp16 bit patterns [N][K/gs], row-major.
  *   biases  IEEE fp16 bit patterns [N][K/gs], row-major.
  * Activations x: bfloat16 bit patterns [M][K], row-major (weights are stored
@@ -70,7 +72,7 @@ extern "C" {
  * qgemv_select.
  *
  * Requirements (else QGEMV_EINVAL / QGEMV_EALIGN):
- *   bits in {2, 4}; group_size in {32, 64, 128}; 1 <= M <= 16;
+ *   bits in {2, 4, 8}; group_size in {32, 64, 128}; 1 <= M <= 16;
  *   1 <= N <= QGEMV_MAX_N; 64 <= K <= QGEMV_MAX_K; K % 64 == 0;
  *   K % group_size == 0; codes, scales, biases, x, y non-NULL and each
  *   16-byte aligned (every device allocation is).
@@ -137,8 +139,9 @@ int qgemv_select(int M, int N, int K, int bits, int group_size);
  * pages' A/B knobs: the specgate-metal README's GGML_METAL_NO_MV_EXT /
  * GGML_METAL_MM_MIN; MLX page, Facts: forced qmv vs qmm sweeps).
  * Returns QGEMV_EUNSUPPORTED if the path cannot run the shape (the MFMA path
- * needs K to be a multiple of 4*group_size and of 128 (4-bit) / 256 (2-bit),
- * and group_size >= 64 for 2-bit codes).  Other arguments as qgemv_small.
+ * needs K to be a multiple of 4*group_size and of 256 (2-bit) / 128 (4-bit) /
+ * 64 (8-bit), group_size >= 64 for 2-bit codes and group_size <= 64 for 8-bit
+ * codes).  Other arguments as qgemv_small.
  */
 int qgemv_run_path(int path, const uint8_t *codes, const uint16_t *scales,
                    const uint16_t *biases, const uint16_t *x, float *y, int M, int N, int K,

@@ -31,7 +31,7 @@ def _check(p, y, M, cols, label):
     assert ok, f"{label}: worst |dy|/tol = {worst:.3g} at {idx}"
 
 
-@pytest.mark.parametrize("N,bits,gs", [(40, 4, 128), (24, 2, 64)])
+@pytest.mark.parametrize("N,bits,gs", [(40, 4, 128), (24, 2, 64), (20, 8, 64)])
 def test_longest_k_every_element(N, bits, gs):
     K = q.MAX_K
     p = synth.make_problem(synth.custom_shape(K, N, bits, gs, seed=11 + N, outliers=True), m_max=16)
@@ -44,7 +44,7 @@ def test_longest_k_every_element(N, bits, gs):
             _check(p, d.run_host(M, path), M, None, f"{path} K={K} N={N} M={M}")
 
 
-@pytest.mark.parametrize("K,bits,gs", [(128, 4, 32), (256, 2, 64)])
+@pytest.mark.parametrize("K,bits,gs", [(128, 4, 32), (256, 2, 64), (128, 8, 32)])
 def test_widest_n_sampled_columns(K, bits, gs):
     N = q.MAX_N
     p = synth.make_problem(synth.custom_shape(K, N, bits, gs, seed=13 + K), m_max=16)

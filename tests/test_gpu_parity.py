@@ -48,6 +48,7 @@ def supported(path, p, M=1):
 UNPACK_SHAPES = [
     (256, 512, 4, 64), (512, 40, 4, 32), (1024, 17, 4, 128),
     (512, 40, 2, 64), (1024, 33, 2, 128), (512, 24, 2, 32),
+    (256, 512, 8, 64), (512, 40, 8, 32), (1024, 17, 8, 128),
 ]
 
 
@@ -84,7 +85,8 @@ def test_unpack_probe_full_size(path, name):
     assert np.array_equal(out.cpu().numpy(), oracle.unpack_codes(p.codes, s.K, s.bits))
 
 
-@pytest.mark.parametrize("bits,gs", [(4, 64), (4, 32), (4, 128), (2, 64), (2, 128), (2, 32)])
+@pytest.mark.parametrize("bits,gs", [(4, 64), (4, 32), (4, 128), (2, 64), (2, 128), (2, 32),
+                                     (8, 32), (8, 64), (8, 128)])
 @pytest.mark.parametrize("path", ["dot", "mfma"])
 def test_unit_scale_onehot_gives_codes_exactly(path, bits, gs):
     K, N, M = 1024, 48, 16
@@ -116,6 +118,8 @@ RAGGED = [
     (640, 40, 4, 32), (1024, 300, 4, 64), (2048, 97, 4, 128), (8192, 33, 4, 64),
     (512, 72, 2, 32), (1280, 300, 2, 64), (2048, 129, 2, 128), (17408, 23, 2, 64),
     (64, 16, 4, 32), (64, 5, 2, 64),
+    (640, 40, 8, 32), (1024, 300, 8, 64), (2048, 97, 8, 128), (8192, 33, 8, 64), (64, 16, 8, 32),
+    (3840, 200, 8, 64),
 ]
 
 
@@ -138,6 +142,7 @@ def test_ragged_shapes_every_element(path, K, N, bits, gs):
 PERSIST = [
     (1024, 4113, 4, 32), (2048, 4500, 4, 64), (3072, 5000, 4, 128), (6144, 4200, 4, 128),
     (1280, 4700, 2, 64), (2048, 9000, 2, 128), (8192, 4500, 4, 128),
+    (1024, 4113, 8, 32), (2048, 4500, 8, 64),
 ]
 
 
@@ -162,7 +167,8 @@ def test_zero_codes(path):
 
 @pytest.mark.parametrize("bits,gs,N,K", [(4, 64, 200, 2048), (2, 64, 200, 2048), (4, 128, 200, 2048),
                                          (4, 64, 4500, 2048), (2, 128, 4500, 2048),
-                                         (4, 128, 300, 8192), (2, 64, 150, 10240)])
+                                         (4, 128, 300, 8192), (2, 64, 150, 10240),
+                                         (8, 64, 200, 2048), (8, 32, 4500, 1024), (8, 64, 150, 10240)])
 @pytest.mark.parametrize("path", ["dot", "mfma"])
 def test_row_of_m_row_call_equals_single_row_call_bitwise(path, bits, gs, N, K):
     import torch
@@ -182,7 +188,8 @@ def test_row_of_m_row_call_equals_single_row_call_bitwise(path, bits, gs, N, K):
         assert np.array_equal(y, singles[:M]), f"M={M}"
 
 
-@pytest.mark.parametrize("name", ["square_k4096_n4096_4b_g64", "layer27b_gate", "layer27b_down"])
+@pytest.mark.parametrize("name", ["square_k4096_n4096_4b_g64", "layer27b_gate", "layer27b_down",
+                                  "mlxbench_k5120_n17408_8b_g64"])
 @pytest.mark.parametrize("path", ["dot", "mfma"])
 def test_repeated_calls_are_bitwise_identical(path, name):
     s = synth.WORKLOADS[name]

@@ -66,6 +66,7 @@ SHAPES = [
     (256, 512, 4, 64), (640, 40, 4, 32), (1024, 300, 4, 64), (2048, 97, 4, 128),
     (8192, 33, 4, 64), (512, 72, 2, 32), (1280, 300, 2, 64), (17408, 23, 2, 64),
     (64, 5, 2, 64), (2048, 4500, 4, 64), (1280, 4700, 2, 64), (5120, 1024, 4, 128),
+    (1024, 300, 8, 64), (2048, 4500, 8, 32), (5120, 1024, 8, 64), (2048, 97, 8, 128),
 ]
 
 
@@ -138,7 +139,8 @@ def test_add_row_of_m_row_call_equals_single_row_call(path, K, N, bits, gs):
 
 FULL = [("square_k4096_n4096_4b_g64", (1, 4, 8)), ("layer27b_k", (1, 8, 16)),
         ("layer27b_gate", (2, 8, 16)), ("layer27b_down", (1, 4, 8, 16)),
-        ("lowram27b_down_k17408_n5120_2b_g64", (2, 12)), ("ffnup_k4096_n12288_4b_g32", (4, 8))]
+        ("lowram27b_down_k17408_n5120_2b_g64", (2, 12)), ("ffnup_k4096_n12288_4b_g32", (4, 8)),
+        ("mlxbench_k5120_n17408_8b_g64", (1, 8, 16))]
 
 
 @pytest.mark.parametrize("name,ms", FULL)

@@ -60,7 +60,8 @@ MIS = A + 4   # not 16-byte aligned
     (1, 64, 96, 4, 32, q.EINVAL),         # K % 64 != 0
     (1, 64, 192, 4, 128, q.EINVAL),       # K % gs != 0
     (1, 64, 256, 3, 64, q.EINVAL),        # bits
-    (1, 64, 256, 8, 64, q.EINVAL),        # bits
+    (1, 64, 256, 6, 64, q.EINVAL),        # bits
+    (1, 64, 256, 16, 64, q.EINVAL),       # bits
     (1, 64, 256, 4, 16, q.EINVAL),        # group size
     (1, 64, 256, 4, 256, q.EINVAL),       # group size
     (1, 64, 262144, 4, 64, q.EINVAL),     # K above the limit
@@ -91,7 +92,7 @@ def test_misaligned_pointers_rejected(which):
 
 @pytest.mark.parametrize("M,N,K,bits,gs,want", [
     (0, 64, 256, 4, 64, q.EINVAL), (17, 64, 256, 4, 64, q.EINVAL), (1, 64, 96, 4, 32, q.EINVAL),
-    (1, 64, 256, 8, 64, q.EINVAL), (1, 64, 256, 4, 16, q.EINVAL),
+    (1, 64, 256, 6, 64, q.EINVAL), (1, 64, 256, 4, 16, q.EINVAL),
 ])
 def test_add_invalid_shapes_rejected(M, N, K, bits, gs, want):
     L = q.lib()
@@ -139,12 +140,15 @@ def test_mfma_path_shape_support():
     assert not sup("mfma", 4, 4096, 192, 4, 32)     # K not a multiple of 128
     assert not sup("mfma", 4, 4096, 640, 4, 128)    # K not a multiple of 4*gs
     assert sup("dot", 4, 4096, 192, 4, 32)
+    assert sup("mfma", 4, 4096, 4096, 8, 32) and sup("mfma", 4, 4096, 4096, 8, 64)
+    assert not sup("mfma", 4, 4096, 4096, 8, 128)   # 8-bit gs128: dot path only
+    assert sup("dot", 4, 4096, 4096, 8, 128)
     # a forced path that cannot run the shape is refused before launch
     assert q.lib().qgemv_run_path(q.PATH_MFMA, A, A, A, A, A, 4, 64, 192, 4, 32, None) == q.EUNSUPPORTED
 
 
 def test_select_returns_a_supported_path_everywhere():
-    for bits in (2, 4):
+    for bits in (2, 4, 8):
         for gs in (32, 64, 128):
             for K in (256, 640, 4096, 5120, 17408):
                 if K % gs:
