@@ -15,7 +15,7 @@ output (written once).
 from __future__ import annotations
 
 __all__ = ["code_bytes", "meta_bytes", "weight_bytes", "algorithmic_bytes", "useful_flops",
-           "metadata_share"]
+           "metadata_share", "fp_weight_bytes", "fp_algorithmic_bytes"]
 
 
 def code_bytes(N: int, K: int, bits: int) -> int:
@@ -33,6 +33,15 @@ def weight_bytes(N: int, K: int, bits: int, group_size: int) -> int:
 
 def algorithmic_bytes(M: int, N: int, K: int, bits: int, group_size: int) -> int:
     return weight_bytes(N, K, bits, group_size) + 2 * M * K + 4 * M * N
+
+
+def fp_weight_bytes(N: int, K: int, bits: int, block: int) -> int:
+    """Block-scaled FP formats: packed elements plus one scale byte per block."""
+    return code_bytes(N, K, bits) + N * (K // block)
+
+
+def fp_algorithmic_bytes(M: int, N: int, K: int, bits: int, block: int) -> int:
+    return fp_weight_bytes(N, K, bits, block) + 2 * M * K + 4 * M * N
 
 
 def useful_flops(M: int, N: int, K: int) -> int:

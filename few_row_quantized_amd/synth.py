@@ -26,6 +26,9 @@ Because the codes are i.i.d. uniform, the packed bytes are i.i.d. uniform over
 
 Draw order per problem: codes, scales, bias noise, x, outlier channels.  The
 second parameter of N(0, 1e-3) is read as a standard deviation.
+
+Block-scaled FP formats (mxfp4, nvfp4, mxfp8) draw element codes and scale
+bytes directly in their storage encodings (see _draw_fp), then x.
 """
 from __future__ import annotations
 
@@ -50,12 +53,21 @@ class Shape:
     # Problems that share `share_key` share codes and x (only scales and
     # biases are redrawn), as in the group-size sweep.
     share_key: Optional[str] = None
+    # Block-scaled floating-point format ("mxfp4", "nvfp4", "mxfp8"); None for
+    # the affine codes.  For these, `bits` is the element width, `group_size`
+    # the scale block, `scales` holds one scale byte per block and `biases` is
+    # empty.
+    fmt: Optional[str] = None
 
 
 def _layer(name: str, K: int, N: int, idx: int) -> Shape:
     return Shape(f"layer27b_{name}", K, N, 4, 128, tuple(range(1, 17)),
                  seed=40000 + 100 * idx, outliers=True)
 
+
+# Element width and scale block of the FP block formats.
+FP_BITS = {"mxfp4": 4, "nvfp4": 4, "mxfp8": 8}
+FP_BLOCK = {"mxfp4": 32, "nvfp4": 16, "mxfp8": 32}
 
 # Workloads.  Names say what they are; seeds are fixed per workload.
 WORKLOADS: Dict[str, Shape] = {s.name: s for s in [
@@ -78,6 +90,12 @@ WORKLOADS: Dict[str, Shape] = {s.name: s for s in [
     Shape("square_k4096_n4096_8b_g64", 4096, 4096, 8, 64, (1, 2, 3, 4, 5, 8), seed=50000),
     Shape("gemma12b_gateup_k3840_n15360_8b_g64", 3840, 15360, 8, 64, (1, 2, 4, 8), seed=50100),
     Shape("mlxbench_k5120_n17408_8b_g64", 5120, 17408, 8, 64, tuple(range(1, 17)), seed=50200),
+    # block-scaled FP modes of qmv_wide (MLX page, Facts: nvfp4, mxfp4 and
+    # mxfp8 speedups on the Gemma-4-12B gate/up shape 15360x3840)
+    *[Shape(f"{pre}_{fmt}", K, N, FP_BITS[fmt], FP_BLOCK[fmt], ms, seed=seed + off, fmt=fmt)
+      for off, fmt in enumerate(("mxfp4", "nvfp4", "mxfp8"))
+      for pre, K, N, ms, seed in (("square_k4096_n4096", 4096, 4096, (1, 2, 3, 4, 5, 8), 60000),
+                                  ("gemma12b_gateup_k3840_n15360", 3840, 15360, (1, 2, 4, 8), 60100))],
 ]}
 
 LAYER27B = [f"layer27b_{p}" for p in ("q", "k", "v", "o", "gate", "up", "down")]
@@ -165,11 +183,43 @@ def _draw_x(rng: np.random.Generator, M: int, K: int, outliers: bool):
     return f32_to_bf16_bits(x32), chans
 
 
+def _draw_fp(rng: np.random.Generator, N: int, K: int, fmt: str):
+    """Elements and scale bytes of a block-scaled FP format.
+
+    FP4 elements: uniform nibbles (every E2M1 value, both zeros).  FP8
+    elements: uniform over the 254 finite E4M3 bytes.  E8M0 scales: exponent
+    uniform in 116..121 (mxfp4, 2^-11..2^-6) or 110..115 (mxfp8, 2^-17..2^-12),
+    so weights span about the 4-bit affine range.  nvfp4 E4M3 scales: exponent
+    field 1..3, mantissa uniform (2^-6 .. 1.875*2^-4), positive."""
+    bits, block = FP_BITS[fmt], FP_BLOCK[fmt]
+    G = K // block
+    if bits == 4:
+        codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    else:
+        v = rng.integers(0, 254, size=(N, K)).astype(np.int64)
+        v = v + (v >= 0x7F)  # skip 0x7F (NaN); 0xFF is never reached
+        codes = v.astype(np.uint8)
+    if fmt == "nvfp4":
+        e = rng.integers(1, 4, size=(N, G))
+        m = rng.integers(0, 8, size=(N, G))
+        scales = ((e << 3) | m).astype(np.uint8)
+    else:
+        lo = 116 if fmt == "mxfp4" else 110
+        scales = rng.integers(lo, lo + 6, size=(N, G)).astype(np.uint8)
+    return codes, scales
+
+
 def make_problem(shape: Shape, m_max: Optional[int] = None, seed: Optional[int] = None) -> Problem:
     """Draw one problem.  x has m_max rows (default: the workload's largest M);
-    an M-row call uses the first M rows."""
+    an M-row call uses the first M rows.  FP formats: codes, scale bytes, x
+    (draw order), biases empty."""
     m_max = m_max or max(shape.m_values)
     base_seed = shape.seed if seed is None else seed
+    if shape.fmt is not None:
+        rng = np.random.default_rng(base_seed)
+        codes, scales = _draw_fp(rng, shape.N, shape.K, shape.fmt)
+        x, chans = _draw_x(rng, m_max, shape.K, shape.outliers)
+        return Problem(shape, codes, scales, np.zeros((shape.N, 0), np.uint16), x, chans, base_seed)
     if shape.share_key is not None and seed is None:
         # Shared codes and x across the group-size sweep; scales/biases per gs.
         shared_seed = min(s.seed for s in WORKLOADS.values() if s.share_key == shape.share_key)
@@ -191,6 +241,13 @@ def custom_shape(K: int, N: int, bits: int, group_size: int, m_values: Sequence[
     """A shape outside the named workloads (tests: ragged tails, edge cases)."""
     return Shape(name or f"custom_k{K}_n{N}_{bits}b_g{group_size}", K, N, bits, group_size,
                  tuple(m_values), seed, outliers)
+
+
+def custom_fp_shape(K: int, N: int, fmt: str, m_values: Sequence[int] = (1,), seed: int = 1234,
+                    outliers: bool = False) -> Shape:
+    """An FP-format shape outside the named workloads."""
+    return Shape(f"custom_k{K}_n{N}_{fmt}", K, N, FP_BITS[fmt], FP_BLOCK[fmt], tuple(m_values),
+                 seed, outliers, fmt=fmt)
 
 
 def special_problem(K: int, N: int, bits: int, group_size: int, M: int, kind: str,

@@ -62,6 +62,14 @@ __all__ = [
     "abs_product_sum",
     "tolerance",
     "check_close",
+    "FP_FORMATS",
+    "e2m1_to_f64",
+    "e4m3_to_f64",
+    "e8m0_to_f64",
+    "fp_elements",
+    "fp_dequantize",
+    "qgemv_fp_reference",
+    "fp_abs_product_sum",
 ]
 
 
@@ -201,3 +209,103 @@ def check_close(y_test, y_ref, abs_sum, rel: float = 1e-3, abs_floor: float = 1e
     idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
     worst = float(ratio[idx])
     return worst <= 1.0, worst, tuple(int(i) for i in idx)
+
+
+# ---------------------------------------------------------------- FP block formats
+#
+# The block-scaled floating-point modes of qmv_wide (MLX page, Facts: qmv_wide
+# covers affine, nvfp4, mxfp4 and mxfp8; their M=8 speedups on the Gemma-4-12B
+# gate/up shape).  The pages name the modes but not their encodings; these
+# decoders follow the public OCP Microscaling Formats (MX) v1.0 specification
+# (element types FP4 E2M1 and FP8 E4M3, shared scale E8M0, block of 32) and,
+# for nvfp4, the same E2M1 elements with an FP8 E4M3 scale per block of 16.
+# Each weight is w[n,k] = scale[n, k // block] * element[n,k]; there is no
+# bias.  Elements are packed along K like the affine codes: two FP4 elements
+# per byte, low nibble first; one FP8 element per byte.
+
+FP_FORMATS = {
+    # name: (element bits, block size, scale type)
+    "mxfp4": (4, 32, "e8m0"),
+    "nvfp4": (4, 16, "e4m3"),
+    "mxfp8": (8, 32, "e8m0"),
+}
+
+
+def e2m1_to_f64(nibbles: np.ndarray) -> np.ndarray:
+    """FP4 E2M1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0.
+    Exponent 0 is subnormal (0 or 0.5); no infinities or NaNs."""
+    v = np.asarray(nibbles, dtype=np.int64) & 0xF
+    sign = np.where(v & 0x8, -1.0, 1.0)
+    e = (v >> 1) & 0x3
+    m = v & 0x1
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, e - 1))
+    return sign * mag
+
+
+def e4m3_to_f64(bytes_: np.ndarray) -> np.ndarray:
+    """FP8 E4M3 (OCP): sign bit 7, exponent bits 6..3 (bias 7), mantissa bits
+    2..0.  Exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN; no
+    infinities (max 448)."""
+    v = np.asarray(bytes_, dtype=np.int64) & 0xFF
+    sign = np.where(v & 0x80, -1.0, 1.0)
+    e = (v >> 3) & 0xF
+    m = v & 0x7
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def e8m0_to_f64(bytes_: np.ndarray) -> np.ndarray:
+    """E8M0 shared scale: 2^(e - 127); e = 255 is NaN."""
+    e = np.asarray(bytes_, dtype=np.int64) & 0xFF
+    return np.where(e == 255, np.nan, np.ldexp(1.0, e - 127))
+
+
+def fp_elements(codes: np.ndarray, K: int, fmt: str) -> np.ndarray:
+    """Packed elements [N, K*bits/8] -> element values [N, K] in fp64 (exact)."""
+    bits, _, _ = FP_FORMATS[fmt]
+    q = unpack_codes(codes, K, bits)  # the raw 4- or 8-bit fields, same packing as affine codes
+    return e2m1_to_f64(q) if bits == 4 else e4m3_to_f64(q)
+
+
+def fp_scales(scales: np.ndarray, fmt: str) -> np.ndarray:
+    _, _, stype = FP_FORMATS[fmt]
+    return e8m0_to_f64(scales) if stype == "e8m0" else e4m3_to_f64(scales)
+
+
+def fp_dequantize(codes: np.ndarray, scales: np.ndarray, K: int, fmt: str) -> np.ndarray:
+    """w[n,k] = scale[n, k // block] * element[n,k] in fp64 (exact: the product
+    of a <= 4-bit and a power-of-two or 4-bit significand)."""
+    _, block, _ = FP_FORMATS[fmt]
+    el = fp_elements(codes, K, fmt)
+    s = fp_scales(scales, fmt)
+    if s.shape != (el.shape[0], K // block):
+        raise ValueError("scales must be [N, K/block]")
+    return s[:, np.arange(K) // block] * el
+
+
+def qgemv_fp_reference(codes, scales, x_bits, M: int, N: int, K: int, fmt: str,
+                       rows: Optional[Sequence[int]] = None, residual=None) -> np.ndarray:
+    """y_ref[m, j] = sum_k x[m,k] * w[n_j, k] (+ residual[m, n_j]) in fp64."""
+    x = bf16_bits_to_f64(np.asarray(x_bits)[:M])
+    if x.shape != (M, K):
+        raise ValueError("x must have at least M rows of length K")
+    n_out = N if rows is None else len(rows)
+    y = np.empty((M, n_out), dtype=np.float64)
+    for start, idx in _row_chunks(N, K, rows):
+        w = fp_dequantize(codes[idx], scales[idx], K, fmt)
+        y[:, start:start + len(idx)] = x @ w.T
+    if residual is not None:
+        y += residual_f64(residual, M, N, rows)
+    return y
+
+
+def fp_abs_product_sum(codes, scales, x_bits, M: int, N: int, K: int, fmt: str,
+                       rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """sum_k |x[m,k] * w[n,k]| in fp64 (the scale of the tolerance)."""
+    x = np.abs(bf16_bits_to_f64(np.asarray(x_bits)[:M]))
+    n_out = N if rows is None else len(rows)
+    out = np.empty((M, n_out), dtype=np.float64)
+    for start, idx in _row_chunks(N, K, rows):
+        out[:, start:start + len(idx)] = x @ np.abs(fp_dequantize(codes[idx], scales[idx], K, fmt)).T
+    return out

@@ -69,7 +69,7 @@ def test_unpack_probe_is_bit_exact(path, K, N, bits, gs):
     assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+@pytest.mark.parametrize("name", [n for n, w in synth.WORKLOADS.items() if w.fmt is None])
 @pytest.mark.parametrize("path", ["dot", "mfma"])
 def test_unpack_probe_full_size(path, name):
     import torch
@@ -205,7 +205,7 @@ def test_repeated_calls_are_bitwise_identical(path, name):
 
 FULL_CASES = []
 for _name, _s in synth.WORKLOADS.items():
-    if _name.startswith("tiny"):
+    if _name.startswith("tiny") or _s.fmt is not None:
         continue
     ms = list(_s.m_values)
     if len(ms) > 6:
