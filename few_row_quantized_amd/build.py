@@ -30,7 +30,8 @@ COMMON_FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
-SOURCES = ["qgemv_api.cpp", "qgemv_dot.hip", "qgemv_dot_add.hip", "qgemv_dot8.hip", "qgemv_mfma.hip",
+SOURCES = ["qgemv_api.cpp", "qgemv_dot.hip", "qgemv_dot_add.hip", "qgemv_dot8.hip", "qgemv_dot_fp.hip",
+           "qgemv_mfma.hip",
            "qgemv_persist.hip", "qgemv_probe.hip"]
 
 

@@ -190,6 +190,114 @@ int qgemv_stream_probe(const uint8_t *buf, size_t nbytes, uint32_t *out, void *s
   return qgemv::launch_stream_probe(buf, nbytes, out, reinterpret_cast<hipStream_t>(stream));
 }
 
+// ---------------------------------------------------------------- FP block formats
+
+}  // extern "C"
+
+namespace {
+
+int fp_bits(int fmt) { return fmt == QGEMV_FMT_MXFP8 ? 8 : 4; }
+int fp_block(int fmt) { return fmt == QGEMV_FMT_NVFP4 ? 16 : 32; }
+
+int validate_fp_shape(int M, int N, int K, int fmt) {
+  if (fmt != QGEMV_FMT_MXFP4 && fmt != QGEMV_FMT_NVFP4 && fmt != QGEMV_FMT_MXFP8) return QGEMV_EINVAL;
+  if (M < 1 || M > QGEMV_MAX_M) return QGEMV_EINVAL;
+  if (N < 1 || N > QGEMV_MAX_N) return QGEMV_EINVAL;
+  if (K < 64 || K > QGEMV_MAX_K || K % 64 != 0) return QGEMV_EINVAL;
+  return QGEMV_OK;
+}
+
+bool fp_path_supported(int path, int K, int fmt) {
+  if (path == QGEMV_PATH_DOT || path == QGEMV_PATH_AUTO) return true;
+  if (path == QGEMV_PATH_MFMA) return qgemv::mfma_supports_fp(K, fmt);
+  return false;
+}
+
+// FP formats are keyed in the measured table by 100 + format.
+int select_path_fp(int M, int N, int K, int fmt) {
+  if (!qgemv::mfma_supports_fp(K, fmt)) return QGEMV_PATH_DOT;
+  const int nc = qgemv::select_n_class(N), kc = qgemv::select_k_class(K);
+  const qgemv::SelectEntry *best = nullptr;
+  int best_d = 1 << 30;
+  for (const auto &e : qgemv::kSelectTable) {
+    if (e.bits != 100 + fmt) continue;
+    const int d = 4 * (e.n_class > nc ? e.n_class - nc : nc - e.n_class) +
+                  (e.k_class > kc ? e.k_class - kc : kc - e.k_class);
+    if (d < best_d) {
+      best_d = d;
+      best = &e;
+    }
+  }
+  if (!best) return M >= 3 ? QGEMV_PATH_MFMA : QGEMV_PATH_DOT;
+  return ((best->mfma_mask >> (M - 1)) & 1u) ? QGEMV_PATH_MFMA : QGEMV_PATH_DOT;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qgemv_select_fp(int M, int N, int K, int format) {
+  const int s = validate_fp_shape(M, N, K, format);
+  if (s != QGEMV_OK) return s;
+  return select_path_fp(M, N, K, format);
+}
+
+int qgemv_path_supported_fp(int path, int M, int N, int K, int format) {
+  const int s = validate_fp_shape(M, N, K, format);
+  if (s != QGEMV_OK) return s;
+  if (path != QGEMV_PATH_AUTO && path != QGEMV_PATH_DOT && path != QGEMV_PATH_MFMA)
+    return QGEMV_EINVAL;
+  return fp_path_supported(path, K, format) ? 1 : 0;
+}
+
+int qgemv_run_path_fp(int path, const uint8_t *codes, const uint8_t *scales, const uint16_t *x,
+                      const float *residual, float *y, int M, int N, int K, int format,
+                      void *stream) {
+  if (path != QGEMV_PATH_AUTO && path != QGEMV_PATH_DOT && path != QGEMV_PATH_MFMA)
+    return QGEMV_EINVAL;
+  const int s = validate_fp_shape(M, N, K, format);
+  if (s != QGEMV_OK) return s;
+  if (!codes || !scales || !x || !y) return QGEMV_EINVAL;
+  if (!aligned(codes, 16) || !aligned(scales, 16) || !aligned(x, 16) || !aligned(y, 16))
+    return QGEMV_EALIGN;
+  if (residual) {
+    if (!aligned(residual, 16)) return QGEMV_EALIGN;
+    if (residual != y) {
+      const uintptr_t r0 = reinterpret_cast<uintptr_t>(residual), y0 = reinterpret_cast<uintptr_t>(y);
+      const uintptr_t len = (uintptr_t)M * (uintptr_t)N * sizeof(float);
+      if (r0 < y0 + len && y0 < r0 + len) return QGEMV_EINVAL;
+    }
+  }
+  if (path == QGEMV_PATH_AUTO) path = select_path_fp(M, N, K, format);
+  if (!fp_path_supported(path, K, format)) return QGEMV_EUNSUPPORTED;
+  // scales travel in the affine scale slot as bytes; biases are unused (a
+  // valid pointer is passed so that no kernel forms an address from null)
+  const uint16_t *sp = reinterpret_cast<const uint16_t *>(scales);
+  QgemvArgs a{codes, sp, sp, x, y, M, N, K, fp_bits(format), fp_block(format)};
+  a.res = residual;
+  a.fmt = format;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return path == QGEMV_PATH_MFMA ? qgemv::launch_mfma(a, st) : qgemv::launch_dot(a, st);
+}
+
+int qgemv_small_fp(const uint8_t *codes, const uint8_t *scales, const uint16_t *x,
+                   const float *residual, float *y, int M, int N, int K, int format,
+                   void *stream) {
+  return qgemv_run_path_fp(QGEMV_PATH_AUTO, codes, scales, x, residual, y, M, N, K, format, stream);
+}
+
+int qgemv_unpack_probe_fp(int path, const uint8_t *codes, uint16_t *out, int N, int K, int format,
+                          void *stream) {
+  const int s = validate_fp_shape(1, N, K, format);
+  if (s != QGEMV_OK) return s;
+  if (path != QGEMV_PATH_DOT && path != QGEMV_PATH_MFMA) return QGEMV_EINVAL;
+  if (!codes || !out) return QGEMV_EINVAL;
+  if (!aligned(codes, 16)) return QGEMV_EALIGN;
+  if (!fp_path_supported(path, K, format)) return QGEMV_EUNSUPPORTED;
+  return qgemv::launch_unpack_probe_fp(path, codes, out, N, K, format,
+                                       reinterpret_cast<hipStream_t>(stream));
+}
+
 const char *qgemv_strerror(int status) {
   switch (status) {
     case QGEMV_OK: return "ok";
@@ -201,6 +309,6 @@ const char *qgemv_strerror(int status) {
   }
 }
 
-int qgemv_version(void) { return 200; }
+int qgemv_version(void) { return 300; }
 
 }  // extern "C"

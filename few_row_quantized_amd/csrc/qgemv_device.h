@@ -141,6 +141,53 @@ __device__ __forceinline__ u32x4_t unpack8_quad(uint32_t w0, uint32_t w1) {
   return u32x4_t{a[0], a[1], b[0], b[1]};
 }
 
+// ---------------------------------------------------------------- block-scaled FP elements
+//
+// FP4 (E2M1) and FP8 (E4M3) elements are exact in bf16, so each is decoded with
+// gfx950's conversion instructions at scale 1.0 (the scale is applied per block
+// in fp32, like the affine scale): one instruction per two elements, natural
+// pair order (the activations keep their memory order).
+enum FpFormat { kAffine = 0, kMxfp4 = 1, kNvfp4 = 2, kMxfp8 = 3 };
+
+// FP4 elements of byte `sel` of w (elements 2*sel, 2*sel+1) as a bf16 pair.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL));
+}
+
+// FP8 elements of half `hi` of w (elements 2*hi, 2*hi+1) as a bf16 pair.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8_pair(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// One code dword as bf16 pairs in natural order: 4 pairs (FP4) or 2 (FP8).
+__device__ __forceinline__ void unpack_fp4_pairs(uint32_t w, uint32_t (&o)[4]) {
+  o[0] = fp4_pair<0>(w);
+  o[1] = fp4_pair<1>(w);
+  o[2] = fp4_pair<2>(w);
+  o[3] = fp4_pair<3>(w);
+}
+__device__ __forceinline__ void unpack_fp8_pairs(uint32_t w, uint32_t (&o)[2]) {
+  o[0] = fp8_pair<false>(w);
+  o[1] = fp8_pair<true>(w);
+}
+
+// Block scales: E8M0 (2^(e-127), 0xFF NaN) and E4M3, to fp32 (exact).
+__device__ __forceinline__ float e8m0_to_float(uint32_t e) {
+  e &= 0xFFu;
+  const uint32_t b = e == 0u ? 0x00400000u : (e == 255u ? 0x7FC00000u : e << 23);
+  return __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ float e4m3_to_float(uint32_t v) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v & 0xFFu, 1.0f, false)[0];
+}
+template <int FMT>
+__device__ __forceinline__ float fp_scale_to_float(uint32_t byte) {
+  if constexpr (FMT == kNvfp4) return e4m3_to_float(byte);
+  return e8m0_to_float(byte);
+}
+
 // ---------------------------------------------------------------- activation pairing
 //
 // Activations are re-paired to match the code pairing.  X[i] holds bf16

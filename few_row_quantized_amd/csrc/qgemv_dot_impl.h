@@ -49,7 +49,9 @@ constexpr int kMaxPasses = 3;  // lane passes (of 64 chunks) per LDS stage, at m
 // ADD: y = product + res (the fused residual sum); res may equal y (each
 // element is read and then written by the same lane), so neither pointer is
 // declared restrict.
-template <int BITS, int M, int R, int NSUB, int P, bool ADD>
+// FMT: kAffine (fp16 scale and bias per group) or a block-scaled FP format
+// (kMxfp4, kNvfp4, kMxfp8: one scale byte per block in `scales`, no bias).
+template <int BITS, int M, int R, int NSUB, int P, bool ADD, int FMT>
 __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *y,
@@ -59,6 +61,11 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
   constexpr int QPS = QUADS / NSUB;     // quads per metadata sub-chunk
   constexpr int SUBW = CW / NSUB;       // weights per sub-chunk
   constexpr int V = ((R * M + 3) / 4) * 4;
+  // activations in memory order (8-bit codes, FP elements) or re-paired to
+  // the split pairing of the 2/4-bit offset codes
+  constexpr bool NATURAL = BITS == 8 || FMT != kAffine;
+  constexpr bool HAS_BIAS = FMT == kAffine;
+  const uint8_t *scales8 = reinterpret_cast<const uint8_t *>(scales);
 
   extern __shared__ uint4 lds[];
   uint4 *xl = lds;                                              // [M][QUADS][kch]
@@ -139,8 +146,12 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
 #pragma unroll
           for (int s = 0; s < NSUB; ++s) {
             const int g = ((c0 + c) * CW + s * SUBW) / gs;
-            sr[t][r][s] = scales[(size_t)n * G + g];
-            br[t][r][s] = biases[(size_t)n * G + g];
+            if constexpr (HAS_BIAS) {
+              sr[t][r][s] = scales[(size_t)n * G + g];
+              br[t][r][s] = biases[(size_t)n * G + g];
+            } else {
+              sr[t][r][s] = scales8[(size_t)n * G + g];
+            }
           }
         }
       }
@@ -165,10 +176,12 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
       float ssum[NSUB];
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) ssum[s] = 0.f;
+      if constexpr (HAS_BIAS) {
 #pragma unroll
-      for (int i = 0; i < CW / 2; ++i)
-        ssum[(2 * i) / SUBW] = dot2_bf16(X[i], 0x3F803F80u, ssum[(2 * i) / SUBW]);
-      if constexpr (BITS == 8) {
+        for (int i = 0; i < CW / 2; ++i)
+          ssum[(2 * i) / SUBW] = dot2_bf16(X[i], 0x3F803F80u, ssum[(2 * i) / SUBW]);
+      }
+      if constexpr (NATURAL) {
         // natural pairs: quad d holds elements 8d..8d+7 in memory order
 #pragma unroll
         for (int d = 0; d < QUADS; ++d)
@@ -204,8 +217,10 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
           }
         }
       }
+      if constexpr (HAS_BIAS) {
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s) xsl[(m * NSUB + s) * kch + cl] = ssum[s];
+        for (int s = 0; s < NSUB; ++s) xsl[(m * NSUB + s) * kch + cl] = ssum[s];
+      }
     };
 #pragma unroll
     for (int j = 0; j < JU; ++j) {
@@ -243,7 +258,18 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             const uint32_t cd[4] = {cw[t][r].x, cw[t][r].y, cw[t][r].z, cw[t][r].w};
-            if constexpr (BITS == 8) {
+            if constexpr (FMT == kMxfp4 || FMT == kNvfp4) {
+              // quad q = code dword q (elements 8q..8q+7, natural pairs)
+              unpack_fp4_pairs(cd[q], pr[r]);
+            } else if constexpr (FMT == kMxfp8) {
+              uint32_t lo[2], hi[2];
+              unpack_fp8_pairs(cd[2 * q], lo);
+              unpack_fp8_pairs(cd[2 * q + 1], hi);
+              pr[r][0] = lo[0];
+              pr[r][1] = lo[1];
+              pr[r][2] = hi[0];
+              pr[r][3] = hi[1];
+            } else if constexpr (BITS == 8) {
               // quad q = code dwords 2q, 2q+1 (codes 8q..8q+7, natural pairs)
               uint32_t lo[2], hi[2];
               unpack8_pairs(cd[2 * q], lo);
@@ -275,17 +301,23 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
             }
           }
         }
-        // fold scale and bias (with the 128 offset) once per sub-chunk
+        // fold the scale (and, for affine codes, the bias with the 128
+        // offset of the 2/4-bit codes) once per sub-chunk
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          const float sc = half_bits_to_float(sr[t][r][s]);
-          // 2/4-bit codes carry the 128 offset, removed with the bias
-          const float bo = BITS == 8 ? half_bits_to_float(br[t][r][s])
-                                     : fmaf(-128.f, sc, half_bits_to_float(br[t][r][s]));
+          if constexpr (!HAS_BIAS) {
+            const float sc = fp_scale_to_float<FMT>(sr[t][r][s]);
 #pragma unroll
-          for (int m = 0; m < M; ++m) {
-            const float xs = xsl[(m * NSUB + s) * kch + c];
-            acc[r][m] = fmaf(sc, d[r][m], fmaf(bo, xs, acc[r][m]));
+            for (int m = 0; m < M; ++m) acc[r][m] = fmaf(sc, d[r][m], acc[r][m]);
+          } else {
+            const float sc = half_bits_to_float(sr[t][r][s]);
+            const float bo = BITS == 8 ? half_bits_to_float(br[t][r][s])
+                                       : fmaf(-128.f, sc, half_bits_to_float(br[t][r][s]));
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+              const float xs = xsl[(m * NSUB + s) * kch + c];
+              acc[r][m] = fmaf(sc, d[r][m], fmaf(bo, xs, acc[r][m]));
+            }
           }
         }
       }
@@ -312,7 +344,7 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
   }
 }
 
-template <int BITS, int M, int R, int NSUB, int P, bool ADD>
+template <int BITS, int M, int R, int NSUB, int P, bool ADD, int FMT>
 int launch_dot_tp(const QgemvArgs &a, hipStream_t stream) {
   constexpr int CW = 128 / BITS;
   constexpr int QUADS = CW / 8;
@@ -332,11 +364,11 @@ int launch_dot_tp(const QgemvArgs &a, hipStream_t stream) {
   const size_t lds = per_chunk * (size_t)kch;
   if (lds > kLdsMax) return QGEMV_EUNSUPPORTED;
   if (!allow_max_dynamic_lds(
-          reinterpret_cast<const void *>(&qgemv_dot_kernel<BITS, M, R, NSUB, P, ADD>)))
+          reinterpret_cast<const void *>(&qgemv_dot_kernel<BITS, M, R, NSUB, P, ADD, FMT>)))
     return QGEMV_EHIP;
   const int rows_per_block = kDotWaves * R;
   const int blocks = (a.N + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL((qgemv_dot_kernel<BITS, M, R, NSUB, P, ADD>), dim3(blocks), dim3(kDotThreads),
+  hipLaunchKernelGGL((qgemv_dot_kernel<BITS, M, R, NSUB, P, ADD, FMT>), dim3(blocks), dim3(kDotThreads),
                      lds, stream, a.codes, a.scales, a.biases, a.x, a.y, a.res, a.N, a.K,
                      a.group_size, kch);
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
@@ -345,12 +377,12 @@ int launch_dot_tp(const QgemvArgs &a, hipStream_t stream) {
 // Lane passes per stage: two when a row has at most 128 chunks (K <= 4096 at
 // 4 bits), which keeps fewer code registers live; three otherwise.  Only for
 // M <= 4, where the dot path is the one that runs.
-template <int BITS, int M, int R, int NSUB, bool ADD>
+template <int BITS, int M, int R, int NSUB, bool ADD, int FMT>
 int launch_dot_t(const QgemvArgs &a, hipStream_t stream) {
   if constexpr (M <= 4) {
-    if (a.K / (128 / BITS) <= 128) return launch_dot_tp<BITS, M, R, NSUB, 2, ADD>(a, stream);
+    if (a.K / (128 / BITS) <= 128) return launch_dot_tp<BITS, M, R, NSUB, 2, ADD, FMT>(a, stream);
   }
-  return launch_dot_tp<BITS, M, R, NSUB, kMaxPasses, ADD>(a, stream);
+  return launch_dot_tp<BITS, M, R, NSUB, kMaxPasses, ADD, FMT>(a, stream);
 }
 
 // rows per wave for each M: enough rows to share each x read (LDS traffic per
@@ -363,19 +395,21 @@ constexpr int dot_rows_per_wave() {
   return M <= 2 ? 2 : (M <= 4 ? 4 : (M <= 8 ? 2 : 1));
 }
 
-template <int BITS, int M, int R, bool ADD>
+template <int BITS, int M, int R, bool ADD, int FMT>
 int launch_dot_r(const QgemvArgs &a, hipStream_t stream) {
-  if constexpr (BITS == 8) {
-    return launch_dot_t<8, M, R, 1, ADD>(a, stream);  // a 16-code chunk never spans two groups
+  if constexpr (FMT == kNvfp4) {
+    return launch_dot_t<4, M, R, 2, ADD, FMT>(a, stream);  // two 16-element blocks per chunk
+  } else if constexpr (BITS == 8) {
+    return launch_dot_t<8, M, R, 1, ADD, FMT>(a, stream);  // a 16-code chunk never spans two groups
   } else if constexpr (BITS == 2) {
-    if (a.group_size == 32) return launch_dot_t<2, M, R, 2, ADD>(a, stream);
-    return launch_dot_t<2, M, R, 1, ADD>(a, stream);
+    if (a.group_size == 32) return launch_dot_t<2, M, R, 2, ADD, FMT>(a, stream);
+    return launch_dot_t<2, M, R, 1, ADD, FMT>(a, stream);
   } else {
-    return launch_dot_t<4, M, R, 1, ADD>(a, stream);
+    return launch_dot_t<4, M, R, 1, ADD, FMT>(a, stream);
   }
 }
 
-template <int BITS, int M, bool ADD>
+template <int BITS, int M, bool ADD, int FMT>
 int launch_dot_m(const QgemvArgs &a, hipStream_t stream) {
   constexpr int R = dot_rows_per_wave<BITS, M>();
   // Few rows (small N): fewer rows per wave, so that every CU gets a
@@ -384,41 +418,42 @@ int launch_dot_m(const QgemvArgs &a, hipStream_t stream) {
   const int cus = device_cu_count();
   if constexpr (R == 4) {
     if (a.N / (kDotWaves * 4) < cus) {
-      if (a.N / (kDotWaves * 2) >= cus) return launch_dot_r<BITS, M, 2, ADD>(a, stream);
-      return launch_dot_r<BITS, M, 1, ADD>(a, stream);
+      if (a.N / (kDotWaves * 2) >= cus) return launch_dot_r<BITS, M, 2, ADD, FMT>(a, stream);
+      return launch_dot_r<BITS, M, 1, ADD, FMT>(a, stream);
     }
   } else if constexpr (R == 2) {
-    if (a.N / (kDotWaves * 2) < cus) return launch_dot_r<BITS, M, 1, ADD>(a, stream);
+    if (a.N / (kDotWaves * 2) < cus) return launch_dot_r<BITS, M, 1, ADD, FMT>(a, stream);
   }
-  return launch_dot_r<BITS, M, R, ADD>(a, stream);
+  return launch_dot_r<BITS, M, R, ADD, FMT>(a, stream);
 }
 
-template <int BITS, bool ADD>
+template <int BITS, bool ADD, int FMT = kAffine>
 int launch_dot_bits(const QgemvArgs &a, hipStream_t stream) {
   switch (a.M) {
-    case 1: return launch_dot_m<BITS, 1, ADD>(a, stream);
-    case 2: return launch_dot_m<BITS, 2, ADD>(a, stream);
-    case 3: return launch_dot_m<BITS, 3, ADD>(a, stream);
-    case 4: return launch_dot_m<BITS, 4, ADD>(a, stream);
-    case 5: return launch_dot_m<BITS, 5, ADD>(a, stream);
-    case 6: return launch_dot_m<BITS, 6, ADD>(a, stream);
-    case 7: return launch_dot_m<BITS, 7, ADD>(a, stream);
-    case 8: return launch_dot_m<BITS, 8, ADD>(a, stream);
-    case 9: return launch_dot_m<BITS, 9, ADD>(a, stream);
-    case 10: return launch_dot_m<BITS, 10, ADD>(a, stream);
-    case 11: return launch_dot_m<BITS, 11, ADD>(a, stream);
-    case 12: return launch_dot_m<BITS, 12, ADD>(a, stream);
-    case 13: return launch_dot_m<BITS, 13, ADD>(a, stream);
-    case 14: return launch_dot_m<BITS, 14, ADD>(a, stream);
-    case 15: return launch_dot_m<BITS, 15, ADD>(a, stream);
-    case 16: return launch_dot_m<BITS, 16, ADD>(a, stream);
+    case 1: return launch_dot_m<BITS, 1, ADD, FMT>(a, stream);
+    case 2: return launch_dot_m<BITS, 2, ADD, FMT>(a, stream);
+    case 3: return launch_dot_m<BITS, 3, ADD, FMT>(a, stream);
+    case 4: return launch_dot_m<BITS, 4, ADD, FMT>(a, stream);
+    case 5: return launch_dot_m<BITS, 5, ADD, FMT>(a, stream);
+    case 6: return launch_dot_m<BITS, 6, ADD, FMT>(a, stream);
+    case 7: return launch_dot_m<BITS, 7, ADD, FMT>(a, stream);
+    case 8: return launch_dot_m<BITS, 8, ADD, FMT>(a, stream);
+    case 9: return launch_dot_m<BITS, 9, ADD, FMT>(a, stream);
+    case 10: return launch_dot_m<BITS, 10, ADD, FMT>(a, stream);
+    case 11: return launch_dot_m<BITS, 11, ADD, FMT>(a, stream);
+    case 12: return launch_dot_m<BITS, 12, ADD, FMT>(a, stream);
+    case 13: return launch_dot_m<BITS, 13, ADD, FMT>(a, stream);
+    case 14: return launch_dot_m<BITS, 14, ADD, FMT>(a, stream);
+    case 15: return launch_dot_m<BITS, 15, ADD, FMT>(a, stream);
+    case 16: return launch_dot_m<BITS, 16, ADD, FMT>(a, stream);
     default: return QGEMV_EINVAL;
   }
 }
 
 // The instantiations of the 2- and 4-bit codes for one value of ADD; the
-// 8-bit ones are launch_dot_bits<8, ADD> (each translation unit that includes
-// this header compiles one set, so they build in parallel).
+// 8-bit ones are launch_dot_bits<8, ADD>, the FP formats'
+// launch_dot_bits<BITS, ADD, FMT> (each translation unit that includes this
+// header compiles one set, so they build in parallel).
 template <bool ADD>
 int launch_dot_impl(const QgemvArgs &a, hipStream_t stream) {
   return a.bits == 4 ? launch_dot_bits<4, ADD>(a, stream) : launch_dot_bits<2, ADD>(a, stream);

@@ -19,6 +19,11 @@ struct QgemvArgs {
   // Fused residual sum: y = product + res (res [M][N] fp32, may equal y);
   // nullptr for the plain product.
   const float *res = nullptr;
+  // Weight format: 0 = affine codes (fp16 scales and biases); otherwise a
+  // block-scaled FP format (FpFormat in qgemv_device.h): `scales` then points
+  // to one scale byte per block, `biases` is unused, bits is the element width
+  // and group_size the block.
+  int fmt = 0;
 };
 
 // LDS of one workgroup: hardware limit on gfx950, and the dot path's
@@ -37,17 +42,21 @@ bool allow_max_dynamic_lds(const void *func);
 int launch_dot(const QgemvArgs &a, hipStream_t stream);
 int launch_dot_add(const QgemvArgs &a, hipStream_t stream);  // a.res != nullptr, 2/4-bit
 int launch_dot8(const QgemvArgs &a, hipStream_t stream);     // 8-bit codes
+int launch_dot_fp(const QgemvArgs &a, hipStream_t stream);   // block-scaled FP formats
 int launch_mfma(const QgemvArgs &a, hipStream_t stream);
 // Persistent MFMA kernel (QGEMV_EUNSUPPORTED when the activations of a
 // wave would not fit its registers).
 int launch_persist(const QgemvArgs &a, hipStream_t stream);
 
-// Shape support of the MFMA path (host check).
+// Shape support of the MFMA path (host check): affine codes, FP formats.
 bool mfma_supports(int K, int bits, int group_size);
+bool mfma_supports_fp(int K, int fmt);
 
 // Probes.
 int launch_unpack_probe(int path, const uint8_t *codes, uint8_t *q_out, int N, int K, int bits,
                         int group_size, hipStream_t stream);
+int launch_unpack_probe_fp(int path, const uint8_t *codes, uint16_t *out, int N, int K, int fmt,
+                           hipStream_t stream);
 int launch_stream_probe(const uint8_t *buf, size_t nbytes, uint32_t *out, hipStream_t stream);
 int stream_probe_blocks(size_t nbytes);
 

@@ -55,7 +55,10 @@ constexpr uint32_t kSplitSentinel = 0x7FC0DEADu;
 // y and res may be the same buffer (in-place residual sum): neither is
 // declared restrict; every element is read before it is written, by the same
 // thread.
-template <int BITS, int GS, int NT, int MAXT, int SPI, int KS, bool PERSIST, bool ADD>
+// FMT: kAffine, or a block-scaled FP format with 32-element blocks (kMxfp4,
+// kMxfp8): one scale byte per block in `scales`, no bias, elements decoded in
+// natural order.
+template <int BITS, int GS, int NT, int MAXT, int SPI, int KS, bool PERSIST, bool ADD, int FMT>
 __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *y,
@@ -67,6 +70,7 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   // activation operands per super-chunk: one per code register (2/4-bit) or
   // per pair of code registers (8-bit)
   constexpr int XR = BITS == 8 ? 2 : 4;
+  constexpr bool HAS_BIAS = FMT == kAffine;
   constexpr int BLKW = 4 * GS;         // codes per bias block (4 groups)
   constexpr int BSC = BLKW / SCW;      // super-chunks per block
   constexpr int CPG = GS / CW;         // chunks per group (1, 2 or 4)
@@ -124,12 +128,14 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   const uint8_t *crow[NT];
   const uint16_t *srow[NT];
   const uint16_t *brow[NT];
+  const uint8_t *srow8[NT];  // FP formats: scale bytes
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int n = min(n_base + 16 * t + col, N - 1);
     crow[t] = codes + (size_t)n * RB + kb * 16;
     srow[t] = scales + (size_t)n * G;
     brow[t] = biases + (size_t)n * G;
+    srow8[t] = reinterpret_cast<const uint8_t *>(scales) + (size_t)n * G;
   }
 
   // residual of the outputs this thread stores in its first NT reduction
@@ -182,8 +188,13 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
       if (bb < nb) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          s4[bb][t] = *reinterpret_cast<const uint2 *>(srow[t] + (size_t)(blk0 + bb) * 4);
-          b4[bb][t] = *reinterpret_cast<const uint2 *>(brow[t] + (size_t)(blk0 + bb) * 4);
+          if constexpr (HAS_BIAS) {
+            s4[bb][t] = *reinterpret_cast<const uint2 *>(srow[t] + (size_t)(blk0 + bb) * 4);
+            b4[bb][t] = *reinterpret_cast<const uint2 *>(brow[t] + (size_t)(blk0 + bb) * 4);
+          } else {
+            // the block's 4 scale bytes
+            s4[bb][t].x = *reinterpret_cast<const uint32_t *>(srow8[t] + (size_t)(blk0 + bb) * 4);
+          }
         }
       }
     }
@@ -202,6 +213,7 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
 #pragma unroll
       for (int uu = 0; uu < BSC; ++uu) {
         const int u = bb * BSC + uu;
+        if constexpr (!HAS_BIAS) continue;  // FP formats: natural order, no bias sums
         if constexpr (BITS == 8) {
           // natural order: only the group sums; step e of the super-chunk
           // holds 8 codes of group (uu*SCW + 32e)/GS of the block
@@ -234,7 +246,7 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
           }
         }
       }
-      xsum[bb] = rows_transpose_reduce4(P);
+      if constexpr (HAS_BIAS) xsum[bb] = rows_transpose_reduce4(P);
     }
 
     // ---- codes, super-chunk by super-chunk in load order
@@ -264,15 +276,26 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
           const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xv[u][e][0]);
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
-            const u32x4_t bw = unpack8_quad(cur[t][2 * e], cur[t][2 * e + 1]);
+            u32x4_t bw;
+            if constexpr (FMT == kMxfp8) {
+              bw = u32x4_t{fp8_pair<false>(cur[t][2 * e]), fp8_pair<true>(cur[t][2 * e]),
+                           fp8_pair<false>(cur[t][2 * e + 1]), fp8_pair<true>(cur[t][2 * e + 1])};
+            } else {
+              bw = unpack8_quad(cur[t][2 * e], cur[t][2 * e + 1]);
+            }
             accg[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 a, __builtin_bit_cast(bf16x8_t, bw), gfirst ? zero4 : accg[t], 0, 0, 0);
           }
           if (glast) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-              const uint32_t sw = (j < 2) ? s4[u / BSC][t].x : s4[u / BSC][t].y;
-              const float sc = half_bits_to_float((j & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+              float sc;
+              if constexpr (HAS_BIAS) {
+                const uint32_t sw = (j < 2) ? s4[u / BSC][t].x : s4[u / BSC][t].y;
+                sc = half_bits_to_float((j & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+              } else {
+                sc = fp_scale_to_float<FMT>(s4[u / BSC][t].x >> (8 * j));
+              }
 #pragma unroll
               for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(sc, accg[t][q], acc[t][q]);
             }
@@ -290,7 +313,11 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
             u32x4_t bw;
-            if constexpr (BITS == 4) {
+            if constexpr (FMT == kMxfp4) {
+              // 8 elements of one dword, natural order
+              bw = u32x4_t{fp4_pair<0>(cur[t][i]), fp4_pair<1>(cur[t][i]), fp4_pair<2>(cur[t][i]),
+                           fp4_pair<3>(cur[t][i])};
+            } else if constexpr (BITS == 4) {
               bw = unpack4_split_quad(cur[t][i], offset_pair);
             } else {
               bw = unpack2_split_quad(cur[t][i], h, offset_pair);
@@ -301,15 +328,20 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
           if (glast) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-              const uint32_t sw = (j < 2) ? s4[u / BSC][t].x : s4[u / BSC][t].y;
-              const float sc = half_bits_to_float((j & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+              float sc;
+              if constexpr (HAS_BIAS) {
+                const uint32_t sw = (j < 2) ? s4[u / BSC][t].x : s4[u / BSC][t].y;
+                sc = half_bits_to_float((j & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+              } else {
+                sc = fp_scale_to_float<FMT>(s4[u / BSC][t].x >> (8 * j));
+              }
 #pragma unroll
               for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(sc, accg[t][q], acc[t][q]);
             }
           }
         }
       }
-      if (scb == BSC - 1) {
+      if (HAS_BIAS && scb == BSC - 1) {
         // bias with the 128 offset: acc += xsum[m][g0+kb] * (b - 128 s)[n][g0+kb]
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -417,14 +449,14 @@ __global__ __launch_bounds__(256) void fill_kernel(uint32_t *__restrict__ y, siz
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) y[i] = v;
 }
 
-template <int BITS, int GS, int NT, bool ADD>
+template <int BITS, int GS, int NT, bool ADD, int FMT>
 int launch_mfma_t(const QgemvArgs &a, hipStream_t stream) {
   constexpr int MAXT = MfmaShape<BITS, GS, NT>::MAXT;
   constexpr int SPI = MfmaShape<BITS, GS, NT>::SPI;
-  const auto kern = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, true, ADD>;
-  const auto kern1 = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, false, ADD>;
-  const auto kern_s = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 2, true, ADD>;
-  const auto kern1_s = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 2, false, ADD>;
+  const auto kern = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, true, ADD, FMT>;
+  const auto kern1 = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, false, ADD, FMT>;
+  const auto kern_s = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 2, true, ADD, FMT>;
+  const auto kern1_s = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 2, false, ADD, FMT>;
   const int nblk = a.K / (4 * GS);
   const int tiles = (a.N + 15) / 16;
   const int cus = device_cu_count();
@@ -464,21 +496,29 @@ int launch_mfma_t(const QgemvArgs &a, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
 }
 
-template <int BITS, int GS>
+template <int BITS, int GS, int FMT = kAffine>
 int launch_mfma_gs(const QgemvArgs &a, hipStream_t stream) {
   // more output columns per workgroup on wide matrices: every workgroup reads
   // all M*K activations, so wider groups cut that traffic per weight byte
   const int tiles = (a.N + 15) / 16;
   const int cus = device_cu_count();
   if (a.res) {
-    if (tiles >= 2 * cus) return launch_mfma_t<BITS, GS, 2, true>(a, stream);
-    return launch_mfma_t<BITS, GS, 1, true>(a, stream);
+    if (tiles >= 2 * cus) return launch_mfma_t<BITS, GS, 2, true, FMT>(a, stream);
+    return launch_mfma_t<BITS, GS, 1, true, FMT>(a, stream);
   }
-  if (tiles >= 2 * cus) return launch_mfma_t<BITS, GS, 2, false>(a, stream);
-  return launch_mfma_t<BITS, GS, 1, false>(a, stream);
+  if (tiles >= 2 * cus) return launch_mfma_t<BITS, GS, 2, false, FMT>(a, stream);
+  return launch_mfma_t<BITS, GS, 1, false, FMT>(a, stream);
 }
 
 }  // namespace
+
+bool mfma_supports_fp(int K, int fmt) {
+  // 32-element blocks only: one MFMA step per block (nvfp4's 16-element blocks
+  // would split a step between two scales)
+  if (fmt == kMxfp4) return K % 128 == 0;
+  if (fmt == kMxfp8) return K % 128 == 0;
+  return false;
+}
 
 bool mfma_supports(int K, int bits, int group_size) {
   if (bits == 2 && group_size < 64) return false;
@@ -490,6 +530,11 @@ bool mfma_supports(int K, int bits, int group_size) {
 }
 
 int launch_mfma(const QgemvArgs &a, hipStream_t stream) {
+  if (a.fmt != kAffine) {
+    if (!mfma_supports_fp(a.K, a.fmt)) return QGEMV_EUNSUPPORTED;
+    if (a.fmt == kMxfp4) return launch_mfma_gs<4, 32, kMxfp4>(a, stream);
+    return launch_mfma_gs<8, 32, kMxfp8>(a, stream);
+  }
   if (!mfma_supports(a.K, a.bits, a.group_size)) return QGEMV_EUNSUPPORTED;
   // more tiles than CUs: the persistent kernel streams several tiles per CU;
   // otherwise one tile group per workgroup in a single pass

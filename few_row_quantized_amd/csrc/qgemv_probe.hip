@@ -127,6 +127,92 @@ __global__ __launch_bounds__(64) void unpack_probe_mfma(const uint8_t *__restric
   }
 }
 
+// FP formats, dot-path decoding: one thread per (row n, 16-byte chunk c);
+// writes the bf16 bit pattern of every element (natural pair order).
+template <int FMT>
+__global__ __launch_bounds__(256) void unpack_probe_fp_dot(const uint8_t *__restrict__ codes,
+                                                           uint16_t *__restrict__ out, int N, int K) {
+  constexpr int BITS = FMT == kMxfp8 ? 8 : 4;
+  constexpr int CW = 128 / BITS;
+  const int NC = K / CW;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)N * NC) return;
+  const int n = (int)(idx / NC);
+  const int c = (int)(idx % NC);
+  const size_t RB = (size_t)K * BITS / 8;
+  const uint4 v = *reinterpret_cast<const uint4 *>(codes + (size_t)n * RB + (size_t)c * 16);
+  const uint32_t cd[4] = {v.x, v.y, v.z, v.w};
+  uint16_t *o = out + (size_t)n * K + (size_t)c * CW;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    if constexpr (BITS == 4) {
+      uint32_t p[4];
+      unpack_fp4_pairs(cd[d], p);  // elements 8d + 2j, 8d + 2j + 1
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o[8 * d + 2 * j] = (uint16_t)(p[j] & 0xFFFFu);
+        o[8 * d + 2 * j + 1] = (uint16_t)(p[j] >> 16);
+      }
+    } else {
+      uint32_t p[2];
+      unpack_fp8_pairs(cd[d], p);  // elements 4d + 2j, 4d + 2j + 1
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        o[4 * d + 2 * j] = (uint16_t)(p[j] & 0xFFFFu);
+        o[4 * d + 2 * j + 1] = (uint16_t)(p[j] >> 16);
+      }
+    }
+  }
+}
+
+// FP formats, MFMA-path decoding (32-element blocks): the same lane mapping,
+// partial row transpose and operand construction as qgemv_mfma_kernel.
+template <int FMT>
+__global__ __launch_bounds__(64) void unpack_probe_fp_mfma(const uint8_t *__restrict__ codes,
+                                                           uint16_t *__restrict__ out, int N, int K) {
+  constexpr int BITS = FMT == kMxfp8 ? 8 : 4;
+  constexpr int CW = 128 / BITS;
+  constexpr int SCW = 4 * CW;
+  constexpr int DW = CW / 4;
+  constexpr int LVL = BITS == 4 ? 2 : 1;  // 32-element blocks: CW / 32 chunks per block
+  const int lane = threadIdx.x;
+  const int col = lane & 15, kb = lane >> 4;
+  const int nsc = K / SCW;
+  const int tile = blockIdx.x / nsc;
+  const int sc = blockIdx.x % nsc;
+  const int n = min(tile * 16 + col, N - 1);
+  const size_t RB = (size_t)K * BITS / 8;
+  const uint4 v = *reinterpret_cast<const uint4 *>(codes + (size_t)n * RB + (size_t)sc * 64 + kb * 16);
+  uint32_t r[4] = {v.x, v.y, v.z, v.w};
+  transpose_rows_lvl<LVL>(r);  // all lanes take part, also those past row N
+  if (tile * 16 + col >= N) return;
+  uint16_t *o = out + (size_t)n * K + (size_t)sc * SCW;
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k0 = lvl_chunk<LVL>(i, kb) * CW + lvl_dword<LVL>(i, kb) * DW;
+      const uint32_t p[4] = {fp4_pair<0>(r[i]), fp4_pair<1>(r[i]), fp4_pair<2>(r[i]), fp4_pair<3>(r[i])};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o[k0 + 2 * j] = (uint16_t)(p[j] & 0xFFFFu);
+        o[k0 + 2 * j + 1] = (uint16_t)(p[j] >> 16);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int k0 = lvl_chunk<LVL>(2 * e, kb) * CW + lvl_dword<LVL>(2 * e, kb) * DW;
+      const uint32_t p[4] = {fp8_pair<false>(r[2 * e]), fp8_pair<true>(r[2 * e]),
+                             fp8_pair<false>(r[2 * e + 1]), fp8_pair<true>(r[2 * e + 1])};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o[k0 + 2 * j] = (uint16_t)(p[j] & 0xFFFFu);
+        o[k0 + 2 * j + 1] = (uint16_t)(p[j] >> 16);
+      }
+    }
+  }
+}
+
 constexpr int kStreamThreads = 256;
 constexpr int kStreamUnroll = 4;
 constexpr int kStreamMaxBlocks = 2048;
@@ -192,6 +278,27 @@ int launch_unpack_probe(int path, const uint8_t *codes, uint8_t *q_out, int N, i
       if (lvl == 1) hipLaunchKernelGGL((unpack_probe_mfma<2, 1>), g, b, 0, stream, codes, q_out, N, K);
       else hipLaunchKernelGGL((unpack_probe_mfma<2, 2>), g, b, 0, stream, codes, q_out, N, K);
     }
+  } else {
+    return QGEMV_EINVAL;
+  }
+  return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}
+
+int launch_unpack_probe_fp(int path, const uint8_t *codes, uint16_t *out, int N, int K, int fmt,
+                           hipStream_t stream) {
+  const int bits = fmt == kMxfp8 ? 8 : 4;
+  const int CW = 128 / bits;
+  if (path == QGEMV_PATH_DOT) {
+    const size_t threads = (size_t)N * (K / CW);
+    const dim3 g((unsigned)((threads + 255) / 256)), b(256);
+    if (fmt == kMxfp4) hipLaunchKernelGGL(unpack_probe_fp_dot<kMxfp4>, g, b, 0, stream, codes, out, N, K);
+    else if (fmt == kNvfp4) hipLaunchKernelGGL(unpack_probe_fp_dot<kNvfp4>, g, b, 0, stream, codes, out, N, K);
+    else hipLaunchKernelGGL(unpack_probe_fp_dot<kMxfp8>, g, b, 0, stream, codes, out, N, K);
+  } else if (path == QGEMV_PATH_MFMA) {
+    const dim3 g(((N + 15) / 16) * (K / (4 * CW))), b(64);
+    if (fmt == kMxfp4) hipLaunchKernelGGL(unpack_probe_fp_mfma<kMxfp4>, g, b, 0, stream, codes, out, N, K);
+    else if (fmt == kMxfp8) hipLaunchKernelGGL(unpack_probe_fp_mfma<kMxfp8>, g, b, 0, stream, codes, out, N, K);
+    else return QGEMV_EUNSUPPORTED;
   } else {
     return QGEMV_EINVAL;
   }

@@ -24,6 +24,11 @@ EUNSUPPORTED = -2
 EALIGN = -3
 EHIP = -4
 
+FMT_MXFP4 = 1
+FMT_NVFP4 = 2
+FMT_MXFP8 = 3
+_FMTS = {"mxfp4": FMT_MXFP4, "nvfp4": FMT_NVFP4, "mxfp8": FMT_MXFP8}
+
 MAX_M = 16
 MAX_K = 131072
 MAX_N = 4194304
@@ -54,6 +59,12 @@ def lib() -> ctypes.CDLL:
         L.qgemv_small_add.argtypes = gemv_add
         L.qgemv_run_path_add.argtypes = [i] + gemv_add
         L.qgemv_select.argtypes = [i, i, i, i, i]
+        gemv_fp = [vp, vp, vp, vp, vp, i, i, i, i, vp]
+        L.qgemv_small_fp.argtypes = gemv_fp
+        L.qgemv_run_path_fp.argtypes = [i] + gemv_fp
+        L.qgemv_select_fp.argtypes = [i, i, i, i]
+        L.qgemv_path_supported_fp.argtypes = [i, i, i, i, i]
+        L.qgemv_unpack_probe_fp.argtypes = [i, vp, vp, i, i, i, vp]
         L.qgemv_path_supported.argtypes = [i, i, i, i, i, i]
         L.qgemv_unpack_probe.argtypes = [i, vp, vp, i, i, i, i, vp]
         L.qgemv_stream_probe.argtypes = [vp, u64, vp, vp]
@@ -62,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.qgemv_strerror.restype = ctypes.c_char_p
         L.qgemv_version.argtypes = []
         for name in ("qgemv_small", "qgemv_run_path", "qgemv_small_add", "qgemv_run_path_add",
+                     "qgemv_small_fp", "qgemv_run_path_fp", "qgemv_select_fp",
+                     "qgemv_path_supported_fp", "qgemv_unpack_probe_fp",
                      "qgemv_select", "qgemv_path_supported",
                      "qgemv_unpack_probe", "qgemv_stream_probe", "qgemv_stream_probe_blocks",
                      "qgemv_version"):
@@ -126,6 +139,36 @@ def qgemv_run_path_add(path, codes, scales, biases, x, residual, y, M: int, N: i
     return _check(lib().qgemv_run_path_add(_path(path), _ptr(codes), _ptr(scales), _ptr(biases),
                                            _ptr(x), _ptr(residual), _ptr(y), M, N, K, bits,
                                            group_size, _stream(stream)), "qgemv_run_path_add")
+
+
+def _fmt(fmt) -> int:
+    return _FMTS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def qgemv_small_fp(codes, scales, x, residual, y, M: int, N: int, K: int, fmt, stream=None) -> int:
+    return _check(lib().qgemv_small_fp(_ptr(codes), _ptr(scales), _ptr(x), _ptr(residual), _ptr(y),
+                                       M, N, K, _fmt(fmt), _stream(stream)), "qgemv_small_fp")
+
+
+def qgemv_run_path_fp(path, codes, scales, x, residual, y, M: int, N: int, K: int, fmt,
+                      stream=None) -> int:
+    return _check(lib().qgemv_run_path_fp(_path(path), _ptr(codes), _ptr(scales), _ptr(x),
+                                          _ptr(residual), _ptr(y), M, N, K, _fmt(fmt),
+                                          _stream(stream)), "qgemv_run_path_fp")
+
+
+def qgemv_select_fp(M: int, N: int, K: int, fmt) -> int:
+    return _check(lib().qgemv_select_fp(M, N, K, _fmt(fmt)), "qgemv_select_fp")
+
+
+def qgemv_path_supported_fp(path, M: int, N: int, K: int, fmt) -> bool:
+    return bool(_check(lib().qgemv_path_supported_fp(_path(path), M, N, K, _fmt(fmt)),
+                       "qgemv_path_supported_fp"))
+
+
+def qgemv_unpack_probe_fp(path, codes, out, N: int, K: int, fmt, stream=None) -> int:
+    return _check(lib().qgemv_unpack_probe_fp(_path(path), _ptr(codes), _ptr(out), N, K, _fmt(fmt),
+                                              _stream(stream)), "qgemv_unpack_probe_fp")
 
 
 def qgemv_select(M: int, N: int, K: int, bits: int, group_size: int) -> int:

@@ -178,6 +178,60 @@ int qgemv_unpack_probe(int path, const uint8_t *codes, uint8_t *q_out, int N, in
 int qgemv_stream_probe(const uint8_t *buf, size_t nbytes, uint32_t *out, void *stream);
 int qgemv_stream_probe_blocks(size_t nbytes);
 
+/*
+ * ---------------------------------------------------------------- FP block formats
+ *
+ * The block-scaled floating-point modes of qmv_wide (MLX page, Facts: qmv_wide
+ * covers affine, nvfp4, mxfp4 and mxfp8, with their M=8 speedups on the
+ * Gemma-4-12B gate/up shape).  Element and scale encodings follow the OCP
+ * Microscaling Formats (MX) v1.0 specification:
+ *   QGEMV_FMT_MXFP4  FP4 E2M1 elements, two per byte (low nibble first);
+ *                    one E8M0 scale byte (2^(e-127)) per 32 elements.
+ *   QGEMV_FMT_NVFP4  FP4 E2M1 elements as above; one FP8 E4M3 scale byte per
+ *                    16 elements (no per-tensor scale: a constant factor the
+ *                    caller can apply to y).
+ *   QGEMV_FMT_MXFP8  FP8 E4M3 elements (OCP: bias 7, no infinities, S.1111.111
+ *                    NaN), one per byte; one E8M0 scale byte per 32 elements.
+ * w[n,k] = scale[n, k/block] * element[n,k]; no bias.
+ *   codes   uint8 [N][K*bits/8] (bits = 4 or 8), row-major, 16-byte aligned.
+ *   scales  uint8 [N][K/block], row-major, 16-byte aligned.
+ *   x       bf16 [M][K]; y fp32 [M][N] as for qgemv_small.
+ *   residual  NULL for the plain product, else fp32 [M][N] added in the
+ *           store exactly as qgemv_small_add (may be y itself, else must not
+ *           overlap it).
+ * Requirements (else QGEMV_EINVAL / QGEMV_EALIGN): format one of the three;
+ * 1 <= M <= 16; 1 <= N <= QGEMV_MAX_N; 64 <= K <= QGEMV_MAX_K, K % 64 == 0.
+ * The MFMA path runs the 32-element-block formats with K % 128 == 0; nvfp4
+ * runs on the dot path.  Elements are decoded exactly (every E2M1 and E4M3
+ * value is a bf16 value) and each block's scale is applied once in fp32 to the
+ * block's partial dot product; tolerance and row invariance as qgemv_small.
+ */
+#define QGEMV_FMT_MXFP4 1
+#define QGEMV_FMT_NVFP4 2
+#define QGEMV_FMT_MXFP8 3
+
+int qgemv_small_fp(const uint8_t *codes, const uint8_t *scales, const uint16_t *x,
+                   const float *residual, float *y, int M, int N, int K, int format,
+                   void *stream);
+
+/* qgemv_run_path_fp -- qgemv_small_fp with an explicit path (as qgemv_run_path). */
+int qgemv_run_path_fp(int path, const uint8_t *codes, const uint8_t *scales, const uint16_t *x,
+                      const float *residual, float *y, int M, int N, int K, int format,
+                      void *stream);
+
+/* qgemv_select_fp / qgemv_path_supported_fp -- as qgemv_select /
+ * qgemv_path_supported, for an FP format.  Host only. */
+int qgemv_select_fp(int M, int N, int K, int format);
+int qgemv_path_supported_fp(int path, int M, int N, int K, int format);
+
+/*
+ * qgemv_unpack_probe_fp -- writes the element values exactly as a path's
+ * kernels decode them, as bf16 bit patterns: out[n][k] (uint16, [N][K]), before
+ * the block scale is applied, for the bit-exact test of the decoding.
+ */
+int qgemv_unpack_probe_fp(int path, const uint8_t *codes, uint16_t *out, int N, int K, int format,
+                          void *stream);
+
 /* qgemv_strerror -- static description of a status code. */
 const char *qgemv_strerror(int status);
 

@@ -191,3 +191,52 @@ def test_product_path_does_not_import_oracle():
                 if isinstance(node, (ast.Import, ast.ImportFrom)):
                     mods = [a.name for a in node.names] if isinstance(node, ast.Import) else [node.module or ""]
                     assert not any(m.split(".")[0] == "oracle" for m in mods), fn
+
+
+# ---------------------------------------------------------------- FP block formats
+
+@pytest.mark.parametrize("M,N,K,fmt,want", [
+    (1, 64, 256, 0, q.EINVAL), (1, 64, 256, 4, q.EINVAL),        # unknown format
+    (0, 64, 256, 1, q.EINVAL), (17, 64, 256, 1, q.EINVAL),        # M
+    (1, 0, 256, 1, q.EINVAL), (1, 64, 96, 1, q.EINVAL),           # N, K % 64
+    (1, 64, q.MAX_K + 64, 3, q.EINVAL),                           # K above the limit
+])
+def test_fp_invalid_shapes_rejected(M, N, K, fmt, want):
+    L = q.lib()
+    assert L.qgemv_small_fp(A, A, A, None, A, M, N, K, fmt, None) == want
+    assert L.qgemv_select_fp(M, N, K, fmt) == want
+    for path in (q.PATH_AUTO, q.PATH_DOT, q.PATH_MFMA):
+        assert L.qgemv_run_path_fp(path, A, A, A, None, A, M, N, K, fmt, None) == want
+
+
+@pytest.mark.parametrize("which", range(4))
+def test_fp_null_and_misaligned_pointers_rejected(which):
+    L = q.lib()
+    ptrs = [A, A, A, A]  # codes, scales, x, y (residual NULL)
+    ptrs[which] = None
+    args = ptrs[:3] + [None] + ptrs[3:]
+    assert L.qgemv_small_fp(*args, 4, 64, 256, q.FMT_MXFP4, None) == q.EINVAL
+    ptrs = [A, A, A, A]
+    ptrs[which] += 4
+    args = ptrs[:3] + [None] + ptrs[3:]
+    assert L.qgemv_small_fp(*args, 4, 64, 256, q.FMT_MXFP4, None) == q.EALIGN
+
+
+def test_fp_residual_overlap_and_alignment():
+    L = q.lib()
+    M, N = 4, 64
+    assert L.qgemv_small_fp(A, A, A, A + N * 4, A, M, N, 256, q.FMT_MXFP8, None) == q.EINVAL
+    assert L.qgemv_small_fp(A, A, A, A + (1 << 24) + 4, A, M, N, 256, q.FMT_MXFP8, None) == q.EALIGN
+
+
+def test_fp_path_support():
+    sup = q.qgemv_path_supported_fp
+    assert sup("mfma", 4, 4096, 4096, "mxfp4") and sup("mfma", 4, 4096, 4096, "mxfp8")
+    assert not sup("mfma", 4, 4096, 4096, "nvfp4")      # 16-element blocks: dot path only
+    assert not sup("mfma", 4, 4096, 192, "mxfp4")       # K not a multiple of 128
+    assert sup("dot", 4, 4096, 192, "nvfp4") and sup("dot", 4, 4096, 192, "mxfp8")
+    for fmt in ("mxfp4", "nvfp4", "mxfp8"):
+        for M in range(1, 17):
+            p = q.qgemv_select_fp(M, 15360, 3840, fmt)
+            assert p in (q.PATH_DOT, q.PATH_MFMA) and sup(p, M, 15360, 3840, fmt)
+    assert q.lib().qgemv_unpack_probe_fp(q.PATH_MFMA, A, A, 64, 256, q.FMT_NVFP4, None) == q.EUNSUPPORTED
