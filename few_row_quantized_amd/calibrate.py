@@ -30,6 +30,9 @@ sys.path.insert(0, os.path.dirname(PKG))
 
 from few_row_quantized_amd import accounting, synth  # noqa: E402
 
+# Table keys of the block-scaled FP formats: bits = 100 + format code.
+FP_CODES = {"mxfp4": 1, "nvfp4": 2, "mxfp8": 3}
+
 # Shape classes of the table (boundaries in elements).
 N_CLASSES = [(0, 2048), (2048, 8192), (8192, 1 << 30)]
 K_CLASSES = [(0, 8192), (8192, 1 << 30)]
@@ -68,26 +71,36 @@ def sweep(names, ms, chain: int, pool_mib: int, log=print):
     for name in names:
         s = synth.WORKLOADS[name]
         p = synth.make_problem(s, m_max=16)
-        W = accounting.weight_bytes(s.N, s.K, s.bits, s.group_size)
+        fp = s.fmt is not None
+        W = (accounting.fp_weight_bytes(s.N, s.K, s.bits, s.group_size) if fp else
+             accounting.weight_bytes(s.N, s.K, s.bits, s.group_size))
         P = max(2, math.ceil(pool_mib * 2 ** 20 / W))
         codes = torch.from_numpy(p.codes).cuda().unsqueeze(0).repeat(P, 1, 1)
-        sc = torch.from_numpy(p.scales.view(np.int16)).cuda().unsqueeze(0).repeat(P, 1, 1)
-        bi = torch.from_numpy(p.biases.view(np.int16)).cuda().unsqueeze(0).repeat(P, 1, 1)
+        sc = torch.from_numpy(p.scales if fp else p.scales.view(np.int16)).cuda().unsqueeze(0).repeat(P, 1, 1)
+        bi = None if fp else torch.from_numpy(p.biases.view(np.int16)).cuda().unsqueeze(0).repeat(P, 1, 1)
         x = torch.from_numpy(p.x.view(np.int16)).cuda()
         y = torch.empty((16, s.N), dtype=torch.float32, device="cuda")
         for M in ms:
             rec = {"workload": name, "K": s.K, "N": s.N, "bits": s.bits, "group_size": s.group_size,
                    "M": M, "weight_bytes": W}
+            if fp:
+                rec["fmt"] = s.fmt
             for path in ("dot", "mfma"):
-                if not q.qgemv_path_supported(path, M, s.N, s.K, s.bits, s.group_size):
+                if fp:
+                    if not q.qgemv_path_supported_fp(path, M, s.N, s.K, s.fmt):
+                        continue
+                elif not q.qgemv_path_supported(path, M, s.N, s.K, s.bits, s.group_size):
                     continue
                 ctr = [0]
 
                 def one():
                     i = ctr[0] % P
                     ctr[0] += 1
-                    q.qgemv_run_path(path, codes[i], sc[i], bi[i], x, y, M, s.N, s.K, s.bits,
-                                     s.group_size)
+                    if fp:
+                        q.qgemv_run_path_fp(path, codes[i], sc[i], x, None, y, M, s.N, s.K, s.fmt)
+                    else:
+                        q.qgemv_run_path(path, codes[i], sc[i], bi[i], x, y, M, s.N, s.K, s.bits,
+                                         s.group_size)
 
                 one()
                 torch.cuda.synchronize()
@@ -110,7 +123,9 @@ def table_from_sweep(rows):
     for r in rows:
         if "mfma_us" not in r or "dot_us" not in r:
             continue
-        key = (r["bits"], r["group_size"], n_class(r["N"]), k_class(r["K"]))
+        # FP formats are keyed by 100 + format code, group size 0
+        key = ((100 + FP_CODES[r["fmt"]], 0) if "fmt" in r else (r["bits"], r["group_size"])) + (
+            n_class(r["N"]), k_class(r["K"]))
         ratios.setdefault(key, {}).setdefault(r["M"], []).append(math.log(r["mfma_us"] / r["dot_us"]))
     table = {}
     for key, per_m in ratios.items():
@@ -134,7 +149,8 @@ def emit_header(table, source: str) -> str:
         "// another; MLX page, Facts: per-architecture batch limits and bit-width",
         "// gating).  This table is measured on MI355X: for each (bits, group size,",
         "// N class, K class) bit M-1 of the mask is set when the MFMA path was the",
-        "// faster one for M activation rows in a forced-path sweep.",
+        "// faster one for M activation rows in a forced-path sweep.  Block-scaled",
+        "// FP formats are keyed by bits = 100 + format (1 mxfp4, 2 nvfp4, 3 mxfp8).",
         "#pragma once",
         "",
         "#include <stdint.h>",
@@ -168,7 +184,8 @@ def emit_header(table, source: str) -> str:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default="select_sweep.json")
-    ap.add_argument("--workloads", default=None, help="comma list; default: all but the tiny one")
+    ap.add_argument("--workloads", default=None,
+                    help="comma list; default: all but the tiny one and the FP formats; 'fp': the FP formats")
     ap.add_argument("--chain", type=int, default=200)
     ap.add_argument("--pool-mib", type=int, default=1024)
     ap.add_argument("--emit-header", default=None, metavar="SWEEP_JSON",
@@ -181,8 +198,11 @@ def main():
         open(path, "w").write(hdr)
         print(f"wrote {path}")
         return
-    names = (args.workloads.split(",") if args.workloads else
-             [n for n, w in synth.WORKLOADS.items() if not n.startswith("tiny") and w.fmt is None])
+    if args.workloads == "fp":
+        names = [n for n, w in synth.WORKLOADS.items() if w.fmt is not None]
+    else:
+        names = (args.workloads.split(",") if args.workloads else
+                 [n for n, w in synth.WORKLOADS.items() if not n.startswith("tiny") and w.fmt is None])
     t0 = time.time()
     rows = sweep(names, list(range(1, 17)), args.chain, args.pool_mib,
                  log=lambda m: print(m, flush=True))
