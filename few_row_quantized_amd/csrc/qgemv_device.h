@@ -173,6 +173,17 @@ __device__ __forceinline__ void unpack_fp8_pairs(uint32_t w, uint32_t (&o)[2]) {
   o[1] = fp8_pair<true>(w);
 }
 
+// FP4 elements of byte SEL of w times a block scale, as a bf16 pair.  The
+// conversion's own scale operand takes only the power of two of its argument,
+// so the product is formed in fp32; for an E4M3 scale it has at most 6
+// significant bits and lies within [2^-10, 2688], so the bf16 truncation is
+// exact (the nvfp4 weights themselves).
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4_pair_scaled(uint32_t w, float sc) {
+  const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+  return bf16_pair_of(f[0] * sc, f[1] * sc);
+}
+
 // Block scales: E8M0 (2^(e-127), 0xFF NaN) and E4M3, to fp32 (exact).
 __device__ __forceinline__ float e8m0_to_float(uint32_t e) {
   e &= 0xFFu;

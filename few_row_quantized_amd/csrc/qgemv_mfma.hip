@@ -55,9 +55,11 @@ constexpr uint32_t kSplitSentinel = 0x7FC0DEADu;
 // y and res may be the same buffer (in-place residual sum): neither is
 // declared restrict; every element is read before it is written, by the same
 // thread.
-// FMT: kAffine, or a block-scaled FP format with 32-element blocks (kMxfp4,
-// kMxfp8): one scale byte per block in `scales`, no bias, elements decoded in
-// natural order.
+// FMT: kAffine, or a block-scaled FP format (one scale byte per block in
+// `scales`, no bias, elements decoded in natural order): kMxfp4 and kMxfp8
+// (32-element blocks, GS = 32, scale folded per block in fp32) or kNvfp4
+// (16-element blocks, laid out as GS = 32; each element is multiplied by its
+// block scale before the MFMA, exactly, so B holds the weights themselves).
 template <int BITS, int GS, int NT, int MAXT, int SPI, int KS, bool PERSIST, bool ADD, int FMT>
 __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   const int b_begin = p_lo + (slice * nbp) / waves;
   const int b_end = p_lo + ((slice + 1) * nbp) / waves;
   const size_t RB = (size_t)K * BITS / 8;
-  const int G = K / GS;
+  const int G = FMT == kNvfp4 ? K / 16 : K / GS;  // scale (or scale-and-bias) entries per row
   // Rows m >= M and columns n >= N only feed outputs that are never stored,
   // so their lanes read valid clamped addresses instead of branching around
   // the loads (a branch would force a wait on every load).
@@ -191,6 +193,9 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
           if constexpr (HAS_BIAS) {
             s4[bb][t] = *reinterpret_cast<const uint2 *>(srow[t] + (size_t)(blk0 + bb) * 4);
             b4[bb][t] = *reinterpret_cast<const uint2 *>(brow[t] + (size_t)(blk0 + bb) * 4);
+          } else if constexpr (FMT == kNvfp4) {
+            // the 8 scale bytes of the block's 128 elements
+            s4[bb][t] = *reinterpret_cast<const uint2 *>(srow8[t] + (size_t)(blk0 + bb) * 8);
           } else {
             // the block's 4 scale bytes
             s4[bb][t].x = *reinterpret_cast<const uint32_t *>(srow8[t] + (size_t)(blk0 + bb) * 4);
@@ -302,8 +307,27 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
           }
         }
       }
+      if constexpr (FMT == kNvfp4) {
+        // register i holds elements 8kb..8kb+7 of chunk i (4x4 transpose), i.e.
+        // 16-element block 2i + kb/2 of the super-chunk: scale them exactly and
+        // accumulate straight into acc
 #pragma unroll
-      for (int i = 0; i < (BITS == 8 ? 0 : 4); ++i) {
+        for (int i = 0; i < 4; ++i) {
+          const int b = 2 * i + (kb >> 1);
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xv[u][i][0]);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const uint32_t sw = b < 4 ? s4[u / BSC][t].x : s4[u / BSC][t].y;
+            const float sc = e4m3_to_float(sw >> (8 * (b & 3)));
+            const u32x4_t bw = u32x4_t{fp4_pair_scaled<0>(cur[t][i], sc), fp4_pair_scaled<1>(cur[t][i], sc),
+                                       fp4_pair_scaled<2>(cur[t][i], sc), fp4_pair_scaled<3>(cur[t][i], sc)};
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bw),
+                                                              acc[t], 0, 0, 0);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < (BITS == 8 || FMT == kNvfp4 ? 0 : 4); ++i) {
         const int j = scb * GPS + i / REGS_G;  // group within the block
 #pragma unroll
         for (int h = 0; h < HS; ++h) {
@@ -513,11 +537,8 @@ int launch_mfma_gs(const QgemvArgs &a, hipStream_t stream) {
 }  // namespace
 
 bool mfma_supports_fp(int K, int fmt) {
-  // 32-element blocks only: one MFMA step per block (nvfp4's 16-element blocks
-  // would split a step between two scales)
-  if (fmt == kMxfp4) return K % 128 == 0;
-  if (fmt == kMxfp8) return K % 128 == 0;
-  return false;
+  (void)fmt;
+  return K % 128 == 0;  // one 128-element block of bias blocks per super-chunk
 }
 
 bool mfma_supports(int K, int bits, int group_size) {
@@ -533,6 +554,7 @@ int launch_mfma(const QgemvArgs &a, hipStream_t stream) {
   if (a.fmt != kAffine) {
     if (!mfma_supports_fp(a.K, a.fmt)) return QGEMV_EUNSUPPORTED;
     if (a.fmt == kMxfp4) return launch_mfma_gs<4, 32, kMxfp4>(a, stream);
+    if (a.fmt == kNvfp4) return launch_mfma_gs<4, 32, kNvfp4>(a, stream);
     return launch_mfma_gs<8, 32, kMxfp8>(a, stream);
   }
   if (!mfma_supports(a.K, a.bits, a.group_size)) return QGEMV_EUNSUPPORTED;

@@ -191,7 +191,11 @@ __global__ __launch_bounds__(64) void unpack_probe_fp_mfma(const uint8_t *__rest
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int k0 = lvl_chunk<LVL>(i, kb) * CW + lvl_dword<LVL>(i, kb) * DW;
-      const uint32_t p[4] = {fp4_pair<0>(r[i]), fp4_pair<1>(r[i]), fp4_pair<2>(r[i]), fp4_pair<3>(r[i])};
+      // nvfp4: the kernel's scaled decode at scale 1.0
+      const uint32_t p[4] = {FMT == kNvfp4 ? fp4_pair_scaled<0>(r[i], 1.0f) : fp4_pair<0>(r[i]),
+                             FMT == kNvfp4 ? fp4_pair_scaled<1>(r[i], 1.0f) : fp4_pair<1>(r[i]),
+                             FMT == kNvfp4 ? fp4_pair_scaled<2>(r[i], 1.0f) : fp4_pair<2>(r[i]),
+                             FMT == kNvfp4 ? fp4_pair_scaled<3>(r[i], 1.0f) : fp4_pair<3>(r[i])};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         o[k0 + 2 * j] = (uint16_t)(p[j] & 0xFFFFu);
@@ -297,8 +301,8 @@ int launch_unpack_probe_fp(int path, const uint8_t *codes, uint16_t *out, int N,
   } else if (path == QGEMV_PATH_MFMA) {
     const dim3 g(((N + 15) / 16) * (K / (4 * CW))), b(64);
     if (fmt == kMxfp4) hipLaunchKernelGGL(unpack_probe_fp_mfma<kMxfp4>, g, b, 0, stream, codes, out, N, K);
-    else if (fmt == kMxfp8) hipLaunchKernelGGL(unpack_probe_fp_mfma<kMxfp8>, g, b, 0, stream, codes, out, N, K);
-    else return QGEMV_EUNSUPPORTED;
+    else if (fmt == kNvfp4) hipLaunchKernelGGL(unpack_probe_fp_mfma<kNvfp4>, g, b, 0, stream, codes, out, N, K);
+    else hipLaunchKernelGGL(unpack_probe_fp_mfma<kMxfp8>, g, b, 0, stream, codes, out, N, K);
   } else {
     return QGEMV_EINVAL;
   }

@@ -201,10 +201,12 @@ int qgemv_stream_probe_blocks(size_t nbytes);
  *           overlap it).
  * Requirements (else QGEMV_EINVAL / QGEMV_EALIGN): format one of the three;
  * 1 <= M <= 16; 1 <= N <= QGEMV_MAX_N; 64 <= K <= QGEMV_MAX_K, K % 64 == 0.
- * The MFMA path runs the 32-element-block formats with K % 128 == 0; nvfp4
- * runs on the dot path.  Elements are decoded exactly (every E2M1 and E4M3
- * value is a bf16 value) and each block's scale is applied once in fp32 to the
- * block's partial dot product; tolerance and row invariance as qgemv_small.
+ * The MFMA path needs K % 128 == 0.  Elements are decoded exactly (every E2M1
+ * and E4M3 value is a bf16 value); each block's scale is applied once in fp32
+ * to the block's partial dot product, except on the MFMA path for nvfp4, where
+ * each element is multiplied by its E4M3 block scale before the product (the
+ * product of an E4M3 and an E2M1 value is itself exact in bf16).  Tolerance
+ * and row invariance as qgemv_small.
  */
 #define QGEMV_FMT_MXFP4 1
 #define QGEMV_FMT_NVFP4 2

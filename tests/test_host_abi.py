@@ -231,12 +231,12 @@ def test_fp_residual_overlap_and_alignment():
 
 def test_fp_path_support():
     sup = q.qgemv_path_supported_fp
-    assert sup("mfma", 4, 4096, 4096, "mxfp4") and sup("mfma", 4, 4096, 4096, "mxfp8")
-    assert not sup("mfma", 4, 4096, 4096, "nvfp4")      # 16-element blocks: dot path only
-    assert not sup("mfma", 4, 4096, 192, "mxfp4")       # K not a multiple of 128
+    for fmt in ("mxfp4", "nvfp4", "mxfp8"):
+        assert sup("mfma", 4, 4096, 4096, fmt)
+        assert not sup("mfma", 4, 4096, 192, fmt)       # K not a multiple of 128
     assert sup("dot", 4, 4096, 192, "nvfp4") and sup("dot", 4, 4096, 192, "mxfp8")
     for fmt in ("mxfp4", "nvfp4", "mxfp8"):
         for M in range(1, 17):
             p = q.qgemv_select_fp(M, 15360, 3840, fmt)
             assert p in (q.PATH_DOT, q.PATH_MFMA) and sup(p, M, 15360, 3840, fmt)
-    assert q.lib().qgemv_unpack_probe_fp(q.PATH_MFMA, A, A, 64, 256, q.FMT_NVFP4, None) == q.EUNSUPPORTED
+    assert q.lib().qgemv_unpack_probe_fp(q.PATH_MFMA, A, A, 64, 192, q.FMT_NVFP4, None) == q.EUNSUPPORTED
