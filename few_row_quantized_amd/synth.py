@@ -273,6 +273,70 @@ def special_problem(K: int, N: int, bits: int, group_size: int, M: int, kind: st
     return p
 
 
+@dataclasses.dataclass(frozen=True)
+class MoeShape:
+    """One MoE expert projection: E experts of [N, K], affine codes; M verify
+    rows, each routed to `topk` distinct experts."""
+
+    name: str
+    E: int
+    K: int
+    N: int
+    bits: int
+    group_size: int
+    topk: int
+    m_values: Tuple[int, ...]
+    seed: int
+
+
+# Qwen3-30B-A3B's expert FFN (named on the MLX page, Facts: the group-size
+# decode study): 128 experts, 8 active per token, hidden size 2048, expert
+# intermediate size 768; gate and up fused into one [1536, 2048] matrix.
+MOE_WORKLOADS: Dict[str, MoeShape] = {s.name: s for s in [
+    MoeShape("moe30b_gateup_e128_k2048_n1536_4b_g64_top8", 128, 2048, 1536, 4, 64, 8,
+             tuple(range(1, 17)), seed=70000),
+    MoeShape("moe30b_down_e128_k768_n2048_4b_g64_top8", 128, 768, 2048, 4, 64, 8,
+             tuple(range(1, 17)), seed=70100),
+]}
+
+
+@dataclasses.dataclass
+class MoeProblem:
+    """codes [E, N, K*bits/8]; scales, biases [E, N, K/gs] fp16 bits; x [Mmax, K]
+    bf16 bits; routing [Mmax, topk] expert ids (distinct per row).  An M-row
+    verify uses pairs p = m*topk + j for m < M: x_idx[p] = m,
+    e_idx[p] = routing[m, j]."""
+
+    shape: MoeShape
+    codes: np.ndarray
+    scales: np.ndarray
+    biases: np.ndarray
+    x: np.ndarray
+    routing: np.ndarray
+
+    def pairs(self, M: int):
+        k = self.shape.topk
+        x_idx = np.repeat(np.arange(M, dtype=np.int32), k)
+        e_idx = self.routing[:M].reshape(-1).astype(np.int32)
+        return x_idx, e_idx
+
+
+def make_moe_problem(shape: MoeShape, m_max: Optional[int] = None) -> MoeProblem:
+    """Expert weights with the 4-bit affine distributions of the dense
+    workloads (drawn expert by expert), x ~ N(0, 1) in bf16, then the routing:
+    each row picks `topk` distinct experts uniformly at random.  Draw order:
+    codes, scales, bias noise, x, routing."""
+    m_max = m_max or max(shape.m_values)
+    rng = np.random.default_rng(shape.seed)
+    codes = _draw_codes(rng, shape.E * shape.N, shape.K, shape.bits).reshape(shape.E, shape.N, -1)
+    s, b = _draw_meta(rng, shape.E * shape.N, shape.K // shape.group_size, shape.bits)
+    scales = s.reshape(shape.E, shape.N, -1)
+    biases = b.reshape(shape.E, shape.N, -1)
+    x, _ = _draw_x(rng, m_max, shape.K, False)
+    routing = np.stack([rng.choice(shape.E, size=shape.topk, replace=False) for _ in range(m_max)])
+    return MoeProblem(shape, codes, scales, biases, x, routing.astype(np.int32))
+
+
 def make_residual(M: int, N: int, seed: int) -> np.ndarray:
     """Residual input of the fused residual sum: float32 [M, N] ~ N(0, 1), drawn
     from its own stream (seed + 1_000_003) so the problem's other draws do not

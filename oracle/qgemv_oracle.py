@@ -70,6 +70,8 @@ __all__ = [
     "fp_dequantize",
     "qgemv_fp_reference",
     "fp_abs_product_sum",
+    "qgemv_gather_reference",
+    "gather_abs_product_sum",
 ]
 
 
@@ -308,4 +310,52 @@ def fp_abs_product_sum(codes, scales, x_bits, M: int, N: int, K: int, fmt: str,
     out = np.empty((M, n_out), dtype=np.float64)
     for start, idx in _row_chunks(N, K, rows):
         out[:, start:start + len(idx)] = x @ np.abs(fp_dequantize(codes[idx], scales[idx], K, fmt)).T
+    return out
+
+
+# ---------------------------------------------------------------- gathered (MoE) verify
+#
+# The MoE form of the verify product (MLX page, Facts: dense and MoE
+# gather_qmm verify; the expert-union cost per verify row is named as
+# unstudied).  Read plainly, as a gathered product over (activation row,
+# expert) pairs: pair p takes activation row x_idx[p] and expert e_idx[p] and
+# yields y[p] = x[x_idx[p]] . dequant(W[e_idx[p]])^T, with the experts'
+# weights stored as E affine-quantized matrices of the same shape.  A fast
+# path reads every expert in the union of e_idx once for all the pairs that
+# use it; the value it reaches is this per-pair product.
+
+def qgemv_gather_reference(codes, scales, biases, x_bits, x_idx, e_idx, N: int, K: int,
+                           bits: int, group_size: int,
+                           rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """y[p, j] = sum_k x[x_idx[p], k] * w_{e_idx[p]}[n_j, k] in fp64.
+
+    codes [E, N, K*bits/8]; scales, biases [E, N, K/gs] fp16 bits; x_bits
+    [X, K] bf16 bits; x_idx, e_idx [P] integers.  Experts are dequantized once
+    each (pairs grouped by expert only to avoid recomputing w; the sums are per
+    pair)."""
+    x_idx = np.asarray(x_idx, dtype=np.int64)
+    e_idx = np.asarray(e_idx, dtype=np.int64)
+    P = len(e_idx)
+    n_out = N if rows is None else len(rows)
+    y = np.empty((P, n_out), dtype=np.float64)
+    x_bits = np.asarray(x_bits)
+    for e in np.unique(e_idx):
+        sel = np.nonzero(e_idx == e)[0]
+        y[sel] = qgemv_reference(codes[e], scales[e], biases[e], x_bits[x_idx[sel]], len(sel), N, K,
+                                 bits, group_size, rows=rows)
+    return y
+
+
+def gather_abs_product_sum(codes, scales, biases, x_bits, x_idx, e_idx, N: int, K: int, bits: int,
+                           group_size: int, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """sum_k |x[x_idx[p], k] * w_{e_idx[p]}[n, k]| per pair (the tolerance scale)."""
+    x_idx = np.asarray(x_idx, dtype=np.int64)
+    e_idx = np.asarray(e_idx, dtype=np.int64)
+    x_bits = np.asarray(x_bits)
+    n_out = N if rows is None else len(rows)
+    out = np.empty((len(e_idx), n_out), dtype=np.float64)
+    for e in np.unique(e_idx):
+        sel = np.nonzero(e_idx == e)[0]
+        out[sel] = abs_product_sum(codes[e], scales[e], biases[e], x_bits[x_idx[sel]], len(sel), N, K,
+                                   bits, group_size, rows=rows)
     return out
