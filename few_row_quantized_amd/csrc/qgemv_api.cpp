@@ -298,6 +298,19 @@ int qgemv_unpack_probe_fp(int path, const uint8_t *codes, uint16_t *out, int N, 
                                        reinterpret_cast<hipStream_t>(stream));
 }
 
+int qgemv_gather(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
+                 const uint16_t *x, const int32_t *x_idx, const int32_t *e_idx, float *y, int P,
+                 int X, int E, int N, int K, int bits, int group_size, void *stream) {
+  const int s = validate(codes, scales, biases, x, y, 1, N, K, bits, group_size);
+  if (s != QGEMV_OK) return s;
+  if (P < 1 || P > QGEMV_MAX_PAIRS || E < 1 || E > QGEMV_MAX_EXPERTS || X < 1) return QGEMV_EINVAL;
+  if (!x_idx || !e_idx) return QGEMV_EINVAL;
+  if (!aligned(x_idx, 4) || !aligned(e_idx, 4)) return QGEMV_EALIGN;
+  if (!qgemv::mfma_supports(K, bits, group_size)) return QGEMV_EUNSUPPORTED;
+  const QgemvArgs a{codes, scales, biases, x, y, 1, N, K, bits, group_size};
+  return qgemv::launch_gather(a, x_idx, e_idx, P, X, E, reinterpret_cast<hipStream_t>(stream));
+}
+
 const char *qgemv_strerror(int status) {
   switch (status) {
     case QGEMV_OK: return "ok";

@@ -1,0 +1,62 @@
+// Gathered (MoE) verify: y[p] = x[x_idx[p]] . dequant(W[e_idx[p]])^T over
+// (activation row, expert) pairs, the MoE form of the verify product (MLX
+// page, Facts: dense and MoE gather_qmm verify, whose expert-union cost per
+// verify row is named as unstudied).
+//
+// Every expert in the union of e_idx is read from HBM once per call, for all
+// the pairs routed to it, by the single-pass MFMA kernel (GATHER variant in
+// qgemv_mfma_impl.h): one workgroup per (expert slot, 16-column tile), the
+// slot-th expert in ascending id order found from a bitmap of the union built
+// in LDS, its pairs gathered in ascending order and taken 16 rows at a time.
+// The host does not know the union size (the routing stays on the device), so
+// the grid covers min(P, E) slots and workgroups past the union exit at once.
+
+#include "qgemv_mfma_impl.h"
+
+namespace qgemv {
+
+namespace {
+
+template <int BITS, int GS>
+int launch_gather_t(const QgemvArgs &a, const GatherArgs &ga, hipStream_t stream) {
+  constexpr int MAXT = MfmaShape<BITS, GS, 1>::MAXT;
+  constexpr int SPI = MfmaShape<BITS, GS, 1>::SPI;
+  const auto kern = qgemv_mfma_kernel<BITS, GS, 1, MAXT, SPI, 1, false, false, kAffine, true>;
+  const int nblk = a.K / (4 * GS);
+  const int waves = pick_waves(nblk, MAXT / 64);
+  const int tiles = (a.N + 15) / 16;
+  const int slots = ga.P < ga.E ? ga.P : ga.E;
+  // at most kMaxPairs * 2^18 workgroups: within the grid limit
+  const unsigned blocks = (unsigned)slots * (unsigned)tiles;
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * waves), 0, stream, a.codes, a.scales, a.biases,
+                     a.x, a.y, static_cast<const float *>(nullptr), 16, a.N, a.K, tiles, ga);
+  return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}
+
+}  // namespace
+
+int launch_gather(const QgemvArgs &a, const int32_t *x_idx, const int32_t *e_idx, int P, int X,
+                  int E, hipStream_t stream) {
+  if (!mfma_supports(a.K, a.bits, a.group_size)) return QGEMV_EUNSUPPORTED;
+  const GatherArgs ga{x_idx, e_idx, P, X, E};
+  if (a.bits == 4) {
+    switch (a.group_size) {
+      case 32: return launch_gather_t<4, 32>(a, ga, stream);
+      case 64: return launch_gather_t<4, 64>(a, ga, stream);
+      case 128: return launch_gather_t<4, 128>(a, ga, stream);
+    }
+  } else if (a.bits == 2) {
+    switch (a.group_size) {
+      case 64: return launch_gather_t<2, 64>(a, ga, stream);
+      case 128: return launch_gather_t<2, 128>(a, ga, stream);
+    }
+  } else {
+    switch (a.group_size) {
+      case 32: return launch_gather_t<8, 32>(a, ga, stream);
+      case 64: return launch_gather_t<8, 64>(a, ga, stream);
+    }
+  }
+  return QGEMV_EUNSUPPORTED;
+}
+
+}  // namespace qgemv

@@ -26,6 +26,11 @@ struct QgemvArgs {
   int fmt = 0;
 };
 
+// Gathered (MoE) verify limits: experts per matrix set and (row, expert) pairs
+// per call.
+constexpr int kMaxExperts = QGEMV_MAX_EXPERTS;
+constexpr int kMaxPairs = QGEMV_MAX_PAIRS;
+
 // LDS of one workgroup: hardware limit on gfx950, and the dot path's
 // preferred x-staging budget (two workgroups per CU).
 constexpr size_t kLdsMax = 160 * 1024;
@@ -55,6 +60,9 @@ bool mfma_supports_fp(int K, int fmt);
 // Probes.
 int launch_unpack_probe(int path, const uint8_t *codes, uint8_t *q_out, int N, int K, int bits,
                         int group_size, hipStream_t stream);
+// Gathered (MoE) verify on the MFMA kernel: y[p] = x[x_idx[p]] . W[e_idx[p]]^T.
+int launch_gather(const QgemvArgs &a, const int32_t *x_idx, const int32_t *e_idx, int P, int X,
+                  int E, hipStream_t stream);
 int launch_unpack_probe_fp(int path, const uint8_t *codes, uint16_t *out, int N, int K, int fmt,
                            hipStream_t stream);
 int launch_stream_probe(const uint8_t *buf, size_t nbytes, uint32_t *out, hipStream_t stream);

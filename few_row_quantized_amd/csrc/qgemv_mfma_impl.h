@@ -1,0 +1,520 @@
+// Single-pass split-K bf16 MFMA kernel of the few-row quantized GEMV
+// (gfx950): the kernel template and its launch-shape helpers, shared by the
+// dense launchers (qgemv_mfma.hip) and the gathered MoE launcher
+// (qgemv_gather.hip).  The design is described in qgemv_mfma.hip.
+#pragma once
+
+#include "qgemv_device.h"
+#include "qgemv_internal.h"
+
+namespace qgemv {
+
+namespace {
+
+// Bit pattern that y holds, before a K-split launch with the residual sum,
+// until the first half of K lands.  A NaN payload that no partial sum can
+// carry: partials derive from bf16 and fp16 inputs, whose NaNs have zero low
+// 13 bits in fp32, and fresh NaNs are the canonical 0x7FC00000.
+constexpr uint32_t kSplitSentinel = 0x7FC0DEADu;
+
+// Gathered (MoE) verify: pair p takes activation row x_idx[p] and expert
+// e_idx[p]; the experts are E matrices [N][K] stored one after another.
+struct GatherArgs {
+  const int32_t *x_idx;
+  const int32_t *e_idx;
+  int P;  // pairs
+  int X;  // activation rows
+  int E;  // experts
+};
+
+// y and res may be the same buffer (in-place residual sum): neither is
+// declared restrict; every element is read before it is written, by the same
+// thread.
+// FMT: kAffine, or a block-scaled FP format (one scale byte per block in
+// `scales`, no bias, elements decoded in natural order): kMxfp4 and kMxfp8
+// (32-element blocks, GS = 32, scale folded per block in fp32) or kNvfp4
+// (16-element blocks, laid out as GS = 32; each element is multiplied by its
+// block scale before the MFMA, exactly, so B holds the weights themselves).
+// GATHER: workgroup b serves expert slot b / ngroups (the slot-th expert, in
+// ascending id order, of the union of e_idx) and tile group b % ngroups; its
+// rows are the pairs routed to that expert (in ascending pair order, 16 at a
+// time), gathered from x and scattered to y[pair].  Slots past the union exit
+// at once.  (NT = 1, KS = 1, not PERSIST, affine codes.)
+template <int BITS, int GS, int NT, int MAXT, int SPI, int KS, bool PERSIST, bool ADD, int FMT,
+          bool GATHER = false>
+__global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
+    const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *y,
+    const float *res, int M, int N, int K, int ngroups, GatherArgs ga) {
+  constexpr int CW = 128 / BITS;       // codes per 16-byte chunk
+  constexpr int SCW = 4 * CW;          // codes per 64-byte super-chunk
+  constexpr int DW = CW / 4;           // codes per dword
+  constexpr int HS = BITS == 2 ? 2 : 1;  // MFMA steps per code dword (8-bit: one per two dwords)
+  // activation operands per super-chunk: one per code register (2/4-bit) or
+  // per pair of code registers (8-bit)
+  constexpr int XR = BITS == 8 ? 2 : 4;
+  constexpr bool HAS_BIAS = FMT == kAffine;
+  constexpr int BLKW = 4 * GS;         // codes per bias block (4 groups)
+  constexpr int BSC = BLKW / SCW;      // super-chunks per block
+  constexpr int CPG = GS / CW;         // chunks per group (1, 2 or 4)
+  constexpr int GPS = 4 / CPG;         // groups per super-chunk
+  // how far the four chunk rows are exchanged so that a register holds one group
+  constexpr int LVL = CPG >= 4 ? 0 : (CPG == 2 ? 1 : 2);
+  constexpr int REGS_G = CPG;          // registers (of one super-chunk) per group
+  // A wave walks its K-slice in batches of UNR super-chunks (whole blocks):
+  // activations, codes and metadata of a batch are issued together, then the
+  // activation work is done while the codes are in flight, then the codes
+  // are consumed in load order.  UNR is compile-time so positions within a
+  // block and register slots are static.
+  constexpr int UNR = SPI > BSC ? SPI : BSC;
+  constexpr int BPB = UNR / BSC;       // blocks per batch
+  static_assert(BSC >= 1 && BLKW % SCW == 0 && UNR % BSC == 0 && CPG >= 1, "block layout");
+
+  __shared__ float red[MAXT / 64][NT][4][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int waves = blockDim.x >> 6;
+  const int col = lane & 15;
+  const int kb = lane >> 4;
+  const int NBLK = K / BLKW;
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t offset_pair = opaque_u32(kOffsetPair);
+  // element offset, within a super-chunk, of the codes register i holds in
+  // this lane's row after the partial transpose
+  int xoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xoff[i] = lvl_chunk<LVL>(i, kb) * CW + lvl_dword<LVL>(i, kb) * DW;
+
+  // Gathered verify: pick this workgroup's expert and its pairs.
+  __shared__ uint32_t gbits[GATHER ? kMaxExperts / 32 : 1];
+  __shared__ int gpairs[GATHER ? kMaxPairs : 1];
+  __shared__ int gmeta[2];
+  int c0 = 0;  // first pair of the current chunk of 16 rows
+  if constexpr (GATHER) {
+    static_assert(NT == 1 && KS == 1 && !PERSIST && !ADD && FMT == kAffine, "gather variant");
+    const int words = (ga.E + 31) >> 5;
+    for (int i = threadIdx.x; i < words; i += blockDim.x) gbits[i] = 0u;
+    __syncthreads();
+    for (int p = threadIdx.x; p < ga.P; p += blockDim.x) {
+      const int e = ga.e_idx[p], xi = ga.x_idx[p];
+      if (e >= 0 && e < ga.E && xi >= 0 && xi < ga.X) atomicOr(&gbits[e >> 5], 1u << (e & 31));
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      // the slot-th set bit of the union bitmap
+      const int slot = (int)blockIdx.x / ngroups;
+      int seen = 0, expert = -1;
+      for (int w = 0; w < words && expert < 0; ++w) {
+        uint32_t b = gbits[w];
+        const int c = __popc(b);
+        if (seen + c > slot) {
+          for (int k = slot - seen; k > 0; --k) b &= b - 1;  // drop the lower set bits
+          expert = 32 * w + __ffs(b) - 1;
+        }
+        seen += c;
+      }
+      gmeta[0] = expert;
+    }
+    __syncthreads();
+    const int expert = gmeta[0];
+    if (expert < 0) return;  // slot past the union (uniform for the workgroup)
+    if (wave == 0) {
+      // pairs of this expert in ascending order (ballot compaction)
+      int base = 0;
+      for (int p0 = 0; p0 < ga.P; p0 += 64) {
+        const int p = p0 + lane;
+        bool hit = false;
+        if (p < ga.P) {
+          const int xi = ga.x_idx[p];
+          hit = ga.e_idx[p] == expert && xi >= 0 && xi < ga.X;
+        }
+        const uint64_t bal = __ballot(hit);
+        if (hit) gpairs[base + __popcll(bal & ((1ull << lane) - 1ull))] = p;
+        base += __popcll(bal);
+      }
+      if (lane == 0) gmeta[1] = base;
+    }
+    __syncthreads();
+    const size_t G_ = (size_t)(K / GS);
+    codes += (size_t)expert * N * ((size_t)K * BITS / 8);
+    scales += (size_t)expert * N * G_;
+    biases += (size_t)expert * N * G_;
+  }
+  // activation row of row m of the current chunk, and its output row
+  auto xrow = [&](const int m) -> size_t { return GATHER ? (size_t)ga.x_idx[gpairs[c0 + m]] : (size_t)m; };
+  auto yrow = [&](const int m) -> size_t { return GATHER ? (size_t)gpairs[c0 + m] : (size_t)m; };
+
+  // One tile group (16*NT output columns over all of K) per call of `group`.
+  auto group = [&](const int tg) {
+  // group tg = (tile group, part of K); with KS = 2 the two halves of K of a
+  // tile group are separate groups whose results are added into y
+  const int kpart = KS == 1 ? 0 : (tg & 1);
+  const int n_base = (KS == 1 ? tg : tg >> 1) * 16 * NT;
+  const int p_lo = KS == 1 ? 0 : (kpart ? NBLK >> 1 : 0);
+  const int nbp = KS == 1 ? NBLK : (kpart ? NBLK - (NBLK >> 1) : NBLK >> 1);
+  // K-slice of this wave.  The slice order is rotated per workgroup (by
+  // blockIdx/8: workgroups are dealt round-robin over the 8 XCDs) so that the
+  // CUs sharing an L2 do not all read the same activation lines at the same
+  // moment.  Partials are reduced in slice order, so results do not depend
+  // on the rotation.
+  const int slice = (wave + (tg >> 3)) % waves;
+  const int b_begin = p_lo + (slice * nbp) / waves;
+  const int b_end = p_lo + ((slice + 1) * nbp) / waves;
+  const size_t RB = (size_t)K * BITS / 8;
+  const int G = FMT == kNvfp4 ? K / 16 : K / GS;  // scale (or scale-and-bias) entries per row
+  // Rows m >= M and columns n >= N only feed outputs that are never stored,
+  // so their lanes read valid clamped addresses instead of branching around
+  // the loads (a branch would force a wait on every load).
+  const uint16_t *xr = x + xrow(col < M ? col : M - 1) * K;
+  const uint8_t *crow[NT];
+  const uint16_t *srow[NT];
+  const uint16_t *brow[NT];
+  const uint8_t *srow8[NT];  // FP formats: scale bytes
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int n = min(n_base + 16 * t + col, N - 1);
+    crow[t] = codes + (size_t)n * RB + kb * 16;
+    srow[t] = scales + (size_t)n * G;
+    brow[t] = biases + (size_t)n * G;
+    srow8[t] = reinterpret_cast<const uint8_t *>(scales) + (size_t)n * G;
+  }
+
+  // residual of the outputs this thread stores in its first NT reduction
+  // steps (all of them when the workgroup has at least 4 waves), loaded ahead
+  // of the weight stream; clamped indices read a valid element, never used
+  float rpre[NT];
+  if constexpr (ADD) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int o = min((int)threadIdx.x + j * (int)blockDim.x, NT * 256 - 1);
+      const int l = o & 63;
+      const int m = min(4 * (l >> 4) + ((o >> 6) & 3), M - 1);
+      const int n = min(n_base + 16 * (o >> 8) + (l & 15), N - 1);
+      rpre[j] = res[yrow(m) * N + n];
+    }
+  }
+
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = zero4;
+
+  for (int blk0 = b_begin; blk0 < b_end; blk0 += BPB) {
+    const int nb = min(BPB, b_end - blk0);  // blocks in this batch (uniform)
+    // ---- issue: activations first (L2), then codes (HBM), then metadata
+    u32x4_t xv[UNR][XR][HS];
+    u32x4_t cv[UNR][NT];
+    uint2 s4[BPB][NT], b4[BPB][NT];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      if (u / BSC < nb) {
+        const int k0 = (blk0 * BSC + u) * SCW;
+#pragma unroll
+        for (int i = 0; i < XR; ++i)
+#pragma unroll
+          for (int l = 0; l < HS; ++l)
+            xv[u][i][l] = *reinterpret_cast<const u32x4_t *>(
+                xr + k0 + (BITS == 8 ? xoff[2 * i] : xoff[i]) + 8 * l);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      if (u / BSC < nb) {
+        const int gsc = blk0 * BSC + u;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) cv[u][t] = load_stream_u32x4(crow[t] + (size_t)gsc * 64);
+      }
+    }
+#pragma unroll
+    for (int bb = 0; bb < BPB; ++bb) {
+      if (bb < nb) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if constexpr (HAS_BIAS) {
+            s4[bb][t] = *reinterpret_cast<const uint2 *>(srow[t] + (size_t)(blk0 + bb) * 4);
+            b4[bb][t] = *reinterpret_cast<const uint2 *>(brow[t] + (size_t)(blk0 + bb) * 4);
+          } else if constexpr (FMT == kNvfp4) {
+            // the 8 scale bytes of the block's 128 elements
+            s4[bb][t] = *reinterpret_cast<const uint2 *>(srow8[t] + (size_t)(blk0 + bb) * 8);
+          } else {
+            // the block's 4 scale bytes
+            s4[bb][t].x = *reinterpret_cast<const uint32_t *>(srow8[t] + (size_t)(blk0 + bb) * 4);
+          }
+        }
+      }
+    }
+    // keep the whole batch of loads ahead of the compute: without this the
+    // scheduler may sink later loads below the first waits and serialize them
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- activation work, overlapping the code loads: re-pair x to the
+    // code pairing and form the per-group activation sums.  xsum of group
+    // g0 + j ends up in row j of this lane's column, i.e. in the A layout of
+    // v_mfma_f32_16x16x4_f32 for the bias product.
+    float xsum[BPB];
+#pragma unroll
+    for (int bb = 0; bb < BPB; ++bb) {
+      float P[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int uu = 0; uu < BSC; ++uu) {
+        const int u = bb * BSC + uu;
+        if constexpr (!HAS_BIAS) continue;  // FP formats: natural order, no bias sums
+        if constexpr (BITS == 8) {
+          // natural order: only the group sums; step e of the super-chunk
+          // holds 8 codes of group (uu*SCW + 32e)/GS of the block
+#pragma unroll
+          for (int e = 0; e < XR; ++e) {
+            const int j = (uu * SCW + 32 * e) / GS;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) P[j] = dot2_bf16(xv[u][e][0][c], 0x3F803F80u, P[j]);
+          }
+          continue;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = uu * GPS + i / REGS_G;  // group within the block
+#pragma unroll
+          for (int l = 0; l < HS; ++l)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) P[j] = dot2_bf16(xv[u][i][l][e], 0x3F803F80u, P[j]);
+          if constexpr (BITS == 4) {
+            const uint32_t X[4] = {xv[u][i][0][0], xv[u][i][0][1], xv[u][i][0][2], xv[u][i][0][3]};
+            xv[u][i][0] = u32x4_t{xpair_stride4(X, 0), xpair_stride4(X, 1), xpair_stride4(X, 2),
+                                  xpair_stride4(X, 3)};
+          } else {
+            const uint32_t X[8] = {xv[u][i][0][0], xv[u][i][0][1], xv[u][i][0][2], xv[u][i][0][3],
+                                   xv[u][i][1][0], xv[u][i][1][1], xv[u][i][1][2], xv[u][i][1][3]};
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              xv[u][i][h] = u32x4_t{xpair_stride8(X, 4 * h + 0), xpair_stride8(X, 4 * h + 1),
+                                    xpair_stride8(X, 4 * h + 2), xpair_stride8(X, 4 * h + 3)};
+          }
+        }
+      }
+      if constexpr (HAS_BIAS) xsum[bb] = rows_transpose_reduce4(P);
+    }
+
+    // ---- codes, super-chunk by super-chunk in load order
+    f32x4_t accg[NT];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      if (u / BSC >= nb) break;
+      const int scb = u % BSC;  // super-chunk within its block
+      uint32_t cur[NT][4];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        cur[t][0] = cv[u][t][0];
+        cur[t][1] = cv[u][t][1];
+        cur[t][2] = cv[u][t][2];
+        cur[t][3] = cv[u][t][3];
+        transpose_rows_lvl<LVL>(cur[t]);
+      }
+      if constexpr (BITS == 8) {
+        // MFMA step e takes code registers 2e, 2e+1 (8 consecutive codes of
+        // this lane's row; the activations at xoff[2e]..+7)
+#pragma unroll
+        for (int e = 0; e < XR; ++e) {
+          const int kk = scb * SCW + 32 * e;  // first code of the step within the block
+          const int j = kk / GS;              // its group within the block
+          const bool gfirst = kk % GS == 0;
+          const bool glast = (kk + 32) % GS == 0;
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xv[u][e][0]);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            u32x4_t bw;
+            if constexpr (FMT == kMxfp8) {
+              bw = u32x4_t{fp8_pair<false>(cur[t][2 * e]), fp8_pair<true>(cur[t][2 * e]),
+                           fp8_pair<false>(cur[t][2 * e + 1]), fp8_pair<true>(cur[t][2 * e + 1])};
+            } else {
+              bw = unpack8_quad(cur[t][2 * e], cur[t][2 * e + 1]);
+            }
+            accg[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                a, __builtin_bit_cast(bf16x8_t, bw), gfirst ? zero4 : accg[t], 0, 0, 0);
+          }
+          if (glast) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              float sc;
+              if constexpr (HAS_BIAS) {
+                const uint32_t sw = (j < 2) ? s4[u / BSC][t].x : s4[u / BSC][t].y;
+                sc = half_bits_to_float((j & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+              } else {
+                sc = fp_scale_to_float<FMT>(s4[u / BSC][t].x >> (8 * j));
+              }
+#pragma unroll
+              for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(sc, accg[t][q], acc[t][q]);
+            }
+          }
+        }
+      }
+      if constexpr (FMT == kNvfp4) {
+        // register i holds elements 8kb..8kb+7 of chunk i (4x4 transpose), i.e.
+        // 16-element block 2i + kb/2 of the super-chunk: scale them exactly and
+        // accumulate straight into acc
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int b = 2 * i + (kb >> 1);
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xv[u][i][0]);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const uint32_t sw = b < 4 ? s4[u / BSC][t].x : s4[u / BSC][t].y;
+            const float sc = e4m3_to_float(sw >> (8 * (b & 3)));
+            const u32x4_t bw = u32x4_t{fp4_pair_scaled<0>(cur[t][i], sc), fp4_pair_scaled<1>(cur[t][i], sc),
+                                       fp4_pair_scaled<2>(cur[t][i], sc), fp4_pair_scaled<3>(cur[t][i], sc)};
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bw),
+                                                              acc[t], 0, 0, 0);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < (BITS == 8 || FMT == kNvfp4 ? 0 : 4); ++i) {
+        const int j = scb * GPS + i / REGS_G;  // group within the block
+#pragma unroll
+        for (int h = 0; h < HS; ++h) {
+          const bool gfirst = (i % REGS_G) == 0 && h == 0;
+          const bool glast = (i % REGS_G) == REGS_G - 1 && h == HS - 1;
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xv[u][i][h]);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            u32x4_t bw;
+            if constexpr (FMT == kMxfp4) {
+              // 8 elements of one dword, natural order
+              bw = u32x4_t{fp4_pair<0>(cur[t][i]), fp4_pair<1>(cur[t][i]), fp4_pair<2>(cur[t][i]),
+                           fp4_pair<3>(cur[t][i])};
+            } else if constexpr (BITS == 4) {
+              bw = unpack4_split_quad(cur[t][i], offset_pair);
+            } else {
+              bw = unpack2_split_quad(cur[t][i], h, offset_pair);
+            }
+            accg[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                a, __builtin_bit_cast(bf16x8_t, bw), gfirst ? zero4 : accg[t], 0, 0, 0);
+          }
+          if (glast) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              float sc;
+              if constexpr (HAS_BIAS) {
+                const uint32_t sw = (j < 2) ? s4[u / BSC][t].x : s4[u / BSC][t].y;
+                sc = half_bits_to_float((j & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+              } else {
+                sc = fp_scale_to_float<FMT>(s4[u / BSC][t].x >> (8 * j));
+              }
+#pragma unroll
+              for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(sc, accg[t][q], acc[t][q]);
+            }
+          }
+        }
+      }
+      if (HAS_BIAS && scb == BSC - 1) {
+        // bias with the 128 offset: acc += xsum[m][g0+kb] * (b - 128 s)[n][g0+kb]
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const uint32_t sw = (kb < 2) ? s4[u / BSC][t].x : s4[u / BSC][t].y;
+          const uint32_t bw = (kb < 2) ? b4[u / BSC][t].x : b4[u / BSC][t].y;
+          const float sc = half_bits_to_float((kb & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+          const float b = half_bits_to_float((kb & 1) ? (bw >> 16) : (bw & 0xFFFFu));
+          const float bo = BITS == 8 ? b : fmaf(-128.f, sc, b);  // 2/4-bit: remove the 128 offset
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum[u / BSC], bo, acc[t], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // split-K reduction over the slices, fixed order
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[slice][t][i][lane] = acc[t][i];
+  __syncthreads();
+  // output o of the tile group: sum over the slices, then store (pre: the
+  // residual rv was prefetched)
+  auto finish = [&](const int o, const bool pre, float rv) {
+    const int t = o >> 8;
+    const int i = (o >> 6) & 3;
+    const int l = o & 63;
+    float s = 0.f;
+    for (int w = 0; w < waves; ++w) s += red[w][t][i][l];
+    const int m = 4 * (l >> 4) + i;
+    const int n = n_base + 16 * t + (l & 15);
+    if (m < M && n < N) {
+      float *dst = y + yrow(m) * N + n;
+      if constexpr (ADD) {
+        if (!pre) rv = res[yrow(m) * N + n];
+      }
+      if constexpr (KS == 1) {
+        *dst = ADD ? s + rv : s;
+      } else if constexpr (!ADD) {
+        // y was zeroed before the launch and receives exactly two addends:
+        // 0 + a + b equals 0 + b + a bit for bit, whichever half lands first
+        unsafeAtomicAdd(dst, s);
+      } else {
+        // y held kSplitSentinel: the first half leaves its partial there, the
+        // second finds it and stores (a + b) + r.  a + b and b + a are the same
+        // float, so the result is the plain product's plus r, whichever half
+        // lands first.
+        const float old = atomicExch(dst, s);
+        if (__builtin_bit_cast(uint32_t, old) != kSplitSentinel) *dst = (old + s) + rv;
+      }
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int o = threadIdx.x + j * blockDim.x;
+    if (o < NT * 256) finish(o, true, ADD ? rpre[j] : 0.f);
+  }
+  for (int o = threadIdx.x + NT * blockDim.x; o < NT * 256; o += blockDim.x) finish(o, false, 0.f);
+  };
+
+  if constexpr (GATHER) {
+    // the expert's pairs, 16 rows at a time
+    const int pairs = gmeta[1];
+    for (c0 = 0; c0 < pairs; c0 += 16) {
+      M = min(16, pairs - c0);
+      if (c0 != 0) __syncthreads();  // reduction buffer drained
+      group((int)blockIdx.x % ngroups);
+    }
+  } else if constexpr (PERSIST) {
+    // Persistent workgroups: the grid holds as many workgroups as the device
+    // runs at once, and each walks tile groups tg, tg + gridDim.x, ... so that
+    // no partial last round of workgroups is left for a few CUs.
+    for (int tg = blockIdx.x; tg < ngroups; tg += gridDim.x) {
+      if (tg != (int)blockIdx.x) __syncthreads();  // reduction buffer drained
+      group(tg);
+    }
+  } else {
+    // one tile group per workgroup (all groups resident at once)
+    group(blockIdx.x);
+  }
+}
+
+// waves per workgroup: spread the bias blocks evenly over at most max_waves
+int pick_waves(int nblk, int max_waves) {
+  if (nblk <= max_waves) return nblk;
+  int best = max_waves;
+  double best_eff = 0.0;
+  for (int w = max_waves; w >= max_waves / 2; --w) {
+    const int per = (nblk + w - 1) / w;
+    const double eff = (double)nblk / (double)(per * w);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = w;
+    }
+  }
+  return best;
+}
+
+// Per-variant launch shape: thread cap (waves per workgroup) and the number of
+// super-chunks in flight per wave, chosen to keep every variant within the
+// register budget of its thread cap without spills.
+template <int BITS, int GS, int NT>
+struct MfmaShape {
+  static constexpr int SPI = (BITS == 4 && GS == 128 && NT == 1) ? 4 : 2;
+  static constexpr int MAXT = (BITS == 4 && NT == 1 && GS <= 64) ? 1024 : 512;
+};
+
+
+
+
+}  // namespace
+
+}  // namespace qgemv

@@ -32,6 +32,8 @@ _FMTS = {"mxfp4": FMT_MXFP4, "nvfp4": FMT_NVFP4, "mxfp8": FMT_MXFP8}
 MAX_M = 16
 MAX_K = 131072
 MAX_N = 4194304
+MAX_EXPERTS = 4096
+MAX_PAIRS = 256
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemv.so")
 
@@ -59,6 +61,7 @@ def lib() -> ctypes.CDLL:
         L.qgemv_small_add.argtypes = gemv_add
         L.qgemv_run_path_add.argtypes = [i] + gemv_add
         L.qgemv_select.argtypes = [i, i, i, i, i]
+        L.qgemv_gather.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
         gemv_fp = [vp, vp, vp, vp, vp, i, i, i, i, vp]
         L.qgemv_small_fp.argtypes = gemv_fp
         L.qgemv_run_path_fp.argtypes = [i] + gemv_fp
@@ -73,7 +76,7 @@ def lib() -> ctypes.CDLL:
         L.qgemv_strerror.restype = ctypes.c_char_p
         L.qgemv_version.argtypes = []
         for name in ("qgemv_small", "qgemv_run_path", "qgemv_small_add", "qgemv_run_path_add",
-                     "qgemv_small_fp", "qgemv_run_path_fp", "qgemv_select_fp",
+                     "qgemv_small_fp", "qgemv_run_path_fp", "qgemv_select_fp", "qgemv_gather",
                      "qgemv_path_supported_fp", "qgemv_unpack_probe_fp",
                      "qgemv_select", "qgemv_path_supported",
                      "qgemv_unpack_probe", "qgemv_stream_probe", "qgemv_stream_probe_blocks",
@@ -169,6 +172,13 @@ def qgemv_path_supported_fp(path, M: int, N: int, K: int, fmt) -> bool:
 def qgemv_unpack_probe_fp(path, codes, out, N: int, K: int, fmt, stream=None) -> int:
     return _check(lib().qgemv_unpack_probe_fp(_path(path), _ptr(codes), _ptr(out), N, K, _fmt(fmt),
                                               _stream(stream)), "qgemv_unpack_probe_fp")
+
+
+def qgemv_gather(codes, scales, biases, x, x_idx, e_idx, y, P: int, X: int, E: int, N: int, K: int,
+                 bits: int, group_size: int, stream=None) -> int:
+    return _check(lib().qgemv_gather(_ptr(codes), _ptr(scales), _ptr(biases), _ptr(x), _ptr(x_idx),
+                                     _ptr(e_idx), _ptr(y), P, X, E, N, K, bits, group_size,
+                                     _stream(stream)), "qgemv_gather")
 
 
 def qgemv_select(M: int, N: int, K: int, bits: int, group_size: int) -> int:

@@ -66,6 +66,8 @@ extern "C" {
 #define QGEMV_MAX_M 16
 #define QGEMV_MAX_K 131072
 #define QGEMV_MAX_N 4194304
+#define QGEMV_MAX_EXPERTS 4096 /* experts per qgemv_gather call */
+#define QGEMV_MAX_PAIRS 256    /* (row, expert) pairs per qgemv_gather call */
 
 /*
  * qgemv_small -- y = x . dequant(W)^T for 1 <= M <= 16, path chosen by
@@ -233,6 +235,37 @@ int qgemv_path_supported_fp(int path, int M, int N, int K, int format);
  */
 int qgemv_unpack_probe_fp(int path, const uint8_t *codes, uint16_t *out, int N, int K, int format,
                           void *stream);
+
+/*
+ * qgemv_gather -- gathered (MoE) verify over (activation row, expert) pairs:
+ *
+ *   y[p] = x[x_idx[p]] . dequant(W[e_idx[p]])^T,   0 <= p < P
+ *
+ * the MoE form of the verify product (MLX page, Facts: dense and MoE
+ * gather_qmm verify; the expert-union cost per verify row).  Every expert in
+ * the union of e_idx is read and dequantized once per call for all the pairs
+ * routed to it, instead of once per pair.
+ *   codes   uint8 [E][N][K*bits/8]; scales, biases fp16 [E][N][K/group_size]:
+ *           E matrices in the affine format of qgemv_small, one after another.
+ *   x       bf16 [X][K] activation rows.
+ *   x_idx, e_idx  int32 [P], DEVICE arrays (the routing stays on the device):
+ *           the activation row and the expert of each pair.
+ *   y       fp32 [P][N], row p written for every valid pair.
+ * A pair whose x_idx is outside [0, X) or e_idx outside [0, E) is skipped and
+ * its row of y is left unchanged (the indices are read on the device; the
+ * host cannot check them without a synchronization).
+ * Requirements (else QGEMV_EINVAL / QGEMV_EALIGN / QGEMV_EUNSUPPORTED):
+ * shape and format as qgemv_run_path with the MFMA path (bits, group_size, N,
+ * K, and the MFMA path's K requirements); 1 <= P <= QGEMV_MAX_PAIRS;
+ * 1 <= E <= QGEMV_MAX_EXPERTS; X >= 1; pointers non-NULL, codes, scales,
+ * biases, x and y 16-byte aligned, x_idx and e_idx 4-byte aligned.
+ * Runs on the MFMA kernel (any number of pairs per expert, 16 rows at a
+ * time); each pair's row has the numerics of the MFMA path and is
+ * deterministic (pairs are taken in ascending order).
+ */
+int qgemv_gather(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
+                 const uint16_t *x, const int32_t *x_idx, const int32_t *e_idx, float *y, int P,
+                 int X, int E, int N, int K, int bits, int group_size, void *stream);
 
 /* qgemv_strerror -- static description of a status code. */
 const char *qgemv_strerror(int status);

@@ -240,3 +240,30 @@ def test_fp_path_support():
             p = q.qgemv_select_fp(M, 15360, 3840, fmt)
             assert p in (q.PATH_DOT, q.PATH_MFMA) and sup(p, M, 15360, 3840, fmt)
     assert q.lib().qgemv_unpack_probe_fp(q.PATH_MFMA, A, A, 64, 192, q.FMT_NVFP4, None) == q.EUNSUPPORTED
+
+
+# ---------------------------------------------------------------- gathered (MoE) verify
+
+def test_gather_validation():
+    L = q.lib()
+    g = L.qgemv_gather
+    ok = dict(P=8, X=2, E=16, N=64, K=256, bits=4, gs=64)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        ptrs = kw.pop("ptrs", None) or [A, A, A, A, A, A, A]
+        return g(*ptrs, a["P"], a["X"], a["E"], a["N"], a["K"], a["bits"], a["gs"], None)
+
+    assert call(P=0) == q.EINVAL and call(P=q.MAX_PAIRS + 1) == q.EINVAL
+    assert call(E=0) == q.EINVAL and call(E=q.MAX_EXPERTS + 1) == q.EINVAL
+    assert call(X=0) == q.EINVAL
+    assert call(bits=3) == q.EINVAL and call(K=96) == q.EINVAL
+    assert call(K=192, gs=32) == q.EUNSUPPORTED  # K not a multiple of 128: no MFMA path
+    assert call(bits=2, gs=32) == q.EUNSUPPORTED
+    for i in range(7):
+        ptrs = [A] * 7
+        ptrs[i] = None
+        assert g(*ptrs, 8, 2, 16, 64, 256, 4, 64, None) == q.EINVAL
+    ptrs = [A] * 7
+    ptrs[4] = A + 2  # x_idx not 4-byte aligned
+    assert g(*ptrs, 8, 2, 16, 64, 256, 4, 64, None) == q.EALIGN
