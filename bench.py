@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
     ap.add_argument("--no-residual", action="store_true",
                     help="skip the fused residual sum (MUL_MAT + ADD) comparison")
+    ap.add_argument("--no-moe", action="store_true",
+                    help="skip the gathered (MoE) verify measurement")
     return ap.parse_args()
 
 
@@ -170,6 +172,11 @@ def main():
     residual = None
     if not args.no_residual:
         residual = measure_residual_sum(s, p, ms, paths, pool, x, copies, args, capture, time_graph)
+    moe = None
+    if not args.no_moe:
+        del pool
+        torch.cuda.empty_cache()
+        moe = measure_moe(args, capture, time_graph)
 
     def cell_json(M, pth, t, t1):
         alg = accounting.algorithmic_bytes(M, s.N, s.K, s.bits, s.group_size)
@@ -231,6 +238,7 @@ def main():
         "roofline": roofline,
         "ceiling": ceiling,
         "residual_sum": residual,
+        "moe_verify": moe,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -294,6 +302,83 @@ def measure_residual_sum(s, p, ms, paths, pool, x, copies, args, capture, time_g
     return {"per_m": out, "bitwise_plain_plus_add": exact,
             "timing": "graph chains per (M, variant), interleaved rounds, median; "
                       "separate = plain call then torch.add(y, r)"}
+
+
+def measure_moe(args, capture, time_graph, name="moe30b_gateup_e128_k2048_n1536_4b_g64_top8",
+                ms=(1, 2, 4, 8, 16)):
+    """Gathered (MoE) verify: per M, one qgemv_gather call over the M*topk
+    (row, expert) pairs, which reads each expert of the union once, against M
+    calls of one row each (the routed experts streamed once per verify row).
+    Weights rotate over copies of the expert set larger than the caches;
+    chains of launches, interleaved rounds, median."""
+    import numpy as np
+    import torch
+    from few_row_quantized_amd import qgemv as q
+    sh = synth.MOE_WORKLOADS[name]
+    p = synth.make_moe_problem(sh, m_max=max(ms))
+    expert_bytes = accounting.weight_bytes(sh.N, sh.K, sh.bits, sh.group_size)
+    total = expert_bytes * sh.E
+    copies = max(2, math.ceil(args.pool_mib * 2 ** 20 / total))
+    codes = torch.from_numpy(p.codes).cuda()
+    sc = torch.from_numpy(p.scales.view(np.int16)).cuda()
+    bi = torch.from_numpy(p.biases.view(np.int16)).cuda()
+    pool = [(codes, sc, bi)] + [(codes.clone(), sc.clone(), bi.clone()) for _ in range(copies - 1)]
+    x = torch.from_numpy(p.x.view(np.int16)).cuda()
+    ys = torch.empty((sh.topk * max(ms), sh.N), dtype=torch.float32, device="cuda")
+    pairs = {}
+    for M in ms:
+        xi, ei = p.pairs(M)
+        pairs[M] = (torch.from_numpy(xi).cuda(), torch.from_numpy(ei).cuda(), len(set(ei.tolist())))
+    rows = {m: (torch.from_numpy(np.zeros(sh.topk, np.int32)).cuda(),
+                torch.from_numpy(p.routing[m].astype(np.int32)).cuda()) for m in range(max(ms))}
+    ctr = [0]
+
+    def one(M, kind):
+        c = pool[ctr[0] % copies]
+        ctr[0] += 1
+        if kind == "gathered":
+            xi, ei, _ = pairs[M]
+            q.qgemv_gather(c[0], c[1], c[2], x, xi, ei, ys, len(xi), M, sh.E, sh.N, sh.K, sh.bits,
+                           sh.group_size)
+        else:
+            for m in range(M):
+                xi, ei = rows[m]
+                q.qgemv_gather(c[0], c[1], c[2], x[m:m + 1], xi, ei, ys[sh.topk * m:], sh.topk, 1,
+                               sh.E, sh.N, sh.K, sh.bits, sh.group_size)
+
+    chain = max(20, args.chain // 8)
+    cells = [(M, k) for M in ms for k in ("gathered", "per_row")]
+    for c in cells:
+        one(*c)
+    torch.cuda.synchronize()
+    graphs = {c: capture(lambda c=c: [one(*c) for _ in range(chain)]) for c in cells}
+    for c in cells:
+        time_graph(graphs[c])
+    samp = {c: [] for c in cells}
+    for _ in range(args.rounds):
+        for c in cells:
+            samp[c].append(time_graph(graphs[c]) / chain)
+    del graphs
+    out = {}
+    t1 = None
+    for M in ms:
+        tg = statistics.median(samp[(M, "gathered")])
+        tr = statistics.median(samp[(M, "per_row")])
+        t1 = t1 or tg
+        union = pairs[M][2]
+        out[str(M)] = {"pairs": M * sh.topk, "union_experts": union, "gathered_us": round(tg * 1e6, 3),
+                       "per_row_us": round(tr * 1e6, 3), "speedup": round(tr / tg, 3),
+                       "t_over_t1": round(tg / t1, 3),
+                       "union_GBps": round(union * expert_bytes / tg / 1e9, 1),
+                       "us_per_verify_row": round(tg * 1e6 / M, 3)}
+        log(f"[bench] moe M={M:2d} pairs={M * sh.topk:3d} union={union:3d} gathered {tg * 1e6:8.2f} us "
+            f"per-row {tr * 1e6:8.2f} us  {union * expert_bytes / tg / 1e9:7.1f} GB/s")
+    del pool
+    torch.cuda.empty_cache()
+    return {"workload": name, "experts": sh.E, "topk": sh.topk, "expert_bytes": expert_bytes,
+            "pool_copies": copies, "per_m": out,
+            "timing": "graph chains; gathered = one qgemv_gather per verify step; per_row = M calls of "
+                      "one row's 8 pairs; interleaved rounds, median"}
 
 
 def measured_traffic(workload, M):

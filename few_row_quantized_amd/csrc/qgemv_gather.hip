@@ -17,20 +17,34 @@ namespace qgemv {
 
 namespace {
 
-template <int BITS, int GS>
-int launch_gather_t(const QgemvArgs &a, const GatherArgs &ga, hipStream_t stream) {
-  constexpr int MAXT = MfmaShape<BITS, GS, 1>::MAXT;
-  constexpr int SPI = MfmaShape<BITS, GS, 1>::SPI;
-  const auto kern = qgemv_mfma_kernel<BITS, GS, 1, MAXT, SPI, 1, false, false, kAffine, true>;
+constexpr int kGatherWideTiles = 64;
+
+template <int BITS, int GS, int NT>
+int launch_gather_nt(const QgemvArgs &a, const GatherArgs &ga, hipStream_t stream) {
+  constexpr int MAXT = MfmaShape<BITS, GS, NT>::MAXT;
+  constexpr int SPI = MfmaShape<BITS, GS, NT>::SPI;
+  const auto kern = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, false, false, kAffine, true>;
   const int nblk = a.K / (4 * GS);
   const int waves = pick_waves(nblk, MAXT / 64);
-  const int tiles = (a.N + 15) / 16;
+  const int groups = ((a.N + 15) / 16 + NT - 1) / NT;
   const int slots = ga.P < ga.E ? ga.P : ga.E;
   // at most kMaxPairs * 2^18 workgroups: within the grid limit
-  const unsigned blocks = (unsigned)slots * (unsigned)tiles;
+  const unsigned blocks = (unsigned)slots * (unsigned)groups;
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * waves), 0, stream, a.codes, a.scales, a.biases,
-                     a.x, a.y, static_cast<const float *>(nullptr), 16, a.N, a.K, tiles, ga);
+                     a.x, a.y, static_cast<const float *>(nullptr), 16, a.N, a.K, groups, ga);
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}
+
+// Two 16-column tiles per workgroup when K is short (at most 4 bias blocks,
+// so at most 4 waves) and the expert has at least 64 tiles: the routing
+// prologue and the activation loads are then shared by twice the weight
+// bytes.  Measured on the 128-expert top-8 shapes at M = 16: 2048 x 768
+// 37.5 -> 29.0 us; 1536 x 2048 (8 blocks) 84.2 -> 87.0 us, so it stays at one.
+template <int BITS, int GS>
+int launch_gather_t(const QgemvArgs &a, const GatherArgs &ga, hipStream_t stream) {
+  if ((a.N + 15) / 16 >= kGatherWideTiles && a.K / (4 * GS) <= 4)
+    return launch_gather_nt<BITS, GS, 2>(a, ga, stream);
+  return launch_gather_nt<BITS, GS, 1>(a, ga, stream);
 }
 
 }  // namespace

@@ -39,7 +39,7 @@ struct GatherArgs {
 // ascending id order, of the union of e_idx) and tile group b % ngroups; its
 // rows are the pairs routed to that expert (in ascending pair order, 16 at a
 // time), gathered from x and scattered to y[pair].  Slots past the union exit
-// at once.  (NT = 1, KS = 1, not PERSIST, affine codes.)
+// at once.  (KS = 1, not PERSIST, affine codes.)
 template <int BITS, int GS, int NT, int MAXT, int SPI, int KS, bool PERSIST, bool ADD, int FMT,
           bool GATHER = false>
 __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
@@ -89,16 +89,22 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   // Gathered verify: pick this workgroup's expert and its pairs.
   __shared__ uint32_t gbits[GATHER ? kMaxExperts / 32 : 1];
   __shared__ int gpairs[GATHER ? kMaxPairs : 1];
+  __shared__ int gexp[GATHER ? kMaxPairs : 1];  // expert of each pair, -1 if invalid
+  __shared__ int gxr[GATHER ? kMaxPairs : 1];   // activation row of each pair
   __shared__ int gmeta[2];
   int c0 = 0;  // first pair of the current chunk of 16 rows
   if constexpr (GATHER) {
-    static_assert(NT == 1 && KS == 1 && !PERSIST && !ADD && FMT == kAffine, "gather variant");
+    static_assert(KS == 1 && !PERSIST && !ADD && FMT == kAffine, "gather variant");
     const int words = (ga.E + 31) >> 5;
     for (int i = threadIdx.x; i < words; i += blockDim.x) gbits[i] = 0u;
     __syncthreads();
+    // the routing is read from memory once and kept in LDS
     for (int p = threadIdx.x; p < ga.P; p += blockDim.x) {
       const int e = ga.e_idx[p], xi = ga.x_idx[p];
-      if (e >= 0 && e < ga.E && xi >= 0 && xi < ga.X) atomicOr(&gbits[e >> 5], 1u << (e & 31));
+      const bool valid = e >= 0 && e < ga.E && xi >= 0 && xi < ga.X;
+      gexp[p] = valid ? e : -1;
+      gxr[p] = xi;
+      if (valid) atomicOr(&gbits[e >> 5], 1u << (e & 31));
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -124,11 +130,7 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
       int base = 0;
       for (int p0 = 0; p0 < ga.P; p0 += 64) {
         const int p = p0 + lane;
-        bool hit = false;
-        if (p < ga.P) {
-          const int xi = ga.x_idx[p];
-          hit = ga.e_idx[p] == expert && xi >= 0 && xi < ga.X;
-        }
+        const bool hit = p < ga.P && gexp[p] == expert;
         const uint64_t bal = __ballot(hit);
         if (hit) gpairs[base + __popcll(bal & ((1ull << lane) - 1ull))] = p;
         base += __popcll(bal);
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     biases += (size_t)expert * N * G_;
   }
   // activation row of row m of the current chunk, and its output row
-  auto xrow = [&](const int m) -> size_t { return GATHER ? (size_t)ga.x_idx[gpairs[c0 + m]] : (size_t)m; };
+  auto xrow = [&](const int m) -> size_t { return GATHER ? (size_t)gxr[gpairs[c0 + m]] : (size_t)m; };
   auto yrow = [&](const int m) -> size_t { return GATHER ? (size_t)gpairs[c0 + m] : (size_t)m; };
 
   // One tile group (16*NT output columns over all of K) per call of `group`.
