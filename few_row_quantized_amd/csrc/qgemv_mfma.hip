@@ -38,6 +38,8 @@
 // (qgemv_persist.hip) unless K is too long for its register-resident
 // activations.
 
+#include <atomic>
+
 #include "qgemv_mfma_impl.h"
 
 namespace qgemv {
@@ -81,14 +83,15 @@ int launch_mfma_t(const QgemvArgs &a, hipStream_t stream) {
                        reinterpret_cast<uint32_t *>(a.y), n, ADD ? kSplitSentinel : 0u);
   }
   // workgroups resident at once for this block size (cached per wave count)
-  static int occ_cache[MAXT / 64 + 1] = {0};
-  int occ = occ_cache[waves];
+  // (the same on every MI355X; concurrent first calls store the same value)
+  static std::atomic<int> occ_cache[MAXT / 64 + 1];
+  int occ = occ_cache[waves].load(std::memory_order_relaxed);
   if (occ == 0) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void *>(kern),
                                                      64 * waves, 0) != hipSuccess ||
         occ <= 0)
       occ = 1;
-    occ_cache[waves] = occ;
+    occ_cache[waves].store(occ, std::memory_order_relaxed);
   }
   const int slots = occ * cus;
   const bool single = groups <= slots;

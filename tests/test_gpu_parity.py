@@ -255,3 +255,49 @@ def test_stream_probe_reads_every_byte():
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
     assert got == np.bitwise_xor.reduce(host)
+
+
+# ---------------------------------------------------------------- concurrency
+
+def test_concurrent_calls_from_host_threads_on_separate_streams():
+    # the library keeps only caches of device properties: calls from several
+    # host threads, each on its own stream (default priority), give the same
+    # bits as the same calls made one after another
+    import threading
+    import torch
+    cases = [(2048, 4500, 4, 64, "mfma"), (1024, 300, 4, 32, "dot"), (5120, 1024, 4, 128, "mfma"),
+             (2048, 97, 8, 64, "auto"), (1280, 300, 2, 64, "dot"), (4096, 512, 8, 32, "mfma")]
+    devs = [DeviceProblem(synth.make_problem(synth.custom_shape(K, N, b, g, seed=K + N), m_max=8))
+            for K, N, b, g, _ in cases]
+    say("concurrency: sequential reference")
+    want = [d.run_host(M, path) for d, (_, _, _, _, path) in zip(devs, cases) for M in (1, 5, 8)]
+    got = [None] * len(want)
+    errors = []
+
+    def worker(i):
+        try:
+            st = torch.cuda.Stream()
+            d, path = devs[i], cases[i][4]
+            outs = []
+            with torch.cuda.stream(st):
+                for M in (1, 5, 8):
+                    y = torch.full((M, d.p.N), float("nan"), dtype=torch.float32, device="cuda:0")
+                    for _ in range(20):
+                        q.qgemv_run_path(path, d.codes, d.scales, d.biases, d.x, y, M, d.p.N, d.p.K,
+                                         d.p.bits, d.p.group_size, stream=st)
+                    outs.append(y)
+            st.synchronize()
+            for j, y in enumerate(outs):
+                got[3 * i + j] = y.cpu().numpy()
+        except Exception as e:  # surfaced below
+            errors.append(repr(e))
+
+    say("concurrency: threads")
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for a, b in zip(want, got):
+        assert np.array_equal(a, b)
