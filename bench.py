@@ -71,7 +71,8 @@ class Pool:
         import torch
         self.P = copies
         c = torch.from_numpy(p.codes).cuda()
-        s = torch.from_numpy(p.scales.view(np.int16)).cuda()
+        fp = p.shape.fmt is not None  # block-scaled FP: scale bytes, no biases
+        s = torch.from_numpy(p.scales if fp else p.scales.view(np.int16)).cuda()
         b = torch.from_numpy(p.biases.view(np.int16)).cuda()
         self.codes = torch.empty((copies,) + tuple(c.shape), dtype=c.dtype, device="cuda")
         self.scales = torch.empty((copies,) + tuple(s.shape), dtype=s.dtype, device="cuda")
@@ -102,23 +103,45 @@ def main():
     s = synth.WORKLOADS[args.workload]
     ms = [int(v) for v in args.m_values.split(",")] if args.m_values else list(s.m_values)
     p = synth.make_problem(s, m_max=max(ms))
-    W = accounting.weight_bytes(s.N, s.K, s.bits, s.group_size)
+    fp = s.fmt is not None
+    W = (accounting.fp_weight_bytes(s.N, s.K, s.bits, s.group_size) if fp else
+         accounting.weight_bytes(s.N, s.K, s.bits, s.group_size))
     copies = 1 if args.hot else max(2, math.ceil(args.pool_mib * 2 ** 20 / W))
     log(f"[bench] {s.name}: W={W} B, pool of {copies} copies ({copies * W / 2**20:.0f} MiB), M={ms}")
     pool = Pool(p, copies)
     x = torch.from_numpy(p.x.view(np.int16)).cuda()
     ys = {M: torch.empty((M, s.N), dtype=torch.float32, device="cuda") for M in ms}
-    paths = {M: (args.path if args.path != "auto" else
-                 {q.PATH_DOT: "dot", q.PATH_MFMA: "mfma"}[q.qgemv_select(M, s.N, s.K, s.bits, s.group_size)])
+    def select(M):
+        return q.qgemv_select_fp(M, s.N, s.K, s.fmt) if fp else q.qgemv_select(M, s.N, s.K, s.bits,
+                                                                               s.group_size)
+
+    def supported(path, M):
+        return (q.qgemv_path_supported_fp(path, M, s.N, s.K, s.fmt) if fp else
+                q.qgemv_path_supported(path, M, s.N, s.K, s.bits, s.group_size))
+
+    paths = {M: (args.path if args.path != "auto" else {q.PATH_DOT: "dot", q.PATH_MFMA: "mfma"}[select(M)])
              for M in ms}
 
     counter = [0]
 
+    def call(path, i, M, y, residual=None):
+        if fp:
+            q.qgemv_run_path_fp(path, pool.codes[i], pool.scales[i], x, residual, y, M, s.N, s.K, s.fmt)
+        elif residual is not None:
+            q.qgemv_run_path_add(path, pool.codes[i], pool.scales[i], pool.biases[i], x, residual, y,
+                                 M, s.N, s.K, s.bits, s.group_size)
+        else:
+            q.qgemv_run_path(path, pool.codes[i], pool.scales[i], pool.biases[i], x, y, M, s.N, s.K,
+                             s.bits, s.group_size)
+
     def launch(M, path=args.path):
         i = counter[0] % copies
         counter[0] += 1
-        q.qgemv_run_path(path, pool.codes[i], pool.scales[i], pool.biases[i], x, ys[M], M,
-                         s.N, s.K, s.bits, s.group_size)
+        call(path, i, M, ys[M])
+
+    def alg_bytes(M):
+        return (accounting.fp_algorithmic_bytes(M, s.N, s.K, s.bits, s.group_size) if fp else
+                accounting.algorithmic_bytes(M, s.N, s.K, s.bits, s.group_size))
 
     def capture(fn):
         g = torch.cuda.CUDAGraph()
@@ -156,8 +179,7 @@ def main():
     # launches each, replayed once to warm up and then once per round, the
     # rounds walking every cell in turn (interleaved), median over rounds
     forced = ["dot", "mfma"] if args.path == "auto" else [args.path]
-    cells = [(M, pth) for M in ms for pth in forced
-             if q.qgemv_path_supported(pth, M, s.N, s.K, s.bits, s.group_size)]
+    cells = [(M, pth) for M in ms for pth in forced if supported(pth, M)]
     graphs = {c: capture(lambda c=c: [launch(c[0], c[1]) for _ in range(args.chain)]) for c in cells}
     for c in cells:
         time_graph(graphs[c])
@@ -171,7 +193,7 @@ def main():
     ceiling = None if args.no_ceiling else measure_ceiling(W, copies, args.chain, capture, time_graph)
     residual = None
     if not args.no_residual:
-        residual = measure_residual_sum(s, p, ms, paths, pool, x, copies, args, capture, time_graph)
+        residual = measure_residual_sum(s, p, ms, paths, call, copies, args, capture, time_graph)
     moe = None
     if not args.no_moe:
         del pool
@@ -179,7 +201,7 @@ def main():
         moe = measure_moe(args, capture, time_graph)
 
     def cell_json(M, pth, t, t1):
-        alg = accounting.algorithmic_bytes(M, s.N, s.K, s.bits, s.group_size)
+        alg = alg_bytes(M)
         d = {"path": pth, "us": round(t * 1e6, 4),
              "us_min_max_over_rounds": [round(min(samples[(M, pth)]) * 1e6, 4),
                                         round(max(samples[(M, pth)]) * 1e6, 4)],
@@ -210,7 +232,7 @@ def main():
 
     # dominant kernel = the (path, M) configuration with the largest time per step
     Mdom = max(ms, key=lambda M: per_m[M])
-    alg = accounting.algorithmic_bytes(Mdom, s.N, s.K, s.bits, s.group_size)
+    alg = alg_bytes(Mdom)
     achieved = alg / per_m[Mdom] / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(s.name, Mdom),
@@ -227,7 +249,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": s.name, "K": s.K, "N": s.N, "bits": s.bits,
-                   "group_size": s.group_size, "m_values": ms, "path": args.path,
+                   "group_size": s.group_size, "format": s.fmt or "affine", "m_values": ms, "path": args.path,
                    "weight_bytes": W, "pool_copies": copies, "seed": p.seed,
                    "timing": "one HIP graph of K steps; each call on the next pool copy"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -244,7 +266,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def measure_residual_sum(s, p, ms, paths, pool, x, copies, args, capture, time_graph):
+def measure_residual_sum(s, p, ms, paths, call, copies, args, capture, time_graph):
     """The fused residual sum y = x W^T + r against the plain product and
     against the plain product followed by a separate fp32 add (torch's
     elementwise kernel, i.e. the unfused MUL_MAT then ADD): per M, the
@@ -263,11 +285,9 @@ def measure_residual_sum(s, p, ms, paths, pool, x, copies, args, capture, time_g
         i = ctr[0] % copies
         ctr[0] += 1
         if kind == "fused":
-            q.qgemv_run_path_add(paths[M], pool.codes[i], pool.scales[i], pool.biases[i], x, rs[M],
-                                 ys[M], M, s.N, s.K, s.bits, s.group_size)
+            call(paths[M], i, M, ys[M], residual=rs[M])
         else:
-            q.qgemv_run_path(paths[M], pool.codes[i], pool.scales[i], pool.biases[i], x, ts[M], M,
-                             s.N, s.K, s.bits, s.group_size)
+            call(paths[M], i, M, ts[M])
             if kind == "separate":
                 torch.add(ts[M], rs[M], out=ys[M])
 
@@ -465,8 +485,11 @@ def cpu_baseline(p, ms, W, budget_s):
         while steps < min_steps or time.perf_counter() - t0 < budget:
             for M in ms:
                 c0 = time.perf_counter()
-                oracle.qgemv_reference(p.codes, p.scales, p.biases, p.x, M, s.N, s.K, s.bits,
-                                       s.group_size)
+                if s.fmt is not None:
+                    oracle.qgemv_fp_reference(p.codes, p.scales, p.x, M, s.N, s.K, s.fmt)
+                else:
+                    oracle.qgemv_reference(p.codes, p.scales, p.biases, p.x, M, s.N, s.K, s.bits,
+                                           s.group_size)
                 times[M].append(time.perf_counter() - c0)
             steps += 1
         med = {M: statistics.median(v) for M, v in times.items()}
