@@ -32,7 +32,7 @@ COMMON_FLAGS = [
 
 SOURCES = ["qgemv_api.cpp", "qgemv_dot.hip", "qgemv_dot_add.hip", "qgemv_dot8.hip", "qgemv_dot_fp.hip",
            "qgemv_mfma.hip",
-           "qgemv_persist.hip", "qgemv_gather.hip", "qgemv_probe.hip"]
+           "qgemv_persist.hip", "qgemv_persist_x.hip", "qgemv_gather.hip", "qgemv_probe.hip"]
 
 
 def hipcc() -> str:

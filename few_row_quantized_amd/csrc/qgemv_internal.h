@@ -36,6 +36,16 @@ constexpr int kMaxPairs = QGEMV_MAX_PAIRS;
 constexpr size_t kLdsMax = 160 * 1024;
 constexpr size_t kDotLdsBudget = 80 * 1024;
 
+// Bit pattern that y holds, before a K-split launch with the residual sum,
+// until the first half of K lands.  A NaN payload that no partial sum can
+// carry: partials derive from bf16 and fp16 inputs, whose NaNs have zero low
+// 13 bits in fp32, and fresh NaNs are the canonical 0x7FC00000.
+constexpr uint32_t kSplitSentinel = 0x7FC0DEADu;
+
+// y[0..n) = v (bit pattern) on `stream`: zero before a K-split launch (two
+// halves added into y), kSplitSentinel before one with the residual sum.
+int launch_fill(float *y, size_t n, uint32_t v, hipStream_t stream);
+
 // Compute units of the current device (cached per device id).
 int device_cu_count();
 
@@ -52,6 +62,10 @@ int launch_mfma(const QgemvArgs &a, hipStream_t stream);
 // Persistent MFMA kernel (QGEMV_EUNSUPPORTED when the activations of a
 // wave would not fit its registers).
 int launch_persist(const QgemvArgs &a, hipStream_t stream);
+// Persistent MFMA kernel with the activations of one half of K staged in LDS
+// (long K): QGEMV_EUNSUPPORTED when they would not fit, for an in-place
+// residual sum, or with fewer tiles than CUs.
+int launch_persist_x(const QgemvArgs &a, hipStream_t stream);
 
 // Shape support of the MFMA path (host check): affine codes, FP formats.
 bool mfma_supports(int K, int bits, int group_size);

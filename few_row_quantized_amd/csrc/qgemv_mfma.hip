@@ -46,9 +46,6 @@ namespace qgemv {
 
 namespace {
 
-
-// y[0..n) = v (bit pattern): zero before a K-split launch, kSplitSentinel
-// before one with the residual sum
 __global__ __launch_bounds__(256) void fill_kernel(uint32_t *__restrict__ y, size_t n, uint32_t v) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) y[i] = v;
 }
@@ -77,10 +74,8 @@ int launch_mfma_t(const QgemvArgs &a, hipStream_t stream) {
   const int waves = pick_waves(nblk / ksplit, MAXT / 64);
   const int groups = (tiles + NT - 1) / NT * ksplit;
   if (ksplit == 2) {
-    const size_t n = (size_t)a.M * a.N;
-    const int fb = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
-    hipLaunchKernelGGL(fill_kernel, dim3(fb), dim3(256), 0, stream,
-                       reinterpret_cast<uint32_t *>(a.y), n, ADD ? kSplitSentinel : 0u);
+    const int st = launch_fill(a.y, (size_t)a.M * a.N, ADD ? kSplitSentinel : 0u, stream);
+    if (st != QGEMV_OK) return st;
   }
   // workgroups resident at once for this block size (cached per wave count)
   // (the same on every MI355X; concurrent first calls store the same value)
@@ -117,6 +112,12 @@ int launch_mfma_gs(const QgemvArgs &a, hipStream_t stream) {
 
 }  // namespace
 
+int launch_fill(float *y, size_t n, uint32_t v, hipStream_t stream) {
+  const int fb = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+  hipLaunchKernelGGL(fill_kernel, dim3(fb), dim3(256), 0, stream, reinterpret_cast<uint32_t *>(y), n, v);
+  return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}
+
 bool mfma_supports_fp(int K, int fmt) {
   (void)fmt;
   return K % 128 == 0;  // one 128-element block of bias blocks per super-chunk
@@ -139,10 +140,14 @@ int launch_mfma(const QgemvArgs &a, hipStream_t stream) {
     return launch_mfma_gs<8, 32, kMxfp8>(a, stream);
   }
   if (!mfma_supports(a.K, a.bits, a.group_size)) return QGEMV_EUNSUPPORTED;
-  // more tiles than CUs: the persistent kernel streams several tiles per CU;
-  // otherwise one tile group per workgroup in a single pass
+  // more tiles than CUs: the persistent kernel streams several tiles per CU,
+  // with the activations in registers, or, for K too long for them, in LDS
+  // (one half of K per workgroup); otherwise one tile group per workgroup in
+  // a single pass
   if ((a.N + 15) / 16 > device_cu_count()) {
-    const int st = launch_persist(a, stream);
+    int st = launch_persist(a, stream);
+    if (st != QGEMV_EUNSUPPORTED) return st;
+    st = launch_persist_x(a, stream);
     if (st != QGEMV_EUNSUPPORTED) return st;
   }
   if (a.bits == 8) {

@@ -11,12 +11,6 @@ namespace qgemv {
 
 namespace {
 
-// Bit pattern that y holds, before a K-split launch with the residual sum,
-// until the first half of K lands.  A NaN payload that no partial sum can
-// carry: partials derive from bf16 and fp16 inputs, whose NaNs have zero low
-// 13 bits in fp32, and fresh NaNs are the canonical 0x7FC00000.
-constexpr uint32_t kSplitSentinel = 0x7FC0DEADu;
-
 // Gathered (MoE) verify: pair p takes activation row x_idx[p] and expert
 // e_idx[p]; the experts are E matrices [N][K] stored one after another.
 struct GatherArgs {

@@ -136,14 +136,21 @@ def test_ragged_shapes_every_element(path, K, N, bits, gs):
 
 
 # More 16-column tiles than CUs: the MFMA path streams several tiles per
-# workgroup (ranges of 1 to 3 tiles, ragged last tile), or falls back to the
-# single-pass kernel when K is too long for the activations to stay in
-# registers (the last shape).
+# workgroup (ranges of 1 to 3 tiles, ragged last tile) with the activations
+# in registers, or, when K is too long for them, with one half of K's
+# activations in LDS per workgroup (K 6656 and up: an odd number of bias
+# blocks, halves of 7 to 24 blocks, 4 to 12 waves, 1 to 4 blocks per wave).
 PERSIST = [
     (1024, 4113, 4, 32), (2048, 4500, 4, 64), (3072, 5000, 4, 128), (6144, 4200, 4, 128),
     (1280, 4700, 2, 64), (2048, 9000, 2, 128), (8192, 4500, 4, 128),
     (1024, 4113, 8, 32), (2048, 4500, 8, 64),
+    (6656, 4200, 4, 128), (8192, 4130, 2, 64), (10240, 4500, 2, 128),
 ]
+
+# Long K with the activations of half of K in LDS, at the sizes where the LDS
+# holds them only for M <= 10 or M <= 8 (larger M takes the single-pass
+# kernel): sampled columns.
+LONG_K_LDS = [(12288, 4104, 4, 64), (12288, 4100, 4, 32), (17408, 4128, 2, 64), (17408, 4200, 4, 128)]
 
 
 @pytest.mark.parametrize("K,N,bits,gs", PERSIST)
@@ -153,6 +160,16 @@ def test_many_tiles_per_cu_every_element(K, N, bits, gs):
     for M in (1, 3, 8, 16):
         say(f"many tiles mfma K={K} N={N} bits={bits} gs={gs} M={M}")
         check_y(p, d.run_host(M, "mfma"), M, label=f"mfma K={K} N={N} M={M}")
+
+
+@pytest.mark.parametrize("K,N,bits,gs", LONG_K_LDS)
+def test_long_k_lds_persistent_sampled_columns(K, N, bits, gs):
+    p = synth.make_problem(synth.custom_shape(K, N, bits, gs, seed=9 * K + N, outliers=True), m_max=16)
+    d = DeviceProblem(p)
+    cols = sample_columns(N, 96, seed=K + N)
+    for M in (1, 2, 7, 8, 9, 16):
+        say(f"long K lds mfma K={K} N={N} bits={bits} gs={gs} M={M}")
+        check_y(p, d.run_host(M, "mfma"), M, cols=cols, label=f"mfma K={K} N={N} M={M}")
 
 
 @pytest.mark.parametrize("path", ["dot", "mfma"])
@@ -168,6 +185,7 @@ def test_zero_codes(path):
 @pytest.mark.parametrize("bits,gs,N,K", [(4, 64, 200, 2048), (2, 64, 200, 2048), (4, 128, 200, 2048),
                                          (4, 64, 4500, 2048), (2, 128, 4500, 2048),
                                          (4, 128, 300, 8192), (2, 64, 150, 10240),
+                                         (4, 128, 4200, 6656), (2, 64, 4130, 8192),
                                          (8, 64, 200, 2048), (8, 32, 4500, 1024), (8, 64, 150, 10240)])
 @pytest.mark.parametrize("path", ["dot", "mfma"])
 def test_row_of_m_row_call_equals_single_row_call_bitwise(path, bits, gs, N, K):

@@ -67,6 +67,8 @@ SHAPES = [
     (8192, 33, 4, 64), (512, 72, 2, 32), (1280, 300, 2, 64), (17408, 23, 2, 64),
     (64, 5, 2, 64), (2048, 4500, 4, 64), (1280, 4700, 2, 64), (5120, 1024, 4, 128),
     (1024, 300, 8, 64), (2048, 4500, 8, 32), (5120, 1024, 8, 64), (2048, 97, 8, 128),
+    # long K, many tiles: halves of K with their activations in LDS
+    (6656, 4200, 4, 128), (8192, 4130, 2, 64),
 ]
 
 
