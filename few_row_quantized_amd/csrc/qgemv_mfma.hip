@@ -99,14 +99,20 @@ int launch_mfma_t(const QgemvArgs &a, hipStream_t stream) {
 template <int BITS, int GS, int FMT = kAffine>
 int launch_mfma_gs(const QgemvArgs &a, hipStream_t stream) {
   // more output columns per workgroup on wide matrices: every workgroup reads
-  // all M*K activations, so wider groups cut that traffic per weight byte
+  // all M*K activations, so wider groups cut that traffic per weight byte;
+  // also on long K with at least a tile per CU once M > 8 (the shapes whose
+  // activations outgrow the LDS of the persistent kernel there; measured on
+  // the 17408-long down projections: 36.0 against 39.6 us at M = 16, and
+  // slower than one tile below M = 8)
   const int tiles = (a.N + 15) / 16;
   const int cus = device_cu_count();
+  const bool wide = tiles >= 2 * cus ||
+                    (FMT == kAffine && BITS != 8 && tiles >= cus && a.K >= 8192 && a.M > 8);
   if (a.res) {
-    if (tiles >= 2 * cus) return launch_mfma_t<BITS, GS, 2, true, FMT>(a, stream);
+    if (wide) return launch_mfma_t<BITS, GS, 2, true, FMT>(a, stream);
     return launch_mfma_t<BITS, GS, 1, true, FMT>(a, stream);
   }
-  if (tiles >= 2 * cus) return launch_mfma_t<BITS, GS, 2, false, FMT>(a, stream);
+  if (wide) return launch_mfma_t<BITS, GS, 2, false, FMT>(a, stream);
   return launch_mfma_t<BITS, GS, 1, false, FMT>(a, stream);
 }
 

@@ -25,7 +25,10 @@
 //   workgroup copies its half of x (M rows) into LDS, already re-paired to
 //   the code pairing of the MFMA operand (elements (e, e+4) of each 8 for
 //   4-bit codes, (e, e+8) of each 16 for 2-bit codes), and forms the
-//   activation sum of every group of that half.
+//   activation sum of every group of that half from the registers: the
+//   lanes holding a group's units reduce their sums by a fixed butterfly
+//   (summing a group from LDS instead, one lane per group, put every lane of
+//   a wave on the same bank: row offsets of GS*2 bytes).
 // * Wave w owns the bias blocks w, w+W, ... of the half.  For each tile its
 //   codes and metadata come through a register ring of S slots (the next
 //   tile's loads are in flight while the current one is multiplied); the
@@ -71,10 +74,12 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
   constexpr int LVL = CPG >= 4 ? 0 : (CPG == 2 ? 1 : 2);
   constexpr int REGS_G = CPG;
   constexpr int UE = BITS == 4 ? 8 : 16;  // elements of one re-pairing unit
+  constexpr int GU = GS / UE;             // units per group (a power of two <= 16)
   // staging units per thread per round: their registers are live next to
   // ring slot 0, so at most 32 VGPRs, 16 when the slot holds 8 super-chunks
   constexpr int XU = (BPW * BSC >= 8 ? 4 : 8) / (UE / 8);
   static_assert(BSC >= 1 && BLKW % SCW == 0 && CPG >= 1 && (BITS == 2 || BITS == 4), "layout");
+  static_assert(GU >= 1 && GU <= 64 && (GU & (GU - 1)) == 0, "group lanes");
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -159,11 +164,13 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
     const int upr = nbp * BLKW / UE;  // units per row
     const int units = M * upr;
     const uint16_t *xh = x + (size_t)p_lo * BLKW;
+    const int rot = 0;  // unit order (a whole number of groups)
+    auto unit_of = [&](int uu) { return uu + rot < units ? uu + rot : uu + rot - units; };
     for (int u0 = 0; u0 < units; u0 += XU * (int)blockDim.x) {
       u32x4_t v[XU][UE / 8];
 #pragma unroll
       for (int j = 0; j < XU; ++j) {
-        const int u = min(u0 + j * (int)blockDim.x + (int)threadIdx.x, units - 1);
+        const int u = unit_of(min(u0 + j * (int)blockDim.x + (int)threadIdx.x, units - 1));
         const int m = u / upr;
         const int c = u - m * upr;
 #pragma unroll
@@ -172,10 +179,22 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
       }
 #pragma unroll
       for (int j = 0; j < XU; ++j) {
-        const int u = u0 + j * (int)blockDim.x + (int)threadIdx.x;
-        if (u < units) {
+        const int uu = u0 + j * (int)blockDim.x + (int)threadIdx.x;
+        // activation sum of the unit, then of its group: units are dealt to
+        // consecutive lanes, so the GU lanes of a group add their sums in a
+        // fixed butterfly (every lane of the wave takes part)
+        float p = 0.f;
+#pragma unroll
+        for (int h = 0; h < UE / 8; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p = dot2_bf16(v[j][h][e], 0x3F803F80u, p);
+#pragma unroll
+        for (int off = 1; off < GU; off <<= 1) p += __shfl_xor(p, off);
+        if (uu < units) {
+          const int u = unit_of(uu);
           const int m = u / upr;
           const int c = u - m * upr;
+          if ((threadIdx.x & (GU - 1)) == 0) xs[m * gpr + c / GU] = p;
           u32x4_t *dst = reinterpret_cast<u32x4_t *>(xl + (size_t)m * pitch + (size_t)c * UE * 2);
           if constexpr (BITS == 4) {
             const uint32_t X[4] = {v[j][0][0], v[j][0][1], v[j][0][2], v[j][0][3]};
@@ -191,23 +210,6 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
           }
         }
       }
-    }
-    __syncthreads();
-    // activation sum of every group of the half (a permutation within each
-    // unit does not change which elements a group holds)
-    const int gh = nbp * 4;
-    for (int u = threadIdx.x; u < M * gh; u += blockDim.x) {
-      const int m = u / gh;
-      const int g = u - m * gh;
-      const u32x4_t *src = reinterpret_cast<const u32x4_t *>(xl + (size_t)m * pitch + (size_t)g * GS * 2);
-      float sum = 0.f;
-#pragma unroll
-      for (int c = 0; c < GS / 8; ++c) {
-        const u32x4_t q = src[c];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sum = dot2_bf16(q[e], 0x3F803F80u, sum);
-      }
-      xs[m * gpr + g] = sum;
     }
     __syncthreads();
   }
