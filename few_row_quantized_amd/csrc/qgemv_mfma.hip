@@ -100,10 +100,10 @@ template <int BITS, int GS, int FMT = kAffine>
 int launch_mfma_gs(const QgemvArgs &a, hipStream_t stream) {
   // more output columns per workgroup on wide matrices: every workgroup reads
   // all M*K activations, so wider groups cut that traffic per weight byte;
-  // also on long K with at least a tile per CU once M > 8 (the shapes whose
-  // activations outgrow the LDS of the persistent kernel there; measured on
-  // the 17408-long down projections: 36.0 against 39.6 us at M = 16, and
-  // slower than one tile below M = 8)
+  // also on long K with at least a tile per CU once M > 8, where the
+  // persistent kernels do not run (an in-place residual sum, K beyond their
+  // reach; measured on the 17408-long down projections: 36.0 against 39.6 us
+  // at M = 16, and slower than one tile below M = 8)
   const int tiles = (a.N + 15) / 16;
   const int cus = device_cu_count();
   const bool wide = tiles >= 2 * cus ||

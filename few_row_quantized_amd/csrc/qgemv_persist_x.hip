@@ -15,7 +15,9 @@
 // persistent kernel reads them once per CU, but a wave holds at most one or
 // two bias blocks of activations in registers, so K beyond ~6144 does not fit.
 // Here the activations of one half of K live in LDS (160 KiB per CU on
-// gfx950), read once per CU and re-read from LDS for every tile.
+// gfx950), read once per CU and re-read from LDS for every tile; when a half
+// does not fit (M above 7 at K = 17408), the half is walked in P phases,
+// each restaging its share of the activations.
 //
 // CDNA4 design:
 // * A persistent grid of one workgroup per CU.  Workgroup b takes half
@@ -29,19 +31,24 @@
 //   lanes holding a group's units reduce their sums by a fixed butterfly
 //   (summing a group from LDS instead, one lane per group, put every lane of
 //   a wave on the same bank: row offsets of GS*2 bytes).
-// * Wave w owns the bias blocks w, w+W, ... of the half.  For each tile its
-//   codes and metadata come through a register ring of S slots (the next
-//   tile's loads are in flight while the current one is multiplied); the
+// * Phase q covers the blocks [q*nb/P, (q+1)*nb/P) of the half; wave w owns
+//   its blocks lo+w, lo+w+W, ...  The workgroup walks (phase, tile) steps in
+//   phase-major order; each step's codes and metadata come through a
+//   register ring of S slots (the next step's loads are in flight while the
+//   current one is multiplied, also across a phase change); the
 //   activation operand of each v_mfma_f32_16x16x32_bf16 is one 16-byte LDS
 //   read per lane (rows m >= M read row M-1: their outputs are never
 //   stored).  Unpack, scale fold and the bias product
 //   (v_mfma_f32_16x16x4_f32 against the group sums) are those of the other
 //   MFMA kernels.
-// * Every S tiles the waves' partial tiles are summed through LDS in block
-//   order and each half is added into y with a float atomic; y was zeroed
-//   before the launch and receives exactly two addends, so 0 + a + b and
-//   0 + b + a are the same float: deterministic, and row m of an M-row call
-//   equals the M = 1 call bit for bit.
+// * Each wave adds its partial 16x16 tile of a step into an LDS slot of its
+//   own per tile (no barrier between steps); after the last step the slots
+//   are summed over the waves in block order and each half is added into y
+//   with a float atomic.  y was zeroed before the launch and receives exactly
+//   two addends, so 0 + a + b and 0 + b + a are the same float:
+//   deterministic, and row m of an M-row call equals the M = 1 call bit for
+//   bit whenever both take the same number of phases (the phase count and
+//   the waves' blocks depend on M through the LDS budget).
 // * Fused residual sum (ADD, "metal : few-row MMA mat-mul and batched copies
 //   for speculative decoding", Overview: MUL_MAT + ADD writes the residual
 //   sum from the store): y is prefilled with kSplitSentinel; the first half
@@ -56,12 +63,16 @@ namespace {
 
 constexpr int kXMaxWaves = 12;  // register budget: 768-thread workgroups
 constexpr int kXRing = 2;       // slots of the code prefetch ring
+// passes over the half of K (activations restaged per pass): a third pass
+// was slower than the single-pass kernel (4-bit down projection, M = 16:
+// 36.6 against 35.8 us)
+constexpr int kXMaxPhases = 2;
 
 template <int BITS, int GS, int BPW, bool ADD>
 __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *__restrict__ y,
-    const float *__restrict__ res, int M, int N, int K) {
+    const float *__restrict__ res, int M, int N, int K, int P, int ntile_max) {
   constexpr int S = kXRing;
   constexpr int CW = 128 / BITS;         // codes per 16-byte chunk
   constexpr int SCW = 4 * CW;            // codes per 64-byte super-chunk
@@ -76,7 +87,7 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
   constexpr int UE = BITS == 4 ? 8 : 16;  // elements of one re-pairing unit
   constexpr int GU = GS / UE;             // units per group (a power of two <= 16)
   // staging units per thread per round: their registers are live next to
-  // ring slot 0, so at most 32 VGPRs, 16 when the slot holds 8 super-chunks
+  // one ring slot, so at most 32 VGPRs, 16 when the slot holds 8 super-chunks
   constexpr int XU = (BPW * BSC >= 8 ? 4 : 8) / (UE / 8);
   static_assert(BSC >= 1 && BLKW % SCW == 0 && CPG >= 1 && (BITS == 2 || BITS == 4), "layout");
   static_assert(GU >= 1 && GU <= 64 && (GU & (GU - 1)) == 0, "group lanes");
@@ -100,77 +111,83 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
   const int p_lo = part ? NBLK >> 1 : 0;
   const int nbp = part ? NBLK - (NBLK >> 1) : NBLK >> 1;  // blocks of this half
   const int nbp_max = NBLK - (NBLK >> 1);
+  const int nbq_max = (nbp_max + P - 1) / P;  // blocks of the longest phase
   const int T = (N + 15) >> 4;
   const int t_first = (int)((unsigned)gp * (unsigned)T / (unsigned)GP);
   const int ntile = (int)((unsigned)(gp + 1) * (unsigned)T / (unsigned)GP) - t_first;
+  const int steps = P * ntile;  // (phase, tile) steps, phase-major
 
-  // LDS: x rows of the half (re-paired bf16, padded pitch), group sums, and
-  // the partial tiles of the waves
+  // LDS: x rows of the phase (re-paired bf16, padded pitch), its group sums,
+  // and one partial 16x16 tile per (tile, wave), added to over the phases
   extern __shared__ uint4 lds[];
-  const int pitch = nbp_max * BLKW * 2 + 16;  // bytes per activation row
-  const int gpr = nbp_max * 4;                // group sums per row
+  const int pitch = nbq_max * BLKW * 2 + 16;  // bytes per activation row
+  const int gpr = nbq_max * 4;                // group sums per row
   uint8_t *xl = reinterpret_cast<uint8_t *>(lds);
   float *xs = reinterpret_cast<float *>(xl + (size_t)M * pitch);
-  float *red = xs + (size_t)M * gpr;  // [S][W][4][64]
+  float *pacc = xs + (size_t)M * gpr;  // [ntile_max][W][4][64]
 
   int xoff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) xoff[i] = lvl_chunk<LVL>(i, kb) * CW + lvl_dword<LVL>(i, kb) * DW;
 
-  // owned blocks (index within the half); a wave past the last block loads a
-  // valid block and skips the arithmetic
-  int lb[BPW];
-  bool own[BPW];
-#pragma unroll
-  for (int k = 0; k < BPW; ++k) {
-    own[k] = wave + k * W < nbp;
-    lb[k] = own[k] ? wave + k * W : nbp - 1;
-  }
+  // phase q takes the blocks [q*nbp/P, (q+1)*nbp/P) of the half; slot k of a
+  // wave is its block lo + wave + k*W (a wave past the phase's last block
+  // loads a valid block and skips the arithmetic)
+  auto phase_lo = [&](int q) { return q * nbp / P; };
+  auto owned = [&](int q, int k, int &blk) {
+    const int lo = phase_lo(q);
+    const int nbq = phase_lo(q + 1) - lo;
+    const bool o = wave + k * W < nbq;
+    blk = lo + (o ? wave + k * W : nbq - 1);
+    return o;
+  };
 
-  // ---- prefetch ring of codes and metadata.  Issues past the last tile are
-  // still made (a branch around loads would make the compiler wait for every
-  // load in flight), but then read the first line of the workgroup's first
-  // tile: one cached line per instruction.
+  // ---- prefetch ring of codes and metadata, one (phase, tile) step per
+  // slot.  Issues past the last step are still made (a branch around loads
+  // would make the compiler wait for every load in flight), but then read
+  // the first line of the workgroup's first tile: one cached line per
+  // instruction.
   u32x4_t cv[S][BPW][BSC];
   uint2 s4[S][BPW], b4[S][BPW];
   const uint64_t crow_dead = (uint64_t)(16 * t_first) * RB;
   const uint64_t mrow_dead = (uint64_t)(16 * t_first) * NG;
-  int it = 0;  // tile step of the next issue
+  int it = 0;  // step of the next issue
   auto issue = [&](const int slot) {
-    const uint64_t m64 = 0ull - (uint64_t)(it < ntile);  // all-ones while live
-    const int n = min(16 * (t_first + it) + col, N - 1);
+    const bool live = it < steps;
+    const int q = live ? it / ntile : 0;
+    const int tt = live ? it - q * ntile : 0;
+    const uint64_t m64 = 0ull - (uint64_t)live;  // all-ones while live
+    const int n = min(16 * (t_first + tt) + col, N - 1);
     const uint64_t crow = (((uint64_t)n * RB + kb * 16) & m64) | (crow_dead & ~m64);
     const uint64_t mrow = (((uint64_t)n * NG) & m64) | (mrow_dead & ~m64);
 #pragma unroll
     for (int k = 0; k < BPW; ++k) {
+      int blk;
+      owned(q, k, blk);
 #pragma unroll
       for (int u = 0; u < BSC; ++u)
-        cv[slot][k][u] = load_stream_u32x4(codes + crow + (size_t)((p_lo + lb[k]) * BSC + u) * 64);
-    }
-#pragma unroll
-    for (int k = 0; k < BPW; ++k) {
-      s4[slot][k] = *reinterpret_cast<const uint2 *>(scales + mrow + (p_lo + lb[k]) * 4);
-      b4[slot][k] = *reinterpret_cast<const uint2 *>(biases + mrow + (p_lo + lb[k]) * 4);
+        cv[slot][k][u] = load_stream_u32x4(codes + crow + (size_t)((p_lo + blk) * BSC + u) * 64);
+      s4[slot][k] = *reinterpret_cast<const uint2 *>(scales + mrow + (p_lo + blk) * 4);
+      b4[slot][k] = *reinterpret_cast<const uint2 *>(biases + mrow + (p_lo + blk) * 4);
     }
     ++it;
   };
-#pragma unroll
-  for (int s = 0; s < S - 1; ++s) issue(s);
 
-  // ---- stage x of the half into LDS, re-paired, XU units per thread at a
-  // time (all loads of a round issued before any is used; clamped indices
-  // read a valid unit and are not stored)
-  {
-    const int upr = nbp * BLKW / UE;  // units per row
+  // ---- stage x of phase q into LDS, re-paired, with the activation sum of
+  // every group, XU units per thread at a time (all loads of a round issued
+  // before any is used; clamped indices read a valid unit and are not
+  // stored).  Units are dealt to consecutive lanes, so the GU lanes holding
+  // a group's units add their sums in a fixed butterfly.
+  auto stage = [&](const int q) {
+    const int lo = phase_lo(q);
+    const int upr = (phase_lo(q + 1) - lo) * BLKW / UE;  // units per row
     const int units = M * upr;
-    const uint16_t *xh = x + (size_t)p_lo * BLKW;
-    const int rot = 0;  // unit order (a whole number of groups)
-    auto unit_of = [&](int uu) { return uu + rot < units ? uu + rot : uu + rot - units; };
+    const uint16_t *xh = x + (size_t)(p_lo + lo) * BLKW;
     for (int u0 = 0; u0 < units; u0 += XU * (int)blockDim.x) {
       u32x4_t v[XU][UE / 8];
 #pragma unroll
       for (int j = 0; j < XU; ++j) {
-        const int u = unit_of(min(u0 + j * (int)blockDim.x + (int)threadIdx.x, units - 1));
+        const int u = min(u0 + j * (int)blockDim.x + (int)threadIdx.x, units - 1);
         const int m = u / upr;
         const int c = u - m * upr;
 #pragma unroll
@@ -179,10 +196,7 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
       }
 #pragma unroll
       for (int j = 0; j < XU; ++j) {
-        const int uu = u0 + j * (int)blockDim.x + (int)threadIdx.x;
-        // activation sum of the unit, then of its group: units are dealt to
-        // consecutive lanes, so the GU lanes of a group add their sums in a
-        // fixed butterfly (every lane of the wave takes part)
+        const int u = u0 + j * (int)blockDim.x + (int)threadIdx.x;
         float p = 0.f;
 #pragma unroll
         for (int h = 0; h < UE / 8; ++h)
@@ -190,8 +204,7 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
           for (int e = 0; e < 4; ++e) p = dot2_bf16(v[j][h][e], 0x3F803F80u, p);
 #pragma unroll
         for (int off = 1; off < GU; off <<= 1) p += __shfl_xor(p, off);
-        if (uu < units) {
-          const int u = unit_of(uu);
+        if (u < units) {
           const int m = u / upr;
           const int c = u - m * upr;
           if ((threadIdx.x & (GU - 1)) == 0) xs[m * gpr + c / GU] = p;
@@ -212,33 +225,46 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
       }
     }
     __syncthreads();
-  }
+  };
 
   // this lane's activation row in LDS (rows m >= M read row M-1)
   const uint8_t *xrow = xl + (size_t)(col < M ? col : M - 1) * pitch;
   const float *xsrow = xs + (col < M ? col : M - 1) * gpr;
 
-  // ---- groups of S tile steps (the unrolled ring); a range always has a
-  // tile (do-while: no guard branch that would let the compiler sink the
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) issue(s);
+
+  // ---- the steps, S at a time (the unrolled ring); a workgroup always has a
+  // step (do-while: no guard branch that would let the compiler sink the
   // prologue loads)
   int j0 = 0;
   do {
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      if (j0 + s >= ntile) break;
+      const int step = j0 + s;
+      if (step >= steps) break;
+      const int q = step / ntile;
+      const int tt = step - q * ntile;
+      if (tt == 0) {
+        if (q != 0) __syncthreads();  // every wave is done with the previous phase
+        stage(q);
+      }
       issue((s + S - 1) % S);
       __builtin_amdgcn_sched_barrier(0);
 
+      const int lo = phase_lo(q);
       f32x4_t acc = zero4;
 #pragma unroll
       for (int k = 0; k < BPW; ++k) {
-        if (!own[k]) continue;  // uniform per wave
+        int blk;
+        if (!owned(q, k, blk)) continue;  // uniform per wave
+        const int lq = blk - lo;          // block within the phase
         f32x4_t accg;
 #pragma unroll
         for (int u = 0; u < BSC; ++u) {
           uint32_t cur[4] = {cv[s][k][u][0], cv[s][k][u][1], cv[s][k][u][2], cv[s][k][u][3]};
           transpose_rows_lvl<LVL>(cur);
-          const int k0 = (lb[k] * BSC + u) * SCW;  // first element of the super-chunk in the half
+          const int k0 = (lq * BSC + u) * SCW;  // first element of the super-chunk in the phase
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int jg = u * GPS + i / REGS_G;  // group within the block
@@ -260,7 +286,7 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
                 const uint32_t sw = (jg < 2) ? s4[s][k].x : s4[s][k].y;
                 const float scl = half_bits_to_float((jg & 1) ? (sw >> 16) : (sw & 0xFFFFu));
 #pragma unroll
-                for (int q = 0; q < 4; ++q) acc[q] = fmaf(scl, accg[q], acc[q]);
+                for (int qq = 0; qq < 4; ++qq) acc[qq] = fmaf(scl, accg[qq], acc[qq]);
               }
             }
           }
@@ -270,57 +296,61 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
         const uint32_t bw = (kb < 2) ? b4[s][k].x : b4[s][k].y;
         const float scl = half_bits_to_float((kb & 1) ? (sw >> 16) : (sw & 0xFFFFu));
         const float b = half_bits_to_float((kb & 1) ? (bw >> 16) : (bw & 0xFFFFu));
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xsrow[lb[k] * 4 + kb], fmaf(-128.f, scl, b), acc,
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xsrow[lq * 4 + kb], fmaf(-128.f, scl, b), acc,
                                                    0, 0, 0);
       }
+      // this wave's partial of tile tt: its own LDS slot, added to over the
+      // phases in phase order
+      float *pa = pacc + (size_t)((tt * W + wave) * 4) * 64 + lane;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[((s * W + wave) * 4 + i) * 64 + lane] = acc[i];
+      for (int i = 0; i < 4; ++i) pa[i * 64] = q == 0 ? acc[i] : pa[i * 64] + acc[i];
     }
+    j0 += S;
+  } while (j0 < steps);
 
-    // ---- sum the partial tiles over the waves in block order and add this
-    // half into y
-    __syncthreads();
-    const int nj = min(S, ntile - j0);
-    for (int o = threadIdx.x; o < nj * 256; o += blockDim.x) {
-      const int s = o >> 8, i = (o >> 6) & 3, l = o & 63;
-      float v = 0.f;
-      for (int w = 0; w < W; ++w) v += red[((s * W + w) * 4 + i) * 64 + l];
-      const int m = 4 * (l >> 4) + i;
-      const int n = 16 * (t_first + j0 + s) + (l & 15);
-      if (m < M && n < N) {
-        float *dst = y + (size_t)m * N + n;
-        if constexpr (!ADD) {
-          unsafeAtomicAdd(dst, v);
-        } else {
-          const float old = atomicExch(dst, v);
-          if (__builtin_bit_cast(uint32_t, old) != kSplitSentinel) *dst = (old + v) + res[(size_t)m * N + n];
-        }
+  // ---- sum each tile's partials over the waves in block order and add this
+  // half into y
+  __syncthreads();
+  for (int o = threadIdx.x; o < ntile * 256; o += blockDim.x) {
+    const int t = o >> 8, i = (o >> 6) & 3, l = o & 63;
+    float v = 0.f;
+    for (int w = 0; w < W; ++w) v += pacc[((t * W + w) * 4 + i) * 64 + l];
+    const int m = 4 * (l >> 4) + i;
+    const int n = 16 * (t_first + t) + (l & 15);
+    if (m < M && n < N) {
+      float *dst = y + (size_t)m * N + n;
+      if constexpr (!ADD) {
+        unsafeAtomicAdd(dst, v);
+      } else {
+        const float old = atomicExch(dst, v);
+        if (__builtin_bit_cast(uint32_t, old) != kSplitSentinel) *dst = (old + v) + res[(size_t)m * N + n];
       }
     }
-    __syncthreads();  // red is rewritten by the next group
-    j0 += S;
-  } while (j0 < ntile);
+  }
 }
 
 // Blocks owned per wave: 4 super-chunks per ring slot, or 8 where a block is
 // 4 super-chunks (4-bit gs128: still within the register budget; with
 // smaller blocks 8 super-chunks bring twice the metadata registers and
-// spill).  Halves of K that need more waves take the single-pass kernel.
+// spill), or 2 where a block is one super-chunk.  The launcher takes the
+// fewest blocks per wave (the most waves) that stay within kXMaxWaves.
 template <int BITS, int GS>
 struct PersistXShape {
   static constexpr int BSC = 4 * GS / (512 / BITS);
+  static constexpr int BPW_SMALL = BSC >= 2 ? 1 : 2;
   static constexpr int BPW_NARROW = BSC >= 4 ? 1 : 4 / BSC;
   static constexpr int BPW_WIDE = BSC == 4 ? 2 : BPW_NARROW;
 };
 
 template <int BITS, int GS, int BPW, bool ADD>
-int launch_persist_x_k(const QgemvArgs &a, int waves, int grid, size_t lds, hipStream_t stream) {
+int launch_persist_x_k(const QgemvArgs &a, int waves, int grid, size_t lds, int phases, int ntile_max,
+                       hipStream_t stream) {
   const auto kern = qgemv_persist_x_kernel<BITS, GS, BPW, ADD>;
   if (!allow_max_dynamic_lds(reinterpret_cast<const void *>(kern))) return QGEMV_EHIP;
   const int st = launch_fill(a.y, (size_t)a.M * a.N, ADD ? kSplitSentinel : 0u, stream);
   if (st != QGEMV_OK) return st;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * waves), lds, stream, a.codes, a.scales, a.biases, a.x,
-                     a.y, a.res, a.M, a.N, a.K);
+                     a.y, a.res, a.M, a.N, a.K, phases, ntile_max);
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
 }
 
@@ -329,23 +359,39 @@ int launch_persist_x_t(const QgemvArgs &a, hipStream_t stream) {
   using Sh = PersistXShape<BITS, GS>;
   const int nblk = a.K / (4 * GS);
   if (nblk < 2) return QGEMV_EUNSUPPORTED;
-  const int nbp_max = nblk - nblk / 2;
+  const int nbp_min = nblk / 2, nbp_max = nblk - nblk / 2;
   const int tiles = (a.N + 15) / 16;
   const int cus = device_cu_count();
   if (tiles < cus) return QGEMV_EUNSUPPORTED;
-  const bool narrow = (nbp_max + Sh::BPW_NARROW - 1) / Sh::BPW_NARROW <= kXMaxWaves;
-  const int bpw = narrow ? Sh::BPW_NARROW : Sh::BPW_WIDE;
-  const int waves = (nbp_max + bpw - 1) / bpw;
-  if (waves > kXMaxWaves) return QGEMV_EUNSUPPORTED;
-  const size_t pitch = (size_t)nbp_max * 4 * GS * 2 + 16;
-  const size_t lds = (size_t)a.M * pitch + (size_t)a.M * nbp_max * 4 * sizeof(float) +
-                     (size_t)kXRing * waves * 256 * sizeof(float);
-  if (lds > kLdsMax) return QGEMV_EUNSUPPORTED;
   // one workgroup per CU, half of them per half of K (every workgroup has
   // at least one tile: tiles >= CUs)
   const int grid = 2 * (cus / 2);
-  if (narrow) return launch_persist_x_k<BITS, GS, Sh::BPW_NARROW, ADD>(a, waves, grid, lds, stream);
-  return launch_persist_x_k<BITS, GS, Sh::BPW_WIDE, ADD>(a, waves, grid, lds, stream);
+  const int ntile_max = (tiles + grid / 2 - 1) / (grid / 2);
+  // fewest phases, then fewest blocks per wave, whose activations, group
+  // sums and partial tiles fit the LDS
+  const int bpws[3] = {Sh::BPW_SMALL, Sh::BPW_NARROW, Sh::BPW_WIDE};
+  for (int phases = 1; phases <= kXMaxPhases && phases <= nbp_min; ++phases) {
+    const int nbq_max = (nbp_max + phases - 1) / phases;
+    for (int variant = 0; variant < 3; ++variant) {
+      // two passes with the 8-super-chunk slots (5 waves on the 4-bit gs128
+      // down projection) were slower than the single-pass kernel: 40.5
+      // against 34.8 us at M = 15
+      if (phases > 1 && variant == 2 && Sh::BPW_WIDE != Sh::BPW_NARROW) continue;
+      const int bpw = bpws[variant];
+      const int waves = (nbq_max + bpw - 1) / bpw;
+      if (waves > kXMaxWaves) continue;
+      const size_t pitch = (size_t)nbq_max * 4 * GS * 2 + 16;
+      const size_t lds = (size_t)a.M * pitch + (size_t)a.M * nbq_max * 4 * sizeof(float) +
+                         (size_t)ntile_max * waves * 256 * sizeof(float);
+      if (lds > kLdsMax) continue;
+      if (variant == 0)
+        return launch_persist_x_k<BITS, GS, Sh::BPW_SMALL, ADD>(a, waves, grid, lds, phases, ntile_max, stream);
+      if (variant == 1)
+        return launch_persist_x_k<BITS, GS, Sh::BPW_NARROW, ADD>(a, waves, grid, lds, phases, ntile_max, stream);
+      return launch_persist_x_k<BITS, GS, Sh::BPW_WIDE, ADD>(a, waves, grid, lds, phases, ntile_max, stream);
+    }
+  }
+  return QGEMV_EUNSUPPORTED;
 }
 
 template <int BITS, int GS>

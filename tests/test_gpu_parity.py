@@ -147,9 +147,9 @@ PERSIST = [
     (6656, 4200, 4, 128), (8192, 4130, 2, 64), (10240, 4500, 2, 128),
 ]
 
-# Long K with the activations of half of K in LDS, at the sizes where the LDS
-# holds them only for M <= 10 or M <= 8 (larger M takes the single-pass
-# kernel): sampled columns.
+# Long K with the activations of half of K in LDS, at sizes where the LDS
+# holds a whole half only up to M = 7 to 10: larger M restages the
+# activations in two or three phases per half.  Sampled columns.
 LONG_K_LDS = [(12288, 4104, 4, 64), (12288, 4100, 4, 32), (17408, 4128, 2, 64), (17408, 4200, 4, 128)]
 
 
