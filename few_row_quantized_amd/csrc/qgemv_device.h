@@ -271,6 +271,25 @@ __device__ __forceinline__ int lvl_dword(int i, int g) {
   return LVL == 0 ? i : (LVL == 1 ? (i & 1) + 2 * (g >> 1) : g);
 }
 
+// MFMA operand lanes and code loads.  The 16x16 MFMA layouts put output
+// column n = lane % 16 in lane n, n+16, n+32, n+48, so a load in that layout
+// (lane (n, c) reading 16-byte piece c of row n's 64-byte super-chunk) has
+// every group of 4 consecutive lanes read 4 different rows; the address
+// unit then spends about four times longer per instruction than on a
+// contiguous read (rocprofv3 TA_BUSY: ~40 against ~16 cycles per load).
+// The MFMA kernels therefore load with lane L reading piece L%4 of row L/4
+// (each lane quad reads 64 contiguous bytes) and move every dword to its
+// operand lane with ds_bpermute: lane (n, c) takes lane 4n + c's data.
+// Measured on MI355X: the square 4-bit MFMA path 6.82 -> 6.51 us at M = 8,
+// the 4-bit FFN-up gs64 persistent kernel 11.98 -> 11.26 us.
+__device__ __forceinline__ int quad_row_lane(int lane) { return 4 * (lane & 15) + (lane >> 4); }
+
+__device__ __forceinline__ void to_operand_lanes(const u32x4_t &loaded, uint32_t (&cur)[4]) {
+  const int src = quad_row_lane((int)(threadIdx.x & 63)) * 4;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) cur[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)loaded[d]);
+}
+
 // P[j] is a per-lane partial for value j (j = 0..3) that must be summed over
 // the four 16-lane rows.  Returns, in row j, the total of value j (lane
 // positions within a row are kept).  Two swap stages, three adds.

@@ -15,12 +15,15 @@
 //   dwords per MFMA step).  A workgroup owns NT tiles of
 //   16 output columns over the whole of K; its waves split K into
 //   contiguous slices of "bias blocks" (4 groups).
-// * Lane (col = lane%16, kb = lane/16) loads 16 contiguous bytes of row
-//   n = col at byte 16*kb of each 64-byte super-chunk, so 16 rows x 64 B are
-//   read per load instruction.  A partial exchange of dwords across the four
-//   16-lane rows (none, v_permlane32_swap, or the full 4x4 transpose with
-//   v_permlane16_swap, as the group size requires) gives every MFMA step 32
-//   codes of one quantization group.
+// * Lane (col = lane%16, kb = lane/16) needs 16 contiguous bytes of row
+//   n = col at byte 16*kb of each 64-byte super-chunk (16 rows x 64 B per
+//   load instruction).  The load itself is made with lane L reading piece
+//   L%4 of row L/4, so that each lane quad reads 64 contiguous bytes, and
+//   ds_bpermute moves the dwords to their operand lanes (to_operand_lanes).
+//   A partial exchange of dwords across the four 16-lane rows (none,
+//   v_permlane32_swap, or the full 4x4 transpose with v_permlane16_swap, as
+//   the group size requires) then gives every MFMA step 32 codes of one
+//   quantization group.
 // * The group's partial product is accumulated by gs/32 MFMAs and folded with
 //   the group scale once: acc += s * acc_g (4 FMAs per lane per group).
 // * Bias and the 128 code offset: sum_g (b - 128 s)[n,g] * xsum[m,g] over the

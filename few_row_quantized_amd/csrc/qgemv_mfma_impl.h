@@ -170,7 +170,8 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int n = min(n_base + 16 * t + col, N - 1);
-    crow[t] = codes + (size_t)n * RB + kb * 16;
+    // codes: lane L reads 16-byte piece L%4 of row L/4 (see quad_row_lane)
+    crow[t] = codes + (size_t)min(n_base + 16 * t + (lane >> 2), N - 1) * RB + (lane & 3) * 16;
     srow[t] = scales + (size_t)n * G;
     brow[t] = biases + (size_t)n * G;
     srow8[t] = reinterpret_cast<const uint8_t *>(scales) + (size_t)n * G;
@@ -299,10 +300,7 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
       uint32_t cur[NT][4];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        cur[t][0] = cv[u][t][0];
-        cur[t][1] = cv[u][t][1];
-        cur[t][2] = cv[u][t][2];
-        cur[t][3] = cv[u][t][3];
+        to_operand_lanes(cv[u][t], cur[t]);
         transpose_rows_lvl<LVL>(cur[t]);
       }
       if constexpr (BITS == 8) {

@@ -127,7 +127,9 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   auto issue = [&](const int slot) {
     const uint64_t m64 = 0ull - (uint64_t)(it < ntile);  // all-ones while live
     const int n = min(16 * (t_first + it) + col, N - 1);
-    const uint64_t crow = (((uint64_t)n * RB + kb * 16) & m64) | (crow_dead & ~m64);
+    // codes: lane L reads 16-byte piece L%4 of row L/4 (see quad_row_lane)
+    const int nq = min(16 * (t_first + it) + (lane >> 2), N - 1);
+    const uint64_t crow = (((uint64_t)nq * RB + (lane & 3) * 16) & m64) | (crow_dead & ~m64);
     const uint64_t mrow = (((uint64_t)n * NG) & m64) | (mrow_dead & ~m64);
 #pragma unroll
     for (int k = 0; k < BPW; ++k) {
@@ -211,7 +213,8 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
         f32x4_t accg;
 #pragma unroll
         for (int u = 0; u < BSC; ++u) {
-          uint32_t cur[4] = {cv[s][k][u][0], cv[s][k][u][1], cv[s][k][u][2], cv[s][k][u][3]};
+          uint32_t cur[4];
+          to_operand_lanes(cv[s][k][u], cur);
           transpose_rows_lvl<LVL>(cur);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {

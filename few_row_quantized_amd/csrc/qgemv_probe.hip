@@ -83,8 +83,11 @@ __global__ __launch_bounds__(64) void unpack_probe_mfma(const uint8_t *__restric
   const int sc = blockIdx.x % nsc;
   const int n = min(tile * 16 + col, N - 1);
   const size_t RB = (size_t)K * BITS / 8;
-  const uint4 v = *reinterpret_cast<const uint4 *>(codes + (size_t)n * RB + (size_t)sc * 64 + kb * 16);
-  uint32_t r[4] = {v.x, v.y, v.z, v.w};
+  // the kernels' load (lane L: piece L%4 of row L/4) and move to operand lanes
+  const int nq = min(tile * 16 + (lane >> 2), N - 1);
+  const u32x4_t v = *reinterpret_cast<const u32x4_t *>(codes + (size_t)nq * RB + (size_t)sc * 64 + (lane & 3) * 16);
+  uint32_t r[4];
+  to_operand_lanes(v, r);
   transpose_rows_lvl<LVL>(r);  // all lanes take part, also those past row N
   if (tile * 16 + col >= N) return;
   uint8_t *qr = q + (size_t)n * K + (size_t)sc * SCW;
@@ -182,8 +185,11 @@ __global__ __launch_bounds__(64) void unpack_probe_fp_mfma(const uint8_t *__rest
   const int sc = blockIdx.x % nsc;
   const int n = min(tile * 16 + col, N - 1);
   const size_t RB = (size_t)K * BITS / 8;
-  const uint4 v = *reinterpret_cast<const uint4 *>(codes + (size_t)n * RB + (size_t)sc * 64 + kb * 16);
-  uint32_t r[4] = {v.x, v.y, v.z, v.w};
+  // the kernels' load (lane L: piece L%4 of row L/4) and move to operand lanes
+  const int nq = min(tile * 16 + (lane >> 2), N - 1);
+  const u32x4_t v = *reinterpret_cast<const u32x4_t *>(codes + (size_t)nq * RB + (size_t)sc * 64 + (lane & 3) * 16);
+  uint32_t r[4];
+  to_operand_lanes(v, r);
   transpose_rows_lvl<LVL>(r);  // all lanes take part, also those past row N
   if (tile * 16 + col >= N) return;
   uint16_t *o = out + (size_t)n * K + (size_t)sc * SCW;
