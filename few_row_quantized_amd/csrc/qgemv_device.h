@@ -280,14 +280,30 @@ __device__ __forceinline__ int lvl_dword(int i, int g) {
 // The MFMA kernels therefore load with lane L reading piece L%4 of row L/4
 // (each lane quad reads 64 contiguous bytes) and move every dword to its
 // operand lane with ds_bpermute: lane (n, c) takes lane 4n + c's data.
-// Measured on MI355X: the square 4-bit MFMA path 6.82 -> 6.51 us at M = 8,
-// the 4-bit FFN-up gs64 persistent kernel 11.98 -> 11.26 us.
+// The same holds for the per-row metadata and, in the single-pass kernel,
+// for the activation operand (row m = lane % 16) once several rows are
+// distinct.  Measured on MI355X: codes alone took the square 4-bit MFMA path
+// from 6.82 to 6.51 us at M = 8 and the 4-bit FFN-up gs64 persistent kernel
+// from 11.98 to 11.26 us; metadata and activations then took the square path
+// to 5.57 us at M = 8 and from 7.77 to 5.86 us at M = 16.
 __device__ __forceinline__ int quad_row_lane(int lane) { return 4 * (lane & 15) + (lane >> 4); }
 
 __device__ __forceinline__ void to_operand_lanes(const u32x4_t &loaded, uint32_t (&cur)[4]) {
   const int src = quad_row_lane((int)(threadIdx.x & 63)) * 4;
 #pragma unroll
   for (int d = 0; d < 4; ++d) cur[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)loaded[d]);
+}
+
+__device__ __forceinline__ u32x4_t to_operand_lanes(const u32x4_t &v) {
+  uint32_t c[4];
+  to_operand_lanes(v, c);
+  return u32x4_t{c[0], c[1], c[2], c[3]};
+}
+
+__device__ __forceinline__ uint2 to_operand_lanes(const uint2 &v) {
+  const int src = quad_row_lane((int)(threadIdx.x & 63)) * 4;
+  return make_uint2((uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v.x),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v.y));
 }
 
 // P[j] is a per-lane partial for value j (j = 0..3) that must be summed over

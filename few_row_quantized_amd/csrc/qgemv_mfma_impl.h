@@ -76,9 +76,16 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   const uint32_t offset_pair = opaque_u32(kOffsetPair);
   // element offset, within a super-chunk, of the codes register i holds in
   // this lane's row after the partial transpose
+  // Activation loads in the quad-row layout (lane L: what lane (L/4, L%4)
+  // needs) once several rows are distinct; with few rows most lanes read the
+  // same row anyway and the move to the operand lanes would only cost (the
+  // data each lane ends up with is the same either way, so results do not
+  // depend on the choice).  Thresholds measured on the square shapes.
+  const bool xquad = FMT != kAffine || M >= (BITS == 8 ? 3 : (LVL == 0 ? 8 : 5));
+  const int xkb = xquad ? (lane & 3) : kb;
   int xoff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) xoff[i] = lvl_chunk<LVL>(i, kb) * CW + lvl_dword<LVL>(i, kb) * DW;
+  for (int i = 0; i < 4; ++i) xoff[i] = lvl_chunk<LVL>(i, xkb) * CW + lvl_dword<LVL>(i, xkb) * DW;
 
   // Gathered verify: pick this workgroup's expert and its pairs.
   __shared__ uint32_t gbits[GATHER ? kMaxExperts / 32 : 1];
@@ -162,19 +169,20 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   // Rows m >= M and columns n >= N only feed outputs that are never stored,
   // so their lanes read valid clamped addresses instead of branching around
   // the loads (a branch would force a wait on every load).
-  const uint16_t *xr = x + xrow(col < M ? col : M - 1) * K;
+  const uint16_t *xr = x + xrow(min(xquad ? (lane >> 2) : col, M - 1)) * K;
   const uint8_t *crow[NT];
   const uint16_t *srow[NT];
   const uint16_t *brow[NT];
   const uint8_t *srow8[NT];  // FP formats: scale bytes
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const int n = min(n_base + 16 * t + col, N - 1);
-    // codes: lane L reads 16-byte piece L%4 of row L/4 (see quad_row_lane)
-    crow[t] = codes + (size_t)min(n_base + 16 * t + (lane >> 2), N - 1) * RB + (lane & 3) * 16;
-    srow[t] = scales + (size_t)n * G;
-    brow[t] = biases + (size_t)n * G;
-    srow8[t] = reinterpret_cast<const uint8_t *>(scales) + (size_t)n * G;
+    // codes and metadata: lane L reads for row L/4 (codes: 16-byte piece L%4;
+    // see quad_row_lane); moved to the operand lanes before use
+    const int nq = min(n_base + 16 * t + (lane >> 2), N - 1);
+    crow[t] = codes + (size_t)nq * RB + (lane & 3) * 16;
+    srow[t] = scales + (size_t)nq * G;
+    brow[t] = biases + (size_t)nq * G;
+    srow8[t] = reinterpret_cast<const uint8_t *>(scales) + (size_t)nq * G;
   }
 
   // residual of the outputs this thread stores in its first NT reduction
@@ -248,6 +256,14 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     // code pairing and form the per-group activation sums.  xsum of group
     // g0 + j ends up in row j of this lane's column, i.e. in the A layout of
     // v_mfma_f32_16x16x4_f32 for the bias product.
+    if (xquad) {
+#pragma unroll
+      for (int u = 0; u < UNR; ++u)
+#pragma unroll
+        for (int i = 0; i < XR; ++i)
+#pragma unroll
+          for (int l = 0; l < HS; ++l) xv[u][i][l] = to_operand_lanes(xv[u][i][l]);
+    }
     float xsum[BPB];
 #pragma unroll
     for (int bb = 0; bb < BPB; ++bb) {
@@ -291,6 +307,13 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
       if constexpr (HAS_BIAS) xsum[bb] = rows_transpose_reduce4(P);
     }
 
+#pragma unroll
+    for (int bb = 0; bb < BPB; ++bb)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        s4[bb][t] = to_operand_lanes(s4[bb][t]);
+        if constexpr (HAS_BIAS) b4[bb][t] = to_operand_lanes(b4[bb][t]);
+      }
     // ---- codes, super-chunk by super-chunk in load order
     f32x4_t accg[NT];
 #pragma unroll

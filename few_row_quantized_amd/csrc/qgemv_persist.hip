@@ -55,6 +55,11 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   constexpr int GPS = 4 / CPG;           // groups per super-chunk
   constexpr int LVL = CPG >= 4 ? 0 : (CPG == 2 ? 1 : 2);
   constexpr int REGS_G = CPG;
+  // metadata loads in the quad-row layout: measured faster for 4-bit codes
+  // with groups of 32 or 64 (FFN-up 4096x12288: 14.2 -> 13.2 us and
+  // 11.3 -> 10.6 us at M = 8), slower by 1-5% with groups of 128 and for
+  // 2-bit codes, where metadata loads are few
+  constexpr bool MQ = BITS == 4 && GS <= 64;
   static_assert(BSC >= 1 && BLKW % SCW == 0 && CPG >= 1, "block layout");
 
   __shared__ float red[S][MAXW][4][64];
@@ -126,11 +131,12 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   int it = 0;  // tile step of the next issue
   auto issue = [&](const int slot) {
     const uint64_t m64 = 0ull - (uint64_t)(it < ntile);  // all-ones while live
-    const int n = min(16 * (t_first + it) + col, N - 1);
-    // codes: lane L reads 16-byte piece L%4 of row L/4 (see quad_row_lane)
+    // codes: lane L reads 16-byte piece L%4 of row L/4 (see quad_row_lane);
+    // metadata the same way where groups are small (MQ), else per column
     const int nq = min(16 * (t_first + it) + (lane >> 2), N - 1);
     const uint64_t crow = (((uint64_t)nq * RB + (lane & 3) * 16) & m64) | (crow_dead & ~m64);
-    const uint64_t mrow = (((uint64_t)n * NG) & m64) | (mrow_dead & ~m64);
+    const int nm = MQ ? nq : min(16 * (t_first + it) + col, N - 1);
+    const uint64_t mrow = (((uint64_t)nm * NG) & m64) | (mrow_dead & ~m64);
 #pragma unroll
     for (int k = 0; k < BPW; ++k) {
 #pragma unroll
@@ -207,6 +213,13 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
       __builtin_amdgcn_sched_barrier(0);
 
       f32x4_t acc = zero4;
+      if constexpr (MQ) {
+#pragma unroll
+        for (int k = 0; k < BPW; ++k) {
+          s4[s][k] = to_operand_lanes(s4[s][k]);
+          b4[s][k] = to_operand_lanes(b4[s][k]);
+        }
+      }
 #pragma unroll
       for (int k = 0; k < BPW; ++k) {
         if (!own[k]) continue;  // uniform per wave
