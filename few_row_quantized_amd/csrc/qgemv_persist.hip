@@ -81,9 +81,13 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   const int NG = K / GS;
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   const uint32_t offset_pair = opaque_u32(kOffsetPair);
+  // activation loads in the quad-row layout once several rows are distinct
+  // (as in the single-pass kernel; results do not depend on the choice)
+  const bool xquad = M >= (LVL == 0 ? 8 : 5);
+  const int xkb = xquad ? (lane & 3) : kb;
   int xoff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) xoff[i] = lvl_chunk<LVL>(i, kb) * CW + lvl_dword<LVL>(i, kb) * DW;
+  for (int i = 0; i < 4; ++i) xoff[i] = lvl_chunk<LVL>(i, xkb) * CW + lvl_dword<LVL>(i, xkb) * DW;
 
   // tile range of this workgroup (the products stay below 2^31: the grid is
   // at most the CU count and T <= 2^18)
@@ -104,7 +108,7 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   // ---- activations of the owned blocks (rows m >= M read row M-1: their
   // outputs are never stored), later re-paired to the code pairing and
   // summed per group into the A layout of the bias MFMA
-  const uint16_t *xr = x + (size_t)(col < M ? col : M - 1) * K;
+  const uint16_t *xr = x + (size_t)min(xquad ? (lane >> 2) : col, M - 1) * K;
   u32x4_t xv[BPW][BSC][4][HS];
   float xsum[BPW];
 #pragma unroll
@@ -155,6 +159,17 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   for (int s = 0; s < S - 1; ++s) issue(s);
   // keep the code loads ahead of the activation work that waits for x
   __builtin_amdgcn_sched_barrier(0);
+
+  if (xquad) {
+#pragma unroll
+    for (int k = 0; k < BPW; ++k)
+#pragma unroll
+      for (int u = 0; u < BSC; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int l = 0; l < HS; ++l) xv[k][u][i][l] = to_operand_lanes(xv[k][u][i][l]);
+  }
 
 #pragma unroll
   for (int k = 0; k < BPW; ++k) {
