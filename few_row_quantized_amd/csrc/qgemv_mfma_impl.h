@@ -76,16 +76,6 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   const uint32_t offset_pair = opaque_u32(kOffsetPair);
   // element offset, within a super-chunk, of the codes register i holds in
   // this lane's row after the partial transpose
-  // Activation loads in the quad-row layout (lane L: what lane (L/4, L%4)
-  // needs) once several rows are distinct; with few rows most lanes read the
-  // same row anyway and the move to the operand lanes would only cost (the
-  // data each lane ends up with is the same either way, so results do not
-  // depend on the choice).  Thresholds measured on the square shapes.
-  const bool xquad = FMT != kAffine || M >= (BITS == 8 ? 3 : (LVL == 0 ? 8 : 5));
-  const int xkb = xquad ? (lane & 3) : kb;
-  int xoff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) xoff[i] = lvl_chunk<LVL>(i, xkb) * CW + lvl_dword<LVL>(i, xkb) * DW;
 
   // Gathered verify: pick this workgroup's expert and its pairs.
   __shared__ uint32_t gbits[GATHER ? kMaxExperts / 32 : 1];
@@ -150,6 +140,17 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
 
   // One tile group (16*NT output columns over all of K) per call of `group`.
   auto group = [&](const int tg) {
+  // Activation loads in the quad-row layout (lane L: what lane (L/4, L%4)
+  // needs) once several rows are distinct; with few rows most lanes read the
+  // same row anyway and the move to the operand lanes would only cost (the
+  // data each lane ends up with is the same either way, so results do not
+  // depend on the choice).  Thresholds measured on the square shapes; M is
+  // the rows of this group (a gathered expert's chunk of pairs).
+  const bool xquad = FMT != kAffine || M >= (BITS == 8 ? 3 : (LVL == 0 ? 8 : 5));
+  const int xkb = xquad ? (lane & 3) : kb;
+  int xoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xoff[i] = lvl_chunk<LVL>(i, xkb) * CW + lvl_dword<LVL>(i, xkb) * DW;
   // group tg = (tile group, part of K); with KS = 2 the two halves of K of a
   // tile group are separate groups whose results are added into y
   const int kpart = KS == 1 ? 0 : (tg & 1);
