@@ -23,11 +23,12 @@
 // * A persistent grid of one workgroup per CU.  Workgroup b takes half
 //   b & 1 of the bias blocks (4 groups) of K and the contiguous range
 //   [g*T/GP, (g+1)*T/GP) of the T 16-column tiles, g = b >> 1, GP = grid/2.
-// * Prologue: the first tile's codes and metadata are requested, then the
-//   workgroup copies its half of x (M rows) into LDS, already re-paired to
+// * Prologue (and each phase change): the next step's codes and metadata
+//   are requested, then the workgroup copies its share of x (M rows of the
+//   phase's blocks) into LDS, already re-paired to
 //   the code pairing of the MFMA operand (elements (e, e+4) of each 8 for
 //   4-bit codes, (e, e+8) of each 16 for 2-bit codes), and forms the
-//   activation sum of every group of that half from the registers: the
+//   activation sum of every group of that share from the registers: the
 //   lanes holding a group's units reduce their sums by a fixed butterfly
 //   (summing a group from LDS instead, one lane per group, put every lane of
 //   a wave on the same bank: row offsets of GS*2 bytes).
