@@ -15,7 +15,7 @@ rounds) give time(M)/time(1) for the dispatcher's choice and for each path,
 and the average launch duration of each kernel.
 
 Prints ONE JSON line (rank 0).  --gpus N with N > 1 exits with a message:
-this build runs on one GPU.
+the library runs on one GPU.
 """
 from __future__ import annotations
 
@@ -87,7 +87,7 @@ class Pool:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1",
                           "n_gpus_requested": args.gpus}))
         sys.exit(2)
 
