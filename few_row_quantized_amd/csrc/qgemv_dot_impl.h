@@ -51,7 +51,14 @@ constexpr int kMaxPasses = 3;  // lane passes (of 64 chunks) per LDS stage, at m
 // declared restrict.
 // FMT: kAffine (fp16 scale and bias per group) or a block-scaled FP format
 // (kMxfp4, kNvfp4, kMxfp8: one scale byte per block in `scales`, no bias).
-template <int BITS, int M, int R, int NSUB, int P, bool ADD, int FMT>
+// XR: with one activation row, each lane loads the x chunks of its own code
+// chunks straight into registers and pairs them there (no LDS staging, no
+// workgroup barrier; the same arithmetic in the same order as the staging,
+// so results are bit for bit those of the staged kernel).  Used where the
+// grid has at most two workgroups per CU: it needs more registers, which
+// costs occupancy on larger grids (measured: square 4096^2 4-bit 4.83 ->
+// 4.56 us at M = 1, 27B gate 13.3 -> 15.2 us).
+template <int BITS, int M, int R, int NSUB, int P, bool ADD, int FMT, bool XR = false>
 __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *y,
@@ -65,6 +72,7 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
   // the split pairing of the 2/4-bit offset codes
   constexpr bool NATURAL = BITS == 8 || FMT != kAffine;
   constexpr bool HAS_BIAS = FMT == kAffine;
+  constexpr bool XREG = XR && M == 1 && (CW / 8) * P <= 16;
   const uint8_t *scales8 = reinterpret_cast<const uint8_t *>(scales);
 
   extern __shared__ uint4 lds[];
@@ -110,7 +118,7 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
     //    lanes past the end read a valid clamped address and ignore the data.
     const int units = M * nc;
     const int npass = (nc + 63) >> 6;  // uniform
-    if (c0 != 0) __syncthreads();      // previous stage fully consumed
+    if (!XREG && c0 != 0) __syncthreads();  // previous stage fully consumed
     // Units are visited in an order rotated per workgroup (by blockIdx/8:
     // workgroups are dealt round-robin over the 8 XCDs) so that the CUs sharing
     // an L2 do not all read the same activation lines at the same moment.
@@ -119,8 +127,19 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
     // staging units per thread loaded ahead: a stage holds at most 64*P
     // chunks, i.e. M*64*P units, so one unit per thread while M*P <= 4, two
     // otherwise (the launcher keeps M*kch within two units per thread)
-    constexpr int JU = M * P <= 4 ? 1 : 2;
-    uint4 xa[JU][CW / 8];
+    constexpr int JU = XREG ? 0 : (M * P <= 4 ? 1 : 2);
+    uint4 xa[JU > 0 ? JU : 1][CW / 8];
+    // XREG: the x chunk of this lane's pass t (clamped past the end)
+    uint4 xg[XREG ? P : 1][CW / 8];
+    if constexpr (XREG) {
+#pragma unroll
+      for (int t = 0; t < P; ++t) {
+        const int c = min(lane + 64 * t, nc - 1);
+#pragma unroll
+        for (int i = 0; i < CW / 8; ++i)
+          xg[t][i] = reinterpret_cast<const uint4 *>(x + (size_t)(c0 + c) * CW)[i];
+      }
+    }
 #pragma unroll
     for (int j = 0; j < JU; ++j) {
       const int u = unit_of(min((int)threadIdx.x + kDotThreads * j, units - 1));
@@ -227,7 +246,7 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
       const int uu = threadIdx.x + kDotThreads * j;
       if (uu < units) stage_unit(unit_of(uu), xa[j]);
     }
-    for (int uu = threadIdx.x + JU * kDotThreads; uu < units; uu += kDotThreads) {
+    for (int uu = threadIdx.x + JU * kDotThreads; !XREG && uu < units; uu += kDotThreads) {
       const int u = unit_of(uu);
       const int m = u / nc;
       const int cl = u - m * nc;
@@ -237,7 +256,53 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
         xv[i] = reinterpret_cast<const uint4 *>(x + (size_t)m * K + (size_t)(c0 + cl) * CW)[i];
       stage_unit(u, xv);
     }
-    __syncthreads();
+    // XREG: pairs and sums of the lane's own chunks, as stage_unit forms them
+    uint4 xq[XREG ? P : 1][QUADS];
+    float xsm[XREG ? P : 1][NSUB];
+    if constexpr (XREG) {
+#pragma unroll
+      for (int t = 0; t < P; ++t) {
+        uint32_t X[CW / 2];
+#pragma unroll
+        for (int i = 0; i < CW / 8; ++i) {
+          X[4 * i] = xg[t][i].x;
+          X[4 * i + 1] = xg[t][i].y;
+          X[4 * i + 2] = xg[t][i].z;
+          X[4 * i + 3] = xg[t][i].w;
+        }
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) xsm[t][s] = 0.f;
+        if constexpr (HAS_BIAS) {
+#pragma unroll
+          for (int i = 0; i < CW / 2; ++i)
+            xsm[t][(2 * i) / SUBW] = dot2_bf16(X[i], 0x3F803F80u, xsm[t][(2 * i) / SUBW]);
+        }
+        if constexpr (NATURAL) {
+#pragma unroll
+          for (int d = 0; d < QUADS; ++d) xq[t][d] = make_uint4(X[4 * d], X[4 * d + 1], X[4 * d + 2], X[4 * d + 3]);
+        } else if constexpr (BITS == 4) {
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const uint32_t Xd[4] = {X[4 * d], X[4 * d + 1], X[4 * d + 2], X[4 * d + 3]};
+            xq[t][d] = make_uint4(xpair_stride4(Xd, 0), xpair_stride4(Xd, 1), xpair_stride4(Xd, 2),
+                                  xpair_stride4(Xd, 3));
+          }
+        } else {
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            uint32_t Xd[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) Xd[i] = X[8 * d + i];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              xq[t][2 * d + h] = make_uint4(xpair_stride8(Xd, 4 * h + 0), xpair_stride8(Xd, 4 * h + 1),
+                                            xpair_stride8(Xd, 4 * h + 2), xpair_stride8(Xd, 4 * h + 3));
+          }
+        }
+      }
+    } else {
+      __syncthreads();
+    }
 
     // 4. multi-row dot products over this stage, in load order
 #pragma unroll
@@ -289,7 +354,7 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
           }
 #pragma unroll
           for (int m = 0; m < M; ++m) {
-            const uint4 xv = xl[(m * QUADS + q) * kch + c];
+            const uint4 xv = XREG ? xq[t][q] : xl[(m * QUADS + q) * kch + c];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
               float a = d[r][m];
@@ -315,7 +380,7 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
                                        : fmaf(-128.f, sc, half_bits_to_float(br[t][r][s]));
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-              const float xs = xsl[(m * NSUB + s) * kch + c];
+              const float xs = XREG ? xsm[t][s] : xsl[(m * NSUB + s) * kch + c];
               acc[r][m] = fmaf(sc, d[r][m], fmaf(bo, xs, acc[r][m]));
             }
           }
@@ -344,7 +409,7 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
   }
 }
 
-template <int BITS, int M, int R, int NSUB, int P, bool ADD, int FMT>
+template <int BITS, int M, int R, int NSUB, int P, bool ADD, int FMT, bool XR = false>
 int launch_dot_tp(const QgemvArgs &a, hipStream_t stream) {
   constexpr int CW = 128 / BITS;
   constexpr int QUADS = CW / 8;
@@ -361,14 +426,15 @@ int launch_dot_tp(const QgemvArgs &a, hipStream_t stream) {
   if (kch < 64) kch = 64;
   if (kch > 64 * P) kch = 64 * P;
   if (kch > NC) kch = NC;  // one stage holds the whole row
-  const size_t lds = per_chunk * (size_t)kch;
+  constexpr bool XREG = XR && M == 1 && (CW / 8) * P <= 16;  // no LDS then
+  const size_t lds = XREG ? 0 : per_chunk * (size_t)kch;
   if (lds > kLdsMax) return QGEMV_EUNSUPPORTED;
   if (!allow_max_dynamic_lds(
-          reinterpret_cast<const void *>(&qgemv_dot_kernel<BITS, M, R, NSUB, P, ADD, FMT>)))
+          reinterpret_cast<const void *>(&qgemv_dot_kernel<BITS, M, R, NSUB, P, ADD, FMT, XR>)))
     return QGEMV_EHIP;
   const int rows_per_block = kDotWaves * R;
   const int blocks = (a.N + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL((qgemv_dot_kernel<BITS, M, R, NSUB, P, ADD, FMT>), dim3(blocks), dim3(kDotThreads),
+  hipLaunchKernelGGL((qgemv_dot_kernel<BITS, M, R, NSUB, P, ADD, FMT, XR>), dim3(blocks), dim3(kDotThreads),
                      lds, stream, a.codes, a.scales, a.biases, a.x, a.y, a.res, a.N, a.K,
                      a.group_size, kch);
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
@@ -379,6 +445,15 @@ int launch_dot_tp(const QgemvArgs &a, hipStream_t stream) {
 // M <= 4, where the dot path is the one that runs.
 template <int BITS, int M, int R, int NSUB, bool ADD, int FMT>
 int launch_dot_t(const QgemvArgs &a, hipStream_t stream) {
+  if constexpr (M == 1) {
+    // one activation row in registers where the grid has at most two
+    // workgroups per CU (see the kernel's XR)
+    const int blocks = (a.N + kDotWaves * R - 1) / (kDotWaves * R);
+    if (blocks <= 2 * device_cu_count()) {
+      if (a.K / (128 / BITS) <= 128) return launch_dot_tp<BITS, M, R, NSUB, 2, ADD, FMT, true>(a, stream);
+      return launch_dot_tp<BITS, M, R, NSUB, kMaxPasses, ADD, FMT, true>(a, stream);
+    }
+  }
   if constexpr (M <= 4) {
     if (a.K / (128 / BITS) <= 128) return launch_dot_tp<BITS, M, R, NSUB, 2, ADD, FMT>(a, stream);
   }
