@@ -51,13 +51,16 @@ constexpr int kMaxPasses = 3;  // lane passes (of 64 chunks) per LDS stage, at m
 // declared restrict.
 // FMT: kAffine (fp16 scale and bias per group) or a block-scaled FP format
 // (kMxfp4, kNvfp4, kMxfp8: one scale byte per block in `scales`, no bias).
-// XR: with one activation row, each lane loads the x chunks of its own code
-// chunks straight into registers and pairs them there (no LDS staging, no
-// workgroup barrier; the same arithmetic in the same order as the staging,
-// so results are bit for bit those of the staged kernel).  Used where the
-// grid has at most two workgroups per CU: it needs more registers, which
-// costs occupancy on larger grids (measured: square 4096^2 4-bit 4.83 ->
-// 4.56 us at M = 1, 27B gate 13.3 -> 15.2 us).
+// XR: with one activation row (two for 8-bit codes and the FP formats, when
+// they fit 16 registers of x per lane), each lane loads the x chunks of its
+// own code chunks straight into registers and pairs them there (no LDS
+// staging, no workgroup barrier; the same arithmetic in the same order as the
+// staging, so results are bit for bit those of the staged kernel).  Used
+// where the grid has at most two workgroups per CU: it needs more registers,
+// which costs occupancy on larger grids (measured: square 4096^2 4-bit 4.83 ->
+// 4.56 us at M = 1, 27B gate 13.3 -> 15.2 us).  At M = 2 on the 4096^2
+// matrices: 8-bit 7.54 -> 6.86 us, mxfp4 5.02 -> 4.69, nvfp4 5.33 -> 5.17,
+// mxfp8 6.80 -> 6.21, but 4-bit affine 5.15 -> 5.29, which keeps the staging.
 template <int BITS, int M, int R, int NSUB, int P, bool ADD, int FMT, bool XR = false>
 __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
@@ -72,7 +75,8 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
   // the split pairing of the 2/4-bit offset codes
   constexpr bool NATURAL = BITS == 8 || FMT != kAffine;
   constexpr bool HAS_BIAS = FMT == kAffine;
-  constexpr bool XREG = XR && M == 1 && (CW / 8) * P <= 16;
+  constexpr bool XREG = XR && (M == 1 || (M == 2 && !(FMT == kAffine && BITS == 4))) &&
+                        M * (CW / 8) * P <= 16;
   const uint8_t *scales8 = reinterpret_cast<const uint8_t *>(scales);
 
   extern __shared__ uint4 lds[];
@@ -129,15 +133,17 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
     // otherwise (the launcher keeps M*kch within two units per thread)
     constexpr int JU = XREG ? 0 : (M * P <= 4 ? 1 : 2);
     uint4 xa[JU > 0 ? JU : 1][CW / 8];
-    // XREG: the x chunk of this lane's pass t (clamped past the end)
-    uint4 xg[XREG ? P : 1][CW / 8];
+    // XREG: the x chunks of this lane's pass t, row m (clamped past the end)
+    uint4 xg[XREG ? P : 1][XREG ? M : 1][CW / 8];
     if constexpr (XREG) {
 #pragma unroll
       for (int t = 0; t < P; ++t) {
         const int c = min(lane + 64 * t, nc - 1);
 #pragma unroll
-        for (int i = 0; i < CW / 8; ++i)
-          xg[t][i] = reinterpret_cast<const uint4 *>(x + (size_t)(c0 + c) * CW)[i];
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+          for (int i = 0; i < CW / 8; ++i)
+            xg[t][m][i] = reinterpret_cast<const uint4 *>(x + (size_t)m * K + (size_t)(c0 + c) * CW)[i];
       }
     }
 #pragma unroll
@@ -257,34 +263,36 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
       stage_unit(u, xv);
     }
     // XREG: pairs and sums of the lane's own chunks, as stage_unit forms them
-    uint4 xq[XREG ? P : 1][QUADS];
-    float xsm[XREG ? P : 1][NSUB];
+    uint4 xq[XREG ? P : 1][XREG ? M : 1][QUADS];
+    float xsm[XREG ? P : 1][XREG ? M : 1][NSUB];
     if constexpr (XREG) {
 #pragma unroll
-      for (int t = 0; t < P; ++t) {
+      for (int t = 0; t < P; ++t)
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
         uint32_t X[CW / 2];
 #pragma unroll
         for (int i = 0; i < CW / 8; ++i) {
-          X[4 * i] = xg[t][i].x;
-          X[4 * i + 1] = xg[t][i].y;
-          X[4 * i + 2] = xg[t][i].z;
-          X[4 * i + 3] = xg[t][i].w;
+          X[4 * i] = xg[t][m][i].x;
+          X[4 * i + 1] = xg[t][m][i].y;
+          X[4 * i + 2] = xg[t][m][i].z;
+          X[4 * i + 3] = xg[t][m][i].w;
         }
 #pragma unroll
-        for (int s = 0; s < NSUB; ++s) xsm[t][s] = 0.f;
+        for (int s = 0; s < NSUB; ++s) xsm[t][m][s] = 0.f;
         if constexpr (HAS_BIAS) {
 #pragma unroll
           for (int i = 0; i < CW / 2; ++i)
-            xsm[t][(2 * i) / SUBW] = dot2_bf16(X[i], 0x3F803F80u, xsm[t][(2 * i) / SUBW]);
+            xsm[t][m][(2 * i) / SUBW] = dot2_bf16(X[i], 0x3F803F80u, xsm[t][m][(2 * i) / SUBW]);
         }
         if constexpr (NATURAL) {
 #pragma unroll
-          for (int d = 0; d < QUADS; ++d) xq[t][d] = make_uint4(X[4 * d], X[4 * d + 1], X[4 * d + 2], X[4 * d + 3]);
+          for (int d = 0; d < QUADS; ++d) xq[t][m][d] = make_uint4(X[4 * d], X[4 * d + 1], X[4 * d + 2], X[4 * d + 3]);
         } else if constexpr (BITS == 4) {
 #pragma unroll
           for (int d = 0; d < 4; ++d) {
             const uint32_t Xd[4] = {X[4 * d], X[4 * d + 1], X[4 * d + 2], X[4 * d + 3]};
-            xq[t][d] = make_uint4(xpair_stride4(Xd, 0), xpair_stride4(Xd, 1), xpair_stride4(Xd, 2),
+            xq[t][m][d] = make_uint4(xpair_stride4(Xd, 0), xpair_stride4(Xd, 1), xpair_stride4(Xd, 2),
                                   xpair_stride4(Xd, 3));
           }
         } else {
@@ -295,7 +303,7 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
             for (int i = 0; i < 8; ++i) Xd[i] = X[8 * d + i];
 #pragma unroll
             for (int h = 0; h < 2; ++h)
-              xq[t][2 * d + h] = make_uint4(xpair_stride8(Xd, 4 * h + 0), xpair_stride8(Xd, 4 * h + 1),
+              xq[t][m][2 * d + h] = make_uint4(xpair_stride8(Xd, 4 * h + 0), xpair_stride8(Xd, 4 * h + 1),
                                             xpair_stride8(Xd, 4 * h + 2), xpair_stride8(Xd, 4 * h + 3));
           }
         }
@@ -354,7 +362,7 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
           }
 #pragma unroll
           for (int m = 0; m < M; ++m) {
-            const uint4 xv = XREG ? xq[t][q] : xl[(m * QUADS + q) * kch + c];
+            const uint4 xv = XREG ? xq[t][m][q] : xl[(m * QUADS + q) * kch + c];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
               float a = d[r][m];
@@ -380,7 +388,7 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
                                        : fmaf(-128.f, sc, half_bits_to_float(br[t][r][s]));
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-              const float xs = XREG ? xsm[t][s] : xsl[(m * NSUB + s) * kch + c];
+              const float xs = XREG ? xsm[t][m][s] : xsl[(m * NSUB + s) * kch + c];
               acc[r][m] = fmaf(sc, d[r][m], fmaf(bo, xs, acc[r][m]));
             }
           }
@@ -426,7 +434,8 @@ int launch_dot_tp(const QgemvArgs &a, hipStream_t stream) {
   if (kch < 64) kch = 64;
   if (kch > 64 * P) kch = 64 * P;
   if (kch > NC) kch = NC;  // one stage holds the whole row
-  constexpr bool XREG = XR && M == 1 && (CW / 8) * P <= 16;  // no LDS then
+  constexpr bool XREG = XR && (M == 1 || (M == 2 && !(FMT == kAffine && BITS == 4))) &&
+                        M * (CW / 8) * P <= 16;  // no LDS then
   const size_t lds = XREG ? 0 : per_chunk * (size_t)kch;
   if (lds > kLdsMax) return QGEMV_EUNSUPPORTED;
   if (!allow_max_dynamic_lds(
@@ -445,8 +454,8 @@ int launch_dot_tp(const QgemvArgs &a, hipStream_t stream) {
 // M <= 4, where the dot path is the one that runs.
 template <int BITS, int M, int R, int NSUB, bool ADD, int FMT>
 int launch_dot_t(const QgemvArgs &a, hipStream_t stream) {
-  if constexpr (M == 1) {
-    // one activation row in registers where the grid has at most two
+  if constexpr (M == 1 || (M == 2 && !(FMT == kAffine && BITS == 4))) {
+    // activation rows in registers where the grid has at most two
     // workgroups per CU (see the kernel's XR)
     const int blocks = (a.N + kDotWaves * R - 1) / (kDotWaves * R);
     if (blocks <= 2 * device_cu_count()) {
