@@ -5,11 +5,22 @@
 //
 // Every expert in the union of e_idx is read from HBM once per call, for all
 // the pairs routed to it, by the single-pass MFMA kernel (GATHER variant in
-// qgemv_mfma_impl.h): one workgroup per (expert slot, 16-column tile), the
-// slot-th expert in ascending id order found from a bitmap of the union built
-// in LDS, its pairs gathered in ascending order and taken 16 rows at a time.
-// The host does not know the union size (the routing stays on the device), so
-// the grid covers min(P, E) slots and workgroups past the union exit at once.
+// qgemv_mfma_impl.h).  The work is the (expert slot, 16-column tile group)
+// items, slots being the union's experts in ascending id order, each with its
+// pairs in ascending order taken 16 rows at a time.  The host does not know
+// the union size (the routing stays on the device), so it plans for
+// min(P, E) slots:
+// * one tile per workgroup: a grid of the workgroups resident at once, each
+//   sorting the routing once and walking the items with the grid stride
+//   (measured on the 128-expert top-8 1536 x 2048 gate/up shape: 80.7 ->
+//   70.4 us at M = 16, 44.6 -> 40.3 at M = 8, 9.9 -> 8.9 at M = 1, against
+//   one workgroup per item with the routing prologue in each);
+// * two tiles per workgroup (short K): one workgroup per item, which finds
+//   its slot's expert from a bitmap of the union and exits when the slot is
+//   past it (there the per-workgroup rank sort cost more than it saved:
+//   2048 x 768 +8 to +17%).
+
+#include <atomic>
 
 #include "qgemv_mfma_impl.h"
 
@@ -28,8 +39,24 @@ int launch_gather_nt(const QgemvArgs &a, const GatherArgs &ga, hipStream_t strea
   const int waves = pick_waves(nblk, MAXT / 64);
   const int groups = ((a.N + 15) / 16 + NT - 1) / NT;
   const int slots = ga.P < ga.E ? ga.P : ga.E;
-  // at most kMaxPairs * 2^18 workgroups: within the grid limit
-  const unsigned blocks = (unsigned)slots * (unsigned)groups;
+  // at most kMaxPairs * 2^18 (slot, tile group) items: within the grid limit.
+  // One tile per workgroup: at most the workgroups resident at once, each
+  // walking the items with the grid stride (the routing is sorted once per
+  // workgroup); two tiles: one workgroup per item.
+  unsigned blocks = (unsigned)slots * (unsigned)groups;
+  if constexpr (NT == 1) {
+    static std::atomic<int> occ_cache[MAXT / 64 + 1];
+    int occ = occ_cache[waves].load(std::memory_order_relaxed);
+    if (occ == 0) {
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void *>(kern),
+                                                       64 * waves, 0) != hipSuccess ||
+          occ <= 0)
+        occ = 1;
+      occ_cache[waves].store(occ, std::memory_order_relaxed);
+    }
+    const unsigned cap = (unsigned)occ * (unsigned)device_cu_count();
+    if (blocks > cap) blocks = cap;
+  }
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * waves), 0, stream, a.codes, a.scales, a.biases,
                      a.x, a.y, static_cast<const float *>(nullptr), 16, a.N, a.K, groups, ga);
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;

@@ -29,11 +29,12 @@ struct GatherArgs {
 // (32-element blocks, GS = 32, scale folded per block in fp32) or kNvfp4
 // (16-element blocks, laid out as GS = 32; each element is multiplied by its
 // block scale before the MFMA, exactly, so B holds the weights themselves).
-// GATHER: workgroup b serves expert slot b / ngroups (the slot-th expert, in
-// ascending id order, of the union of e_idx) and tile group b % ngroups; its
-// rows are the pairs routed to that expert (in ascending pair order, 16 at a
-// time), gathered from x and scattered to y[pair].  Slots past the union exit
-// at once.  (KS = 1, not PERSIST, affine codes.)
+// GATHER: the rows of a (slot, tile group) item are the pairs routed to the
+// slot's expert (slots: the union of e_idx in ascending id order; pairs in
+// ascending order, 16 at a time), gathered from x and scattered to y[pair].
+// With one tile per workgroup the grid walks the items with its stride;
+// with two, workgroup b serves item b and exits if its slot is past the
+// union.  (KS = 1, not PERSIST, affine codes.)
 template <int BITS, int GS, int NT, int MAXT, int SPI, int KS, bool PERSIST, bool ADD, int FMT,
           bool GATHER = false>
 __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
@@ -77,66 +78,132 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   // element offset, within a super-chunk, of the codes register i holds in
   // this lane's row after the partial transpose
 
-  // Gathered verify: pick this workgroup's expert and its pairs.
-  __shared__ uint32_t gbits[GATHER ? kMaxExperts / 32 : 1];
-  __shared__ int gpairs[GATHER ? kMaxPairs : 1];
-  __shared__ int gexp[GATHER ? kMaxPairs : 1];  // expert of each pair, -1 if invalid
-  __shared__ int gxr[GATHER ? kMaxPairs : 1];   // activation row of each pair
+  // Gathered verify.  The routing is read once per workgroup into LDS.
+  // GSORT (one tile per workgroup): the valid pairs are ordered by
+  // (expert, pair) with a stable rank sort, the runs of equal experts (the
+  // union in ascending id order) become slots, and the workgroup walks the
+  // (slot, tile group) items with the grid stride.  Otherwise (two tiles per
+  // workgroup, short K): workgroup b serves slot b / ngroups alone, found as
+  // the slot-th set bit of a union bitmap, and compacts that expert's pairs.
+  // Either way a slot's pairs are in ascending order, so each expert sees the
+  // same 16-row chunks.
+  constexpr bool GSORT = GATHER && NT == 1;
+  __shared__ uint32_t gbits[GATHER && !GSORT ? kMaxExperts / 32 : 1];
+  __shared__ int gexp[GATHER ? kMaxPairs : 1];        // expert of each pair, -1 if invalid
+  __shared__ int gxr[GATHER ? kMaxPairs : 1];         // activation row of each pair
+  __shared__ int gsorted[GATHER ? kMaxPairs : 1];     // pairs of the slots, in slot order
+  __shared__ int gstart[GSORT ? kMaxPairs + 1 : 1];   // first position of each slot
+  __shared__ int gslot_exp[GSORT ? kMaxPairs : 1];    // expert of each slot
   __shared__ int gmeta[2];
-  int c0 = 0;  // first pair of the current chunk of 16 rows
+  int c0 = 0;     // first pair of the current chunk of 16 rows
+  int pbase = 0;  // first position in gsorted of the current slot
+  const uint8_t *const codes0 = codes;
+  const uint16_t *const scales0 = scales;
+  const uint16_t *const biases0 = biases;
   if constexpr (GATHER) {
     static_assert(KS == 1 && !PERSIST && !ADD && FMT == kAffine, "gather variant");
     const int words = (ga.E + 31) >> 5;
-    for (int i = threadIdx.x; i < words; i += blockDim.x) gbits[i] = 0u;
-    __syncthreads();
-    // the routing is read from memory once and kept in LDS
+    if constexpr (!GSORT) {
+      for (int i = threadIdx.x; i < words; i += blockDim.x) gbits[i] = 0u;
+      __syncthreads();
+    }
     for (int p = threadIdx.x; p < ga.P; p += blockDim.x) {
       const int e = ga.e_idx[p], xi = ga.x_idx[p];
       const bool valid = e >= 0 && e < ga.E && xi >= 0 && xi < ga.X;
       gexp[p] = valid ? e : -1;
       gxr[p] = xi;
-      if (valid) atomicOr(&gbits[e >> 5], 1u << (e & 31));
+      if constexpr (!GSORT) {
+        if (valid) atomicOr(&gbits[e >> 5], 1u << (e & 31));
+      }
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      // the slot-th set bit of the union bitmap
-      const int slot = (int)blockIdx.x / ngroups;
-      int seen = 0, expert = -1;
-      for (int w = 0; w < words && expert < 0; ++w) {
-        uint32_t b = gbits[w];
-        const int c = __popc(b);
-        if (seen + c > slot) {
-          for (int k = slot - seen; k > 0; --k) b &= b - 1;  // drop the lower set bits
-          expert = 32 * w + __ffs(b) - 1;
+    if constexpr (GSORT) {
+      // position of a valid pair: valid pairs with a smaller expert, or the
+      // same expert and a smaller index, come before it
+      for (int p = threadIdx.x; p < ga.P; p += blockDim.x) {
+        const int e = gexp[p];
+        if (e < 0) continue;
+        int rank = 0;
+        for (int q = 0; q < ga.P; ++q) {
+          const int f = gexp[q];
+          rank += (f >= 0 && (f < e || (f == e && q < p))) ? 1 : 0;
         }
-        seen += c;
+        gsorted[rank] = p;
       }
-      gmeta[0] = expert;
-    }
-    __syncthreads();
-    const int expert = gmeta[0];
-    if (expert < 0) return;  // slot past the union (uniform for the workgroup)
-    if (wave == 0) {
-      // pairs of this expert in ascending order (ballot compaction)
-      int base = 0;
-      for (int p0 = 0; p0 < ga.P; p0 += 64) {
-        const int p = p0 + lane;
-        const bool hit = p < ga.P && gexp[p] == expert;
-        const uint64_t bal = __ballot(hit);
-        if (hit) gpairs[base + __popcll(bal & ((1ull << lane) - 1ull))] = p;
-        base += __popcll(bal);
+      int nvalid = 0;
+      if (wave == 0) {
+        for (int p0 = 0; p0 < ga.P; p0 += 64) {
+          const int p = p0 + lane;
+          nvalid += __popcll(__ballot(p < ga.P && gexp[p] >= 0));
+        }
       }
-      if (lane == 0) gmeta[1] = base;
+      __syncthreads();
+      if (wave == 0) {
+        // slot boundaries: a position whose expert differs from the one before
+        int base = 0;
+        for (int i0 = 0; i0 < nvalid; i0 += 64) {
+          const int i = i0 + lane;
+          int e = -1;
+          bool first = false;
+          if (i < nvalid) {
+            e = gexp[gsorted[i]];
+            first = i == 0 || gexp[gsorted[i - 1]] != e;
+          }
+          const uint64_t bal = __ballot(first);
+          if (first) {
+            const int sl = base + __popcll(bal & ((1ull << lane) - 1ull));
+            gstart[sl] = i;
+            gslot_exp[sl] = e;
+          }
+          base += __popcll(bal);
+        }
+        if (lane == 0) {
+          gmeta[0] = base;
+          gstart[base] = nvalid;
+        }
+      }
+      __syncthreads();
+    } else {
+      if (threadIdx.x == 0) {
+        // the slot-th set bit of the union bitmap
+        const int slot = (int)blockIdx.x / ngroups;
+        int seen = 0, expert = -1;
+        for (int w = 0; w < words && expert < 0; ++w) {
+          uint32_t b = gbits[w];
+          const int c = __popc(b);
+          if (seen + c > slot) {
+            for (int k = slot - seen; k > 0; --k) b &= b - 1;  // drop the lower set bits
+            expert = 32 * w + __ffs(b) - 1;
+          }
+          seen += c;
+        }
+        gmeta[0] = expert;
+      }
+      __syncthreads();
+      const int expert = gmeta[0];
+      if (expert < 0) return;  // slot past the union (uniform for the workgroup)
+      if (wave == 0) {
+        // pairs of this expert in ascending order (ballot compaction)
+        int base = 0;
+        for (int p0 = 0; p0 < ga.P; p0 += 64) {
+          const int p = p0 + lane;
+          const bool hit = p < ga.P && gexp[p] == expert;
+          const uint64_t bal = __ballot(hit);
+          if (hit) gsorted[base + __popcll(bal & ((1ull << lane) - 1ull))] = p;
+          base += __popcll(bal);
+        }
+        if (lane == 0) gmeta[1] = base;
+      }
+      __syncthreads();
+      const size_t G_ = (size_t)(K / GS);
+      codes = codes0 + (size_t)expert * N * ((size_t)K * BITS / 8);
+      scales = scales0 + (size_t)expert * N * G_;
+      biases = biases0 + (size_t)expert * N * G_;
     }
-    __syncthreads();
-    const size_t G_ = (size_t)(K / GS);
-    codes += (size_t)expert * N * ((size_t)K * BITS / 8);
-    scales += (size_t)expert * N * G_;
-    biases += (size_t)expert * N * G_;
   }
   // activation row of row m of the current chunk, and its output row
-  auto xrow = [&](const int m) -> size_t { return GATHER ? (size_t)gxr[gpairs[c0 + m]] : (size_t)m; };
-  auto yrow = [&](const int m) -> size_t { return GATHER ? (size_t)gpairs[c0 + m] : (size_t)m; };
+  auto xrow = [&](const int m) -> size_t { return GATHER ? (size_t)gxr[gsorted[pbase + c0 + m]] : (size_t)m; };
+  auto yrow = [&](const int m) -> size_t { return GATHER ? (size_t)gsorted[pbase + c0 + m] : (size_t)m; };
 
   // One tile group (16*NT output columns over all of K) per call of `group`.
   auto group = [&](const int tg) {
@@ -483,7 +550,28 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   for (int o = threadIdx.x + NT * blockDim.x; o < NT * 256; o += blockDim.x) finish(o, false, 0.f);
   };
 
-  if constexpr (GATHER) {
+  if constexpr (GSORT) {
+    // items (slot, tile group) in slot-major order, walked with the grid
+    // stride; each slot's pairs are taken 16 rows at a time
+    const int items = gmeta[0] * ngroups;
+    const size_t G_ = (size_t)(K / GS);
+    bool first = true;
+    for (int w = blockIdx.x; w < items; w += gridDim.x) {
+      const int slot = w / ngroups;
+      const int expert = gslot_exp[slot];
+      codes = codes0 + (size_t)expert * N * ((size_t)K * BITS / 8);
+      scales = scales0 + (size_t)expert * N * G_;
+      biases = biases0 + (size_t)expert * N * G_;
+      pbase = gstart[slot];
+      const int pairs = gstart[slot + 1] - pbase;
+      for (c0 = 0; c0 < pairs; c0 += 16) {
+        M = min(16, pairs - c0);
+        if (!first) __syncthreads();  // reduction buffer drained
+        first = false;
+        group(w - slot * ngroups);
+      }
+    }
+  } else if constexpr (GATHER) {
     // the expert's pairs, 16 rows at a time
     const int pairs = gmeta[1];
     for (c0 = 0; c0 < pairs; c0 += 16) {
