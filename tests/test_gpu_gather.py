@@ -132,3 +132,23 @@ def test_full_size_sampled_columns(name):
         y = d.run(x_idx, e_idx)
         assert np.all(np.isfinite(y))
         check(p, y, x_idx, e_idx, cols=cols, label=f"{name} M={M}")
+
+
+def test_full_size_pair_rows_equal_the_dense_mfma_path_bitwise():
+    # 16 verify rows on the 128-expert gate/up shape: the union's (expert, tile)
+    # items outnumber the resident workgroups, so each workgroup walks several
+    import torch
+    s = synth.MOE_WORKLOADS["moe30b_gateup_e128_k2048_n1536_4b_g64_top8"]
+    p = synth.make_moe_problem(s)
+    d = MoeDevice(p)
+    x_idx, e_idx = p.pairs(16)
+    say(f"gather full-size vs dense mfma bitwise, pairs={len(e_idx)} union={len(set(e_idx.tolist()))}")
+    y = d.run(x_idx, e_idx)
+    rng = np.random.default_rng(11)
+    for i in sorted(rng.choice(len(e_idx), size=24, replace=False).tolist()):
+        e, r = int(e_idx[i]), int(x_idx[i])
+        yd = torch.empty((1, s.N), dtype=torch.float32, device="cuda:0")
+        q.qgemv_run_path("mfma", d.codes[e], d.scales[e], d.biases[e], d.x[r:r + 1].clone(), yd, 1,
+                         s.N, s.K, s.bits, s.group_size)
+        torch.cuda.synchronize()
+        assert np.array_equal(yd.cpu().numpy()[0], y[i]), f"pair {i} (expert {e}, row {r})"
