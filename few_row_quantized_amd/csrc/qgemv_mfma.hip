@@ -35,7 +35,9 @@
 // * Fused residual sum (ADD, "metal : few-row MMA mat-mul and batched copies
 //   for speculative decoding", Overview: MUL_MAT + ADD writes the residual
 //   sum from the store): each thread loads the residual of the outputs it
-//   will store at the start of its tile group and adds it in the store, so
+//   will store right after its wave's first batch of loads (ahead of them, it
+//   sat in front of the batch's first wait: square 4096^2 M = 3 fused
+//   5.60 -> 5.34 us against 5.25 plain) and adds it in the store, so
 //   y = fl(product + r), bit for bit the plain call and a separate fp32 add.
 // Shapes with more 16-column tiles than CUs go to the persistent kernel
 // (qgemv_persist.hip) unless K is too long for its register-resident

@@ -257,16 +257,18 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   // steps (all of them when the workgroup has at least 4 waves), loaded ahead
   // of the weight stream; clamped indices read a valid element, never used
   float rpre[NT];
-  if constexpr (ADD) {
+  auto load_res = [&]() {
+    if constexpr (ADD) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int o = min((int)threadIdx.x + j * (int)blockDim.x, NT * 256 - 1);
-      const int l = o & 63;
-      const int m = min(4 * (l >> 4) + ((o >> 6) & 3), M - 1);
-      const int n = min(n_base + 16 * (o >> 8) + (l & 15), N - 1);
-      rpre[j] = res[yrow(m) * N + n];
+      for (int j = 0; j < NT; ++j) {
+        const int o = min((int)threadIdx.x + j * (int)blockDim.x, NT * 256 - 1);
+        const int l = o & 63;
+        const int m = min(4 * (l >> 4) + ((o >> 6) & 3), M - 1);
+        const int n = min(n_base + 16 * (o >> 8) + (l & 15), N - 1);
+        rpre[j] = res[yrow(m) * N + n];
+      }
     }
-  }
+  };
 
   f32x4_t acc[NT];
 #pragma unroll
@@ -315,6 +317,11 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
           }
         }
       }
+    }
+    // the residual is read after the first batch's loads, so that the
+    // batch's first wait does not wait for it too
+    if constexpr (ADD) {
+      if (blk0 == b_begin) load_res();
     }
     // keep the whole batch of loads ahead of the compute: without this the
     // scheduler may sink later loads below the first waits and serialize them
@@ -503,6 +510,9 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
         }
       }
     }
+  }
+  if constexpr (ADD) {
+    if (b_begin >= b_end) load_res();  // a wave without blocks
   }
 
   // split-K reduction over the slices, fixed order
