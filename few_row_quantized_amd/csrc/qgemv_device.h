@@ -1,13 +1,20 @@
 // Device helpers for the few-row quantized GEMV kernels (gfx950, wave64).
 //
-// 2- and 4-bit codes become bf16 values 128+q: for 0 <= q < 128 the bf16 bit
-// pattern of 128+q is 0x4300 | q (exponent of 2^7, q in the 7 mantissa bits),
-// so one AND-OR places two codes into the two halves of a dword as an exact
-// bf16 pair.  Dot products of these pairs with bf16 activations are exact per
-// product in fp32; the 128 offset is removed once per group through the
-// group's activation sum (128 * sum x), folded together with the bias.
-// 8-bit codes (0..255) do not fit that pattern; they are converted exactly
-// without an offset (unpack8_pairs).
+// Codes become exact bf16 values q with no offset.  A byte 0000qqqq read as
+// an FP8 E4M3 number is q * 2^-9 for every q in 0..15 (exponent field 0 holds
+// 0..7 as subnormals m * 2^-9, field 1 holds 8..15 as (8 + m) * 2^-9), so the
+// gfx950 scaled conversion FP8 -> bf16 at scale 2^9 turns two such bytes into
+// the exact bf16 pair (q_a, q_b) in one instruction: 2- and 4-bit fields are
+// first spread into bytes with one shift-and-mask per four fields.  Dot
+// products of these pairs with bf16 activations are exact per product in
+// fp32.  8-bit codes (0..255) are converted exactly through fp32
+// (unpack8_pairs).
+//
+// The affine bias goes through an integer zero point (zero_point): each group
+// is applied as s * sum (q - z) x + b' * sum x, the first sum formed as the
+// difference of two products run through the same arithmetic (codes against
+// x, the constant z against x).  A group whose weights are all exactly zero
+// then contributes exactly 0.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -19,8 +26,6 @@ typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-constexpr uint32_t kOffsetPair = 0x43004300u;  // bf16(128) in both halves
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
@@ -48,74 +53,54 @@ __device__ __forceinline__ u32x4_t load_stream_u32x4(const void *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
 }
 
-// A value the compiler cannot see through, kept in a VGPR.  Used for the
-// OR operand of the unpack so that AND+OR fuse into one v_and_or_b32 (a VOP3
-// instruction on gfx9 takes at most one literal/SGPR operand).
-__device__ __forceinline__ uint32_t opaque_u32(uint32_t v) {
-  uint32_t r;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
-  return r;
-}
-
 // ---------------------------------------------------------------- code unpack
 //
-// 4-bit "offset" pairing (dot path): dword w holds codes j = 0..7 (nibble j).
-// Pair p (p = 0..3) = codes (p, p+4).
-// `off` holds kOffsetPair (pass opaque_u32(kOffsetPair) for a fused AND-OR).
-__device__ __forceinline__ void unpack4_split_pairs(uint32_t w, uint32_t (&o)[4],
-                                                    uint32_t off = kOffsetPair) {
-  o[0] = (w & 0x000F000Fu) | off;
-  o[1] = ((w >> 4) & 0x000F000Fu) | off;
-  o[2] = ((w >> 8) & 0x000F000Fu) | off;
-  o[3] = ((w >> 12) & 0x000F000Fu) | off;
+// Two codes held in bytes 2*HI and 2*HI+1 of `bytes` (each 0..15) as the
+// exact bf16 pair (code of the lower byte in the low half).
+constexpr float kCodeScale = 512.0f;  // 2^9: E4M3 byte q -> q
+template <bool HI>
+__device__ __forceinline__ uint32_t code_pair(uint32_t bytes) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(bytes, kCodeScale, HI));
 }
 
-// 4-bit "natural" pairing (MFMA path): pair p = codes (2p, 2p+1), i.e. the two
-// nibbles of byte p, so the activation operand keeps its memory order.
-__device__ __forceinline__ void unpack4_natural_pairs(uint32_t w, uint32_t (&o)[4]) {
-  const uint32_t h = w >> 4;
-  // byte p of w -> byte 0, byte p of (w >> 4) -> byte 2, zeros elsewhere.
-  o[0] = (perm_b32(h, w, 0x0c040c00u) & 0x000F000Fu) | kOffsetPair;
-  o[1] = (perm_b32(h, w, 0x0c050c01u) & 0x000F000Fu) | kOffsetPair;
-  o[2] = (perm_b32(h, w, 0x0c060c02u) & 0x000F000Fu) | kOffsetPair;
-  o[3] = (perm_b32(h, w, 0x0c070c03u) & 0x000F000Fu) | kOffsetPair;
+// 4-bit codes: dword w holds codes j = 0..7 (nibble j, low nibble first).
+// Pairs (0, 2), (1, 3), (4, 6), (5, 7): the low nibbles of the four bytes are
+// codes 0, 2, 4, 6 and the high nibbles 1, 3, 5, 7.  Seven instructions per
+// eight codes.  The activations are paired to match (xpair4).
+__device__ __forceinline__ u32x4_t unpack4_quad(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6 in bytes 0..3
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
+  return u32x4_t{code_pair<false>(lo), code_pair<false>(hi), code_pair<true>(lo), code_pair<true>(hi)};
+}
+__device__ __forceinline__ void unpack4_pairs(uint32_t w, uint32_t (&o)[4]) {
+  const u32x4_t v = unpack4_quad(w);
+  o[0] = v[0];
+  o[1] = v[1];
+  o[2] = v[2];
+  o[3] = v[3];
 }
 
-// Same, as the 4-dword MFMA operand; `off` holds kOffsetPair (opaque_u32).
-__device__ __forceinline__ u32x4_t unpack4_natural_quad(uint32_t w, uint32_t off) {
-  const uint32_t h = w >> 4;
-  u32x4_t o;
-  o[0] = (perm_b32(h, w, 0x0c040c00u) & 0x000F000Fu) | off;
-  o[1] = (perm_b32(h, w, 0x0c050c01u) & 0x000F000Fu) | off;
-  o[2] = (perm_b32(h, w, 0x0c060c02u) & 0x000F000Fu) | off;
-  o[3] = (perm_b32(h, w, 0x0c070c03u) & 0x000F000Fu) | off;
-  return o;
-}
-
-// 2-bit pairing (both paths): dword w holds codes j = 0..15 (crumb j).
-// Pair j (j = 0..7) = codes (j, j+8).
-__device__ __forceinline__ void unpack2_split_pairs(uint32_t w, uint32_t (&o)[8],
-                                                    uint32_t off = kOffsetPair) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) o[j] = ((w >> (2 * j)) & 0x00030003u) | off;
-}
-
-// 4-bit split pairing as the 4-dword MFMA operand (pairs (p, p+4)).
-__device__ __forceinline__ u32x4_t unpack4_split_quad(uint32_t w, uint32_t off) {
-  u32x4_t o;
-  o[0] = (w & 0x000F000Fu) | off;
-  o[1] = ((w >> 4) & 0x000F000Fu) | off;
-  o[2] = ((w >> 8) & 0x000F000Fu) | off;
-  o[3] = ((w >> 12) & 0x000F000Fu) | off;
-  return o;
-}
-
-// Half h (h = 0, 1) of the 2-bit pairing as an MFMA operand: pairs 4h..4h+3.
-__device__ __forceinline__ u32x4_t unpack2_split_quad(uint32_t w, int h, uint32_t off) {
+// 2-bit codes: dword w holds codes j = 0..15 (crumb j, lowest crumb first).
+// (w >> 2e) & 0x03030303 holds codes e, e+4, e+8, e+12 in bytes 0..3, so half
+// h (codes 8h..8h+7) is the pairs (8h + e, 8h + e + 4), e = 0..3.  Fifteen
+// instructions per sixteen codes.  The activations of each half are paired
+// to match (xpair_stride4).
+__device__ __forceinline__ u32x4_t unpack2_quad(uint32_t w, int h) {
   u32x4_t o;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) o[e] = ((w >> (2 * (4 * h + e))) & 0x00030003u) | off;
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t c = (w >> (2 * e)) & 0x03030303u;
+    o[e] = h ? code_pair<true>(c) : code_pair<false>(c);
+  }
   return o;
+}
+__device__ __forceinline__ void unpack2_pairs(uint32_t w, uint32_t (&o)[8]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t c = (w >> (2 * e)) & 0x03030303u;
+    o[e] = code_pair<false>(c);
+    o[4 + e] = code_pair<true>(c);
+  }
 }
 
 // 8-bit codes: byte j of dword w is code j (0..255).  Every code is exact in
@@ -199,22 +184,61 @@ __device__ __forceinline__ float fp_scale_to_float(uint32_t byte) {
   return e8m0_to_float(byte);
 }
 
+// ---------------------------------------------------------------- zero point
+//
+// w = s*q + b = s*(q - z) + b' with the integer zero point z = round(-b/s),
+// clamped to the code range [0, zmax], and b' = b + z*s (one fma).  The
+// kernels form sum (q - z)*x as the difference of two products that run
+// through identical arithmetic -- the codes against x, and the bf16 pair
+// (z, z) in every code slot against x -- and add b' * sum x.  When every
+// weight of the group is exactly zero (b = -z*s for an integer z in range),
+// the two products see identical operands and give identical bits, and b' is
+// exactly 0 (fma of the exact product z*s with b = -z*s), so the group adds
+// exactly 0, whatever z; for other groups z only re-centres the codes.  The
+// reciprocal is approximate, but -b * rcp(s) lies within a few ulps of an
+// integer z <= 255 when b = -z*s, so the rounding finds z.  A zero scale
+// gives z = 0 and b' = b.
+struct ZeroPoint {
+  uint32_t zpair;  // bf16 (z, z)
+  float bres;      // b' = b + z*s
+};
+__device__ __forceinline__ ZeroPoint zero_point(float s, float b, int zmax) {
+  const float r = s != 0.f ? __builtin_amdgcn_rcpf(s) : 0.f;
+  // clamped in fp32 first (fmaxf takes 0 over a NaN), so the conversion is in
+  // range; the round trip through int turns -0 into +0
+  const int zi = (int)fminf(fmaxf(rintf(-b * r), 0.f), (float)zmax);
+  const float z = (float)zi;
+  const uint32_t zb = __builtin_bit_cast(uint32_t, z);  // z is exact in bf16: the upper half
+  return ZeroPoint{perm_b32(zb, zb, 0x03020302u), fmaf(z, s, b)};
+}
+
 // ---------------------------------------------------------------- activation pairing
 //
 // Activations are re-paired to match the code pairing.  X[i] holds bf16
 // elements (2i, 2i+1) of a run of consecutive activations.
 //
-// pair of elements (e, e+4) from X[0..3] (4-bit offset pairing), e = 0..3
+// 4-bit pairing: pair e of (0, 2), (1, 3), (4, 6), (5, 7) from X[0..3]
+__device__ __forceinline__ uint32_t xpair4(const uint32_t (&X)[4], int e) {
+  return (e & 1) ? perm_b32(X[2 * (e >> 1) + 1], X[2 * (e >> 1)], 0x07060302u)
+                 : perm_b32(X[2 * (e >> 1) + 1], X[2 * (e >> 1)], 0x05040100u);
+}
+
+// 2-bit pairing of one half: pair (e, e+4) from X[0..3], e = 0..3
 __device__ __forceinline__ uint32_t xpair_stride4(const uint32_t (&X)[4], int e) {
   return (e & 1) ? perm_b32(X[(e >> 1) + 2], X[e >> 1], 0x07060302u)
                  : perm_b32(X[(e >> 1) + 2], X[e >> 1], 0x05040100u);
 }
 
-// pair of elements (e, e+8) from X[0..7] (2-bit pairing), e = 0..7
-__device__ __forceinline__ uint32_t xpair_stride8(const uint32_t (&X)[8], int e) {
-  return (e & 1) ? perm_b32(X[(e >> 1) + 4], X[e >> 1], 0x07060302u)
-                 : perm_b32(X[(e >> 1) + 4], X[e >> 1], 0x05040100u);
+// The four pairs of 8 consecutive activations (one u32x4 in memory order)
+// in the pairing of BITS-bit codes (2 or 4).
+template <int BITS>
+__device__ __forceinline__ u32x4_t pair_activations(const u32x4_t &v) {
+  const uint32_t X[4] = {v[0], v[1], v[2], v[3]};
+  if constexpr (BITS == 4) return u32x4_t{xpair4(X, 0), xpair4(X, 1), xpair4(X, 2), xpair4(X, 3)};
+  return u32x4_t{xpair_stride4(X, 0), xpair_stride4(X, 1), xpair_stride4(X, 2), xpair_stride4(X, 3)};
 }
+
+constexpr uint32_t kOnesPair = 0x3F803F80u;  // bf16 (1.0, 1.0)
 
 // ---------------------------------------------------------------- lane exchange
 //

@@ -11,8 +11,8 @@
 // CDNA4 design:
 // * One v_mfma_f32_16x16x32_bf16 computes a 16(m) x 16(n) tile over 32 k.
 //   A = activations (rows m >= M repeat row M-1 and are never stored),
-//   B = weights as exact bf16 values 128+q (2/4-bit) or q (8-bit, two code
-//   dwords per MFMA step).  A workgroup owns NT tiles of
+//   B = weights as exact bf16 code values q (2/4-bit: one code dword per
+//   step or half-step; 8-bit: two code dwords per MFMA step).  A workgroup owns NT tiles of
 //   16 output columns over the whole of K; its waves split K into
 //   contiguous slices of "bias blocks" (4 groups).
 // * Lane (col = lane%16, kb = lane/16) needs 16 contiguous bytes of row
@@ -26,10 +26,13 @@
 //   quantization group.
 // * The group's partial product is accumulated by gs/32 MFMAs and folded with
 //   the group scale once: acc += s * acc_g (4 FMAs per lane per group).
-// * Bias and the 128 code offset: sum_g (b - 128 s)[n,g] * xsum[m,g] over the
-//   4 groups of a block is one v_mfma_f32_16x16x4_f32, with the per-group
-//   activation sums xsum (dot2 against ones, then a row transpose-reduce)
-//   formed while the codes are still in flight.
+// * Bias through the group's integer zero point z = round(-b/s)
+//   (zero_point): each step also runs the MFMA with B = z in every slot of
+//   the column and with B = bf16 ones, and the group is folded as
+//   acc += s * (P_codes - P_z) + b' * P_ones, b' = b + z*s.  A group whose
+//   weights are all exactly zero gives P_codes == P_z bit for bit (the same
+//   operands) and b' == 0, so it adds exactly 0 whatever z; elsewhere the
+//   difference is between products of the size of the weights' codes.
 // * Partial tiles of the waves are summed through LDS in slice order
 //   (deterministic, no atomics) and rows m < M are stored.
 // * Fused residual sum (ADD, "metal : few-row MMA mat-mul and batched copies

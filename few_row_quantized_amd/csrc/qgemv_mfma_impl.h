@@ -74,7 +74,9 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   const int kb = lane >> 4;
   const int NBLK = K / BLKW;
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-  const uint32_t offset_pair = opaque_u32(kOffsetPair);
+  // B operand of bf16 ones: the MFMA steps run on it give the group sums of
+  // the activations in the output layout
+  const bf16x8_t ones8 = __builtin_bit_cast(bf16x8_t, u32x4_t{kOnesPair, kOnesPair, kOnesPair, kOnesPair});
   // element offset, within a super-chunk, of the codes register i holds in
   // this lane's row after the partial transpose
 
@@ -273,6 +275,7 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   f32x4_t acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = zero4;
+  constexpr int ZMAX = (1 << BITS) - 1;  // largest code
 
   for (int blk0 = b_begin; blk0 < b_end; blk0 += BPB) {
     const int nb = min(BPB, b_end - blk0);  // blocks in this batch (uniform)
@@ -327,10 +330,9 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     // scheduler may sink later loads below the first waits and serialize them
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- activation work, overlapping the code loads: re-pair x to the
-    // code pairing and form the per-group activation sums.  xsum of group
-    // g0 + j ends up in row j of this lane's column, i.e. in the A layout of
-    // v_mfma_f32_16x16x4_f32 for the bias product.
+    // ---- activation work, overlapping the code loads: move x to the operand
+    // lanes (quad-row loads) and re-pair 2/4-bit activations to the code
+    // pairing (8-bit codes and FP elements keep the memory order)
     if (xquad) {
 #pragma unroll
       for (int u = 0; u < UNR; ++u)
@@ -339,47 +341,13 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
 #pragma unroll
           for (int l = 0; l < HS; ++l) xv[u][i][l] = to_operand_lanes(xv[u][i][l]);
     }
-    float xsum[BPB];
+    if constexpr (HAS_BIAS && BITS != 8) {
 #pragma unroll
-    for (int bb = 0; bb < BPB; ++bb) {
-      float P[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < UNR; ++u)
 #pragma unroll
-      for (int uu = 0; uu < BSC; ++uu) {
-        const int u = bb * BSC + uu;
-        if constexpr (!HAS_BIAS) continue;  // FP formats: natural order, no bias sums
-        if constexpr (BITS == 8) {
-          // natural order: only the group sums; step e of the super-chunk
-          // holds 8 codes of group (uu*SCW + 32e)/GS of the block
+        for (int i = 0; i < XR; ++i)
 #pragma unroll
-          for (int e = 0; e < XR; ++e) {
-            const int j = (uu * SCW + 32 * e) / GS;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) P[j] = dot2_bf16(xv[u][e][0][c], 0x3F803F80u, P[j]);
-          }
-          continue;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = uu * GPS + i / REGS_G;  // group within the block
-#pragma unroll
-          for (int l = 0; l < HS; ++l)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) P[j] = dot2_bf16(xv[u][i][l][e], 0x3F803F80u, P[j]);
-          if constexpr (BITS == 4) {
-            const uint32_t X[4] = {xv[u][i][0][0], xv[u][i][0][1], xv[u][i][0][2], xv[u][i][0][3]};
-            xv[u][i][0] = u32x4_t{xpair_stride4(X, 0), xpair_stride4(X, 1), xpair_stride4(X, 2),
-                                  xpair_stride4(X, 3)};
-          } else {
-            const uint32_t X[8] = {xv[u][i][0][0], xv[u][i][0][1], xv[u][i][0][2], xv[u][i][0][3],
-                                   xv[u][i][1][0], xv[u][i][1][1], xv[u][i][1][2], xv[u][i][1][3]};
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-              xv[u][i][h] = u32x4_t{xpair_stride8(X, 4 * h + 0), xpair_stride8(X, 4 * h + 1),
-                                    xpair_stride8(X, 4 * h + 2), xpair_stride8(X, 4 * h + 3)};
-          }
-        }
-      }
-      if constexpr (HAS_BIAS) xsum[bb] = rows_transpose_reduce4(P);
+          for (int l = 0; l < HS; ++l) xv[u][i][l] = pair_activations<BITS>(xv[u][i][l]);
     }
 
 #pragma unroll
@@ -389,8 +357,60 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
         s4[bb][t] = to_operand_lanes(s4[bb][t]);
         if constexpr (HAS_BIAS) b4[bb][t] = to_operand_lanes(b4[bb][t]);
       }
+    // Affine groups, per tile: at the group's first step its zero point z
+    // (zero_point) becomes the B operand zq of a second MFMA chain; at its
+    // last step acc += s * (codes' product - zero point's) + b' * (sum of x),
+    // the sums from the chain against ones.  FP formats: acc += scale * product.
+    u32x4_t zq[NT];
+    float bres[NT];
+    auto group_start = [&](const int bb, const int j) {
+      if constexpr (HAS_BIAS) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const uint32_t sw = (j < 2) ? s4[bb][t].x : s4[bb][t].y;
+          const uint32_t bw = (j < 2) ? b4[bb][t].x : b4[bb][t].y;
+          const ZeroPoint zp = zero_point(half_bits_to_float((j & 1) ? (sw >> 16) : (sw & 0xFFFFu)),
+                                          half_bits_to_float((j & 1) ? (bw >> 16) : (bw & 0xFFFFu)), ZMAX);
+          zq[t] = u32x4_t{zp.zpair, zp.zpair, zp.zpair, zp.zpair};
+          bres[t] = zp.bres;
+        }
+      }
+    };
+    auto fold = [&](const int bb, const int j, const f32x4_t (&pg)[NT], const f32x4_t (&pz)[NT],
+                    const f32x4_t &xg) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if constexpr (HAS_BIAS) {
+          const uint32_t sw = (j < 2) ? s4[bb][t].x : s4[bb][t].y;
+          const float sc = half_bits_to_float((j & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(sc, pg[t][q] - pz[t][q], fmaf(bres[t], xg[q], acc[t][q]));
+        } else {
+          const float sc = fp_scale_to_float<FMT>(s4[bb][t].x >> (8 * j));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(sc, pg[t][q], acc[t][q]);
+        }
+      }
+    };
+    // one step of a group: codes (B = bw[t]), zero points and ones against A
+    auto step = [&](const bf16x8_t &a, const u32x4_t (&bw)[NT], const bool gfirst, f32x4_t (&pg)[NT],
+                    f32x4_t (&pz)[NT], f32x4_t &xg) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        pg[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bw[t]),
+                                                        gfirst ? zero4 : pg[t], 0, 0, 0);
+      if constexpr (HAS_BIAS) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          pz[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, zq[t]),
+                                                          gfirst ? zero4 : pz[t], 0, 0, 0);
+        xg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ones8, gfirst ? zero4 : xg, 0, 0, 0);
+      }
+    };
     // ---- codes, super-chunk by super-chunk in load order
-    f32x4_t accg[NT];
+    f32x4_t accg[NT], accz[NT], accx = zero4;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) accz[t] = zero4;
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       if (u / BSC >= nb) break;
@@ -411,32 +431,19 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
           const bool gfirst = kk % GS == 0;
           const bool glast = (kk + 32) % GS == 0;
           const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xv[u][e][0]);
+          if (gfirst) group_start(u / BSC, j);
+          u32x4_t bw[NT];
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
-            u32x4_t bw;
             if constexpr (FMT == kMxfp8) {
-              bw = u32x4_t{fp8_pair<false>(cur[t][2 * e]), fp8_pair<true>(cur[t][2 * e]),
-                           fp8_pair<false>(cur[t][2 * e + 1]), fp8_pair<true>(cur[t][2 * e + 1])};
+              bw[t] = u32x4_t{fp8_pair<false>(cur[t][2 * e]), fp8_pair<true>(cur[t][2 * e]),
+                              fp8_pair<false>(cur[t][2 * e + 1]), fp8_pair<true>(cur[t][2 * e + 1])};
             } else {
-              bw = unpack8_quad(cur[t][2 * e], cur[t][2 * e + 1]);
-            }
-            accg[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                a, __builtin_bit_cast(bf16x8_t, bw), gfirst ? zero4 : accg[t], 0, 0, 0);
-          }
-          if (glast) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-              float sc;
-              if constexpr (HAS_BIAS) {
-                const uint32_t sw = (j < 2) ? s4[u / BSC][t].x : s4[u / BSC][t].y;
-                sc = half_bits_to_float((j & 1) ? (sw >> 16) : (sw & 0xFFFFu));
-              } else {
-                sc = fp_scale_to_float<FMT>(s4[u / BSC][t].x >> (8 * j));
-              }
-#pragma unroll
-              for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(sc, accg[t][q], acc[t][q]);
+              bw[t] = unpack8_quad(cur[t][2 * e], cur[t][2 * e + 1]);
             }
           }
+          step(a, bw, gfirst, accg, accz, accx);
+          if (glast) fold(u / BSC, j, accg, accz, accx);
         }
       }
       if constexpr (FMT == kNvfp4) {
@@ -466,47 +473,22 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
           const bool gfirst = (i % REGS_G) == 0 && h == 0;
           const bool glast = (i % REGS_G) == REGS_G - 1 && h == HS - 1;
           const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xv[u][i][h]);
+          if (gfirst) group_start(u / BSC, j);
+          u32x4_t bw[NT];
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
-            u32x4_t bw;
             if constexpr (FMT == kMxfp4) {
               // 8 elements of one dword, natural order
-              bw = u32x4_t{fp4_pair<0>(cur[t][i]), fp4_pair<1>(cur[t][i]), fp4_pair<2>(cur[t][i]),
-                           fp4_pair<3>(cur[t][i])};
+              bw[t] = u32x4_t{fp4_pair<0>(cur[t][i]), fp4_pair<1>(cur[t][i]), fp4_pair<2>(cur[t][i]),
+                              fp4_pair<3>(cur[t][i])};
             } else if constexpr (BITS == 4) {
-              bw = unpack4_split_quad(cur[t][i], offset_pair);
+              bw[t] = unpack4_quad(cur[t][i]);
             } else {
-              bw = unpack2_split_quad(cur[t][i], h, offset_pair);
-            }
-            accg[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                a, __builtin_bit_cast(bf16x8_t, bw), gfirst ? zero4 : accg[t], 0, 0, 0);
-          }
-          if (glast) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-              float sc;
-              if constexpr (HAS_BIAS) {
-                const uint32_t sw = (j < 2) ? s4[u / BSC][t].x : s4[u / BSC][t].y;
-                sc = half_bits_to_float((j & 1) ? (sw >> 16) : (sw & 0xFFFFu));
-              } else {
-                sc = fp_scale_to_float<FMT>(s4[u / BSC][t].x >> (8 * j));
-              }
-#pragma unroll
-              for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(sc, accg[t][q], acc[t][q]);
+              bw[t] = unpack2_quad(cur[t][i], h);
             }
           }
-        }
-      }
-      if (HAS_BIAS && scb == BSC - 1) {
-        // bias with the 128 offset: acc += xsum[m][g0+kb] * (b - 128 s)[n][g0+kb]
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const uint32_t sw = (kb < 2) ? s4[u / BSC][t].x : s4[u / BSC][t].y;
-          const uint32_t bw = (kb < 2) ? b4[u / BSC][t].x : b4[u / BSC][t].y;
-          const float sc = half_bits_to_float((kb & 1) ? (sw >> 16) : (sw & 0xFFFFu));
-          const float b = half_bits_to_float((kb & 1) ? (bw >> 16) : (bw & 0xFFFFu));
-          const float bo = BITS == 8 ? b : fmaf(-128.f, sc, b);  // 2/4-bit: remove the 128 offset
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum[u / BSC], bo, acc[t], 0, 0, 0);
+          step(a, bw, gfirst, accg, accz, accx);
+          if (glast) fold(u / BSC, j, accg, accz, accx);
         }
       }
     }

@@ -13,9 +13,8 @@
 //   contiguous range of 16-column tiles [g*T/G, (g+1)*T/G) over the whole of K.
 // * Its W waves split K into bias blocks (4 groups): wave w owns the blocks
 //   vw, vw+W, ... (vw = w rotated per workgroup) for every tile, so its
-//   activation operands and the per-group activation sums of the bias term
-//   are loaded, re-paired and summed once and then stay in registers while
-//   the workgroup walks its tiles.
+//   activation operands are loaded and re-paired once and then stay in
+//   registers while the workgroup walks its tiles.
 // * Codes and group metadata of the next tile are prefetched into a ring of
 //   S register slots while the current tile is unpacked and multiplied, so a
 //   CU keeps weight bytes in flight from its first tile to its last.
@@ -27,8 +26,8 @@
 //   is loaded when their first tile starts and added in the store, so
 //   y = fl(product + r), bit for bit the plain call and a separate fp32 add.
 // The inner MFMA step (code layout, partial lane transpose, unpack to exact
-// bf16 128+q, per-group scale fold, bias product by v_mfma_f32_16x16x4_f32)
-// is the one of the single-pass kernel.
+// bf16 q, per-group scale fold, bias through the zero point and the MFMA of
+// the activations against bf16 ones) is the one of the single-pass kernel.
 
 #include "qgemv_device.h"
 #include "qgemv_internal.h"
@@ -80,7 +79,8 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   const size_t RB = (size_t)K * BITS / 8;
   const int NG = K / GS;
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-  const uint32_t offset_pair = opaque_u32(kOffsetPair);
+  const bf16x8_t ones8 = __builtin_bit_cast(bf16x8_t, u32x4_t{kOnesPair, kOnesPair, kOnesPair, kOnesPair});
+  constexpr int ZMAX = (1 << BITS) - 1;  // largest code
   // activation loads in the quad-row layout once several rows are distinct
   // (results do not depend on the choice; from M = 5 for every group size
   // here: 27B q at M = 7, 9.44 -> 8.91 us)
@@ -107,11 +107,9 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   }
 
   // ---- activations of the owned blocks (rows m >= M read row M-1: their
-  // outputs are never stored), later re-paired to the code pairing and
-  // summed per group into the A layout of the bias MFMA
+  // outputs are never stored), later re-paired to the code pairing
   const uint16_t *xr = x + (size_t)min(xquad ? (lane >> 2) : col, M - 1) * K;
   u32x4_t xv[BPW][BSC][4][HS];
-  float xsum[BPW];
 #pragma unroll
   for (int k = 0; k < BPW; ++k)
 #pragma unroll
@@ -173,35 +171,13 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   }
 
 #pragma unroll
-  for (int k = 0; k < BPW; ++k) {
-    float P[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < BPW; ++k)
 #pragma unroll
-    for (int u = 0; u < BSC; ++u) {
+    for (int u = 0; u < BSC; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = u * GPS + i / REGS_G;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int l = 0; l < HS; ++l)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) P[j] = dot2_bf16(xv[k][u][i][l][e], 0x3F803F80u, P[j]);
-        if constexpr (BITS == 4) {
-          const uint32_t X[4] = {xv[k][u][i][0][0], xv[k][u][i][0][1], xv[k][u][i][0][2],
-                                 xv[k][u][i][0][3]};
-          xv[k][u][i][0] = u32x4_t{xpair_stride4(X, 0), xpair_stride4(X, 1), xpair_stride4(X, 2),
-                                   xpair_stride4(X, 3)};
-        } else {
-          const uint32_t X[8] = {xv[k][u][i][0][0], xv[k][u][i][0][1], xv[k][u][i][0][2],
-                                 xv[k][u][i][0][3], xv[k][u][i][1][0], xv[k][u][i][1][1],
-                                 xv[k][u][i][1][2], xv[k][u][i][1][3]};
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-            xv[k][u][i][h] = u32x4_t{xpair_stride8(X, 4 * h + 0), xpair_stride8(X, 4 * h + 1),
-                                     xpair_stride8(X, 4 * h + 2), xpair_stride8(X, 4 * h + 3)};
-        }
-      }
-    }
-    xsum[k] = rows_transpose_reduce4(P);
-  }
+        for (int l = 0; l < HS; ++l) xv[k][u][i][l] = pair_activations<BITS>(xv[k][u][i][l]);
 
   // ---- groups of S tile steps (the unrolled ring); a range always has a
   // tile (do-while: no guard branch that would let the compiler sink the
@@ -239,7 +215,11 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
 #pragma unroll
       for (int k = 0; k < BPW; ++k) {
         if (!own[k]) continue;  // uniform per wave
-        f32x4_t accg;
+        // codes', zero point's and ones' products of the current group (see
+        // the single-pass kernel)
+        f32x4_t accg, accz, accx;
+        u32x4_t zq;
+        float bres;
 #pragma unroll
         for (int u = 0; u < BSC; ++u) {
           uint32_t cur[4];
@@ -252,30 +232,30 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
             for (int h = 0; h < HS; ++h) {
               const bool gfirst = (i % REGS_G) == 0 && h == 0;
               const bool glast = (i % REGS_G) == REGS_G - 1 && h == HS - 1;
-              u32x4_t bw;
-              if constexpr (BITS == 4) {
-                bw = unpack4_split_quad(cur[i], offset_pair);
-              } else {
-                bw = unpack2_split_quad(cur[i], h, offset_pair);
+              const uint32_t sw = (jg < 2) ? s4[s][k].x : s4[s][k].y;
+              const float scl = half_bits_to_float((jg & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+              if (gfirst) {
+                const uint32_t bw16 = (jg < 2) ? b4[s][k].x : b4[s][k].y;
+                const ZeroPoint zp =
+                    zero_point(scl, half_bits_to_float((jg & 1) ? (bw16 >> 16) : (bw16 & 0xFFFFu)), ZMAX);
+                zq = u32x4_t{zp.zpair, zp.zpair, zp.zpair, zp.zpair};
+                bres = zp.bres;
               }
-              accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(bf16x8_t, xv[k][u][i][h]), __builtin_bit_cast(bf16x8_t, bw),
-                  gfirst ? zero4 : accg, 0, 0, 0);
+              const u32x4_t bw = BITS == 4 ? unpack4_quad(cur[i]) : unpack2_quad(cur[i], h);
+              const bf16x8_t a8 = __builtin_bit_cast(bf16x8_t, xv[k][u][i][h]);
+              accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, __builtin_bit_cast(bf16x8_t, bw),
+                                                            gfirst ? zero4 : accg, 0, 0, 0);
+              accz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, __builtin_bit_cast(bf16x8_t, zq),
+                                                            gfirst ? zero4 : accz, 0, 0, 0);
+              accx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, ones8, gfirst ? zero4 : accx, 0, 0, 0);
               if (glast) {
-                const uint32_t sw = (jg < 2) ? s4[s][k].x : s4[s][k].y;
-                const float scl = half_bits_to_float((jg & 1) ? (sw >> 16) : (sw & 0xFFFFu));
 #pragma unroll
-                for (int q = 0; q < 4; ++q) acc[q] = fmaf(scl, accg[q], acc[q]);
+                for (int q = 0; q < 4; ++q)
+                  acc[q] = fmaf(scl, accg[q] - accz[q], fmaf(bres, accx[q], acc[q]));
               }
             }
           }
         }
-        // bias with the 128 offset: acc += xsum[m][g0+kb] * (b - 128 s)[n][g0+kb]
-        const uint32_t sw = (kb < 2) ? s4[s][k].x : s4[s][k].y;
-        const uint32_t bw = (kb < 2) ? b4[s][k].x : b4[s][k].y;
-        const float scl = half_bits_to_float((kb & 1) ? (sw >> 16) : (sw & 0xFFFFu));
-        const float b = half_bits_to_float((kb & 1) ? (bw >> 16) : (bw & 0xFFFFu));
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum[k], fmaf(-128.f, scl, b), acc, 0, 0, 0);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[s][wave][i][lane] = acc[i];

@@ -8,15 +8,10 @@ namespace qgemv {
 
 namespace {
 
-// Extract q from a bf16 pair half 0x4300|q; anything else marks an encoding error.
+// Extract q from a bf16 pair half that should hold the exact value q;
+// anything else marks an encoding error (0xFF: outside the 2- and 4-bit
+// ranges, and for 8-bit codes an error shows wherever the code is not 255).
 __device__ __forceinline__ uint8_t code_of(uint32_t half16) {
-  return ((half16 & 0xFF80u) == 0x4300u) ? (uint8_t)(half16 & 0x7Fu) : (uint8_t)0xFF;
-}
-
-// Extract q from a bf16 pair half that should hold the exact value q
-// (8-bit codes); anything else marks an encoding error (0xFF, which a true
-// code 255 shares: such an error shows only where the code is not 255).
-__device__ __forceinline__ uint8_t code8_of(uint32_t half16) {
   const float f = bf16_bits_to_float(half16);
   return (f >= 0.f && f <= 255.f && f == (float)(int)f) ? (uint8_t)(int)f : (uint8_t)0xFF;
 }
@@ -43,24 +38,26 @@ __global__ __launch_bounds__(256) void unpack_probe_dot(const uint8_t *__restric
       unpack8_pairs(cd[d], p);  // pairs (4d, 4d+1), (4d+2, 4d+3)
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        qr[4 * d + 2 * e] = code8_of(p[e] & 0xFFFFu);
-        qr[4 * d + 2 * e + 1] = code8_of(p[e] >> 16);
+        qr[4 * d + 2 * e] = code_of(p[e] & 0xFFFFu);
+        qr[4 * d + 2 * e + 1] = code_of(p[e] >> 16);
       }
     } else if constexpr (BITS == 4) {
       uint32_t p[4];
-      unpack4_split_pairs(cd[d], p);
+      unpack4_pairs(cd[d], p);  // pair e: codes 8d + 4(e/2) + e%2 and that + 2
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        qr[8 * d + e] = code_of(p[e] & 0xFFFFu);
-        qr[8 * d + e + 4] = code_of(p[e] >> 16);
+        const int k = 8 * d + 4 * (e >> 1) + (e & 1);
+        qr[k] = code_of(p[e] & 0xFFFFu);
+        qr[k + 2] = code_of(p[e] >> 16);
       }
     } else {
       uint32_t p[8];
-      unpack2_split_pairs(cd[d], p);
+      unpack2_pairs(cd[d], p);  // pair j: codes 16d + 8(j/4) + j%4 and that + 4
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        qr[16 * d + e] = code_of(p[e] & 0xFFFFu);
-        qr[16 * d + e + 8] = code_of(p[e] >> 16);
+      for (int j = 0; j < 8; ++j) {
+        const int k = 16 * d + 8 * (j >> 2) + (j & 3);
+        qr[k] = code_of(p[j] & 0xFFFFu);
+        qr[k + 4] = code_of(p[j] >> 16);
       }
     }
   }
@@ -91,7 +88,6 @@ __global__ __launch_bounds__(64) void unpack_probe_mfma(const uint8_t *__restric
   transpose_rows_lvl<LVL>(r);  // all lanes take part, also those past row N
   if (tile * 16 + col >= N) return;
   uint8_t *qr = q + (size_t)n * K + (size_t)sc * SCW;
-  const uint32_t off = kOffsetPair;
   if constexpr (BITS == 8) {
     // MFMA step e: registers 2e, 2e+1 = 8 consecutive codes from k0(2e)
 #pragma unroll
@@ -100,8 +96,8 @@ __global__ __launch_bounds__(64) void unpack_probe_mfma(const uint8_t *__restric
       const u32x4_t p = unpack8_quad(r[2 * e], r[2 * e + 1]);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        qr[k0 + 2 * c] = code8_of(p[c] & 0xFFFFu);
-        qr[k0 + 2 * c + 1] = code8_of(p[c] >> 16);
+        qr[k0 + 2 * c] = code_of(p[c] & 0xFFFFu);
+        qr[k0 + 2 * c + 1] = code_of(p[c] >> 16);
       }
     }
     return;
@@ -110,20 +106,21 @@ __global__ __launch_bounds__(64) void unpack_probe_mfma(const uint8_t *__restric
   for (int i = 0; i < 4; ++i) {
     const int k0 = lvl_chunk<LVL>(i, kb) * CW + lvl_dword<LVL>(i, kb) * DW;
     if constexpr (BITS == 4) {
-      const u32x4_t p = unpack4_split_quad(r[i], off);  // pair e: codes k0+e, k0+e+4
+      const u32x4_t p = unpack4_quad(r[i]);  // pair e: codes k0 + 4(e/2) + e%2 and that + 2
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        qr[k0 + e] = code_of(p[e] & 0xFFFFu);
-        qr[k0 + e + 4] = code_of(p[e] >> 16);
+        const int k = k0 + 4 * (e >> 1) + (e & 1);
+        qr[k] = code_of(p[e] & 0xFFFFu);
+        qr[k + 2] = code_of(p[e] >> 16);
       }
     } else {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const u32x4_t p = unpack2_split_quad(r[i], h, off);  // pair e: codes k0+4h+e, +8
+        const u32x4_t p = unpack2_quad(r[i], h);  // pair e: codes k0 + 8h + e and that + 4
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          qr[k0 + 4 * h + e] = code_of(p[e] & 0xFFFFu);
-          qr[k0 + 4 * h + e + 8] = code_of(p[e] >> 16);
+          qr[k0 + 8 * h + e] = code_of(p[e] & 0xFFFFu);
+          qr[k0 + 8 * h + e + 4] = code_of(p[e] >> 16);
         }
       }
     }

@@ -251,16 +251,36 @@ def custom_fp_shape(K: int, N: int, fmt: str, m_values: Sequence[int] = (1,), se
 
 
 def special_problem(K: int, N: int, bits: int, group_size: int, M: int, kind: str,
-                    seed: int = 7) -> Problem:
+                    seed: int = 7, outliers: bool = False) -> Problem:
     """Structured inputs with closed-form results.
 
     kind = "zero_codes": every code 0 (w = bias).
     kind = "unit_scale_onehot": scale 1.0, bias 0.0, random codes, x row m = e_{k_m}
       (one-hot at column k_m = (m * 37 + 5) % K); then y[m, n] = q[n, k_m] exactly.
+    kind = "zero_weights": every code of row n equals the zero point z_n = n mod 2^bits
+      (rows cycle through all code values) and b = -z_n * s exactly: each scale is
+      drawn as usual, then rounded to the 11 - bitlength(z_n) significant bits that
+      keep z_n * s exact in fp16.  Every weight dequantizes to exactly 0, so
+      y[m, n] = 0 (x keeps its outlier channels when `outliers`).
     """
-    shape = custom_shape(K, N, bits, group_size, (M,), seed=seed, name=f"{kind}_k{K}_n{N}")
+    shape = custom_shape(K, N, bits, group_size, (M,), seed=seed, name=f"{kind}_k{K}_n{N}",
+                         outliers=outliers)
     p = make_problem(shape, m_max=M, seed=seed)
-    if kind == "zero_codes":
+    if kind == "zero_weights":
+        z = np.arange(N, dtype=np.int64) % (1 << bits)
+        per_byte = 8 // bits
+        byte = np.zeros(N, dtype=np.int64)
+        for j in range(per_byte):
+            byte |= z << (bits * j)
+        p.codes[:] = byte.astype(np.uint8)[:, None]
+        s = p.scales.view(np.float16).astype(np.float64)
+        keep = 11 - np.array([int(v).bit_length() for v in z])  # significant bits of s
+        mant, expo = np.frexp(s)
+        s = np.ldexp(np.round(np.ldexp(mant, keep[:, None])), expo - keep[:, None])
+        p.scales[:] = f64_to_fp16_bits(s)
+        p.biases[:] = f64_to_fp16_bits(-z[:, None] * s)
+        assert np.array_equal(p.biases.view(np.float16).astype(np.float64), -z[:, None] * s)
+    elif kind == "zero_codes":
         p.codes[:] = 0
     elif kind == "unit_scale_onehot":
         p.scales[:] = np.float16(1.0).view(np.uint16)

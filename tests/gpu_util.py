@@ -36,11 +36,53 @@ class DeviceProblem:
         return self.run(M, path).cpu().numpy()
 
 
-def sample_columns(N: int, count: int, seed: int = 0) -> np.ndarray:
-    """Spread of output columns for sampled checks: both ends, every tile
-    edge near them, and random columns."""
-    rng = np.random.default_rng(seed)
-    fixed = {0, 1, 15, 16, 17, 31, N // 2, N - 17, N - 16, N - 2, N - 1}
-    fixed = {c for c in fixed if 0 <= c < N}
-    rest = rng.choice(N, size=min(count, N), replace=False)
-    return np.array(sorted(fixed | set(int(c) for c in rest)))
+class OracleRows:
+    """The fp64 oracle's y and sum|x*w| for the first rows of a problem,
+    computed once; rows of the oracle do not depend on how many are asked
+    for (a pinned invariant), so an M-row call is checked against the first M
+    rows (for the gathered product: the first pairs)."""
+
+    def __init__(self, ref: np.ndarray, absum: np.ndarray, cols=None):
+        self.ref, self.absum, self.cols = ref, absum, cols
+
+    @classmethod
+    def affine(cls, p, m_max: int, cols=None):
+        import oracle
+        ref = oracle.qgemv_reference(p.codes, p.scales, p.biases, p.x, m_max, p.N, p.K, p.bits,
+                                     p.group_size, rows=cols)
+        absum = oracle.abs_product_sum(p.codes, p.scales, p.biases, p.x, m_max, p.N, p.K, p.bits,
+                                       p.group_size, rows=cols)
+        return cls(ref, absum, cols)
+
+    @classmethod
+    def fp(cls, p, m_max: int, cols=None):
+        import oracle
+        fmt = p.shape.fmt
+        ref = oracle.qgemv_fp_reference(p.codes, p.scales, p.x, m_max, p.N, p.K, fmt, rows=cols)
+        absum = oracle.fp_abs_product_sum(p.codes, p.scales, p.x, m_max, p.N, p.K, fmt, rows=cols)
+        return cls(ref, absum, cols)
+
+    @classmethod
+    def gather(cls, p, x_idx, e_idx, cols=None):
+        import oracle
+        s = p.shape
+        ref = oracle.qgemv_gather_reference(p.codes, p.scales, p.biases, p.x, x_idx, e_idx, s.N, s.K,
+                                            s.bits, s.group_size, rows=cols)
+        absum = oracle.gather_abs_product_sum(p.codes, p.scales, p.biases, p.x, x_idx, e_idx, s.N,
+                                              s.K, s.bits, s.group_size, rows=cols)
+        return cls(ref, absum, cols)
+
+    def check(self, y: np.ndarray, M: int, label: str = "", residual=None) -> float:
+        """Every element (of the selected columns) of the first M rows within
+        the tolerance; with a residual r, within the fused sum's bar
+        1e-3*S + 1e-6 + 2^-23*(|r| + S).  Returns the worst |dy|/tol."""
+        import oracle
+        yy = y if self.cols is None else y[:, self.cols]
+        ref, absum = self.ref[:M], self.absum[:M]
+        if residual is None:
+            ok, worst, idx = oracle.check_close(yy, ref, absum)
+        else:
+            r = residual[:M] if self.cols is None else residual[:M][:, self.cols]
+            ok, worst, idx = oracle.check_close(yy, ref + r.astype(np.float64), absum, residual_abs=r)
+        assert ok, f"{label}: worst |dy|/tol = {worst:.3g} at {idx}"
+        return worst

@@ -19,7 +19,7 @@ import oracle
 from few_row_quantized_amd import qgemv as q
 from few_row_quantized_amd import synth
 
-from gpu_util import sample_columns, say
+from gpu_util import OracleRows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -220,18 +220,18 @@ FULL = [(n, s.m_values) for n, s in synth.WORKLOADS.items() if s.fmt is not None
 
 
 @pytest.mark.parametrize("name,ms", FULL)
-def test_full_size_sampled_columns(name, ms):
+def test_full_size_every_element(name, ms):
     import torch
     s = synth.WORKLOADS[name]
     p = synth.make_problem(s)
     d = FpDevice(p)
-    cols = sample_columns(s.N, 96, seed=s.seed)
+    orc = OracleRows.fp(p, max(ms))
     for path in paths_for(p):
         for M in ms:
             say(f"fp full {name} {path} M={M}")
             y = d.run(M, path)
             assert np.all(np.isfinite(y))
-            check(p, y, M, cols=cols, label=f"{name} {path} M={M}")
+            orc.check(y, M, label=f"{name} {path} M={M}")
     say(f"fp full unpack {name}")
     for path in ("dot", "mfma"):
         if not q.qgemv_path_supported_fp(path, 1, s.N, s.K, s.fmt):

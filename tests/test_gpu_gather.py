@@ -1,8 +1,8 @@
 """GPU parity of the gathered (MoE) verify, qgemv_gather, through the C ABI
 against the fp64 oracle.
 
-Bars: every element within 1e-3 * sum|x w| + 1e-6 of the oracle (sampled
-columns at full size); each pair's row bitwise equal to the dense MFMA path's
+Bars: every element within 1e-3 * sum|x w| + 1e-6 of the oracle, full
+sizes included; each pair's row bitwise equal to the dense MFMA path's
 M=1 result on that (row, expert) (same kernel body and reduction order);
 repeated calls bitwise identical; pairs with invalid indices leave their row
 of y untouched.
@@ -14,7 +14,7 @@ import oracle
 from few_row_quantized_amd import qgemv as q
 from few_row_quantized_amd import synth
 
-from gpu_util import sample_columns, say
+from gpu_util import OracleRows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -121,17 +121,20 @@ def test_pair_rows_equal_the_dense_mfma_path_bitwise_and_repeat():
 
 
 @pytest.mark.parametrize("name", list(synth.MOE_WORKLOADS))
-def test_full_size_sampled_columns(name):
+def test_full_size_every_element(name):
+    # pairs(M) are the first 8*M pairs of pairs(16): one oracle evaluation
     s = synth.MOE_WORKLOADS[name]
     p = synth.make_moe_problem(s)
     d = MoeDevice(p)
-    cols = sample_columns(s.N, 64, seed=s.seed)
-    for M in (1, 4, 8, 16):
+    xa, ea = p.pairs(16)
+    orc = OracleRows.gather(p, xa, ea)
+    for M in (1, 2, 4, 8, 16):
         x_idx, e_idx = p.pairs(M)
+        assert np.array_equal(x_idx, xa[:len(x_idx)]) and np.array_equal(e_idx, ea[:len(e_idx)])
         say(f"gather full {name} M={M} pairs={len(e_idx)} union={len(set(e_idx.tolist()))}")
         y = d.run(x_idx, e_idx)
         assert np.all(np.isfinite(y))
-        check(p, y, x_idx, e_idx, cols=cols, label=f"{name} M={M}")
+        orc.check(y, len(e_idx), label=f"{name} M={M}")
 
 
 def test_full_size_pair_rows_equal_the_dense_mfma_path_bitwise():

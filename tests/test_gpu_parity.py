@@ -14,7 +14,7 @@ import oracle
 from few_row_quantized_amd import qgemv as q
 from few_row_quantized_amd import synth
 
-from gpu_util import DeviceProblem, sample_columns, say
+from gpu_util import DeviceProblem, OracleRows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -149,7 +149,7 @@ PERSIST = [
 
 # Long K with the activations of half of K in LDS, at sizes where the LDS
 # holds a whole half only up to M = 7 to 10: larger M restages the
-# activations in two or three phases per half.  Sampled columns.
+# activations in two or three phases per half.
 LONG_K_LDS = [(12288, 4104, 4, 64), (12288, 4100, 4, 32), (17408, 4128, 2, 64), (17408, 4200, 4, 128)]
 
 
@@ -163,13 +163,13 @@ def test_many_tiles_per_cu_every_element(K, N, bits, gs):
 
 
 @pytest.mark.parametrize("K,N,bits,gs", LONG_K_LDS)
-def test_long_k_lds_persistent_sampled_columns(K, N, bits, gs):
+def test_long_k_lds_persistent_every_element(K, N, bits, gs):
     p = synth.make_problem(synth.custom_shape(K, N, bits, gs, seed=9 * K + N, outliers=True), m_max=16)
     d = DeviceProblem(p)
-    cols = sample_columns(N, 96, seed=K + N)
+    orc = OracleRows.affine(p, 16)
     for M in (1, 2, 7, 8, 9, 16):
         say(f"long K lds mfma K={K} N={N} bits={bits} gs={gs} M={M}")
-        check_y(p, d.run_host(M, "mfma"), M, cols=cols, label=f"mfma K={K} N={N} M={M}")
+        orc.check(d.run_host(M, "mfma"), M, label=f"mfma K={K} N={N} M={M}")
 
 
 @pytest.mark.parametrize("path", ["dot", "mfma"])
@@ -219,24 +219,21 @@ def test_repeated_calls_are_bitwise_identical(path, name):
     assert np.array_equal(a, b)
 
 
-# ---------------------------------------------------------------- full sizes, sampled columns
+# ---------------------------------------------------------------- full sizes, every element
 
-FULL_CASES = []
-for _name, _s in synth.WORKLOADS.items():
-    if _name.startswith("tiny") or _s.fmt is not None:
-        continue
-    ms = list(_s.m_values)
-    if len(ms) > 6:
-        ms = sorted(set([ms[0], ms[1], 4, 5, 8, ms[-1]]) & set(ms))
-    FULL_CASES.append((_name, tuple(ms)))
+FULL_CASES = [(_n, tuple(_s.m_values)) for _n, _s in synth.WORKLOADS.items()
+              if not _n.startswith("tiny") and _s.fmt is None]
 
 
 @pytest.mark.parametrize("name,ms", FULL_CASES)
-def test_full_size_sampled_columns(name, ms):
+def test_full_size_every_element(name, ms):
+    # one oracle evaluation at the largest M; every element of every M, on
+    # both paths and the dispatcher (the bench's launch configuration)
     s = synth.WORKLOADS[name]
     p = synth.make_problem(s)
     d = DeviceProblem(p)
-    cols = sample_columns(s.N, 96, seed=s.seed)
+    orc = OracleRows.affine(p, max(ms))
+    worst = 0.0
     for path in PATHS:
         if not supported(path, p):
             continue
@@ -244,7 +241,8 @@ def test_full_size_sampled_columns(name, ms):
             say(f"full {name} {path} M={M}")
             y = d.run_host(M, path)
             assert np.all(np.isfinite(y)), "non-finite output"
-            check_y(p, y, M, cols=cols, label=f"{name} {path} M={M}")
+            worst = max(worst, orc.check(y, M, label=f"{name} {path} M={M}"))
+    say(f"full {name}: worst |dy|/tol = {worst:.3g}")
 
 
 def test_auto_path_matches_select():

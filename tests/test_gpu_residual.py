@@ -3,7 +3,7 @@ qgemv_run_path_add) through the C ABI.
 
 Bars:
 * every element within 1e-3 * sum|x w| + 1e-6 + 2^-23 * (|r| + sum|x w|) of
-  the fp64 oracle (sampled columns at full size);
+  the fp64 oracle, full sizes included;
 * bit for bit the plain product of the same path followed by one fp32 add
   (numpy's IEEE round-to-nearest-even add), out of place and in place -- the
   in-place call on a shape where the MFMA path splits K is held to the
@@ -17,7 +17,7 @@ import oracle
 from few_row_quantized_amd import qgemv as q
 from few_row_quantized_amd import synth
 
-from gpu_util import DeviceProblem, sample_columns, say
+from gpu_util import DeviceProblem, OracleRows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -146,13 +146,13 @@ FULL = [("square_k4096_n4096_4b_g64", (1, 4, 8)), ("layer27b_k", (1, 8, 16)),
 
 
 @pytest.mark.parametrize("name,ms", FULL)
-def test_add_full_size_sampled_columns(name, ms):
+def test_add_full_size_every_element(name, ms):
     import torch
     s = synth.WORKLOADS[name]
     p = synth.make_problem(s)
     d = DeviceProblem(p)
     r = synth.make_residual(max(ms), s.N, seed=p.seed)
-    cols = sample_columns(s.N, 64, seed=s.seed)
+    orc = OracleRows.affine(p, max(ms))
     for path in PATHS:
         if not supported(path, p):
             continue
@@ -161,7 +161,7 @@ def test_add_full_size_sampled_columns(name, ms):
             r_dev = torch.from_numpy(r[:M].copy()).to(d.device)
             y = run_add(d, M, r_dev, path).cpu().numpy()
             assert np.all(np.isfinite(y)), "non-finite output"
-            check_add(p, y, r, M, cols=cols, label=f"{name} {path} M={M}")
+            orc.check(y, M, label=f"{name} {path} M={M}", residual=r)
             assert np.array_equal(y, fp32_add(d.run_host(M, path), r[:M]))
 
 

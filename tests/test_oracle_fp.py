@@ -243,3 +243,128 @@ def test_generator_fp_distributions():
     p4 = synth.make_problem(s4, m_max=1)
     assert p4.scales.shape == (4096, 256)
     assert np.all(np.isfinite(oracle.e4m3_to_f64(p4.scales))) and (p4.scales < 0x80).all()
+
+
+# ---------------------------------------------------------------- the tolerance scale
+#
+# fp_abs_product_sum sets the bound of every FP-format parity check, so it is
+# pinned on its own: exact rational brute force with this file's decoders,
+# closed forms (a one-hot row gives |w| of one column; flipping the sign of x
+# changes nothing; with x >= 0 and w >= 0 it equals y), and planted mistakes.
+
+def exact_fp_abs(p, M):
+    fmt, K, N = p.shape.fmt, p.K, p.N
+    bits, block = synth.FP_BITS[fmt], synth.FP_BLOCK[fmt]
+    xs = [[frac_bf16(int(v)) for v in p.x[m]] for m in range(M)]
+    out = [[Fraction(0)] * N for _ in range(M)]
+    for n in range(N):
+        big = int.from_bytes(bytes(p.codes[n].tolist()), "little")
+        els = [(big >> (bits * k)) & ((1 << bits) - 1) for k in range(K)]
+        dec = frac_e2m1 if bits == 4 else frac_e4m3
+        sdec = frac_e8m0 if fmt.startswith("mx") else frac_e4m3
+        w = [sdec(int(p.scales[n, k // block])) * dec(els[k]) for k in range(K)]
+        for m in range(M):
+            out[m][n] = sum(abs(xs[m][k] * w[k]) for k in range(K))
+    return out
+
+
+def abs_sum(p, M, rows=None):
+    return oracle.fp_abs_product_sum(p.codes, p.scales, p.x, M, p.N, p.K, p.shape.fmt, rows=rows)
+
+
+@pytest.mark.parametrize("fmt,K,N,M", [("mxfp4", 64, 5, 2), ("nvfp4", 64, 4, 3), ("mxfp8", 96, 4, 2)])
+def test_abs_product_sum_matches_exact_rational(fmt, K, N, M):
+    p = synth.make_problem(synth.custom_fp_shape(K, N, fmt, seed=400 + K + N), m_max=M)
+    got = abs_sum(p, M)
+    want = exact_fp_abs(p, M)
+    for m in range(M):
+        for n in range(N):
+            assert want[m][n] > 0
+            assert abs(Fraction(got[m, n]) - want[m][n]) <= Fraction(K) * Fraction(2) ** -52 * want[m][n]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_abs_product_sum_onehot_gives_magnitude_of_one_weight(fmt):
+    K, N = 64, 5
+    p = synth.make_problem(synth.custom_fp_shape(K, N, fmt, seed=41), m_max=2)
+    bits, block = synth.FP_BITS[fmt], synth.FP_BLOCK[fmt]
+    k = 37  # second nvfp4 block of the first 32, second half of an mx block
+    p.x[:] = 0
+    p.x[0, k] = 0xC000  # -2.0: the sign of x must not matter
+    p.x[1, k] = 0x3F80  # 1.0
+    got = abs_sum(p, 2)
+    for n in range(N):
+        big = int.from_bytes(bytes(p.codes[n].tolist()), "little")
+        el = (big >> (bits * k)) & ((1 << bits) - 1)
+        dec = frac_e2m1 if bits == 4 else frac_e4m3
+        sdec = frac_e8m0 if fmt.startswith("mx") else frac_e4m3
+        w = abs(sdec(int(p.scales[n, k // block])) * dec(el))
+        assert got[0, n] == float(2 * w) and got[1, n] == float(w), (fmt, n)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_abs_product_sum_sign_and_same_sign_closed_forms(fmt):
+    K, N = 128, 6
+    p = synth.make_problem(synth.custom_fp_shape(K, N, fmt, seed=43), m_max=2)
+    base = abs_sum(p, 2)
+    # flipping the sign bit of every activation leaves every |x*w| unchanged
+    q = synth.make_problem(synth.custom_fp_shape(K, N, fmt, seed=43), m_max=2)
+    q.x ^= np.uint16(0x8000)
+    assert np.array_equal(abs_sum(q, 2), base)
+    # non-negative x and non-negative weights: the sum of |x*w| is y itself
+    bits = synth.FP_BITS[fmt]
+    if bits == 4:
+        q.codes &= np.uint8(0x77)  # clear both nibbles' sign bits
+    else:
+        q.codes &= np.uint8(0x7F)
+        q.codes[q.codes == 0x7F] = 0x7E  # keep clear of the NaN pattern
+    q.x &= np.uint16(0x7FFF)
+    y = oracle.qgemv_fp_reference(q.codes, q.scales, q.x, 2, N, K, fmt)
+    a = abs_sum(q, 2)
+    assert np.allclose(a, y, rtol=K * 2.0 ** -52, atol=0)
+    # and never below |y| (triangle inequality) on signed data
+    ys = oracle.qgemv_fp_reference(p.codes, p.scales, p.x, 2, N, K, fmt)
+    assert np.all(base >= np.abs(ys) * (1 - K * 2.0 ** -52))
+
+
+def _abs_pins():
+    try:
+        for fmt, K, N, M in [("mxfp4", 64, 5, 2), ("nvfp4", 64, 4, 3), ("mxfp8", 96, 4, 2)]:
+            test_abs_product_sum_matches_exact_rational(fmt, K, N, M)
+        for fmt in FMTS:
+            test_abs_product_sum_onehot_gives_magnitude_of_one_weight(fmt)
+            test_abs_product_sum_sign_and_same_sign_closed_forms(fmt)
+    except AssertionError:
+        return False
+    return True
+
+
+def _abs_inflated(codes, scales, x_bits, M, N, K, fmt, rows=None):
+    return 2.0 * qo._orig_fp_abs(codes, scales, x_bits, M, N, K, fmt, rows)
+
+
+def _abs_dropped_on_w(codes, scales, x_bits, M, N, K, fmt, rows=None):
+    # |x| @ w^T: the magnitude taken of the activations only
+    x = np.abs(qo.bf16_bits_to_f64(np.asarray(x_bits)[:M]))
+    idx = np.arange(N) if rows is None else np.asarray(rows)
+    return x @ qo.fp_dequantize(codes[idx], scales[idx], K, fmt).T
+
+
+def _abs_nvfp4_block32(codes, scales, x_bits, M, N, K, fmt, rows=None):
+    x = np.abs(qo.bf16_bits_to_f64(np.asarray(x_bits)[:M]))
+    idx = np.arange(N) if rows is None else np.asarray(rows)
+    return x @ np.abs(_nvfp4_block32(codes[idx], scales[idx], K, fmt)).T
+
+
+def _abs_x_row0(codes, scales, x_bits, M, N, K, fmt, rows=None):
+    xb = np.repeat(np.asarray(x_bits)[:1], M, axis=0)
+    return qo._orig_fp_abs(codes, scales, xb, M, N, K, fmt, rows)
+
+
+@pytest.mark.parametrize("mutant", [_abs_inflated, _abs_dropped_on_w, _abs_nvfp4_block32, _abs_x_row0])
+def test_abs_pins_catch_planted_mistakes(monkeypatch, mutant):
+    assert _abs_pins(), "pins must pass on the unmodified oracle"
+    monkeypatch.setattr(qo, "_orig_fp_abs", qo.fp_abs_product_sum, raising=False)
+    monkeypatch.setattr(qo, "fp_abs_product_sum", mutant)
+    monkeypatch.setattr(oracle, "fp_abs_product_sum", mutant)
+    assert not _abs_pins(), f"planted mistake {mutant.__name__} went unnoticed"

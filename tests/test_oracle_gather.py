@@ -117,3 +117,109 @@ def test_moe_generator_routing():
     x_idx, e_idx = p.pairs(4)
     assert x_idx.tolist() == [0] * 8 + [1] * 8 + [2] * 8 + [3] * 8
     assert e_idx.tolist() == p.routing[:4].reshape(-1).tolist()
+
+
+# ---------------------------------------------------------------- the tolerance scale
+#
+# gather_abs_product_sum sets the bound of every MoE parity check: pinned by
+# exact rational brute force, a one-hot closed form (|w| of the routed
+# expert's column, whatever the sign of x), and planted mistakes.
+
+def abs_run(p, x_idx, e_idx, rows=None):
+    s = p.shape
+    return oracle.gather_abs_product_sum(p.codes, p.scales, p.biases, p.x, x_idx, e_idx, s.N, s.K,
+                                         s.bits, s.group_size, rows=rows)
+
+
+def test_abs_product_sum_matches_exact_rational_brute_force():
+    p = tiny(E=4, N=3, K=64, gs=32, X=3, seed=11)
+    s = p.shape
+    x_idx = np.array([2, 1, 0, 1, 2])
+    e_idx = np.array([0, 3, 3, 1, 2])
+    got = abs_run(p, x_idx, e_idx)
+    for i in range(len(e_idx)):
+        e, r = int(e_idx[i]), int(x_idx[i])
+        xs = [frac_bf16(int(v)) for v in p.x[r]]
+        for n in range(s.N):
+            q = bitstream_codes(p.codes[e, n], s.K, s.bits)
+            w = [frac_fp16(int(p.scales[e, n, k // s.group_size])) * q[k] +
+                 frac_fp16(int(p.biases[e, n, k // s.group_size])) for k in range(s.K)]
+            want = sum(abs(xs[k] * w[k]) for k in range(s.K))
+            assert want > 0
+            assert abs(Fraction(got[i, n]) - want) <= Fraction(s.K) * Fraction(2) ** -52 * want, (i, n)
+
+
+def test_abs_product_sum_onehot_gives_magnitude_of_the_routed_weight():
+    p = tiny()
+    s = p.shape
+    cols = [3, 70, 126]
+    p.x[:] = 0
+    p.x[0, cols[0]] = 0xBF80  # -1.0
+    p.x[1, cols[1]] = 0x4000  # 2.0
+    p.x[2, cols[2]] = 0xC040  # -3.0
+    mag = [1, 2, 3]
+    x_idx = np.array([1, 0, 2, 2, 0, 1])
+    e_idx = np.array([4, 4, 0, 3, 1, 2])
+    got = abs_run(p, x_idx, e_idx)
+    for i in range(len(e_idx)):
+        e, r = int(e_idx[i]), int(x_idx[i])
+        k = cols[r]
+        for n in range(s.N):
+            q = bitstream_codes(p.codes[e, n], s.K, s.bits)[k]
+            w = frac_fp16(int(p.scales[e, n, k // s.group_size])) * q + \
+                frac_fp16(int(p.biases[e, n, k // s.group_size]))
+            assert got[i, n] == float(mag[r] * abs(w)), (i, n)
+
+
+def test_abs_product_sum_is_at_least_the_magnitude_of_y():
+    p = tiny(seed=12)
+    x_idx = np.array([0, 1, 2, 0])
+    e_idx = np.array([3, 3, 1, 0])
+    a = abs_run(p, x_idx, e_idx)
+    y = run(p, x_idx, e_idx)
+    assert np.all(a >= np.abs(y) * (1 - 128 * 2.0 ** -52))
+    assert np.array_equal(abs_run(p, x_idx, e_idx, rows=[1, 4]), a[:, [1, 4]])
+
+
+def _abs_pins():
+    try:
+        test_abs_product_sum_matches_exact_rational_brute_force()
+        test_abs_product_sum_onehot_gives_magnitude_of_the_routed_weight()
+        test_abs_product_sum_is_at_least_the_magnitude_of_y()
+    except AssertionError:
+        return False
+    return True
+
+
+def _abs_inflated(codes, scales, biases, x_bits, x_idx, e_idx, N, K, bits, gs, rows=None):
+    return 2.0 * qo._orig_gabs(codes, scales, biases, x_bits, x_idx, e_idx, N, K, bits, gs, rows)
+
+
+def _abs_wrong_row(codes, scales, biases, x_bits, x_idx, e_idx, N, K, bits, gs, rows=None):
+    return qo._orig_gabs(codes, scales, biases, x_bits, (np.asarray(x_idx) + 1) % len(x_bits), e_idx,
+                         N, K, bits, gs, rows)
+
+
+def _abs_wrong_expert(codes, scales, biases, x_bits, x_idx, e_idx, N, K, bits, gs, rows=None):
+    return qo._orig_gabs(codes, scales, biases, x_bits, x_idx, (np.asarray(e_idx) + 1) % len(codes),
+                         N, K, bits, gs, rows)
+
+
+def _abs_dropped_on_w(codes, scales, biases, x_bits, x_idx, e_idx, N, K, bits, gs, rows=None):
+    out = []
+    x = np.abs(qo.bf16_bits_to_f64(np.asarray(x_bits)))
+    idx = np.arange(N) if rows is None else np.asarray(rows)
+    for r, e in zip(np.asarray(x_idx), np.asarray(e_idx)):
+        q = qo.unpack_codes(codes[e][idx], K, bits)
+        w = qo.dequantize(q, scales[e][idx], biases[e][idx], gs)
+        out.append(x[r] @ w.T)
+    return np.array(out)
+
+
+@pytest.mark.parametrize("mutant", [_abs_inflated, _abs_wrong_row, _abs_wrong_expert, _abs_dropped_on_w])
+def test_abs_pins_catch_planted_mistakes(monkeypatch, mutant):
+    assert _abs_pins()
+    monkeypatch.setattr(qo, "_orig_gabs", qo.gather_abs_product_sum, raising=False)
+    monkeypatch.setattr(qo, "gather_abs_product_sum", mutant)
+    monkeypatch.setattr(oracle, "gather_abs_product_sum", mutant)
+    assert not _abs_pins(), f"{mutant.__name__} went unnoticed"
