@@ -7,14 +7,14 @@
 // the exact bf16 pair (q_a, q_b) in one instruction: 2- and 4-bit fields are
 // first spread into bytes with one shift-and-mask per four fields.  Dot
 // products of these pairs with bf16 activations are exact per product in
-// fp32.  8-bit codes (0..255) are converted exactly through fp32
+// fp32, and the bias is applied through the group's activation sum with no
+// offset to remove.  8-bit codes (0..255) are converted exactly through fp32
 // (unpack8_pairs).
 //
-// The affine bias goes through an integer zero point (zero_point): each group
-// is applied as s * sum (q - z) x + b' * sum x, the first sum formed as the
-// difference of two products run through the same arithmetic (codes against
-// x, the constant z against x).  A group whose weights are all exactly zero
-// then contributes exactly 0.
+// Zero weights are exact (zero_weights): each lane tracks whether every group
+// it has folded dequantizes to exactly zero and then returns exactly 0, so a
+// row of zero weights gives y = 0 whatever the fp32 rounding of the factored
+// sum s * sum(q x) + b * sum(x) would leave.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,6 +39,16 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t b16) {
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// 16-bit field f (0..3) of the 64 bits {v.x, v.y} (the fp16 scales or biases
+// of a block's 4 groups), for a lane-dependent f: a bit-field select of the
+// word and a shift, all in registers (written as a ?: on the vector members,
+// the compiler may go through private memory).
+__device__ __forceinline__ uint32_t field16(uint2 v, int f) {
+  const uint32_t m = 0u - (uint32_t)(f < 2);  // all ones for fields 0 and 1
+  const uint32_t w = (v.x & m) | (v.y & ~m);  // one bit-field insert
+  return (w >> (16 * (f & 1))) & 0xFFFFu;
 }
 
 // v_perm_b32: bytes of {hi_src, lo_src} selected by `sel` (0-3: lo_src, 4-7: hi_src, 0x0c: zero).
@@ -184,32 +194,61 @@ __device__ __forceinline__ float fp_scale_to_float(uint32_t byte) {
   return e8m0_to_float(byte);
 }
 
-// ---------------------------------------------------------------- zero point
+// ---------------------------------------------------------------- zero weights
 //
-// w = s*q + b = s*(q - z) + b' with the integer zero point z = round(-b/s),
-// clamped to the code range [0, zmax], and b' = b + z*s (one fma).  The
-// kernels form sum (q - z)*x as the difference of two products that run
-// through identical arithmetic -- the codes against x, and the bf16 pair
-// (z, z) in every code slot against x -- and add b' * sum x.  When every
-// weight of the group is exactly zero (b = -z*s for an integer z in range),
-// the two products see identical operands and give identical bits, and b' is
-// exactly 0 (fma of the exact product z*s with b = -z*s), so the group adds
-// exactly 0, whatever z; for other groups z only re-centres the codes.  The
-// reciprocal is approximate, but -b * rcp(s) lies within a few ulps of an
-// integer z <= 255 when b = -z*s, so the rounding finds z.  A zero scale
-// gives z = 0 and b' = b.
-struct ZeroPoint {
-  uint32_t zpair;  // bf16 (z, z)
-  float bres;      // b' = b + z*s
-};
-__device__ __forceinline__ ZeroPoint zero_point(float s, float b, int zmax) {
-  const float r = s != 0.f ? __builtin_amdgcn_rcpf(s) : 0.f;
-  // clamped in fp32 first (fmaxf takes 0 over a NaN), so the conversion is in
-  // range; the round trip through int turns -0 into +0
-  const int zi = (int)fminf(fmaxf(rintf(-b * r), 0.f), (float)zmax);
-  const float z = (float)zi;
-  const uint32_t zb = __builtin_bit_cast(uint32_t, z);  // z is exact in bf16: the upper half
-  return ZeroPoint{perm_b32(zb, zb, 0x03020302u), fmaf(z, s, b)};
+// A group whose codes all equal c and whose fma(s, c, b) is exactly 0 holds
+// only zero weights: its exact contribution is 0.  The kernels fold such
+// groups like any other (s * sum(q x) + b * sum(x) leaves an fp32 rounding
+// residue of the size of s * c * sum(x)), but each lane ORs into a word `nz`
+// every trace of a nonzero weight it folds: the differences between its code
+// words and the group's first (and between that word and itself rotated by
+// one field), and the magnitude bits of s*c + b.  A partial whose nz is still
+// 0 at the end held only zero weights and is stored as exactly 0, its exact
+// value.  Plain bitwise ORs, no comparisons: the optimizer keeps the loops as
+// they are (a chain of boolean tests made it branch around the accumulation,
+// at a large register cost).
+
+// Makes v opaque at this point: the trace of each code word is then formed
+// while the word is in hand (left free, the optimizer gathers a group's
+// traces at its end and keeps all of its code words live until then).
+__device__ __forceinline__ void pin(uint32_t &v) { asm volatile("" : "+v"(v)); }
+
+// Trace of non-uniform BITS-bit fields within w (0 iff all fields equal).
+template <int BITS>
+__device__ __forceinline__ uint32_t fields_spread(uint32_t w) {
+  return w ^ __builtin_amdgcn_alignbit(w, w, BITS);
+}
+
+// The value of the lowest BITS-bit field of w.
+template <int BITS>
+__device__ __forceinline__ float low_field(uint32_t w) {
+  return (float)(w & ((1u << BITS) - 1u));
+}
+
+// Trace of a nonzero group weight s*c + b (its magnitude bits).
+__device__ __forceinline__ uint32_t weight_trace(float s, float c, float b) {
+  return __builtin_bit_cast(uint32_t, fmaf(s, c, b)) & 0x7FFFFFFFu;
+}
+
+// acc where nz != 0, else exactly 0.  The mask passes through an empty asm
+// statement so that the select stays a select.
+__device__ __forceinline__ uint32_t keep_mask(uint32_t nz) {
+  uint32_t m = nz != 0u ? 0xFFFFFFFFu : 0u;
+  asm volatile("" : "+v"(m));
+  return m;
+}
+__device__ __forceinline__ float unless_zero(float acc, uint32_t keep) {
+  return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, acc) & keep);
+}
+
+// MFMA operand layout: lanes 16*rho + c (rho = 0..3) hold the four quarters of
+// column c's codes.  The OR of nz over the column's four lanes, in each of
+// them (two row swaps).
+__device__ __forceinline__ uint32_t column_or(uint32_t nz) {
+  auto a = __builtin_amdgcn_permlane32_swap(nz, nz, false, false);
+  const uint32_t h = a[0] | a[1];
+  auto b = __builtin_amdgcn_permlane16_swap(h, h, false, false);
+  return b[0] | b[1];
 }
 
 // ---------------------------------------------------------------- activation pairing

@@ -13,18 +13,18 @@
 // * The M activation rows are staged in LDS once per workgroup, already
 //   re-paired to match the code pairing (elements (0,2), (1,3), (4,6), (5,7)
 //   of each 8 for 4-bit codes, (e, e+4) of each 8 for 2-bit codes), together
-//   with the activation sum of every lane chunk, formed by the same chain of
-//   v_dot2 over the same pairs as the code products.  K is staged in pieces
-//   when M*K does not fit the LDS budget.
+//   with the activation sum of every lane chunk.  K is staged in pieces when
+//   M*K does not fit the LDS budget.
 // * Each code dword is unpacked once into exact bf16 pairs q (no offset) and
-//   used for all M rows with v_dot2c_f32_bf16.  The group's scale and bias are
-//   applied once per lane chunk and row: acc += s*(d - dz) + b'*sum(x), where
-//   dz is the same chain of v_dot2 run with the group's zero point z in every
-//   code slot and b' = b + z*s (zero_point), i.e. the scale is folded out of
-//   the inner loop (MLX page, Facts: the qmv_wide tuning bullet) and metadata
-//   is read directly per group, not cached across lanes (same page: the
-//   scale-caching patch regressed).  A chunk whose weights are all zero has
-//   d == dz bit for bit and b' == 0, so it adds exactly 0.
+//   used for all M rows with v_dot2c_f32_bf16.  The group's scale and bias
+//   are applied once per lane chunk and row: acc += s*d + b*sum(x), i.e. the
+//   scale is folded out of the inner loop (MLX page, Facts: the qmv_wide
+//   tuning bullet) and metadata is read directly per group, not cached across
+//   lanes (same page: the scale-caching patch regressed).
+// * Zero weights: a lane whose chunks of row r all hold zero weights (every
+//   code equal to c and fma(s, c, b) == 0) contributes exactly 0 for that
+//   row (see zero_weights in qgemv_device.h), so a row of zero weights gives
+//   y = 0 exactly.
 // * The R*M per-lane partial sums are reduced across the wave with
 //   permlane32/permlane16 swaps and a DPP butterfly, then stored.
 // * Fused residual sum (ADD): the residual elements a lane will store are
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
   constexpr int SUBW = CW / NSUB;       // weights per sub-chunk
   constexpr int V = ((R * M + 3) / 4) * 4;
   // activations in memory order (8-bit codes, FP elements) or re-paired to
-  // the pairing of the 2/4-bit codes
+  // the split pairing of the 2/4-bit offset codes
   constexpr bool NATURAL = BITS == 8 || FMT != kAffine;
   constexpr bool HAS_BIAS = FMT == kAffine;
   constexpr bool XREG = XR && (M == 1 || (M == 2 && !(FMT == kAffine && BITS == 4))) &&
@@ -114,39 +114,11 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
-  constexpr int ZMAX = (1 << BITS) - 1;  // largest code
-
-  // The quads of one 16-byte code chunk's activations in the code pairing
-  // (memory order for 8-bit codes and FP elements), and the activation sum
-  // of each metadata sub-chunk.
-  auto pair_chunk = [](const uint4 (&xv)[CW / 8], uint4 (&qd)[QUADS], float (&ssum)[NSUB]) {
+  // traces of nonzero weights in row r's chunks of this lane (affine codes;
+  // see zero weights in qgemv_device.h); the FP formats never need them
+  uint32_t nz[R];
 #pragma unroll
-    for (int j = 0; j < QUADS; ++j) {
-      if constexpr (NATURAL) {
-        qd[j] = xv[j];
-      } else {
-        // quad j: the 8 activations of code dword j (4-bit) or of half j & 1
-        // of code dword j >> 1 (2-bit), i.e. xv[j] either way
-        const u32x4_t p = pair_activations<BITS>(u32x4_t{xv[j].x, xv[j].y, xv[j].z, xv[j].w});
-        qd[j] = make_uint4(p[0], p[1], p[2], p[3]);
-      }
-    }
-#pragma unroll
-    for (int sb = 0; sb < NSUB; ++sb) {
-      float a = 0.f;
-      if constexpr (HAS_BIAS) {
-#pragma unroll
-        for (int qq = 0; qq < QPS; ++qq) {
-          const uint4 v = qd[sb * QPS + qq];
-          a = dot2_bf16(kOnesPair, v.x, a);
-          a = dot2_bf16(kOnesPair, v.y, a);
-          a = dot2_bf16(kOnesPair, v.z, a);
-          a = dot2_bf16(kOnesPair, v.w, a);
-        }
-      }
-      ssum[sb] = a;
-    }
-  };
+  for (int r = 0; r < R; ++r) nz[r] = HAS_BIAS ? 0u : 1u;
 
   for (int c0 = 0; c0 < NC; c0 += kch) {
     const int nc = min(kch, NC - c0);
@@ -225,14 +197,60 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
     auto stage_unit = [&](int u, const uint4 (&xv)[CW / 8]) {
       const int m = u / nc;
       const int cl = u - m * nc;
-      uint4 qd[QUADS];
-      float ssum[NSUB];
-      pair_chunk(xv, qd, ssum);
+      uint32_t X[CW / 2];
 #pragma unroll
-      for (int d = 0; d < QUADS; ++d) xl[(m * QUADS + d) * kch + cl] = qd[d];
+      for (int i = 0; i < CW / 8; ++i) {
+        X[4 * i] = xv[i].x;
+        X[4 * i + 1] = xv[i].y;
+        X[4 * i + 2] = xv[i].z;
+        X[4 * i + 3] = xv[i].w;
+      }
+      float ssum[NSUB];
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) ssum[s] = 0.f;
       if constexpr (HAS_BIAS) {
 #pragma unroll
-        for (int sb = 0; sb < NSUB; ++sb) xsl[(m * NSUB + sb) * kch + cl] = ssum[sb];
+        for (int i = 0; i < CW / 2; ++i)
+          ssum[(2 * i) / SUBW] = dot2_bf16(X[i], 0x3F803F80u, ssum[(2 * i) / SUBW]);
+      }
+      if constexpr (NATURAL) {
+        // natural pairs: quad d holds elements 8d..8d+7 in memory order
+#pragma unroll
+        for (int d = 0; d < QUADS; ++d)
+          xl[(m * QUADS + d) * kch + cl] = make_uint4(X[4 * d], X[4 * d + 1], X[4 * d + 2], X[4 * d + 3]);
+      } else if constexpr (BITS == 4) {
+        // code dword d covers elements 8d..8d+7; pairs (0,2), (1,3), (4,6), (5,7)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t Xd[4] = {X[4 * d], X[4 * d + 1], X[4 * d + 2], X[4 * d + 3]};
+          uint4 q;
+          q.x = xpair4(Xd, 0);
+          q.y = xpair4(Xd, 1);
+          q.z = xpair4(Xd, 2);
+          q.w = xpair4(Xd, 3);
+          xl[(m * QUADS + d) * kch + cl] = q;
+        }
+      } else {
+        // code dword d covers elements 16d..16d+15; quad (d, h) holds half h,
+        // elements 16d+8h..16d+8h+7, paired (e, e+4)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t Xd[4] = {X[8 * d + 4 * h], X[8 * d + 4 * h + 1], X[8 * d + 4 * h + 2],
+                                    X[8 * d + 4 * h + 3]};
+            uint4 q;
+            q.x = xpair_stride4(Xd, 0);
+            q.y = xpair_stride4(Xd, 1);
+            q.z = xpair_stride4(Xd, 2);
+            q.w = xpair_stride4(Xd, 3);
+            xl[(m * QUADS + 2 * d + h) * kch + cl] = q;
+          }
+        }
+      }
+      if constexpr (HAS_BIAS) {
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) xsl[(m * NSUB + s) * kch + cl] = ssum[s];
       }
     };
 #pragma unroll
@@ -257,7 +275,44 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
 #pragma unroll
       for (int t = 0; t < P; ++t)
 #pragma unroll
-        for (int m = 0; m < M; ++m) pair_chunk(xg[t][m], xq[t][m], xsm[t][m]);
+      for (int m = 0; m < M; ++m) {
+        uint32_t X[CW / 2];
+#pragma unroll
+        for (int i = 0; i < CW / 8; ++i) {
+          X[4 * i] = xg[t][m][i].x;
+          X[4 * i + 1] = xg[t][m][i].y;
+          X[4 * i + 2] = xg[t][m][i].z;
+          X[4 * i + 3] = xg[t][m][i].w;
+        }
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) xsm[t][m][s] = 0.f;
+        if constexpr (HAS_BIAS) {
+#pragma unroll
+          for (int i = 0; i < CW / 2; ++i)
+            xsm[t][m][(2 * i) / SUBW] = dot2_bf16(X[i], 0x3F803F80u, xsm[t][m][(2 * i) / SUBW]);
+        }
+        if constexpr (NATURAL) {
+#pragma unroll
+          for (int d = 0; d < QUADS; ++d) xq[t][m][d] = make_uint4(X[4 * d], X[4 * d + 1], X[4 * d + 2], X[4 * d + 3]);
+        } else if constexpr (BITS == 4) {
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const uint32_t Xd[4] = {X[4 * d], X[4 * d + 1], X[4 * d + 2], X[4 * d + 3]};
+            xq[t][m][d] = make_uint4(xpair4(Xd, 0), xpair4(Xd, 1), xpair4(Xd, 2), xpair4(Xd, 3));
+          }
+        } else {
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const uint32_t Xd[4] = {X[8 * d + 4 * h], X[8 * d + 4 * h + 1], X[8 * d + 4 * h + 2],
+                                      X[8 * d + 4 * h + 3]};
+              xq[t][m][2 * d + h] = make_uint4(xpair_stride4(Xd, 0), xpair_stride4(Xd, 1),
+                                               xpair_stride4(Xd, 2), xpair_stride4(Xd, 3));
+            }
+          }
+        }
+      }
     } else {
       __syncthreads();
     }
@@ -269,21 +324,12 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
       if (t >= npass || c >= nc) continue;
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) {
-        // d: codes against x; dz: the zero point against x, same chain
-        float d[R][M], dz[HAS_BIAS ? R : 1][HAS_BIAS ? M : 1];
-        ZeroPoint zp[HAS_BIAS ? R : 1];
+        float d[R][M];
+        uint32_t zc0[R];  // first code dword of the sub-chunk, row r
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
           for (int m = 0; m < M; ++m) d[r][m] = 0.f;
-        if constexpr (HAS_BIAS) {
-#pragma unroll
-          for (int r = 0; r < R; ++r) {
-            zp[r] = zero_point(half_bits_to_float(sr[t][r][s]), half_bits_to_float(br[t][r][s]), ZMAX);
-#pragma unroll
-            for (int m = 0; m < M; ++m) dz[r][m] = 0.f;
-          }
-        }
 #pragma unroll
         for (int qq = 0; qq < QPS; ++qq) {
           const int q = s * QPS + qq;
@@ -291,6 +337,19 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             const uint32_t cd[4] = {cw[t][r].x, cw[t][r].y, cw[t][r].z, cw[t][r].w};
+            if constexpr (HAS_BIAS) {
+              // quad q reads code dword q (4-bit), q >> 1 (2-bit) or 2q, 2q + 1
+              // (8-bit): traces of their differences from the sub-chunk's
+              // first word, and of that word's own spread
+              const int dq = BITS == 8 ? 2 * q : (BITS == 4 ? q : (q >> 1));
+              if (qq == 0) {
+                zc0[r] = cd[dq];
+                nz[r] |= fields_spread<BITS>(cd[dq]);
+              } else if (BITS != 2 || (q & 1) == 0) {
+                nz[r] |= cd[dq] ^ zc0[r];
+              }
+              if constexpr (BITS == 8) nz[r] |= cd[dq + 1] ^ zc0[r];
+            }
             if constexpr (FMT == kMxfp4 || FMT == kNvfp4) {
               // quad q = code dword q (elements 8q..8q+7, natural pairs)
               unpack_fp4_pairs(cd[q], pr[r]);
@@ -331,15 +390,6 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
               a = dot2_bf16(pr[r][2], xv.z, a);
               a = dot2_bf16(pr[r][3], xv.w, a);
               d[r][m] = a;
-              if constexpr (HAS_BIAS) {
-                const uint32_t zz = zp[r].zpair;
-                float c = dz[r][m];
-                c = dot2_bf16(zz, xv.x, c);
-                c = dot2_bf16(zz, xv.y, c);
-                c = dot2_bf16(zz, xv.z, c);
-                c = dot2_bf16(zz, xv.w, c);
-                dz[r][m] = c;
-              }
             }
           }
         }
@@ -352,11 +402,14 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
             for (int m = 0; m < M; ++m) acc[r][m] = fmaf(sc, d[r][m], acc[r][m]);
           } else {
             const float sc = half_bits_to_float(sr[t][r][s]);
+            const float bo = half_bits_to_float(br[t][r][s]);
 #pragma unroll
             for (int m = 0; m < M; ++m) {
               const float xs = XREG ? xsm[t][m][s] : xsl[(m * NSUB + s) * kch + c];
-              acc[r][m] = fmaf(sc, d[r][m] - dz[r][m], fmaf(zp[r].bres, xs, acc[r][m]));
+              acc[r][m] = fmaf(sc, d[r][m], fmaf(bo, xs, acc[r][m]));
             }
+            // trace of the sub-chunk's weight s*c + b (c: its first code)
+            nz[r] |= weight_trace(sc, low_field<BITS>(zc0[r]), bo);
           }
         }
       }
@@ -365,8 +418,11 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
 
   // 5. reduce over the 64 lanes and store y[m][row0 + r]
   float v[V];
+  uint32_t keep[R];
 #pragma unroll
-  for (int i = 0; i < V; ++i) v[i] = (i < R * M) ? acc[i / M][i % M] : 0.f;
+  for (int r = 0; r < R; ++r) keep[r] = keep_mask(nz[r]);
+#pragma unroll
+  for (int i = 0; i < V; ++i) v[i] = (i < R * M) ? unless_zero(acc[i / M][i % M], keep[i / M]) : 0.f;
   float red[V / 4];
   wave_reduce_multi<V>(v, red);
   const int rho = lane >> 4;

@@ -26,13 +26,16 @@
 //   quantization group.
 // * The group's partial product is accumulated by gs/32 MFMAs and folded with
 //   the group scale once: acc += s * acc_g (4 FMAs per lane per group).
-// * Bias through the group's integer zero point z = round(-b/s)
-//   (zero_point): each step also runs the MFMA with B = z in every slot of
-//   the column and with B = bf16 ones, and the group is folded as
-//   acc += s * (P_codes - P_z) + b' * P_ones, b' = b + z*s.  A group whose
-//   weights are all exactly zero gives P_codes == P_z bit for bit (the same
-//   operands) and b' == 0, so it adds exactly 0 whatever z; elsewhere the
-//   difference is between products of the size of the weights' codes.
+// * Bias: sum_g b[n,g] * xsum[m,g] over the 4 groups of a block is one
+//   v_mfma_f32_16x16x4_f32, with the per-group activation sums xsum (dot2
+//   against ones, then a row transpose-reduce) formed while the codes are
+//   still in flight.
+// * Zero weights: a lane's column of a tile whose groups so far all held
+//   zero weights (codes all equal to c in the column's four lanes and
+//   s*c + b exactly 0) keeps a flag; a flagged partial is stored as exactly 0,
+//   its exact value, so a row of zero weights gives y = 0 (the factored sum
+//   would leave a rounding residue of the size of s*c*sum(x)).  The test runs
+//   only while some lane of the wave is flagged.
 // * Partial tiles of the waves are summed through LDS in slice order
 //   (deterministic, no atomics) and rows m < M are stored.
 // * Fused residual sum (ADD, "metal : few-row MMA mat-mul and batched copies

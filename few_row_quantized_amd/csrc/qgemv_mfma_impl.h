@@ -74,9 +74,6 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   const int kb = lane >> 4;
   const int NBLK = K / BLKW;
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-  // B operand of bf16 ones: the MFMA steps run on it give the group sums of
-  // the activations in the output layout
-  const bf16x8_t ones8 = __builtin_bit_cast(bf16x8_t, u32x4_t{kOnesPair, kOnesPair, kOnesPair, kOnesPair});
   // element offset, within a super-chunk, of the codes register i holds in
   // this lane's row after the partial transpose
 
@@ -275,7 +272,16 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   f32x4_t acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = zero4;
-  constexpr int ZMAX = (1 << BITS) - 1;  // largest code
+  // Zero weights (affine codes): nz[t] collects traces of nonzero weights in
+  // this lane's quarter of tile t's groups (see zero weights in
+  // qgemv_device.h); zc0 is the current group's first code word.  The FP
+  // formats never need it.
+  uint32_t nz[NT], zc0[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    nz[t] = HAS_BIAS ? 0u : 1u;
+    zc0[t] = 0u;
+  }
 
   for (int blk0 = b_begin; blk0 < b_end; blk0 += BPB) {
     const int nb = min(BPB, b_end - blk0);  // blocks in this batch (uniform)
@@ -330,9 +336,10 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     // scheduler may sink later loads below the first waits and serialize them
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- activation work, overlapping the code loads: move x to the operand
-    // lanes (quad-row loads) and re-pair 2/4-bit activations to the code
-    // pairing (8-bit codes and FP elements keep the memory order)
+    // ---- activation work, overlapping the code loads: re-pair x to the
+    // code pairing and form the per-group activation sums.  xsum of group
+    // g0 + j ends up in row j of this lane's column, i.e. in the A layout of
+    // v_mfma_f32_16x16x4_f32 for the bias product.
     if (xquad) {
 #pragma unroll
       for (int u = 0; u < UNR; ++u)
@@ -341,13 +348,37 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
 #pragma unroll
           for (int l = 0; l < HS; ++l) xv[u][i][l] = to_operand_lanes(xv[u][i][l]);
     }
-    if constexpr (HAS_BIAS && BITS != 8) {
+    float xsum[BPB];
 #pragma unroll
-      for (int u = 0; u < UNR; ++u)
+    for (int bb = 0; bb < BPB; ++bb) {
+      float P[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < XR; ++i)
+      for (int uu = 0; uu < BSC; ++uu) {
+        const int u = bb * BSC + uu;
+        if constexpr (!HAS_BIAS) continue;  // FP formats: natural order, no bias sums
+        if constexpr (BITS == 8) {
+          // natural order: only the group sums; step e of the super-chunk
+          // holds 8 codes of group (uu*SCW + 32e)/GS of the block
+#pragma unroll
+          for (int e = 0; e < XR; ++e) {
+            const int j = (uu * SCW + 32 * e) / GS;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) P[j] = dot2_bf16(xv[u][e][0][c], 0x3F803F80u, P[j]);
+          }
+          continue;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = uu * GPS + i / REGS_G;  // group within the block
+#pragma unroll
+          for (int l = 0; l < HS; ++l)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) P[j] = dot2_bf16(xv[u][i][l][e], 0x3F803F80u, P[j]);
 #pragma unroll
           for (int l = 0; l < HS; ++l) xv[u][i][l] = pair_activations<BITS>(xv[u][i][l]);
+        }
+      }
+      if constexpr (HAS_BIAS) xsum[bb] = rows_transpose_reduce4(P);
     }
 
 #pragma unroll
@@ -357,60 +388,33 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
         s4[bb][t] = to_operand_lanes(s4[bb][t]);
         if constexpr (HAS_BIAS) b4[bb][t] = to_operand_lanes(b4[bb][t]);
       }
-    // Affine groups, per tile: at the group's first step its zero point z
-    // (zero_point) becomes the B operand zq of a second MFMA chain; at its
-    // last step acc += s * (codes' product - zero point's) + b' * (sum of x),
-    // the sums from the chain against ones.  FP formats: acc += scale * product.
-    u32x4_t zq[NT];
-    float bres[NT];
-    auto group_start = [&](const int bb, const int j) {
-      if constexpr (HAS_BIAS) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const uint32_t sw = (j < 2) ? s4[bb][t].x : s4[bb][t].y;
-          const uint32_t bw = (j < 2) ? b4[bb][t].x : b4[bb][t].y;
-          const ZeroPoint zp = zero_point(half_bits_to_float((j & 1) ? (sw >> 16) : (sw & 0xFFFFu)),
-                                          half_bits_to_float((j & 1) ? (bw >> 16) : (bw & 0xFFFFu)), ZMAX);
-          zq[t] = u32x4_t{zp.zpair, zp.zpair, zp.zpair, zp.zpair};
-          bres[t] = zp.bres;
-        }
-      }
-    };
-    auto fold = [&](const int bb, const int j, const f32x4_t (&pg)[NT], const f32x4_t (&pz)[NT],
-                    const f32x4_t &xg) {
+    // zero-weight traces of group j: the step's code words against the
+    // group's first (and that word's own spread), then the group's weight
+    // s*c + b (c: the first code) at its last step
+    auto zero_step = [&](const bool gfirst, const uint32_t (&w)[NT], const int nw, const uint32_t (&w2)[NT]) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        if constexpr (HAS_BIAS) {
-          const uint32_t sw = (j < 2) ? s4[bb][t].x : s4[bb][t].y;
-          const float sc = half_bits_to_float((j & 1) ? (sw >> 16) : (sw & 0xFFFFu));
-#pragma unroll
-          for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(sc, pg[t][q] - pz[t][q], fmaf(bres[t], xg[q], acc[t][q]));
+        if (gfirst) {
+          zc0[t] = w[t];
+          nz[t] |= fields_spread<BITS>(w[t]);
         } else {
-          const float sc = fp_scale_to_float<FMT>(s4[bb][t].x >> (8 * j));
-#pragma unroll
-          for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(sc, pg[t][q], acc[t][q]);
+          nz[t] |= w[t] ^ zc0[t];
         }
+        if (nw == 2) nz[t] |= w2[t] ^ zc0[t];
+        pin(nz[t]);
       }
     };
-    // one step of a group: codes (B = bw[t]), zero points and ones against A
-    auto step = [&](const bf16x8_t &a, const u32x4_t (&bw)[NT], const bool gfirst, f32x4_t (&pg)[NT],
-                    f32x4_t (&pz)[NT], f32x4_t &xg) {
+    auto zero_group = [&](const int bb, const int j) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        pg[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bw[t]),
-                                                        gfirst ? zero4 : pg[t], 0, 0, 0);
-      if constexpr (HAS_BIAS) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-          pz[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, zq[t]),
-                                                          gfirst ? zero4 : pz[t], 0, 0, 0);
-        xg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ones8, gfirst ? zero4 : xg, 0, 0, 0);
+      for (int t = 0; t < NT; ++t) {
+        const uint2 sw_v = s4[bb][t];
+        const uint2 bw_v = b4[bb][t];
+        nz[t] |= weight_trace(half_bits_to_float(field16(sw_v, j)), low_field<BITS>(zc0[t]),
+                              half_bits_to_float(field16(bw_v, j)));
       }
     };
     // ---- codes, super-chunk by super-chunk in load order
-    f32x4_t accg[NT], accz[NT], accx = zero4;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) accz[t] = zero4;
+    f32x4_t accg[NT];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       if (u / BSC >= nb) break;
@@ -431,19 +435,42 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
           const bool gfirst = kk % GS == 0;
           const bool glast = (kk + 32) % GS == 0;
           const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xv[u][e][0]);
-          if (gfirst) group_start(u / BSC, j);
-          u32x4_t bw[NT];
+          if constexpr (HAS_BIAS) {
+            uint32_t w[NT], w2[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              w[t] = cur[t][2 * e];
+              w2[t] = cur[t][2 * e + 1];
+            }
+            zero_step(gfirst, w, 2, w2);
+            if (glast) zero_group(u / BSC, j);
+          }
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
+            u32x4_t bw;
             if constexpr (FMT == kMxfp8) {
-              bw[t] = u32x4_t{fp8_pair<false>(cur[t][2 * e]), fp8_pair<true>(cur[t][2 * e]),
-                              fp8_pair<false>(cur[t][2 * e + 1]), fp8_pair<true>(cur[t][2 * e + 1])};
+              bw = u32x4_t{fp8_pair<false>(cur[t][2 * e]), fp8_pair<true>(cur[t][2 * e]),
+                           fp8_pair<false>(cur[t][2 * e + 1]), fp8_pair<true>(cur[t][2 * e + 1])};
             } else {
-              bw[t] = unpack8_quad(cur[t][2 * e], cur[t][2 * e + 1]);
+              bw = unpack8_quad(cur[t][2 * e], cur[t][2 * e + 1]);
+            }
+            accg[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                a, __builtin_bit_cast(bf16x8_t, bw), gfirst ? zero4 : accg[t], 0, 0, 0);
+          }
+          if (glast) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              float sc;
+              if constexpr (HAS_BIAS) {
+                const uint2 sw_v = s4[u / BSC][t];
+                sc = half_bits_to_float(field16(sw_v, j));
+              } else {
+                sc = fp_scale_to_float<FMT>(s4[u / BSC][t].x >> (8 * j));
+              }
+#pragma unroll
+              for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(sc, accg[t][q], acc[t][q]);
             }
           }
-          step(a, bw, gfirst, accg, accz, accx);
-          if (glast) fold(u / BSC, j, accg, accz, accx);
         }
       }
       if constexpr (FMT == kNvfp4) {
@@ -473,22 +500,51 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
           const bool gfirst = (i % REGS_G) == 0 && h == 0;
           const bool glast = (i % REGS_G) == REGS_G - 1 && h == HS - 1;
           const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xv[u][i][h]);
-          if (gfirst) group_start(u / BSC, j);
-          u32x4_t bw[NT];
+          if constexpr (HAS_BIAS) {
+            uint32_t w[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) w[t] = cur[t][i];
+            if (h == 0) zero_step(gfirst, w, 1, w);
+            if (glast) zero_group(u / BSC, j);
+          }
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
+            u32x4_t bw;
             if constexpr (FMT == kMxfp4) {
               // 8 elements of one dword, natural order
-              bw[t] = u32x4_t{fp4_pair<0>(cur[t][i]), fp4_pair<1>(cur[t][i]), fp4_pair<2>(cur[t][i]),
-                              fp4_pair<3>(cur[t][i])};
+              bw = u32x4_t{fp4_pair<0>(cur[t][i]), fp4_pair<1>(cur[t][i]), fp4_pair<2>(cur[t][i]),
+                           fp4_pair<3>(cur[t][i])};
             } else if constexpr (BITS == 4) {
-              bw[t] = unpack4_quad(cur[t][i]);
+              bw = unpack4_quad(cur[t][i]);
             } else {
-              bw[t] = unpack2_quad(cur[t][i], h);
+              bw = unpack2_quad(cur[t][i], h);
+            }
+            accg[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                a, __builtin_bit_cast(bf16x8_t, bw), gfirst ? zero4 : accg[t], 0, 0, 0);
+          }
+          if (glast) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              float sc;
+              if constexpr (HAS_BIAS) {
+                const uint2 sw_v = s4[u / BSC][t];
+                sc = half_bits_to_float(field16(sw_v, j));
+              } else {
+                sc = fp_scale_to_float<FMT>(s4[u / BSC][t].x >> (8 * j));
+              }
+#pragma unroll
+              for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(sc, accg[t][q], acc[t][q]);
             }
           }
-          step(a, bw, gfirst, accg, accz, accx);
-          if (glast) fold(u / BSC, j, accg, accz, accx);
+        }
+      }
+      if (HAS_BIAS && scb == BSC - 1) {
+        // bias: acc += xsum[m][g0+kb] * b[n][g0+kb]
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const uint2 bw_v = b4[u / BSC][t];
+          const float b = half_bits_to_float(field16(bw_v, kb));
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum[u / BSC], b, acc[t], 0, 0, 0);
         }
       }
     }
@@ -497,11 +553,14 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     if (b_begin >= b_end) load_res();  // a wave without blocks
   }
 
-  // split-K reduction over the slices, fixed order
+  // split-K reduction over the slices, fixed order; a partial whose column
+  // held only zero weights (no trace in any of its four lanes) is exactly 0
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+  for (int t = 0; t < NT; ++t) {
+    const uint32_t keep = keep_mask(column_or(nz[t]));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[slice][t][i][lane] = acc[t][i];
+    for (int i = 0; i < 4; ++i) red[slice][t][i][lane] = unless_zero(acc[t][i], keep);
+  }
   __syncthreads();
   // output o of the tile group: sum over the slices, then store (pre: the
   // residual rv was prefetched)

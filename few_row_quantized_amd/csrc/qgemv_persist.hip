@@ -13,8 +13,9 @@
 //   contiguous range of 16-column tiles [g*T/G, (g+1)*T/G) over the whole of K.
 // * Its W waves split K into bias blocks (4 groups): wave w owns the blocks
 //   vw, vw+W, ... (vw = w rotated per workgroup) for every tile, so its
-//   activation operands are loaded and re-paired once and then stay in
-//   registers while the workgroup walks its tiles.
+//   activation operands and the per-group activation sums of the bias term
+//   are loaded, re-paired and summed once and then stay in registers while
+//   the workgroup walks its tiles.
 // * Codes and group metadata of the next tile are prefetched into a ring of
 //   S register slots while the current tile is unpacked and multiplied, so a
 //   CU keeps weight bytes in flight from its first tile to its last.
@@ -26,8 +27,8 @@
 //   is loaded when their first tile starts and added in the store, so
 //   y = fl(product + r), bit for bit the plain call and a separate fp32 add.
 // The inner MFMA step (code layout, partial lane transpose, unpack to exact
-// bf16 q, per-group scale fold, bias through the zero point and the MFMA of
-// the activations against bf16 ones) is the one of the single-pass kernel.
+// bf16 q, per-group scale fold, bias product by v_mfma_f32_16x16x4_f32,
+// zero-weight flags) is the one of the single-pass kernel.
 
 #include "qgemv_device.h"
 #include "qgemv_internal.h"
@@ -79,8 +80,6 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   const size_t RB = (size_t)K * BITS / 8;
   const int NG = K / GS;
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-  const bf16x8_t ones8 = __builtin_bit_cast(bf16x8_t, u32x4_t{kOnesPair, kOnesPair, kOnesPair, kOnesPair});
-  constexpr int ZMAX = (1 << BITS) - 1;  // largest code
   // activation loads in the quad-row layout once several rows are distinct
   // (results do not depend on the choice; from M = 5 for every group size
   // here: 27B q at M = 7, 9.44 -> 8.91 us)
@@ -107,9 +106,11 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   }
 
   // ---- activations of the owned blocks (rows m >= M read row M-1: their
-  // outputs are never stored), later re-paired to the code pairing
+  // outputs are never stored), later re-paired to the code pairing and
+  // summed per group into the A layout of the bias MFMA
   const uint16_t *xr = x + (size_t)min(xquad ? (lane >> 2) : col, M - 1) * K;
   u32x4_t xv[BPW][BSC][4][HS];
+  float xsum[BPW];
 #pragma unroll
   for (int k = 0; k < BPW; ++k)
 #pragma unroll
@@ -171,13 +172,23 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   }
 
 #pragma unroll
-  for (int k = 0; k < BPW; ++k)
+  for (int k = 0; k < BPW; ++k) {
+    float P[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < BSC; ++u)
+    for (int u = 0; u < BSC; ++u) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        const int j = u * GPS + i / REGS_G;
+#pragma unroll
+        for (int l = 0; l < HS; ++l)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) P[j] = dot2_bf16(xv[k][u][i][l][e], 0x3F803F80u, P[j]);
 #pragma unroll
         for (int l = 0; l < HS; ++l) xv[k][u][i][l] = pair_activations<BITS>(xv[k][u][i][l]);
+      }
+    }
+    xsum[k] = rows_transpose_reduce4(P);
+  }
 
   // ---- groups of S tile steps (the unrolled ring); a range always has a
   // tile (do-while: no guard branch that would let the compiler sink the
@@ -205,6 +216,9 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
       __builtin_amdgcn_sched_barrier(0);
 
       f32x4_t acc = zero4;
+      // traces of nonzero weights in this lane's quarter of the column (see
+      // zero weights in qgemv_device.h)
+      uint32_t nz = 0u;
       if constexpr (MQ) {
 #pragma unroll
         for (int k = 0; k < BPW; ++k) {
@@ -215,11 +229,8 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
 #pragma unroll
       for (int k = 0; k < BPW; ++k) {
         if (!own[k]) continue;  // uniform per wave
-        // codes', zero point's and ones' products of the current group (see
-        // the single-pass kernel)
-        f32x4_t accg, accz, accx;
-        u32x4_t zq;
-        float bres;
+        f32x4_t accg;
+        uint32_t zc0 = 0u;  // the current group's first code word
 #pragma unroll
         for (int u = 0; u < BSC; ++u) {
           uint32_t cur[4];
@@ -232,33 +243,45 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
             for (int h = 0; h < HS; ++h) {
               const bool gfirst = (i % REGS_G) == 0 && h == 0;
               const bool glast = (i % REGS_G) == REGS_G - 1 && h == HS - 1;
-              const uint32_t sw = (jg < 2) ? s4[s][k].x : s4[s][k].y;
-              const float scl = half_bits_to_float((jg & 1) ? (sw >> 16) : (sw & 0xFFFFu));
-              if (gfirst) {
-                const uint32_t bw16 = (jg < 2) ? b4[s][k].x : b4[s][k].y;
-                const ZeroPoint zp =
-                    zero_point(scl, half_bits_to_float((jg & 1) ? (bw16 >> 16) : (bw16 & 0xFFFFu)), ZMAX);
-                zq = u32x4_t{zp.zpair, zp.zpair, zp.zpair, zp.zpair};
-                bres = zp.bres;
+              if (h == 0) {
+                // zero-weight traces: code words against the group's first,
+                // then the group's weight s*c + b at its last word
+                if (gfirst) {
+                  zc0 = cur[i];
+                  nz |= fields_spread<BITS>(cur[i]);
+                } else {
+                  nz |= cur[i] ^ zc0;
+                }
+                pin(nz);
+                if ((i % REGS_G) == REGS_G - 1) {
+                  const uint2 sw_v = s4[s][k];
+                  const uint2 bw16_v = b4[s][k];
+                  nz |= weight_trace(half_bits_to_float(field16(sw_v, jg)), low_field<BITS>(zc0),
+                                     half_bits_to_float(field16(bw16_v, jg)));
+                }
               }
               const u32x4_t bw = BITS == 4 ? unpack4_quad(cur[i]) : unpack2_quad(cur[i], h);
-              const bf16x8_t a8 = __builtin_bit_cast(bf16x8_t, xv[k][u][i][h]);
-              accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, __builtin_bit_cast(bf16x8_t, bw),
-                                                            gfirst ? zero4 : accg, 0, 0, 0);
-              accz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, __builtin_bit_cast(bf16x8_t, zq),
-                                                            gfirst ? zero4 : accz, 0, 0, 0);
-              accx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, ones8, gfirst ? zero4 : accx, 0, 0, 0);
+              accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8_t, xv[k][u][i][h]), __builtin_bit_cast(bf16x8_t, bw),
+                  gfirst ? zero4 : accg, 0, 0, 0);
               if (glast) {
+                const uint2 sw_v = s4[s][k];
+                const float scl = half_bits_to_float(field16(sw_v, jg));
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                  acc[q] = fmaf(scl, accg[q] - accz[q], fmaf(bres, accx[q], acc[q]));
+                for (int q = 0; q < 4; ++q) acc[q] = fmaf(scl, accg[q], acc[q]);
               }
             }
           }
         }
+        // bias: acc += xsum[m][g0+kb] * b[n][g0+kb]
+        const uint2 bw_v = b4[s][k];
+        const float b = half_bits_to_float(field16(bw_v, kb));
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum[k], b, acc, 0, 0, 0);
       }
+      // a partial whose column held only zero weights is exactly 0
+      const uint32_t keep = keep_mask(column_or(nz));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[s][wave][i][lane] = acc[i];
+      for (int i = 0; i < 4; ++i) red[s][wave][i][lane] = unless_zero(acc[i], keep);
     }
 
     // ---- sum the group's partial tiles over the waves in block order

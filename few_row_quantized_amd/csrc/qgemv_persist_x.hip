@@ -27,7 +27,11 @@
 //   are requested, then the workgroup copies its share of x (M rows of the
 //   phase's blocks) into LDS, already re-paired to the code pairing of the
 //   MFMA operand (elements (0,2), (1,3), (4,6), (5,7) of each 8 for 4-bit
-//   codes, (e, e+4) of each 8 for 2-bit codes).
+//   codes, (e, e+4) of each 8 for 2-bit codes), and forms the
+//   activation sum of every group of that share from the registers: the
+//   lanes holding a group's units reduce their sums by a fixed butterfly
+//   (summing a group from LDS instead, one lane per group, put every lane of
+//   a wave on the same bank: row offsets of GS*2 bytes).
 // * Phase q covers the blocks [q*nb/P, (q+1)*nb/P) of the half; wave w owns
 //   its blocks lo+w, lo+w+W, ...  The workgroup walks (phase, tile) steps in
 //   phase-major order; each step's codes and metadata come through a
@@ -35,8 +39,9 @@
 //   current one is multiplied, also across a phase change); the
 //   activation operand of each v_mfma_f32_16x16x32_bf16 is one 16-byte LDS
 //   read per lane (rows m >= M read row M-1: their outputs are never
-//   stored).  Unpack, scale fold and the bias (zero point and the MFMA
-//   steps against bf16 ones) are those of the other MFMA kernels.
+//   stored).  Unpack, scale fold, the bias product (v_mfma_f32_16x16x4_f32
+//   against the group sums) and the zero-weight flags are those of the
+//   other MFMA kernels.
 // * Each wave adds its partial 16x16 tile of a step into an LDS slot of its
 //   own per tile (no barrier between steps); after the last step the slots
 //   are summed over the waves in block order and each half is added into y
@@ -85,11 +90,13 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
   // 11.3 -> 10.6 us at M = 8), slower by 1-5% with groups of 128 and for
   // 2-bit codes, where metadata loads are few
   constexpr bool MQ = BITS == 4 && GS <= 64;
-  constexpr int UE = 8;  // elements of one re-pairing unit (16 bytes)
+  constexpr int UE = BITS == 4 ? 8 : 16;  // elements of one re-pairing unit
+  constexpr int GU = GS / UE;             // units per group (a power of two <= 16)
   // staging units per thread per round: their registers are live next to
   // one ring slot, so at most 32 VGPRs, 16 when the slot holds 8 super-chunks
-  constexpr int XU = BPW * BSC >= 8 ? 4 : 8;
+  constexpr int XU = (BPW * BSC >= 8 ? 4 : 8) / (UE / 8);
   static_assert(BSC >= 1 && BLKW % SCW == 0 && CPG >= 1 && (BITS == 2 || BITS == 4), "layout");
+  static_assert(GU >= 1 && GU <= 64 && (GU & (GU - 1)) == 0, "group lanes");
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -100,8 +107,6 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
   const size_t RB = (size_t)K * BITS / 8;
   const int NG = K / GS;
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-  const bf16x8_t ones8 = __builtin_bit_cast(bf16x8_t, u32x4_t{kOnesPair, kOnesPair, kOnesPair, kOnesPair});
-  constexpr int ZMAX = (1 << BITS) - 1;  // largest code
 
   // half of K and tile range of this workgroup (products stay below 2^31:
   // the grid is at most twice the CU count and T <= 2^18)
@@ -117,12 +122,14 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
   const int ntile = (int)((unsigned)(gp + 1) * (unsigned)T / (unsigned)GP) - t_first;
   const int steps = P * ntile;  // (phase, tile) steps, phase-major
 
-  // LDS: x rows of the phase (re-paired bf16, padded pitch) and one partial
-  // 16x16 tile per (tile, wave), added to over the phases
+  // LDS: x rows of the phase (re-paired bf16, padded pitch), its group sums,
+  // and one partial 16x16 tile per (tile, wave), added to over the phases
   extern __shared__ uint4 lds[];
   const int pitch = nbq_max * BLKW * 2 + 16;  // bytes per activation row
+  const int gpr = nbq_max * 4;                // group sums per row
   uint8_t *xl = reinterpret_cast<uint8_t *>(lds);
-  float *pacc = reinterpret_cast<float *>(xl + (size_t)M * pitch);  // [ntile_max][W][4][64]
+  float *xs = reinterpret_cast<float *>(xl + (size_t)M * pitch);
+  float *pacc = xs + (size_t)M * gpr;  // [ntile_max][W][4][64]
 
   int xoff[4];
 #pragma unroll
@@ -174,31 +181,44 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
     ++it;
   };
 
-  // ---- stage x of phase q into LDS, re-paired, XU units of 8 activations
-  // per thread at a time (all loads of a round issued before any is used;
-  // clamped indices read a valid unit and are not stored)
+  // ---- stage x of phase q into LDS, re-paired, with the activation sum of
+  // every group, XU units per thread at a time (all loads of a round issued
+  // before any is used; clamped indices read a valid unit and are not
+  // stored).  Units are dealt to consecutive lanes, so the GU lanes holding
+  // a group's units add their sums in a fixed butterfly.
   auto stage = [&](const int q) {
     const int lo = phase_lo(q);
     const int upr = (phase_lo(q + 1) - lo) * BLKW / UE;  // units per row
     const int units = M * upr;
     const uint16_t *xh = x + (size_t)(p_lo + lo) * BLKW;
     for (int u0 = 0; u0 < units; u0 += XU * (int)blockDim.x) {
-      u32x4_t v[XU];
+      u32x4_t v[XU][UE / 8];
 #pragma unroll
       for (int j = 0; j < XU; ++j) {
         const int u = min(u0 + j * (int)blockDim.x + (int)threadIdx.x, units - 1);
         const int m = u / upr;
         const int c = u - m * upr;
-        v[j] = *reinterpret_cast<const u32x4_t *>(xh + (size_t)m * K + (size_t)c * UE);
+#pragma unroll
+        for (int h = 0; h < UE / 8; ++h)
+          v[j][h] = *reinterpret_cast<const u32x4_t *>(xh + (size_t)m * K + (size_t)c * UE + 8 * h);
       }
 #pragma unroll
       for (int j = 0; j < XU; ++j) {
         const int u = u0 + j * (int)blockDim.x + (int)threadIdx.x;
+        float p = 0.f;
+#pragma unroll
+        for (int h = 0; h < UE / 8; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p = dot2_bf16(v[j][h][e], 0x3F803F80u, p);
+#pragma unroll
+        for (int off = 1; off < GU; off <<= 1) p += __shfl_xor(p, off);
         if (u < units) {
           const int m = u / upr;
           const int c = u - m * upr;
-          *reinterpret_cast<u32x4_t *>(xl + (size_t)m * pitch + (size_t)c * UE * 2) =
-              pair_activations<BITS>(v[j]);
+          if ((threadIdx.x & (GU - 1)) == 0) xs[m * gpr + c / GU] = p;
+          u32x4_t *dst = reinterpret_cast<u32x4_t *>(xl + (size_t)m * pitch + (size_t)c * UE * 2);
+#pragma unroll
+          for (int h = 0; h < UE / 8; ++h) dst[h] = pair_activations<BITS>(v[j][h]);
         }
       }
     }
@@ -207,6 +227,7 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
 
   // this lane's activation row in LDS (rows m >= M read row M-1)
   const uint8_t *xrow = xl + (size_t)(col < M ? col : M - 1) * pitch;
+  const float *xsrow = xs + (col < M ? col : M - 1) * gpr;
 
 #pragma unroll
   for (int s = 0; s < S - 1; ++s) issue(s);
@@ -231,6 +252,9 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
 
       const int lo = phase_lo(q);
       f32x4_t acc = zero4;
+      // traces of nonzero weights in this lane's quarter of the column (see
+      // zero weights in qgemv_device.h)
+      uint32_t nz = 0u;
       if constexpr (MQ) {
 #pragma unroll
         for (int k = 0; k < BPW; ++k) {
@@ -243,11 +267,8 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
         int blk;
         if (!owned(q, k, blk)) continue;  // uniform per wave
         const int lq = blk - lo;          // block within the phase
-        // codes', zero point's and ones' products of the current group (see
-        // the single-pass kernel)
-        f32x4_t accg, accz, accx;
-        u32x4_t zq;
-        float bres;
+        f32x4_t accg;
+        uint32_t zc0 = 0u;  // the current group's first code word
 #pragma unroll
         for (int u = 0; u < BSC; ++u) {
           uint32_t cur[4];
@@ -262,36 +283,51 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
               const bool gfirst = (i % REGS_G) == 0 && h == 0;
               const bool glast = (i % REGS_G) == REGS_G - 1 && h == HS - 1;
               const u32x4_t av = *reinterpret_cast<const u32x4_t *>(xrow + (size_t)(k0 + xoff[i] + 8 * h) * 2);
-              const uint32_t sw = (jg < 2) ? s4[s][k].x : s4[s][k].y;
-              const float scl = half_bits_to_float((jg & 1) ? (sw >> 16) : (sw & 0xFFFFu));
-              if (gfirst) {
-                const uint32_t bw16 = (jg < 2) ? b4[s][k].x : b4[s][k].y;
-                const ZeroPoint zp =
-                    zero_point(scl, half_bits_to_float((jg & 1) ? (bw16 >> 16) : (bw16 & 0xFFFFu)), ZMAX);
-                zq = u32x4_t{zp.zpair, zp.zpair, zp.zpair, zp.zpair};
-                bres = zp.bres;
+              if (h == 0) {
+                // zero-weight traces: code words against the group's first,
+                // then the group's weight s*c + b at its last word
+                if (gfirst) {
+                  zc0 = cur[i];
+                  nz |= fields_spread<BITS>(cur[i]);
+                } else {
+                  nz |= cur[i] ^ zc0;
+                }
+                pin(nz);
+                if ((i % REGS_G) == REGS_G - 1) {
+                  const uint2 sw_v = s4[s][k];
+                  const uint2 bw16_v = b4[s][k];
+                  nz |= weight_trace(half_bits_to_float(field16(sw_v, jg)), low_field<BITS>(zc0),
+                                     half_bits_to_float(field16(bw16_v, jg)));
+                }
               }
               const u32x4_t bw = BITS == 4 ? unpack4_quad(cur[i]) : unpack2_quad(cur[i], h);
-              const bf16x8_t a8 = __builtin_bit_cast(bf16x8_t, av);
-              accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, __builtin_bit_cast(bf16x8_t, bw),
+              accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                            __builtin_bit_cast(bf16x8_t, bw),
                                                             gfirst ? zero4 : accg, 0, 0, 0);
-              accz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, __builtin_bit_cast(bf16x8_t, zq),
-                                                            gfirst ? zero4 : accz, 0, 0, 0);
-              accx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, ones8, gfirst ? zero4 : accx, 0, 0, 0);
               if (glast) {
+                const uint2 sw_v = s4[s][k];
+                const float scl = half_bits_to_float(field16(sw_v, jg));
 #pragma unroll
-                for (int qq = 0; qq < 4; ++qq)
-                  acc[qq] = fmaf(scl, accg[qq] - accz[qq], fmaf(bres, accx[qq], acc[qq]));
+                for (int qq = 0; qq < 4; ++qq) acc[qq] = fmaf(scl, accg[qq], acc[qq]);
               }
             }
           }
         }
+        // bias: acc += xsum[m][g0+kb] * b[n][g0+kb]
+        const uint2 bw_v = b4[s][k];
+        const float b = half_bits_to_float(field16(bw_v, kb));
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xsrow[lq * 4 + kb], b, acc, 0, 0, 0);
       }
       // this wave's partial of tile tt: its own LDS slot, added to over the
       // phases in phase order
       float *pa = pacc + (size_t)((tt * W + wave) * 4) * 64 + lane;
+      // a partial whose column held only zero weights is exactly 0
+      const uint32_t keep = keep_mask(column_or(nz));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pa[i * 64] = q == 0 ? acc[i] : pa[i * 64] + acc[i];
+      for (int i = 0; i < 4; ++i) {
+        const float a = unless_zero(acc[i], keep);
+        pa[i * 64] = q == 0 ? a : pa[i * 64] + a;
+      }
     }
     j0 += S;
   } while (j0 < steps);
@@ -369,7 +405,8 @@ int launch_persist_x_t(const QgemvArgs &a, hipStream_t stream) {
       const int waves = (nbq_max + bpw - 1) / bpw;
       if (waves > kXMaxWaves) continue;
       const size_t pitch = (size_t)nbq_max * 4 * GS * 2 + 16;
-      const size_t lds = (size_t)a.M * pitch + (size_t)ntile_max * waves * 256 * sizeof(float);
+      const size_t lds = (size_t)a.M * pitch + (size_t)a.M * nbq_max * 4 * sizeof(float) +
+                         (size_t)ntile_max * waves * 256 * sizeof(float);
       if (lds > kLdsMax) continue;
       if (variant == 0)
         return launch_persist_x_k<BITS, GS, Sh::BPW_SMALL, ADD>(a, waves, grid, lds, phases, ntile_max, stream);
