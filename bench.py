@@ -422,8 +422,9 @@ def measured_traffic(workload, M):
 
 def measure_ceiling(W, copies, chain, capture, time_graph):
     """Pure streaming read of W bytes per launch (qgemv_stream_probe) over the
-    same rotating-pool protocol, and the same probe on a tiny buffer (the
-    per-launch floor of a graph chain)."""
+    same rotating-pool protocol, for each loads-per-thread setting of the
+    probe; the ceiling is the fastest.  Also the same probe on a tiny buffer
+    (the per-launch floor of a graph chain)."""
     import torch
     from few_row_quantized_amd import qgemv as q
     nbytes = (W + 15) // 16 * 16
@@ -432,24 +433,31 @@ def measure_ceiling(W, copies, chain, capture, time_graph):
     small = 64 * 1024
     sout = torch.empty(q.qgemv_stream_probe_blocks(small), dtype=torch.int32, device="cuda")
     ctr = [0]
+    per_cfg = {}
+    for u in (2, 4, 8, 16):
+        def one(u=u):
+            i = ctr[0] % copies
+            ctr[0] += 1
+            q.qgemv_stream_probe(buf[i], nbytes, out, u)
 
-    def one():
-        i = ctr[0] % copies
-        ctr[0] += 1
-        q.qgemv_stream_probe(buf[i], nbytes, out)
-
-    one()
-    g = capture(lambda: [one() for _ in range(chain)])
-    time_graph(g)
-    t = time_graph(g, reps=2) / (2 * chain)
-    gs = capture(lambda: [q.qgemv_stream_probe(buf[0], small, sout) for _ in range(chain)])
+        one()
+        g = capture(lambda: [one() for _ in range(chain)])
+        time_graph(g)
+        per_cfg[u] = time_graph(g, reps=2) / (2 * chain)
+    best = min(per_cfg, key=per_cfg.get)
+    t = per_cfg[best]
+    gs = capture(lambda: [q.qgemv_stream_probe(buf[0], small, sout, 4) for _ in range(chain)])
     time_graph(gs)
     tf = time_graph(gs, reps=2) / (2 * chain)
-    log(f"[bench] stream probe {nbytes} B: {t * 1e6:.3f} us/launch = {nbytes / t / 1e9:.1f} GB/s; "
-        f"64 KiB floor {tf * 1e6:.3f} us")
+    log(f"[bench] stream probe {nbytes} B: best {t * 1e6:.3f} us/launch ({best} loads/thread) = "
+        f"{nbytes / t / 1e9:.1f} GB/s; by loads/thread "
+        + ", ".join(f"{u}: {v * 1e6:.3f}" for u, v in per_cfg.items())
+        + f"; 64 KiB floor {tf * 1e6:.3f} us")
     del buf
     return {"stream_probe_bytes": nbytes, "stream_probe_us": round(t * 1e6, 4),
             "stream_probe_GBps": round(nbytes / t / 1e9, 1),
+            "stream_probe_loads_per_thread": best,
+            "stream_probe_us_by_loads_per_thread": {str(u): round(v * 1e6, 4) for u, v in per_cfg.items()},
             "launch_floor_us_64KiB": round(tf * 1e6, 4)}
 
 
@@ -498,6 +506,9 @@ def cpu_baseline(p, ms, W, budget_s):
                 "wall_s": round(time.perf_counter() - t0, 1)}
 
     threads = blas_threads()
+    blas = [{"library": i.get("internal_api"), "version": i.get("version"),
+             "threading_layer": i.get("threading_layer"), "num_threads": i.get("num_threads")}
+            for i in threadpool_info() if i.get("user_api") == "blas"]
     multi = run(budget_s * 2 / 3, 3)
     with threadpool_limits(limits=1, user_api="blas"):
         single = run(0.0, 3)
@@ -505,7 +516,7 @@ def cpu_baseline(p, ms, W, budget_s):
             "sample": f"{multi['steps']} verify steps (one oracle call per M in {ms}) of {s.name}; "
                       f"median call time per M; numpy fp64 unpack + dequantize + BLAS matmul",
             "median_ms_per_call": multi["median_ms_per_call"], "wall_s": multi["wall_s"],
-            "one_thread": single, "cpu_count": os.cpu_count(), "cpu_model": cpu_model()}
+            "one_thread": single, "cpu_count": os.cpu_count(), "cpu_model": cpu_model(), "blas": blas}
 
 
 if __name__ == "__main__":

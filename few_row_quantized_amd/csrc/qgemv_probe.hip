@@ -220,10 +220,15 @@ __global__ __launch_bounds__(64) void unpack_probe_fp_mfma(const uint8_t *__rest
   }
 }
 
+// Streaming read: each thread reads U 16-byte pieces, consecutive threads
+// consecutive pieces (1 KiB contiguous per wave instruction), the U loads of
+// a thread one grid-width apart and all issued before any is used, with
+// non-temporal loads like the weight stream of the kernels.  The launcher
+// picks U; the data is XOR-folded so that the loads cannot be dropped.
 constexpr int kStreamThreads = 256;
-constexpr int kStreamUnroll = 4;
-constexpr int kStreamMaxBlocks = 2048;
+constexpr int kStreamMinUnroll = 2;
 
+template <int U>
 __global__ __launch_bounds__(kStreamThreads) void stream_probe_kernel(const uint4 *__restrict__ buf,
                                                                       size_t n16,
                                                                       uint32_t *__restrict__ out) {
@@ -231,16 +236,16 @@ __global__ __launch_bounds__(kStreamThreads) void stream_probe_kernel(const uint
   const size_t stride = (size_t)gridDim.x * kStreamThreads;
   size_t i = (size_t)blockIdx.x * kStreamThreads + threadIdx.x;
   uint32_t h = 0;
-  for (; i + (kStreamUnroll - 1) * stride < n16; i += kStreamUnroll * stride) {
-    uint4 v[kStreamUnroll];
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    u32x4_t v[U];
 #pragma unroll
-    for (int u = 0; u < kStreamUnroll; ++u) v[u] = buf[i + u * stride];
+    for (int u = 0; u < U; ++u) v[u] = load_stream_u32x4(buf + i + u * stride);
 #pragma unroll
-    for (int u = 0; u < kStreamUnroll; ++u) h ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    for (int u = 0; u < U; ++u) h ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
   for (; i < n16; i += stride) {
-    const uint4 v = buf[i];
-    h ^= v.x ^ v.y ^ v.z ^ v.w;
+    const u32x4_t v = load_stream_u32x4(buf + i);
+    h ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }
   // xor over the wave, then over the block
 #pragma unroll
@@ -252,6 +257,12 @@ __global__ __launch_bounds__(kStreamThreads) void stream_probe_kernel(const uint
     for (int w = 0; w < kStreamThreads / 64; ++w) t ^= part[w];
     out[blockIdx.x] = t;
   }
+}
+
+int stream_blocks(size_t nbytes, int unroll) {
+  const size_t n16 = nbytes / 16;
+  size_t blocks = (n16 + (size_t)kStreamThreads * unroll - 1) / ((size_t)kStreamThreads * unroll);
+  return blocks < 1 ? 1 : (int)blocks;
 }
 
 }  // namespace
@@ -312,18 +323,19 @@ int launch_unpack_probe_fp(int path, const uint8_t *codes, uint16_t *out, int N,
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
 }
 
-int stream_probe_blocks(size_t nbytes) {
-  const size_t n16 = nbytes / 16;
-  size_t blocks = (n16 + (size_t)kStreamThreads * kStreamUnroll - 1) / ((size_t)kStreamThreads * kStreamUnroll);
-  if (blocks < 1) blocks = 1;
-  if (blocks > (size_t)kStreamMaxBlocks) blocks = kStreamMaxBlocks;
-  return (int)blocks;
-}
+int stream_probe_blocks(size_t nbytes) { return stream_blocks(nbytes, kStreamMinUnroll); }
 
-int launch_stream_probe(const uint8_t *buf, size_t nbytes, uint32_t *out, hipStream_t stream) {
-  const int blocks = stream_probe_blocks(nbytes);
-  hipLaunchKernelGGL(stream_probe_kernel, dim3(blocks), dim3(kStreamThreads), 0, stream,
-                     reinterpret_cast<const uint4 *>(buf), nbytes / 16, out);
+int launch_stream_probe(const uint8_t *buf, size_t nbytes, uint32_t *out, int unroll, hipStream_t stream) {
+  const auto *b16 = reinterpret_cast<const uint4 *>(buf);
+  const size_t n16 = nbytes / 16;
+  const int blocks = stream_blocks(nbytes, unroll);
+  switch (unroll) {
+    case 2: hipLaunchKernelGGL(stream_probe_kernel<2>, dim3(blocks), dim3(kStreamThreads), 0, stream, b16, n16, out); break;
+    case 4: hipLaunchKernelGGL(stream_probe_kernel<4>, dim3(blocks), dim3(kStreamThreads), 0, stream, b16, n16, out); break;
+    case 8: hipLaunchKernelGGL(stream_probe_kernel<8>, dim3(blocks), dim3(kStreamThreads), 0, stream, b16, n16, out); break;
+    case 16: hipLaunchKernelGGL(stream_probe_kernel<16>, dim3(blocks), dim3(kStreamThreads), 0, stream, b16, n16, out); break;
+    default: return QGEMV_EINVAL;
+  }
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
 }
 

@@ -143,6 +143,35 @@ def test_unit_scale_onehot_gives_elements_exactly(fmt):
             assert np.array_equal(y[m], els[:, synth.onehot_column(m, K)].astype(np.float32)), f"{path} row {m}"
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_every_scale_byte_decodes_exactly(fmt):
+    # every E8M0 scale byte 0..254 (0x00 is 2^-127, an fp32 subnormal) and
+    # every finite E4M3 scale byte (negative and subnormal included), through
+    # the real kernels: row n's blocks all carry scale byte n, every element
+    # is 1.0 and row m of x is one-hot, so y[m, n] is the decoded scale itself
+    K, M = 256, 16
+    vals = np.arange(255, dtype=np.uint8) if fmt.startswith("mx") else \
+        np.array([v for v in range(256) if v not in (0x7F, 0xFF)], dtype=np.uint8)
+    N = len(vals)
+    p = synth.make_problem(synth.custom_fp_shape(K, N, fmt, seed=23), m_max=M)
+    p.codes[:] = 0x22 if synth.FP_BITS[fmt] == 4 else 0x38  # E2M1 / E4M3 1.0
+    p.scales[:] = vals[:, None]
+    p.x[:] = 0
+    for m in range(M):
+        p.x[m, synth.onehot_column(m, K)] = 0x3F80
+    want = (oracle.e8m0_to_f64(vals) if fmt.startswith("mx") else oracle.e4m3_to_f64(vals)).astype(np.float32)
+    assert np.all(np.isfinite(want))
+    d = FpDevice(p)
+    for path in paths_for(p, M):
+        for MM in (1, 2, 5, 16):
+            say(f"fp every scale byte {path} {fmt} M={MM}")
+            y = d.run(MM, path)
+            for m in range(MM):
+                # float equality: bit equality except that the product of a
+                # -0 scale may be stored as +0
+                assert np.array_equal(y[m], want), f"{path} M={MM} row {m}: scale bytes {vals[y[m] != want][:8]}"
+
+
 # ---------------------------------------------------------------- every element
 
 RAGGED = [(256, 512), (640, 40), (1024, 300), (2048, 97), (8192, 33), (128, 16), (3840, 200)]
