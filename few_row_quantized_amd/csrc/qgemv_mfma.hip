@@ -110,15 +110,16 @@ int launch_mfma_t(const QgemvArgs &a, hipStream_t stream) {
 template <int BITS, int GS, int FMT = kAffine>
 int launch_mfma_gs(const QgemvArgs &a, hipStream_t stream) {
   // more output columns per workgroup on wide matrices: every workgroup reads
-  // all M*K activations, so wider groups cut that traffic per weight byte;
-  // also on long K with at least a tile per CU once M > 8, where the
-  // persistent kernels do not run (an in-place residual sum, K beyond their
-  // reach; measured on the 17408-long down projections: 36.0 against 39.6 us
-  // at M = 16, and slower than one tile below M = 8)
+  // all M*K activations, so wider groups cut that traffic per weight byte.
+  // The choice depends on the shape only: the two-tile kernel has half the
+  // thread cap, so it splits K into other wave slices, and a choice by M
+  // would make the rows of an M-row call differ in the last bits from the
+  // single-row calls.  (Two tiles on long K once M > 8 measured 36.0 against
+  // 39.6 us at M = 16 on the 17408-long down projection where the
+  // persistent kernels do not run, and slower than one tile below M = 8.)
   const int tiles = (a.N + 15) / 16;
   const int cus = device_cu_count();
-  const bool wide = tiles >= 2 * cus ||
-                    (FMT == kAffine && BITS != 8 && tiles >= cus && a.K >= 8192 && a.M > 8);
+  const bool wide = tiles >= 2 * cus;
   if (a.res) {
     if (wide) return launch_mfma_t<BITS, GS, 2, true, FMT>(a, stream);
     return launch_mfma_t<BITS, GS, 1, true, FMT>(a, stream);

@@ -68,7 +68,16 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   __shared__ float red[MAXT / 64][NT][4][64];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // floor(a / waves) for 0 <= a <= 65536 through a reciprocal, in scalar
+  // registers: the true quotient's fraction is a multiple of 1/waves, so a
+  // half-step margin (>= 1/32 for waves <= 16) absorbs the reciprocal's and
+  // the product's rounding (< 0.02 at these sizes).  Used for the slice
+  // rotation (tile group / 8 <= 65536) and the slice bounds (<= 16 * 1024).
+  const float rwaves = __builtin_amdgcn_rcpf((float)(blockDim.x >> 6));
+  auto div_waves = [&](const int a) -> int {
+    return __builtin_amdgcn_readfirstlane((int)(((float)a + 0.5f) * rwaves));
+  };
   const int waves = blockDim.x >> 6;
   const int col = lane & 15;
   const int kb = lane >> 4;
@@ -228,9 +237,10 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   // CUs sharing an L2 do not all read the same activation lines at the same
   // moment.  Partials are reduced in slice order, so results do not depend
   // on the rotation.
-  const int slice = (wave + (tg >> 3)) % waves;
-  const int b_begin = p_lo + (slice * nbp) / waves;
-  const int b_end = p_lo + ((slice + 1) * nbp) / waves;
+  const int rot = (tg >> 3) - div_waves(tg >> 3) * waves;
+  const int slice = wave + rot < waves ? wave + rot : wave + rot - waves;
+  const int b_begin = p_lo + div_waves(slice * nbp);
+  const int b_end = p_lo + div_waves((slice + 1) * nbp);
   const size_t RB = (size_t)K * BITS / 8;
   const int G = FMT == kNvfp4 ? K / 16 : K / GS;  // scale (or scale-and-bias) entries per row
   // Rows m >= M and columns n >= N only feed outputs that are never stored,

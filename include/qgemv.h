@@ -83,10 +83,22 @@ extern "C" {
  * group's partial dot product and the bias once to the group's activation sum
  * (scale hoisted out of the inner loop, MLX page, Facts: the qmv_wide tuning
  * bullet).  Result within 1e-3 * sum_k |x_k w_k| + 1e-6 of the exact value.
- * Within one path, row m of an M-row call equals (bitwise) the M=1 call on
- * x[m]: per-row accumulation order does not depend on M, and results are
- * deterministic (where the MFMA path splits K over two workgroups, y receives
- * exactly two float additions onto zero, which commute bit for bit).
+ * An output column n whose dequantized weights w[n][*] are all exactly zero
+ * gives exactly 0 (exactly r with the residual sum).
+ * Results are deterministic (where the MFMA path splits K over two
+ * workgroups, y receives exactly two float additions onto zero, which
+ * commute bit for bit).  Within one path, row m of an M-row call equals
+ * (bitwise) the M=1 call on x[m] whenever both calls run the same kernel
+ * configuration, whose per-row accumulation order depends on the shape
+ * alone.  One case depends on M: on the MFMA path, with more 16-column
+ * tiles than compute units and K too long for the register-resident
+ * persistent kernel (K > 4096 for 4-bit codes in groups of 32 or 64, K >
+ * 6144 otherwise), the long-K kernel takes its phase count and
+ * blocks per wave from an LDS budget that grows with M, and the single-pass
+ * kernel runs beyond the largest M that budget holds.  Rows of calls on
+ * different sides of such a threshold agree within the tolerance above, not
+ * bit for bit (K = 17408, N = 5120, 4-bit, group size 128: M = 1..7, 8..14
+ * and 15..16 are three configurations).
  */
 int qgemv_small(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
                 const uint16_t *x, float *y, int M, int N, int K, int bits, int group_size,

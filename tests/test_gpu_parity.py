@@ -186,7 +186,8 @@ def test_zero_codes(path):
                                          (4, 64, 4500, 2048), (2, 128, 4500, 2048),
                                          (4, 128, 300, 8192), (2, 64, 150, 10240),
                                          (4, 128, 4200, 6656), (2, 64, 4130, 8192),
-                                         (8, 64, 200, 2048), (8, 32, 4500, 1024), (8, 64, 150, 10240)])
+                                         (8, 64, 200, 2048), (8, 32, 4500, 1024), (8, 64, 150, 10240),
+                                         (4, 64, 4096, 8192)])
 @pytest.mark.parametrize("path", ["dot", "mfma"])
 def test_row_of_m_row_call_equals_single_row_call_bitwise(path, bits, gs, N, K):
     import torch
@@ -204,6 +205,34 @@ def test_row_of_m_row_call_equals_single_row_call_bitwise(path, bits, gs, N, K):
     for M in (2, 3, 4, 5, 8, 12, 16):
         y = d.run_host(M, path)
         assert np.array_equal(y, singles[:M]), f"M={M}"
+
+
+@pytest.mark.parametrize("bits,gs,N,K", [(4, 128, 4200, 17408), (2, 64, 4130, 17408)])
+def test_long_k_row_invariance_by_configuration(bits, gs, N, K):
+    # Long K with more tiles than CUs: the long-K kernel's configuration
+    # depends on M through its LDS budget (tests/kernel_config.py mirrors the
+    # launch search).  Rows agree bit for bit within a configuration, and with
+    # the oracle's tolerance across configurations.
+    import torch
+    from kernel_config import mfma_configuration
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    p = synth.make_problem(synth.custom_shape(K, N, bits, gs, seed=78), m_max=16)
+    d = DeviceProblem(p)
+    orc = OracleRows.affine(p, 16)
+    say(f"long-K row invariance bits={bits} gs={gs} N={N} K={K} cus={cus}")
+    first = {}  # configuration -> (M, y) of its smallest M
+    configs = set()
+    for M in range(1, 17):
+        cfg = mfma_configuration(M, N, K, bits, gs, cus)
+        configs.add(cfg)
+        y = d.run_host(M, "mfma")
+        orc.check(y, M, f"M={M} {cfg}")
+        if cfg in first:
+            M0, y0 = first[cfg]
+            assert np.array_equal(y[:M0], y0), f"M={M} differs from M={M0} within {cfg}"
+        else:
+            first[cfg] = (M, y)
+    assert len(configs) >= 2, "the shape should cross a configuration threshold"
 
 
 @pytest.mark.parametrize("name", ["square_k4096_n4096_4b_g64", "layer27b_gate", "layer27b_down",
