@@ -235,9 +235,19 @@ def main():
     alg = alg_bytes(Mdom)
     achieved = alg / per_m[Mdom] / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(s.name, Mdom),
-                "kernel": f"qgemv_{paths[Mdom]}_kernel M={Mdom}",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(s.name, Mdom, paths[Mdom]),
+                "kernel": f"{paths[Mdom]} path M={Mdom}",
                 "bytes_per_launch": alg, "avg_launch_us": round(per_m[Mdom] * 1e6, 4)}
+    # the same figure from the committed rocprofv3 trace's average kernel
+    # duration (no launch gaps; the profiler's own overhead included)
+    prof = profiled_kernel_us(s.name, Mdom, paths[Mdom])
+    if prof:
+        a_p = alg / (prof["avg_us"] * 1e-6) / 1e9
+        roofline.update({"achieved_rocprof": round(a_p, 1), "frac_rocprof": round(a_p / HBM_PEAK_GBS, 4),
+                         "rocprof_avg_us": prof["avg_us"], "rocprof_kernel": prof["kernel"],
+                         "rocprof_dispatches": prof["dispatches"], "rocprof_file": prof["file"]})
+    if ceiling:
+        roofline["frac_of_stream_probe"] = round(ceiling["stream_probe_us"] / (per_m[Mdom] * 1e6), 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -401,30 +411,52 @@ def measure_moe(args, capture, time_graph, name="moe30b_gateup_e128_k2048_n1536_
                       "one row's 8 pairs; interleaved rounds, median"}
 
 
-def measured_traffic(workload, M):
-    """HBM bytes per launch (read + write) from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE passes for this workload, scaled by the counters'
-    reading of kernels of known size.  None when no such profile exists or
-    when the kernel sources changed since it was taken."""
+def csrc_sha256():
     import glob
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
-    if not os.path.exists(path):
-        return None
-    rec = json.load(open(path))
     srcs = sorted(glob.glob(os.path.join(ROOT, "few_row_quantized_amd", "csrc", "*")))
-    sha = hashlib.sha256(b"".join(open(f, "rb").read() for f in srcs)).hexdigest()
-    t = rec.get("per_m", {}).get(str(M))
-    if rec.get("csrc_sha256") != sha or t is None:
+    return hashlib.sha256(b"".join(open(f, "rb").read() for f in srcs)).hexdigest()
+
+
+def profiled_kernel_us(workload, M, path):
+    """Average duration (us) of the (path, M) cell's GEMV kernel in the
+    committed rocprofv3 kernel trace of this workload (start to end of each
+    dispatch, the timed chains of a bench run under the profiler), with the
+    file it comes from.  None when no such trace exists or when the kernel
+    sources changed since it was taken."""
+    rel = os.path.join("profiles", f"kernel_trace_{workload}.json")
+    path_json = os.path.join(ROOT, rel)
+    if not os.path.exists(path_json):
+        return None
+    rec = json.load(open(path_json))
+    cell = rec.get("cells", {}).get(f"{path}/{M}")
+    if rec.get("csrc_sha256") != csrc_sha256() or cell is None:
+        return None
+    return {"avg_us": cell["avg_us"], "dispatches": cell["dispatches"], "kernel": cell["kernel"],
+            "file": rel}
+
+
+def measured_traffic(workload, M, path):
+    """HBM bytes per launch (read + write) of the (path, M) cell from the
+    committed rocprofv3 FETCH_SIZE / WRITE_SIZE passes for this workload,
+    each scaled by the counters' reading of a device copy of known size in
+    the same run.  None when no such profile exists or when the kernel
+    sources changed since it was taken."""
+    fn = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
+    if not os.path.exists(fn):
+        return None
+    rec = json.load(open(fn))
+    t = rec.get("cells", {}).get(f"{path}/{M}")
+    if rec.get("csrc_sha256") != csrc_sha256() or t is None or t.get("read_bytes") is None:
         return None
     return t["read_bytes"] + t["write_bytes"]
 
 
 def measure_ceiling(W, copies, chain, capture, time_graph):
     """Pure streaming read of W bytes per launch (qgemv_stream_probe) over the
-    same rotating-pool protocol, for each loads-per-thread setting of the
-    probe; the ceiling is the fastest.  Also the same probe on a tiny buffer
-    (the per-launch floor of a graph chain)."""
+    same rotating-pool protocol, for each layout and loads-per-thread setting
+    of the probe; the ceiling is the fastest.  Also the same probe on a tiny
+    buffer (the per-launch floor of a graph chain)."""
     import torch
     from few_row_quantized_amd import qgemv as q
     nbytes = (W + 15) // 16 * 16
@@ -434,30 +466,33 @@ def measure_ceiling(W, copies, chain, capture, time_graph):
     sout = torch.empty(q.qgemv_stream_probe_blocks(small), dtype=torch.int32, device="cuda")
     ctr = [0]
     per_cfg = {}
-    for u in (2, 4, 8, 16):
-        def one(u=u):
-            i = ctr[0] % copies
-            ctr[0] += 1
-            q.qgemv_stream_probe(buf[i], nbytes, out, u)
+    for layout in (0, 1):
+        for u in (1, 2, 4, 8, 16):
+            def one(u=u, layout=layout):
+                i = ctr[0] % copies
+                ctr[0] += 1
+                q.qgemv_stream_probe(buf[i], nbytes, out, u, layout)
 
-        one()
-        g = capture(lambda: [one() for _ in range(chain)])
-        time_graph(g)
-        per_cfg[u] = time_graph(g, reps=2) / (2 * chain)
+            one()
+            g = capture(lambda: [one() for _ in range(chain)])
+            time_graph(g)
+            per_cfg[(layout, u)] = time_graph(g, reps=2) / (2 * chain)
     best = min(per_cfg, key=per_cfg.get)
     t = per_cfg[best]
-    gs = capture(lambda: [q.qgemv_stream_probe(buf[0], small, sout, 4) for _ in range(chain)])
+    gs = capture(lambda: [q.qgemv_stream_probe(buf[0], small, sout, 4, 0) for _ in range(chain)])
     time_graph(gs)
     tf = time_graph(gs, reps=2) / (2 * chain)
-    log(f"[bench] stream probe {nbytes} B: best {t * 1e6:.3f} us/launch ({best} loads/thread) = "
-        f"{nbytes / t / 1e9:.1f} GB/s; by loads/thread "
-        + ", ".join(f"{u}: {v * 1e6:.3f}" for u, v in per_cfg.items())
+    names = {0: "grid-stride", 1: "wave-contiguous"}
+    log(f"[bench] stream probe {nbytes} B: best {t * 1e6:.3f} us/launch ({names[best[0]]}, {best[1]} "
+        f"loads/thread) = {nbytes / t / 1e9:.1f} GB/s; "
+        + ", ".join(f"{names[l]}/{u}: {v * 1e6:.3f}" for (l, u), v in per_cfg.items())
         + f"; 64 KiB floor {tf * 1e6:.3f} us")
     del buf
     return {"stream_probe_bytes": nbytes, "stream_probe_us": round(t * 1e6, 4),
             "stream_probe_GBps": round(nbytes / t / 1e9, 1),
-            "stream_probe_loads_per_thread": best,
-            "stream_probe_us_by_loads_per_thread": {str(u): round(v * 1e6, 4) for u, v in per_cfg.items()},
+            "stream_probe_layout": names[best[0]], "stream_probe_loads_per_thread": best[1],
+            "stream_probe_us_by_setting": {f"{names[l]}/{u}": round(v * 1e6, 4)
+                                           for (l, u), v in per_cfg.items()},
             "launch_floor_us_64KiB": round(tf * 1e6, 4)}
 
 

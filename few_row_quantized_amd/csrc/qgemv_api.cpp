@@ -187,12 +187,15 @@ int qgemv_unpack_probe(int path, const uint8_t *codes, uint8_t *q_out, int N, in
 int qgemv_stream_probe_blocks(size_t nbytes) { return qgemv::stream_probe_blocks(nbytes); }
 
 int qgemv_stream_probe(const uint8_t *buf, size_t nbytes, uint32_t *out, int loads_per_thread,
-                       void *stream) {
+                       int layout, void *stream) {
   if (!buf || !out || nbytes == 0 || nbytes % 16 != 0) return QGEMV_EINVAL;
-  if (loads_per_thread != 2 && loads_per_thread != 4 && loads_per_thread != 8 && loads_per_thread != 16)
+  if (loads_per_thread != 1 && loads_per_thread != 2 && loads_per_thread != 4 && loads_per_thread != 8 &&
+      loads_per_thread != 16)
     return QGEMV_EINVAL;
+  if (layout != 0 && layout != 1) return QGEMV_EINVAL;
   if (!aligned(buf, 16) || !aligned(out, 4)) return QGEMV_EALIGN;
-  return qgemv::launch_stream_probe(buf, nbytes, out, loads_per_thread, reinterpret_cast<hipStream_t>(stream));
+  return qgemv::launch_stream_probe(buf, nbytes, out, loads_per_thread, layout,
+                                    reinterpret_cast<hipStream_t>(stream));
 }
 
 // ---------------------------------------------------------------- FP block formats

@@ -79,7 +79,7 @@ int launch_gather(const QgemvArgs &a, const int32_t *x_idx, const int32_t *e_idx
                   int E, hipStream_t stream);
 int launch_unpack_probe_fp(int path, const uint8_t *codes, uint16_t *out, int N, int K, int fmt,
                            hipStream_t stream);
-int launch_stream_probe(const uint8_t *buf, size_t nbytes, uint32_t *out, int unroll,
+int launch_stream_probe(const uint8_t *buf, size_t nbytes, uint32_t *out, int unroll, int layout,
                         hipStream_t stream);
 int stream_probe_blocks(size_t nbytes);
 

@@ -221,21 +221,38 @@ __global__ __launch_bounds__(64) void unpack_probe_fp_mfma(const uint8_t *__rest
 }
 
 // Streaming read: each thread reads U 16-byte pieces, consecutive threads
-// consecutive pieces (1 KiB contiguous per wave instruction), the U loads of
-// a thread one grid-width apart and all issued before any is used, with
-// non-temporal loads like the weight stream of the kernels.  The launcher
-// picks U; the data is XOR-folded so that the loads cannot be dropped.
+// consecutive pieces (1 KiB contiguous per wave instruction), all issued
+// before any is used, with non-temporal loads like the weight stream of the
+// kernels.  The U loads of a thread are one grid-width apart (CONTIG false)
+// or 1 KiB apart, so that each wave reads U KiB in one piece (CONTIG true).
+// The launcher picks U and the layout; the data is XOR-folded so that the
+// loads cannot be dropped.
 constexpr int kStreamThreads = 256;
-constexpr int kStreamMinUnroll = 2;
+constexpr int kStreamMinUnroll = 1;
 
-template <int U>
+template <int U, bool CONTIG>
 __global__ __launch_bounds__(kStreamThreads) void stream_probe_kernel(const uint4 *__restrict__ buf,
                                                                       size_t n16,
                                                                       uint32_t *__restrict__ out) {
   __shared__ uint32_t part[kStreamThreads / 64];
-  const size_t stride = (size_t)gridDim.x * kStreamThreads;
-  size_t i = (size_t)blockIdx.x * kStreamThreads + threadIdx.x;
   uint32_t h = 0;
+  if constexpr (CONTIG) {
+    // wave w of the grid reads pieces [w*U*64, (w+1)*U*64); pieces past the
+    // end re-read the last one and are not folded
+    const size_t w = (size_t)blockIdx.x * (kStreamThreads / 64) + (threadIdx.x >> 6);
+    const size_t i0 = w * U * 64 + (threadIdx.x & 63);
+    u32x4_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t iu = i0 + (size_t)u * 64;
+      v[u] = load_stream_u32x4(buf + (iu < n16 ? iu : n16 - 1));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i0 + (size_t)u * 64 < n16) h ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  const size_t stride = (size_t)gridDim.x * kStreamThreads;
+  size_t i = CONTIG ? n16 : (size_t)blockIdx.x * kStreamThreads + threadIdx.x;
   for (; i + (U - 1) * stride < n16; i += U * stride) {
     u32x4_t v[U];
 #pragma unroll
@@ -325,18 +342,31 @@ int launch_unpack_probe_fp(int path, const uint8_t *codes, uint16_t *out, int N,
 
 int stream_probe_blocks(size_t nbytes) { return stream_blocks(nbytes, kStreamMinUnroll); }
 
-int launch_stream_probe(const uint8_t *buf, size_t nbytes, uint32_t *out, int unroll, hipStream_t stream) {
-  const auto *b16 = reinterpret_cast<const uint4 *>(buf);
-  const size_t n16 = nbytes / 16;
-  const int blocks = stream_blocks(nbytes, unroll);
+template <bool CONTIG>
+int launch_stream_probe_l(const uint4 *b16, size_t n16, int blocks, uint32_t *out, int unroll,
+                          hipStream_t stream) {
+  const dim3 g(blocks), b(kStreamThreads);
   switch (unroll) {
-    case 2: hipLaunchKernelGGL(stream_probe_kernel<2>, dim3(blocks), dim3(kStreamThreads), 0, stream, b16, n16, out); break;
-    case 4: hipLaunchKernelGGL(stream_probe_kernel<4>, dim3(blocks), dim3(kStreamThreads), 0, stream, b16, n16, out); break;
-    case 8: hipLaunchKernelGGL(stream_probe_kernel<8>, dim3(blocks), dim3(kStreamThreads), 0, stream, b16, n16, out); break;
-    case 16: hipLaunchKernelGGL(stream_probe_kernel<16>, dim3(blocks), dim3(kStreamThreads), 0, stream, b16, n16, out); break;
+    case 1: hipLaunchKernelGGL((stream_probe_kernel<1, CONTIG>), g, b, 0, stream, b16, n16, out); break;
+    case 2: hipLaunchKernelGGL((stream_probe_kernel<2, CONTIG>), g, b, 0, stream, b16, n16, out); break;
+    case 4: hipLaunchKernelGGL((stream_probe_kernel<4, CONTIG>), g, b, 0, stream, b16, n16, out); break;
+    case 8: hipLaunchKernelGGL((stream_probe_kernel<8, CONTIG>), g, b, 0, stream, b16, n16, out); break;
+    case 16: hipLaunchKernelGGL((stream_probe_kernel<16, CONTIG>), g, b, 0, stream, b16, n16, out); break;
     default: return QGEMV_EINVAL;
   }
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}
+
+int launch_stream_probe(const uint8_t *buf, size_t nbytes, uint32_t *out, int unroll, int layout,
+                        hipStream_t stream) {
+  const auto *b16 = reinterpret_cast<const uint4 *>(buf);
+  const size_t n16 = nbytes / 16;
+  // both layouts: one workgroup per 256 * unroll pieces (at most
+  // stream_probe_blocks(nbytes), the count for the smallest unroll)
+  const int blocks = stream_blocks(nbytes, unroll);
+  if (layout == 0) return launch_stream_probe_l<false>(b16, n16, blocks, out, unroll, stream);
+  if (layout == 1) return launch_stream_probe_l<true>(b16, n16, blocks, out, unroll, stream);
+  return QGEMV_EINVAL;
 }
 
 }  // namespace qgemv

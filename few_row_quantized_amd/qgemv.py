@@ -70,7 +70,7 @@ def lib() -> ctypes.CDLL:
         L.qgemv_unpack_probe_fp.argtypes = [i, vp, vp, i, i, i, vp]
         L.qgemv_path_supported.argtypes = [i, i, i, i, i, i]
         L.qgemv_unpack_probe.argtypes = [i, vp, vp, i, i, i, i, vp]
-        L.qgemv_stream_probe.argtypes = [vp, u64, vp, i, vp]
+        L.qgemv_stream_probe.argtypes = [vp, u64, vp, i, i, vp]
         L.qgemv_stream_probe_blocks.argtypes = [u64]
         L.qgemv_strerror.argtypes = [i]
         L.qgemv_strerror.restype = ctypes.c_char_p
@@ -196,8 +196,9 @@ def qgemv_unpack_probe(path, codes, q_out, N: int, K: int, bits: int, group_size
                                            group_size, _stream(stream)), "qgemv_unpack_probe")
 
 
-def qgemv_stream_probe(buf, nbytes: int, out, loads_per_thread: int = 4, stream=None) -> int:
-    return _check(lib().qgemv_stream_probe(_ptr(buf), nbytes, _ptr(out), loads_per_thread,
+def qgemv_stream_probe(buf, nbytes: int, out, loads_per_thread: int = 4, layout: int = 0,
+                       stream=None) -> int:
+    return _check(lib().qgemv_stream_probe(_ptr(buf), nbytes, _ptr(out), loads_per_thread, layout,
                                            _stream(stream)), "qgemv_stream_probe")
 
 

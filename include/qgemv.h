@@ -185,15 +185,18 @@ int qgemv_unpack_probe(int path, const uint8_t *codes, uint8_t *q_out, int N, in
  * qgemv_stream_probe -- read-only streaming kernel over `nbytes` bytes of
  * `buf` (16-byte aligned, nbytes a multiple of 16): every byte is loaded once
  * with non-temporal 128-bit loads (1 KiB contiguous per wave instruction,
- * `loads_per_thread` loads in flight per thread: 2, 4, 8 or 16), folded with
- * XOR, and one uint32 per workgroup is written to
- * out[0 .. qgemv_stream_probe_blocks(nbytes)-1] (enough for every
- * loads_per_thread).  The fastest loads_per_thread at a byte count is the
- * bandwidth ceiling a pure read of that many bytes reaches, measured the
- * same way as the GEMV kernels.  EINVAL for another loads_per_thread.
+ * `loads_per_thread` loads in flight per thread: 1, 2, 4, 8 or 16), folded with
+ * XOR, and one uint32 per 256-thread workgroup is written to
+ * out[0 .. qgemv_stream_probe_blocks(nbytes)-1] (enough for every setting;
+ * the XOR of all of them is the XOR of the buffer's 32-bit words).
+ * layout 0: a thread's loads are one grid-width apart; layout 1: they are
+ * 1 KiB apart, so that each wave reads loads_per_thread KiB in one piece.
+ * The fastest setting at a byte count is the bandwidth ceiling a pure read of
+ * that many bytes reaches, measured the same way as the GEMV kernels.
+ * EINVAL for another loads_per_thread or layout.
  */
 int qgemv_stream_probe(const uint8_t *buf, size_t nbytes, uint32_t *out, int loads_per_thread,
-                       void *stream);
+                       int layout, void *stream);
 int qgemv_stream_probe_blocks(size_t nbytes);
 
 /*

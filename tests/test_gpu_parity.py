@@ -295,12 +295,13 @@ def test_stream_probe_reads_every_byte():
     host = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint32)
     buf = torch.from_numpy(host.view(np.uint8)).to("cuda:0")
     nb = q.qgemv_stream_probe_blocks(nbytes)
-    for u in (2, 4, 8, 16):
-        out = torch.zeros(nb, dtype=torch.int32, device="cuda:0")
-        q.qgemv_stream_probe(buf, nbytes, out, u)
-        torch.cuda.synchronize()
-        got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
-        assert got == np.bitwise_xor.reduce(host), f"loads per thread {u}"
+    for layout in (0, 1):
+        for u in (1, 2, 4, 8, 16):
+            out = torch.zeros(nb, dtype=torch.int32, device="cuda:0")
+            q.qgemv_stream_probe(buf, nbytes, out, u, layout)
+            torch.cuda.synchronize()
+            got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+            assert got == np.bitwise_xor.reduce(host), f"layout {layout}, loads per thread {u}"
 
 
 # ---------------------------------------------------------------- concurrency

@@ -161,12 +161,14 @@ def test_select_returns_a_supported_path_everywhere():
 
 def test_stream_probe_validation():
     L = q.lib()
-    assert L.qgemv_stream_probe(None, 1024, A, 4, None) == q.EINVAL
-    assert L.qgemv_stream_probe(A, 1000, A, 4, None) == q.EINVAL
-    assert L.qgemv_stream_probe(A, 0, A, 4, None) == q.EINVAL
-    for bad in (0, 1, 3, 32):
-        assert L.qgemv_stream_probe(A, 1024, A, bad, None) == q.EINVAL
-    assert L.qgemv_stream_probe(MIS, 1024, A, 4, None) == q.EALIGN
+    assert L.qgemv_stream_probe(None, 1024, A, 4, 0, None) == q.EINVAL
+    assert L.qgemv_stream_probe(A, 1000, A, 4, 0, None) == q.EINVAL
+    assert L.qgemv_stream_probe(A, 0, A, 4, 0, None) == q.EINVAL
+    for bad in (0, 3, 32):
+        assert L.qgemv_stream_probe(A, 1024, A, bad, 0, None) == q.EINVAL
+    for bad in (-1, 2):
+        assert L.qgemv_stream_probe(A, 1024, A, 4, bad, None) == q.EINVAL
+    assert L.qgemv_stream_probe(MIS, 1024, A, 4, 1, None) == q.EALIGN
     assert 1 <= q.qgemv_stream_probe_blocks(16) <= q.qgemv_stream_probe_blocks(1 << 30)
 
 
