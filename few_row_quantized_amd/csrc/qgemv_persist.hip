@@ -55,6 +55,10 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   constexpr int GPS = 4 / CPG;           // groups per super-chunk
   constexpr int LVL = CPG >= 4 ? 0 : (CPG == 2 ? 1 : 2);
   constexpr int REGS_G = CPG;
+  // codes of two consecutive super-chunks as whole 128-byte lines (8 rows per
+  // load, pair_to_operand_lanes) where a block has an even number of them;
+  // otherwise lane quads on 64 bytes (to_operand_lanes)
+  constexpr bool LINES = BSC % 2 == 0;
   // metadata loads in the quad-row layout: measured faster for 4-bit codes
   // with groups of 32 or 64 (FFN-up 4096x12288: 14.2 -> 13.2 us and
   // 11.3 -> 10.6 us at M = 8), slower by 1-5% with groups of 128 and for
@@ -138,14 +142,22 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
     // codes: lane L reads 16-byte piece L%4 of row L/4 (see quad_row_lane);
     // metadata the same way where groups are small (MQ), else per column
     const int nq = min(16 * (t_first + it) + (lane >> 2), N - 1);
-    const uint64_t crow = (((uint64_t)nq * RB + (lane & 3) * 16) & m64) | (crow_dead & ~m64);
+    const int nl = min(16 * (t_first + it) + (lane >> 3), N - 1);      // LINES: rows 0-7
+    const int nl8 = min(16 * (t_first + it) + 8 + (lane >> 3), N - 1);  // rows 8-15
+    const uint64_t crow = LINES ? (((uint64_t)nl * RB + (lane & 7) * 16) & m64) | (crow_dead & ~m64)
+                                : (((uint64_t)nq * RB + (lane & 3) * 16) & m64) | (crow_dead & ~m64);
+    const uint64_t crow8 = (((uint64_t)nl8 * RB + (lane & 7) * 16) & m64) | (crow_dead & ~m64);
     const int nm = MQ ? nq : min(16 * (t_first + it) + col, N - 1);
     const uint64_t mrow = (((uint64_t)nm * NG) & m64) | (mrow_dead & ~m64);
 #pragma unroll
     for (int k = 0; k < BPW; ++k) {
 #pragma unroll
-      for (int u = 0; u < BSC; ++u)
-        cv[slot][k][u] = load_stream_u32x4(codes + crow + (size_t)(blk[k] * BSC + u) * 64);
+      for (int u = 0; u < BSC; ++u) {
+        if constexpr (LINES)
+          cv[slot][k][u] = load_stream_u32x4(codes + ((u & 1) ? crow8 : crow) + (size_t)(blk[k] * BSC + (u & ~1)) * 64);
+        else
+          cv[slot][k][u] = load_stream_u32x4(codes + crow + (size_t)(blk[k] * BSC + u) * 64);
+      }
     }
 #pragma unroll
     for (int k = 0; k < BPW; ++k) {
@@ -234,7 +246,14 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
 #pragma unroll
         for (int u = 0; u < BSC; ++u) {
           uint32_t cur[4];
-          to_operand_lanes(cv[s][k][u], cur);
+          if constexpr (LINES) {
+            if (u & 1)
+              pair_to_operand_lanes<1>(cv[s][k][u & ~1], cv[s][k][u | 1], cur);
+            else
+              pair_to_operand_lanes<0>(cv[s][k][u & ~1], cv[s][k][u | 1], cur);
+          } else {
+            to_operand_lanes(cv[s][k][u], cur);
+          }
           transpose_rows_lvl<LVL>(cur);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
