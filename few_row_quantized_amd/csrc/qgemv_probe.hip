@@ -63,11 +63,39 @@ __global__ __launch_bounds__(256) void unpack_probe_dot(const uint8_t *__restric
   }
 }
 
+// The MFMA kernels' code loads for super-chunk sc of 16-row tile `tile`,
+// moved to the operand lanes: whole 128-byte lines of two super-chunks
+// (LINES: lane L on piece L%8 of row L/8, then rows 8-15; the persistent
+// kernel where a bias block holds an even number of super-chunks) or lane
+// quads on 64 bytes (lane L: piece L%4 of row L/4; the other kernels).
+template <bool LINES>
+__device__ __forceinline__ void probe_load_operands(const uint8_t *codes, size_t RB, int tile, int sc, int N,
+                                                    uint32_t (&r)[4]) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (LINES) {
+    const size_t off = (size_t)(sc & ~1) * 64 + (lane & 7) * 16;
+    const int na = min(tile * 16 + (lane >> 3), N - 1), nb = min(tile * 16 + 8 + (lane >> 3), N - 1);
+    const u32x4_t a = *reinterpret_cast<const u32x4_t *>(codes + (size_t)na * RB + off);
+    const u32x4_t b = *reinterpret_cast<const u32x4_t *>(codes + (size_t)nb * RB + off);
+    if (sc & 1)
+      pair_to_operand_lanes<1>(a, b, r);
+    else
+      pair_to_operand_lanes<0>(a, b, r);
+  } else {
+    const int nq = min(tile * 16 + (lane >> 2), N - 1);
+    const u32x4_t v =
+        *reinterpret_cast<const u32x4_t *>(codes + (size_t)nq * RB + (size_t)sc * 64 + (lane & 3) * 16);
+    to_operand_lanes(v, r);
+  }
+}
+
 // MFMA-path decoding: one wave per (16-row tile, 64-byte super-chunk), same
 // lane-to-address mapping, partial row transpose (level LVL, chosen by the
-// group size) and unpack as qgemv_mfma_kernel; each B-operand slot is written
-// to the column it stands for.
-template <int BITS, int LVL>
+// group size) and unpack as the MFMA kernels; each B-operand slot is written
+// to the column it stands for.  Where both load forms apply (LINES) the
+// operands of the two must agree register for register; a lane where they
+// do not writes 0xFF (no 2- or 4-bit code) over its first code.
+template <int BITS, int LVL, bool LINES>
 __global__ __launch_bounds__(64) void unpack_probe_mfma(const uint8_t *__restrict__ codes,
                                                         uint8_t *__restrict__ q, int N, int K) {
   constexpr int CW = 128 / BITS;
@@ -80,11 +108,16 @@ __global__ __launch_bounds__(64) void unpack_probe_mfma(const uint8_t *__restric
   const int sc = blockIdx.x % nsc;
   const int n = min(tile * 16 + col, N - 1);
   const size_t RB = (size_t)K * BITS / 8;
-  // the kernels' load (lane L: piece L%4 of row L/4) and move to operand lanes
-  const int nq = min(tile * 16 + (lane >> 2), N - 1);
-  const u32x4_t v = *reinterpret_cast<const u32x4_t *>(codes + (size_t)nq * RB + (size_t)sc * 64 + (lane & 3) * 16);
   uint32_t r[4];
-  to_operand_lanes(v, r);
+  probe_load_operands<false>(codes, RB, tile, sc, N, r);
+  bool differ = false;
+  if constexpr (LINES) {
+    static_assert(BITS != 8, "8-bit codes take the single-pass kernel only");
+    uint32_t r2[4];
+    probe_load_operands<true>(codes, RB, tile, sc, N, r2);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) differ |= r2[d] != r[d];
+  }
   transpose_rows_lvl<LVL>(r);  // all lanes take part, also those past row N
   if (tile * 16 + col >= N) return;
   uint8_t *qr = q + (size_t)n * K + (size_t)sc * SCW;
@@ -125,6 +158,7 @@ __global__ __launch_bounds__(64) void unpack_probe_mfma(const uint8_t *__restric
       }
     }
   }
+  if (differ) qr[lvl_chunk<LVL>(0, kb) * CW + lvl_dword<LVL>(0, kb) * DW] = 0xFF;
 }
 
 // FP formats, dot-path decoding: one thread per (row n, 16-byte chunk c);
@@ -182,11 +216,8 @@ __global__ __launch_bounds__(64) void unpack_probe_fp_mfma(const uint8_t *__rest
   const int sc = blockIdx.x % nsc;
   const int n = min(tile * 16 + col, N - 1);
   const size_t RB = (size_t)K * BITS / 8;
-  // the kernels' load (lane L: piece L%4 of row L/4) and move to operand lanes
-  const int nq = min(tile * 16 + (lane >> 2), N - 1);
-  const u32x4_t v = *reinterpret_cast<const u32x4_t *>(codes + (size_t)nq * RB + (size_t)sc * 64 + (lane & 3) * 16);
   uint32_t r[4];
-  to_operand_lanes(v, r);
+  probe_load_operands<false>(codes, RB, tile, sc, N, r);
   transpose_rows_lvl<LVL>(r);  // all lanes take part, also those past row N
   if (tile * 16 + col >= N) return;
   uint16_t *o = out + (size_t)n * K + (size_t)sc * SCW;
@@ -302,16 +333,22 @@ int launch_unpack_probe(int path, const uint8_t *codes, uint8_t *q_out, int N, i
     const int cpg = group_size / CW;  // chunks per group -> exchange level
     const int lvl = cpg >= 4 ? 0 : (cpg == 2 ? 1 : 2);
     const dim3 g(blocks), b(64);
+    // the persistent kernel (2- and 4-bit codes) loads whole lines where a bias
+    // block (4 groups) holds an even number of 64-byte super-chunks
+    const bool lines = (group_size * bits / 128) % 2 == 0;
     if (bits == 8) {
-      if (lvl == 0) hipLaunchKernelGGL((unpack_probe_mfma<8, 0>), g, b, 0, stream, codes, q_out, N, K);
-      else hipLaunchKernelGGL((unpack_probe_mfma<8, 1>), g, b, 0, stream, codes, q_out, N, K);
+      if (lvl == 0) hipLaunchKernelGGL((unpack_probe_mfma<8, 0, false>), g, b, 0, stream, codes, q_out, N, K);
+      else hipLaunchKernelGGL((unpack_probe_mfma<8, 1, false>), g, b, 0, stream, codes, q_out, N, K);
     } else if (bits == 4) {
-      if (lvl == 0) hipLaunchKernelGGL((unpack_probe_mfma<4, 0>), g, b, 0, stream, codes, q_out, N, K);
-      else if (lvl == 1) hipLaunchKernelGGL((unpack_probe_mfma<4, 1>), g, b, 0, stream, codes, q_out, N, K);
-      else hipLaunchKernelGGL((unpack_probe_mfma<4, 2>), g, b, 0, stream, codes, q_out, N, K);
+      if (lvl == 0 && lines) hipLaunchKernelGGL((unpack_probe_mfma<4, 0, true>), g, b, 0, stream, codes, q_out, N, K);
+      else if (lvl == 0) hipLaunchKernelGGL((unpack_probe_mfma<4, 0, false>), g, b, 0, stream, codes, q_out, N, K);
+      else if (lvl == 1 && lines) hipLaunchKernelGGL((unpack_probe_mfma<4, 1, true>), g, b, 0, stream, codes, q_out, N, K);
+      else if (lvl == 1) hipLaunchKernelGGL((unpack_probe_mfma<4, 1, false>), g, b, 0, stream, codes, q_out, N, K);
+      else hipLaunchKernelGGL((unpack_probe_mfma<4, 2, false>), g, b, 0, stream, codes, q_out, N, K);
     } else {
-      if (lvl == 1) hipLaunchKernelGGL((unpack_probe_mfma<2, 1>), g, b, 0, stream, codes, q_out, N, K);
-      else hipLaunchKernelGGL((unpack_probe_mfma<2, 2>), g, b, 0, stream, codes, q_out, N, K);
+      if (lvl == 1 && lines) hipLaunchKernelGGL((unpack_probe_mfma<2, 1, true>), g, b, 0, stream, codes, q_out, N, K);
+      else if (lvl == 1) hipLaunchKernelGGL((unpack_probe_mfma<2, 1, false>), g, b, 0, stream, codes, q_out, N, K);
+      else hipLaunchKernelGGL((unpack_probe_mfma<2, 2, false>), g, b, 0, stream, codes, q_out, N, K);
     }
   } else {
     return QGEMV_EINVAL;
