@@ -96,6 +96,10 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
   // one ring slot, so at most 32 VGPRs, 16 when the slot holds 8 super-chunks
   constexpr int XU = (BPW * BSC >= 8 ? 4 : 8) / (UE / 8);
   static_assert(BSC >= 1 && BLKW % SCW == 0 && CPG >= 1 && (BITS == 2 || BITS == 4), "layout");
+  // codes of two consecutive super-chunks as whole 128-byte lines (8 rows per
+  // load, pair_to_operand_lanes) where a block has an even number of them;
+  // otherwise lane quads on 64 bytes (to_operand_lanes)
+  constexpr bool LINES = BSC % 2 == 0;
   static_assert(GU >= 1 && GU <= 64 && (GU & (GU - 1)) == 0, "group lanes");
 
   const int lane = threadIdx.x & 63;
@@ -165,7 +169,11 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
     // codes: lane L reads 16-byte piece L%4 of row L/4 (see quad_row_lane);
     // metadata the same way where groups are small (MQ), else per column
     const int nq = min(16 * (t_first + tt) + (lane >> 2), N - 1);
-    const uint64_t crow = (((uint64_t)nq * RB + (lane & 3) * 16) & m64) | (crow_dead & ~m64);
+    const int nl = min(16 * (t_first + tt) + (lane >> 3), N - 1);      // LINES: rows 0-7
+    const int nl8 = min(16 * (t_first + tt) + 8 + (lane >> 3), N - 1);  // rows 8-15
+    const uint64_t crow = LINES ? (((uint64_t)nl * RB + (lane & 7) * 16) & m64) | (crow_dead & ~m64)
+                                : (((uint64_t)nq * RB + (lane & 3) * 16) & m64) | (crow_dead & ~m64);
+    const uint64_t crow8 = (((uint64_t)nl8 * RB + (lane & 7) * 16) & m64) | (crow_dead & ~m64);
     const int nm = MQ ? nq : min(16 * (t_first + tt) + col, N - 1);
     const uint64_t mrow = (((uint64_t)nm * NG) & m64) | (mrow_dead & ~m64);
 #pragma unroll
@@ -173,8 +181,13 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
       int blk;
       owned(q, k, blk);
 #pragma unroll
-      for (int u = 0; u < BSC; ++u)
-        cv[slot][k][u] = load_stream_u32x4(codes + crow + (size_t)((p_lo + blk) * BSC + u) * 64);
+      for (int u = 0; u < BSC; ++u) {
+        if constexpr (LINES)
+          cv[slot][k][u] =
+              load_stream_u32x4(codes + ((u & 1) ? crow8 : crow) + (size_t)((p_lo + blk) * BSC + (u & ~1)) * 64);
+        else
+          cv[slot][k][u] = load_stream_u32x4(codes + crow + (size_t)((p_lo + blk) * BSC + u) * 64);
+      }
       s4[slot][k] = *reinterpret_cast<const uint2 *>(scales + mrow + (p_lo + blk) * 4);
       b4[slot][k] = *reinterpret_cast<const uint2 *>(biases + mrow + (p_lo + blk) * 4);
     }
@@ -272,7 +285,14 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
 #pragma unroll
         for (int u = 0; u < BSC; ++u) {
           uint32_t cur[4];
-          to_operand_lanes(cv[s][k][u], cur);
+          if constexpr (LINES) {
+            if (u & 1)
+              pair_to_operand_lanes<1>(cv[s][k][u & ~1], cv[s][k][u | 1], cur);
+            else
+              pair_to_operand_lanes<0>(cv[s][k][u & ~1], cv[s][k][u | 1], cur);
+          } else {
+            to_operand_lanes(cv[s][k][u], cur);
+          }
           transpose_rows_lvl<LVL>(cur);
           const int k0 = (lq * BSC + u) * SCW;  // first element of the super-chunk in the phase
 #pragma unroll
