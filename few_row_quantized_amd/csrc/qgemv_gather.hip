@@ -36,7 +36,12 @@ int launch_gather_nt(const QgemvArgs &a, const GatherArgs &ga, hipStream_t strea
   constexpr int SPI = MfmaShape<BITS, GS, NT>::SPI;
   const auto kern = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, false, false, kAffine, true>;
   const int nblk = a.K / (4 * GS);
-  const int waves = pick_waves(nblk, MAXT / 64);
+  // at most 4 waves (K-slices) per item: more workgroups resident per CU, so
+  // more items' loads in flight (128-expert top-8 1536 x 2048 gate/up: 70.3 ->
+  // 60.2 us at M = 16, 40.0 -> 33.8 at M = 8, 8.74 -> 8.75 at M = 1; 2 waves:
+  // 56.5 at M = 16 but 9.75 at M = 1).  Fixed by the shape, so a pair's row
+  // does not depend on the other pairs of the call.
+  const int waves = pick_waves(nblk, MAXT / 64 < 4 ? MAXT / 64 : 4);
   const int groups = ((a.N + 15) / 16 + NT - 1) / NT;
   const int slots = ga.P < ga.E ? ga.P : ga.E;
   // at most kMaxPairs * 2^18 (slot, tile group) items: within the grid limit.
