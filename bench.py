@@ -412,10 +412,21 @@ def measure_moe(args, capture, time_graph, name="moe30b_gateup_e128_k2048_n1536_
 
 
 def csrc_sha256():
+    """sha256 of the kernel sources with comments and blank lines removed: a
+    profile stays valid across edits of comments only, and goes stale with
+    any change of code."""
     import glob
     import hashlib
+    import re
     srcs = sorted(glob.glob(os.path.join(ROOT, "few_row_quantized_amd", "csrc", "*")))
-    return hashlib.sha256(b"".join(open(f, "rb").read() for f in srcs)).hexdigest()
+    h = hashlib.sha256()
+    for f in srcs:
+        text = open(f, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)  # block comments
+        text = re.sub(r"//[^\n]*", "", text)                # line comments
+        lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+        h.update(os.path.basename(f).encode() + b"\0" + "\n".join(lines).encode() + b"\0")
+    return h.hexdigest()
 
 
 def profiled_kernel_us(workload, M, path):

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kDotThreads) void qgemv_dot_kernel(
   constexpr int SUBW = CW / NSUB;       // weights per sub-chunk
   constexpr int V = ((R * M + 3) / 4) * 4;
   // activations in memory order (8-bit codes, FP elements) or re-paired to
-  // the split pairing of the 2/4-bit offset codes
+  // the split pairing in which the 2/4-bit codes are decoded
   constexpr bool NATURAL = BITS == 8 || FMT != kAffine;
   constexpr bool HAS_BIAS = FMT == kAffine;
   constexpr bool XREG = XR && (M == 1 || (M == 2 && !(FMT == kAffine && BITS == 4))) &&

@@ -18,7 +18,9 @@
 //   the workgroup walks its tiles.
 // * Codes and group metadata of the next tile are prefetched into a ring of
 //   S register slots while the current tile is unpacked and multiplied, so a
-//   CU keeps weight bytes in flight from its first tile to its last.
+//   CU keeps weight bytes in flight from its first tile to its last.  Codes
+//   come as whole 128-byte lines (8 rows per load) where a bias block holds
+//   an even number of 64-byte super-chunks (pair_to_operand_lanes).
 // * Every S tiles the waves' partial 16x16 tiles are summed through LDS in
 //   block order (deterministic, no atomics) and rows m < M are stored.
 // * Fused residual sum (ADD, "metal : few-row MMA mat-mul and batched copies
@@ -139,8 +141,10 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   int it = 0;  // tile step of the next issue
   auto issue = [&](const int slot) {
     const uint64_t m64 = 0ull - (uint64_t)(it < ntile);  // all-ones while live
-    // codes: lane L reads 16-byte piece L%4 of row L/4 (see quad_row_lane);
-    // metadata the same way where groups are small (MQ), else per column
+    // codes: whole 128-byte lines (LINES: lane L on piece L%8 of row L/8,
+    // rows 8-15 in a second load) or lane quads (piece L%4 of row L/4, see
+    // quad_row_lane); metadata in lane quads where groups are small (MQ),
+    // else per column
     const int nq = min(16 * (t_first + it) + (lane >> 2), N - 1);
     const int nl = min(16 * (t_first + it) + (lane >> 3), N - 1);      // LINES: rows 0-7
     const int nl8 = min(16 * (t_first + it) + 8 + (lane >> 3), N - 1);  // rows 8-15

@@ -36,7 +36,9 @@
 //   its blocks lo+w, lo+w+W, ...  The workgroup walks (phase, tile) steps in
 //   phase-major order; each step's codes and metadata come through a
 //   register ring of S slots (the next step's loads are in flight while the
-//   current one is multiplied, also across a phase change); the
+//   current one is multiplied, also across a phase change; codes as whole
+//   128-byte lines where a bias block holds an even number of 64-byte
+//   super-chunks, as in the register-resident persistent kernel); the
 //   activation operand of each v_mfma_f32_16x16x32_bf16 is one 16-byte LDS
 //   read per lane (rows m >= M read row M-1: their outputs are never
 //   stored).  Unpack, scale fold, the bias product (v_mfma_f32_16x16x4_f32
@@ -166,8 +168,10 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
     const int q = live ? it / ntile : 0;
     const int tt = live ? it - q * ntile : 0;
     const uint64_t m64 = 0ull - (uint64_t)live;  // all-ones while live
-    // codes: lane L reads 16-byte piece L%4 of row L/4 (see quad_row_lane);
-    // metadata the same way where groups are small (MQ), else per column
+    // codes: whole 128-byte lines (LINES: lane L on piece L%8 of row L/8,
+    // rows 8-15 in a second load) or lane quads (piece L%4 of row L/4, see
+    // quad_row_lane); metadata in lane quads where groups are small (MQ),
+    // else per column
     const int nq = min(16 * (t_first + tt) + (lane >> 2), N - 1);
     const int nl = min(16 * (t_first + tt) + (lane >> 3), N - 1);      // LINES: rows 0-7
     const int nl8 = min(16 * (t_first + tt) + 8 + (lane >> 3), N - 1);  // rows 8-15

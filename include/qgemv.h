@@ -170,10 +170,11 @@ int qgemv_path_supported(int path, int M, int N, int K, int bits, int group_size
 /*
  * qgemv_unpack_probe -- writes the integer codes exactly as a path's kernels
  * decode them: q_out[n][k] (uint8, [N][K], row-major) for every n < N, k < K.
- * The kernels turn codes into bf16 values 128+q in registers; this probe runs
- * the same device routines (same loads, lane exchanges and bit operations)
- * and writes back q, so the decoded codes can be compared bit-exactly with
- * the format's definition.  path: QGEMV_PATH_DOT or QGEMV_PATH_MFMA (the two
+ * The kernels turn codes into exact bf16 values q in registers; this probe
+ * runs the same device routines (same loads, lane exchanges and conversions;
+ * on the MFMA path both of its load forms, which must agree) and writes back
+ * q, so the decoded codes can be compared bit-exactly with the format's
+ * definition.  path: QGEMV_PATH_DOT or QGEMV_PATH_MFMA (the two
  * paths pair codes differently).  Requirements as qgemv_run_path for that
  * path (group_size only selects the MFMA layout, pass the one you will use);
  * q_out non-NULL.
