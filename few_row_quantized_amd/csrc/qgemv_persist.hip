@@ -42,7 +42,7 @@ namespace {
 // y and res may be the same buffer (in-place residual sum): neither is
 // declared restrict; every element is read before it is written, by the same
 // thread.
-template <int BITS, int GS, int BPW, int S, int MAXW, bool ADD>
+template <int BITS, int GS, int BPW, int S, int MAXW, bool ADD, bool PAIRK>
 __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *y,
@@ -58,9 +58,13 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   constexpr int LVL = CPG >= 4 ? 0 : (CPG == 2 ? 1 : 2);
   constexpr int REGS_G = CPG;
   // codes of two consecutive super-chunks as whole 128-byte lines (8 rows per
-  // load, pair_to_operand_lanes) where a block has an even number of them;
-  // otherwise lane quads on 64 bytes (to_operand_lanes)
-  constexpr bool LINES = BSC % 2 == 0;
+  // load, pair_to_operand_lanes): the two halves of a block where a block has
+  // an even number of them, or (PAIRK: one super-chunk per block, two blocks
+  // per wave, an even block count) the wave's two blocks, which PAIRK makes
+  // adjacent; otherwise lane quads on 64 bytes (to_operand_lanes).  The
+  // wave's super-chunks j = k * BSC + u then pair as (j & ~1, j | 1).
+  static_assert(!PAIRK || (BPW == 2 && BSC == 1), "block pairs need two one-super-chunk blocks per wave");
+  constexpr bool LINES = BSC % 2 == 0 || PAIRK;
   // metadata loads in the quad-row layout: measured faster for 4-bit codes
   // with groups of 32 or 64 (FFN-up 4096x12288: 14.2 -> 13.2 us and
   // 11.3 -> 10.6 us at M = 8), slower by 1-5% with groups of 128 and for
@@ -101,14 +105,15 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   const int t_first = (int)(blockIdx.x * (unsigned)T / gridDim.x);
   const int ntile = (int)((blockIdx.x + 1) * (unsigned)T / gridDim.x) - t_first;
 
-  // owned blocks; a wave past the last block loads a valid block and skips
-  // the arithmetic
+  // owned blocks (vw, vw + W, ...; PAIRK: vw*BPW, vw*BPW + 1, adjacent); a
+  // wave past the last block loads a valid block and skips the arithmetic
   int blk[BPW];
   bool own[BPW];
 #pragma unroll
   for (int k = 0; k < BPW; ++k) {
-    own[k] = vw + k * W < nblk;
-    blk[k] = own[k] ? vw + k * W : nblk - 1;
+    const int b = PAIRK ? vw * BPW + k : vw + k * W;
+    own[k] = b < nblk;
+    blk[k] = own[k] ? b : nblk - 1;
   }
 
   // ---- activations of the owned blocks (rows m >= M read row M-1: their
@@ -158,7 +163,8 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
 #pragma unroll
       for (int u = 0; u < BSC; ++u) {
         if constexpr (LINES)
-          cv[slot][k][u] = load_stream_u32x4(codes + ((u & 1) ? crow8 : crow) + (size_t)(blk[k] * BSC + (u & ~1)) * 64);
+          cv[slot][k][u] = load_stream_u32x4(codes + (((k * BSC + u) & 1) ? crow8 : crow) +
+                                             (size_t)((blk[k] * BSC + u) & ~1) * 64);
         else
           cv[slot][k][u] = load_stream_u32x4(codes + crow + (size_t)(blk[k] * BSC + u) * 64);
       }
@@ -251,10 +257,11 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
         for (int u = 0; u < BSC; ++u) {
           uint32_t cur[4];
           if constexpr (LINES) {
-            if (u & 1)
-              pair_to_operand_lanes<1>(cv[s][k][u & ~1], cv[s][k][u | 1], cur);
+            const int ja = (k * BSC + u) & ~1, jb = (k * BSC + u) | 1;  // the pair's two super-chunks
+            if ((k * BSC + u) & 1)
+              pair_to_operand_lanes<1>(cv[s][ja / BSC][ja % BSC], cv[s][jb / BSC][jb % BSC], cur);
             else
-              pair_to_operand_lanes<0>(cv[s][k][u & ~1], cv[s][k][u | 1], cur);
+              pair_to_operand_lanes<0>(cv[s][ja / BSC][ja % BSC], cv[s][jb / BSC][jb % BSC], cur);
           } else {
             to_operand_lanes(cv[s][k][u], cur);
           }
@@ -359,7 +366,15 @@ int launch_persist_t(const QgemvArgs &a, hipStream_t stream) {
   const int tiles = (a.N + 15) / 16;
   const int cus = device_cu_count();
   const int G = tiles < cus ? tiles : cus;
-  hipLaunchKernelGGL((qgemv_persist_kernel<BITS, GS, BPW, S, MAXW, ADD>), dim3(G), dim3(64 * waves),
+  // the wave's two one-super-chunk blocks as whole lines where every wave has
+  // two (an even block count)
+  constexpr bool CAN_PAIRK = BPW == 2 && 4 * GS * BITS == 512;
+  if (CAN_PAIRK && nblk % 2 == 0) {
+    hipLaunchKernelGGL((qgemv_persist_kernel<BITS, GS, BPW, S, MAXW, ADD, CAN_PAIRK>), dim3(G), dim3(64 * waves),
+                       0, stream, a.codes, a.scales, a.biases, a.x, a.y, a.res, a.M, a.N, a.K);
+    return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+  }
+  hipLaunchKernelGGL((qgemv_persist_kernel<BITS, GS, BPW, S, MAXW, ADD, false>), dim3(G), dim3(64 * waves),
                      0, stream, a.codes, a.scales, a.biases, a.x, a.y, a.res, a.M, a.N, a.K);
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
 }

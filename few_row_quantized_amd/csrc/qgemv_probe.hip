@@ -334,8 +334,10 @@ int launch_unpack_probe(int path, const uint8_t *codes, uint8_t *q_out, int N, i
     const int lvl = cpg >= 4 ? 0 : (cpg == 2 ? 1 : 2);
     const dim3 g(blocks), b(64);
     // the persistent kernel (2- and 4-bit codes) loads whole lines where a bias
-    // block (4 groups) holds an even number of 64-byte super-chunks
-    const bool lines = (group_size * bits / 128) % 2 == 0;
+    // block (4 groups) holds an even number of 64-byte super-chunks, or one
+    // super-chunk with an even number of them per row (pairs of blocks)
+    const int nsc = K / (4 * CW);
+    const bool lines = (group_size * bits / 128) % 2 == 0 || (group_size * bits == 128 && nsc % 2 == 0);
     if (bits == 8) {
       if (lvl == 0) hipLaunchKernelGGL((unpack_probe_mfma<8, 0, false>), g, b, 0, stream, codes, q_out, N, K);
       else hipLaunchKernelGGL((unpack_probe_mfma<8, 1, false>), g, b, 0, stream, codes, q_out, N, K);
@@ -344,10 +346,12 @@ int launch_unpack_probe(int path, const uint8_t *codes, uint8_t *q_out, int N, i
       else if (lvl == 0) hipLaunchKernelGGL((unpack_probe_mfma<4, 0, false>), g, b, 0, stream, codes, q_out, N, K);
       else if (lvl == 1 && lines) hipLaunchKernelGGL((unpack_probe_mfma<4, 1, true>), g, b, 0, stream, codes, q_out, N, K);
       else if (lvl == 1) hipLaunchKernelGGL((unpack_probe_mfma<4, 1, false>), g, b, 0, stream, codes, q_out, N, K);
+      else if (lines) hipLaunchKernelGGL((unpack_probe_mfma<4, 2, true>), g, b, 0, stream, codes, q_out, N, K);
       else hipLaunchKernelGGL((unpack_probe_mfma<4, 2, false>), g, b, 0, stream, codes, q_out, N, K);
     } else {
       if (lvl == 1 && lines) hipLaunchKernelGGL((unpack_probe_mfma<2, 1, true>), g, b, 0, stream, codes, q_out, N, K);
       else if (lvl == 1) hipLaunchKernelGGL((unpack_probe_mfma<2, 1, false>), g, b, 0, stream, codes, q_out, N, K);
+      else if (lines) hipLaunchKernelGGL((unpack_probe_mfma<2, 2, true>), g, b, 0, stream, codes, q_out, N, K);
       else hipLaunchKernelGGL((unpack_probe_mfma<2, 2, false>), g, b, 0, stream, codes, q_out, N, K);
     }
   } else {
