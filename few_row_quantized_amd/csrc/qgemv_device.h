@@ -389,6 +389,38 @@ __device__ __forceinline__ u32x4_t to_operand_lanes(const u32x4_t &v) {
   return u32x4_t{c[0], c[1], c[2], c[3]};
 }
 
+// Compact activation operands for few rows.  With R = 16 / XG distinct rows
+// (R = 4 or 8), one 16-byte load per lane carries XG operands: lane
+// 16*kb + XG*q + g holds operand g's piece for K-part kb of row q.  One DPP
+// quad permutation per dword then gives operand g to every lane of the
+// 16-lane row kb: lane (kb, a) takes lane 16*kb + XG*(a / XG) + g, i.e. row
+// a / XG.  The MFMA row a thus holds activation row a / XG (each row XG
+// times), and output row a is stored as row a / XG when a % XG == 0.  A
+// quad permutation never leaves its row of 16 lanes and moves no data
+// through LDS, so XG operands cost one load instruction and 4 VALU moves
+// instead of XG loads (and, in the quad-row layout, 4*XG ds_bpermutes).
+template <int XG, int G>
+__device__ __forceinline__ uint32_t compact_pick_dword(uint32_t v) {
+  static_assert((XG == 2 || XG == 4) && G >= 0 && G < XG, "compact operand");
+  // quad_perm selectors: [G, G, G, G] (XG = 4) or [G, G, 2 + G, 2 + G] (XG = 2)
+  constexpr int ctrl = XG == 4 ? G * 0x55 : G * 0x55 + 0xA0;
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, ctrl, 0xF, 0xF, false);
+}
+
+template <int XG>
+__device__ __forceinline__ u32x4_t compact_pick(const u32x4_t &v, const int g) {
+  u32x4_t r;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    // g is a compile-time constant once the caller's loops are unrolled
+    if (g == 0) r[d] = compact_pick_dword<XG, 0>(v[d]);
+    else if (g == 1) r[d] = compact_pick_dword<XG, 1>(v[d]);
+    else if (g == 2) r[d] = compact_pick_dword<XG, XG == 4 ? 2 : 0>(v[d]);
+    else r[d] = compact_pick_dword<XG, XG == 4 ? 3 : 1>(v[d]);
+  }
+  return r;
+}
+
 __device__ __forceinline__ uint2 to_operand_lanes(const uint2 &v) {
   const int src = quad_row_lane((int)(threadIdx.x & 63)) * 4;
   return make_uint2((uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v.x),

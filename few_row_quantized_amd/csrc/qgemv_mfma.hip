@@ -10,7 +10,9 @@
 //
 // CDNA4 design:
 // * One v_mfma_f32_16x16x32_bf16 computes a 16(m) x 16(n) tile over 32 k.
-//   A = activations (rows m >= M repeat row M-1 and are never stored),
+//   A = activations (rows m >= M repeat row M-1 and are never stored; with
+//   at most 4 or 8 rows each row fills 4 or 2 MFMA rows, loaded compactly:
+//   compact_pick in qgemv_device.h),
 //   B = weights as exact bf16 code values q (2/4-bit: one code dword per
 //   step or half-step; 8-bit: two code dwords per MFMA step).  A workgroup owns NT tiles of
 //   16 output columns over the whole of K; its waves split K into
@@ -61,14 +63,49 @@ __global__ __launch_bounds__(256) void fill_kernel(uint32_t *__restrict__ y, siz
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) y[i] = v;
 }
 
+// Workgroups of `waves` waves of kernel `kern` resident on one CU (cached per
+// kernel and wave count: the same on every MI355X; concurrent first calls
+// store the same value).
+template <const void *(*KERN)()>
+int resident_per_cu(int waves, std::atomic<int> (&cache)[17]) {
+  int occ = cache[waves].load(std::memory_order_relaxed);
+  if (occ == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, KERN(), 64 * waves, 0) != hipSuccess || occ <= 0)
+      occ = 1;
+    cache[waves].store(occ, std::memory_order_relaxed);
+  }
+  return occ;
+}
+
+template <int BITS, int GS, int NT, bool ADD, int FMT, int XC, int KS, bool PERSIST>
+const void *mfma_kernel_ptr() {
+  constexpr int MAXT = MfmaShape<BITS, GS, NT>::MAXT;
+  constexpr int SPI = MfmaShape<BITS, GS, NT>::SPI;
+  return reinterpret_cast<const void *>(
+      qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, KS, PERSIST, ADD, FMT, false, XC>);
+}
+
+// Launch with XC compact activation rows (0: none).  The persistent grid
+// takes no compact variant.
+template <int BITS, int GS, int NT, bool ADD, int FMT, int XC>
+int launch_mfma_k(const QgemvArgs &a, int ksplit, bool single, int waves, int grid, int groups,
+                  hipStream_t stream) {
+  constexpr int MAXT = MfmaShape<BITS, GS, NT>::MAXT;
+  constexpr int SPI = MfmaShape<BITS, GS, NT>::SPI;
+  const auto kern = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, XC == 0, ADD, FMT, false, XC>;
+  const auto kern1 = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, false, ADD, FMT, false, XC>;
+  const auto kern_s = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 2, XC == 0, ADD, FMT, false, XC>;
+  const auto kern1_s = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 2, false, ADD, FMT, false, XC>;
+  const auto k = ksplit == 1 ? (single ? kern1 : kern) : (single ? kern1_s : kern_s);
+  hipLaunchKernelGGL(k, dim3(grid), dim3(64 * waves), 0, stream, a.codes, a.scales, a.biases, a.x,
+                     a.y, a.res, a.M, a.N, a.K, groups, GatherArgs{});
+  return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}
+
 template <int BITS, int GS, int NT, bool ADD, int FMT>
 int launch_mfma_t(const QgemvArgs &a, hipStream_t stream) {
   constexpr int MAXT = MfmaShape<BITS, GS, NT>::MAXT;
-  constexpr int SPI = MfmaShape<BITS, GS, NT>::SPI;
-  const auto kern = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, true, ADD, FMT>;
-  const auto kern1 = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, false, ADD, FMT>;
-  const auto kern_s = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 2, true, ADD, FMT>;
-  const auto kern1_s = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 2, false, ADD, FMT>;
+  static_assert(MAXT / 64 <= 16, "wave cap");
   const int nblk = a.K / (4 * GS);
   const int tiles = (a.N + 15) / 16;
   const int cus = device_cu_count();
@@ -84,27 +121,36 @@ int launch_mfma_t(const QgemvArgs &a, hipStream_t stream) {
                                                                                                 : 1;
   const int waves = pick_waves(nblk / ksplit, MAXT / 64);
   const int groups = (tiles + NT - 1) / NT * ksplit;
+  // one tile group per workgroup when all are resident at once, else the
+  // persistent grid (one per resident workgroup, walking the groups)
+  static std::atomic<int> occ0[17], occ4[2][17], occ8[2][17];
+  const int slots = resident_per_cu<mfma_kernel_ptr<BITS, GS, NT, ADD, FMT, 0, 1, true>>(waves, occ0) * cus;
+  const bool single = groups <= slots;
   if (ksplit == 2) {
     const int st = launch_fill(a.y, (size_t)a.M * a.N, ADD ? kSplitSentinel : 0u, stream);
     if (st != QGEMV_OK) return st;
   }
-  // workgroups resident at once for this block size (cached per wave count)
-  // (the same on every MI355X; concurrent first calls store the same value)
-  static std::atomic<int> occ_cache[MAXT / 64 + 1];
-  int occ = occ_cache[waves].load(std::memory_order_relaxed);
-  if (occ == 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void *>(kern),
-                                                     64 * waves, 0) != hipSuccess ||
-        occ <= 0)
-      occ = 1;
-    occ_cache[waves].store(occ, std::memory_order_relaxed);
+  const int grid = single ? groups : slots;
+  // Activations of up to 4 or 8 rows in compact loads (compact_pick: 4 or 2
+  // times fewer activation load instructions per batch; square 4096^2 M = 2:
+  // 4-bit 5.55 -> 5.39 us, 8-bit 6.95 -> 6.54, mxfp4 5.55 -> 5.25, nvfp4
+  // 5.91 -> 5.37; 27B k 6.79 -> 6.63), with one tile per workgroup and only
+  // where all the workgroups of the compact variant, which holds more
+  // registers, are resident at once.  Two tiles per workgroup measured slower
+  // with them (8-bit 3840 x 15360 at M = 2: 19.6 -> 23.2 us).  The arithmetic
+  // is the same either way.
+  if constexpr (NT == 1) {
+    auto fits = [&](const int occ) { return groups <= occ * cus; };
+    if (single && a.M <= 4 &&
+        fits(ksplit == 1 ? resident_per_cu<mfma_kernel_ptr<BITS, GS, NT, ADD, FMT, 4, 1, false>>(waves, occ4[0])
+                         : resident_per_cu<mfma_kernel_ptr<BITS, GS, NT, ADD, FMT, 4, 2, false>>(waves, occ4[1])))
+      return launch_mfma_k<BITS, GS, NT, ADD, FMT, 4>(a, ksplit, single, waves, grid, groups, stream);
+    if (single && a.M <= 8 &&
+        fits(ksplit == 1 ? resident_per_cu<mfma_kernel_ptr<BITS, GS, NT, ADD, FMT, 8, 1, false>>(waves, occ8[0])
+                         : resident_per_cu<mfma_kernel_ptr<BITS, GS, NT, ADD, FMT, 8, 2, false>>(waves, occ8[1])))
+      return launch_mfma_k<BITS, GS, NT, ADD, FMT, 8>(a, ksplit, single, waves, grid, groups, stream);
   }
-  const int slots = occ * cus;
-  const bool single = groups <= slots;
-  const auto k = ksplit == 1 ? (single ? kern1 : kern) : (single ? kern1_s : kern_s);
-  hipLaunchKernelGGL(k, dim3(single ? groups : slots), dim3(64 * waves), 0, stream, a.codes,
-                     a.scales, a.biases, a.x, a.y, a.res, a.M, a.N, a.K, groups, GatherArgs{});
-  return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+  return launch_mfma_k<BITS, GS, NT, ADD, FMT, 0>(a, ksplit, single, waves, grid, groups, stream);
 }
 
 template <int BITS, int GS, int FMT = kAffine>

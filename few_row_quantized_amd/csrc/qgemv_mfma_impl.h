@@ -36,7 +36,7 @@ struct GatherArgs {
 // with two, workgroup b serves item b and exits if its slot is past the
 // union.  (KS = 1, not PERSIST, affine codes.)
 template <int BITS, int GS, int NT, int MAXT, int SPI, int KS, bool PERSIST, bool ADD, int FMT,
-          bool GATHER = false>
+          bool GATHER = false, int XC = 0>
 __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *y,
@@ -64,6 +64,18 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   constexpr int UNR = SPI > BSC ? SPI : BSC;
   constexpr int BPB = UNR / BSC;       // blocks per batch
   static_assert(BSC >= 1 && BLKW % SCW == 0 && UNR % BSC == 0 && CPG >= 1, "block layout");
+  // compact activation loads: XG operands per load, NLD loads per batch; a
+  // load holds operands of one block, and the operands of a load cover part
+  // of one super-chunk (LPU loads each) or whole super-chunks (SPL each)
+  static_assert(XC == 0 || ((XC == 4 || XC == 8) && !GATHER), "compact activation rows");
+  constexpr int XG = XC ? 16 / XC : 1;
+  constexpr int OPS = XR * HS;        // activation operands per super-chunk
+  constexpr int NGR = UNR * OPS;      // activation operands per batch
+  constexpr int NLD = NGR / XG;
+  constexpr int LPU = OPS >= XG ? OPS / XG : 1;
+  constexpr int SPL = OPS >= XG ? 1 : XG / OPS;
+  static_assert(NGR % XG == 0 && (OPS % XG == 0 || XG % OPS == 0) && (BSC * OPS) % XG == 0,
+                "compact activation layout");
 
   __shared__ float red[MAXT / 64][NT][4][64];
 
@@ -221,7 +233,7 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   // data each lane ends up with is the same either way, so results do not
   // depend on the choice).  Thresholds measured on the square shapes; M is
   // the rows of this group (a gathered expert's chunk of pairs).
-  const bool xquad = FMT != kAffine || M >= (BITS == 8 ? 3 : (LVL == 0 ? 8 : 5));
+  const bool xquad = XC == 0 && (FMT != kAffine || M >= (BITS == 8 ? 3 : (LVL == 0 ? 8 : 5)));
   const int xkb = xquad ? (lane & 3) : kb;
   int xoff[4];
 #pragma unroll
@@ -247,6 +259,22 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   // so their lanes read valid clamped addresses instead of branching around
   // the loads (a branch would force a wait on every load).
   const uint16_t *xr = x + xrow(min(xquad ? (lane >> 2) : col, M - 1)) * K;
+  // Compact activation loads (XC = 4 or 8 rows, M <= XC; see compact_pick):
+  // load ld of a batch carries operands ld*XG .. ld*XG + XG-1 of the batch,
+  // numbered (u, i, l) -> (u*OPS + i*HS + l); this lane holds operand
+  // ld*XG + lane%XG of row (lane%16)/XG at its K-part kb.  Its element
+  // offset within the batch is (ld / LPU)*SPL*SCW + xlp[ld % LPU].
+  const uint16_t *xrc = x + (size_t)min((lane & 15) / XG, M - 1) * K;
+  int xlp[LPU];
+  if constexpr (XC != 0) {
+#pragma unroll
+    for (int p = 0; p < LPU; ++p) {
+      const int f = p * XG + (lane & (XG - 1));  // operand within the load's first super-chunk
+      const int u = f / OPS, i = (f % OPS) / HS, l = f % HS;
+      const int ii = BITS == 8 ? 2 * i : i;
+      xlp[p] = u * SCW + lvl_chunk<LVL>(ii, kb) * CW + lvl_dword<LVL>(ii, kb) * DW + 8 * l;
+    }
+  }
   const uint8_t *crow[NT];
   const uint16_t *srow[NT];
   const uint16_t *brow[NT];
@@ -272,7 +300,7 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
       for (int j = 0; j < NT; ++j) {
         const int o = min((int)threadIdx.x + j * (int)blockDim.x, NT * 256 - 1);
         const int l = o & 63;
-        const int m = min(4 * (l >> 4) + ((o >> 6) & 3), M - 1);
+        const int m = min((4 * (l >> 4) + ((o >> 6) & 3)) / XG, M - 1);
         const int n = min(n_base + 16 * (o >> 8) + (l & 15), N - 1);
         rpre[j] = res[yrow(m) * N + n];
       }
@@ -297,18 +325,31 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     const int nb = min(BPB, b_end - blk0);  // blocks in this batch (uniform)
     // ---- issue: activations first (L2), then codes (HBM), then metadata
     u32x4_t xv[UNR][XR][HS];
+    u32x4_t cx[XC ? NLD : 1];
     u32x4_t cv[UNR][NT];
     uint2 s4[BPB][NT], b4[BPB][NT];
+    if constexpr (XC != 0) {
+      // a load of a block past the batch reads the batch's first operands
+      // (never used)
+      const uint16_t *xb = xrc + (size_t)blk0 * BSC * SCW;
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      if (u / BSC < nb) {
-        const int k0 = (blk0 * BSC + u) * SCW;
+      for (int ld = 0; ld < NLD; ++ld) {
+        const int blk = ld * XG / (BSC * OPS);
+        cx[ld] = *reinterpret_cast<const u32x4_t *>(
+            xb + (blk < nb ? (ld / LPU) * SPL * SCW + xlp[ld % LPU] : xlp[0]));
+      }
+    } else {
 #pragma unroll
-        for (int i = 0; i < XR; ++i)
+      for (int u = 0; u < UNR; ++u) {
+        if (u / BSC < nb) {
+          const int k0 = (blk0 * BSC + u) * SCW;
 #pragma unroll
-          for (int l = 0; l < HS; ++l)
-            xv[u][i][l] = *reinterpret_cast<const u32x4_t *>(
-                xr + k0 + (BITS == 8 ? xoff[2 * i] : xoff[i]) + 8 * l);
+          for (int i = 0; i < XR; ++i)
+#pragma unroll
+            for (int l = 0; l < HS; ++l)
+              xv[u][i][l] = *reinterpret_cast<const u32x4_t *>(
+                  xr + k0 + (BITS == 8 ? xoff[2 * i] : xoff[i]) + 8 * l);
+        }
       }
     }
 #pragma unroll
@@ -350,7 +391,17 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     // code pairing and form the per-group activation sums.  xsum of group
     // g0 + j ends up in row j of this lane's column, i.e. in the A layout of
     // v_mfma_f32_16x16x4_f32 for the bias product.
-    if (xquad) {
+    if constexpr (XC != 0) {
+#pragma unroll
+      for (int u = 0; u < UNR; ++u)
+#pragma unroll
+        for (int i = 0; i < XR; ++i)
+#pragma unroll
+          for (int l = 0; l < HS; ++l) {
+            const int f = (u * XR + i) * HS + l;
+            xv[u][i][l] = compact_pick<XG>(cx[f / XG], f % XG);
+          }
+    } else if (xquad) {
 #pragma unroll
       for (int u = 0; u < UNR; ++u)
 #pragma unroll
@@ -580,7 +631,9 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     const int l = o & 63;
     float s = 0.f;
     for (int w = 0; w < waves; ++w) s += red[w][t][i][l];
-    const int m = 4 * (l >> 4) + i;
+    // MFMA row a holds activation row a / XG (compact loads: each row XG times)
+    const int a = 4 * (l >> 4) + i;
+    const int m = a % XG == 0 ? a / XG : M;
     const int n = n_base + 16 * t + (l & 15);
     if (m < M && n < N) {
       float *dst = y + yrow(m) * N + n;

@@ -15,7 +15,8 @@
 //   vw, vw+W, ... (vw = w rotated per workgroup) for every tile, so its
 //   activation operands and the per-group activation sums of the bias term
 //   are loaded, re-paired and summed once and then stay in registers while
-//   the workgroup walks its tiles.
+//   the workgroup walks its tiles (up to 4 or 8 rows in compact loads, each
+//   row filling 4 or 2 MFMA rows: compact_pick in qgemv_device.h).
 // * Codes and group metadata of the next tile are prefetched into a ring of
 //   S register slots while the current tile is unpacked and multiplied, so a
 //   CU keeps weight bytes in flight from its first tile to its last.  Codes
@@ -42,7 +43,7 @@ namespace {
 // y and res may be the same buffer (in-place residual sum): neither is
 // declared restrict; every element is read before it is written, by the same
 // thread.
-template <int BITS, int GS, int BPW, int S, int MAXW, bool ADD, bool PAIRK>
+template <int BITS, int GS, int BPW, int S, int MAXW, bool ADD, bool PAIRK, int XC>
 __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *y,
@@ -71,6 +72,12 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   // 2-bit codes, where metadata loads are few
   constexpr bool MQ = BITS == 4 && GS <= 64;
   static_assert(BSC >= 1 && BLKW % SCW == 0 && CPG >= 1, "block layout");
+  // compact activation loads (XC = 4 or 8 rows, M <= XC; see compact_pick):
+  // XG operands per load, LPU loads per super-chunk
+  static_assert(XC == 0 || XC == 4 || XC == 8, "compact activation rows");
+  constexpr int XG = XC ? 16 / XC : 1;
+  constexpr int OPS = 4 * HS;  // activation operands per super-chunk
+  constexpr int LPU = OPS / XG;
 
   __shared__ float red[S][MAXW][4][64];
 
@@ -93,7 +100,7 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   // activation loads in the quad-row layout once several rows are distinct
   // (results do not depend on the choice; from M = 5 for every group size
   // here: 27B q at M = 7, 9.44 -> 8.91 us)
-  const bool xquad = M >= 5;
+  const bool xquad = XC == 0 && M >= 5;
   const int xkb = xquad ? (lane & 3) : kb;
   int xoff[4];
 #pragma unroll
@@ -122,17 +129,39 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   const uint16_t *xr = x + (size_t)min(xquad ? (lane >> 2) : col, M - 1) * K;
   u32x4_t xv[BPW][BSC][4][HS];
   float xsum[BPW];
+  // compact loads: load p of a super-chunk carries its operands p*XG ..
+  // p*XG + XG-1 (operand (i, l) -> i*HS + l); this lane holds operand
+  // p*XG + lane%XG of row (lane%16)/XG at its K-part kb
+  u32x4_t cx[XC ? BPW : 1][XC ? BSC : 1][LPU];
+  if constexpr (XC != 0) {
+    const uint16_t *xrc = x + (size_t)min((lane & 15) / XG, M - 1) * K;
+    int xlp[LPU];
 #pragma unroll
-  for (int k = 0; k < BPW; ++k)
-#pragma unroll
-    for (int u = 0; u < BSC; ++u) {
-      const int k0 = (blk[k] * BSC + u) * SCW;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int l = 0; l < HS; ++l)
-          xv[k][u][i][l] = *reinterpret_cast<const u32x4_t *>(xr + k0 + xoff[i] + 8 * l);
+    for (int p = 0; p < LPU; ++p) {
+      const int f = p * XG + (lane & (XG - 1));
+      const int i = f / HS, l = f % HS;
+      xlp[p] = lvl_chunk<LVL>(i, kb) * CW + lvl_dword<LVL>(i, kb) * DW + 8 * l;
     }
+#pragma unroll
+    for (int k = 0; k < BPW; ++k)
+#pragma unroll
+      for (int u = 0; u < BSC; ++u)
+#pragma unroll
+        for (int p = 0; p < LPU; ++p)
+          cx[k][u][p] = *reinterpret_cast<const u32x4_t *>(xrc + (blk[k] * BSC + u) * SCW + xlp[p]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < BPW; ++k)
+#pragma unroll
+      for (int u = 0; u < BSC; ++u) {
+        const int k0 = (blk[k] * BSC + u) * SCW;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int l = 0; l < HS; ++l)
+            xv[k][u][i][l] = *reinterpret_cast<const u32x4_t *>(xr + k0 + xoff[i] + 8 * l);
+      }
+  }
 
   // ---- prefetch ring of codes and metadata.  Issues past the last tile are
   // still made (a branch around loads would make the compiler wait for every
@@ -182,7 +211,19 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   // keep the code loads ahead of the activation work that waits for x
   __builtin_amdgcn_sched_barrier(0);
 
-  if (xquad) {
+  if constexpr (XC != 0) {
+#pragma unroll
+    for (int k = 0; k < BPW; ++k)
+#pragma unroll
+      for (int u = 0; u < BSC; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int l = 0; l < HS; ++l) {
+            const int f = i * HS + l;
+            xv[k][u][i][l] = compact_pick<XG>(cx[k][u][f / XG], f % XG);
+          }
+  } else if (xquad) {
 #pragma unroll
     for (int k = 0; k < BPW; ++k)
 #pragma unroll
@@ -226,7 +267,7 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
       for (int j = 0; j < S; ++j) {
         const int o = min((int)threadIdx.x + j * (int)blockDim.x, S * 256 - 1);
         const int l = o & 63;
-        const int m = min(4 * (l >> 4) + ((o >> 6) & 3), M - 1);
+        const int m = min((4 * (l >> 4) + ((o >> 6) & 3)) / XG, M - 1);
         const int n = min(16 * (t_first + j0 + (o >> 8)) + (l & 15), N - 1);
         rpre[j] = res[(size_t)m * N + n];
       }
@@ -324,7 +365,9 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
         const int pw = w >= rot ? w - rot : w - rot + W;  // wave acting as virtual wave w
         v += red[s][pw][i][l];
       }
-      const int m = 4 * (l >> 4) + i;
+      // MFMA row a holds activation row a / XG (compact loads: each row XG times)
+      const int a = 4 * (l >> 4) + i;
+      const int m = a % XG == 0 ? a / XG : M;
       const int n = 16 * (t_first + j0 + s) + (l & 15);
       if (m < M && n < N) {
         if constexpr (ADD) {
@@ -355,7 +398,7 @@ struct PersistShape {
   static constexpr int S = 2;
 };
 
-template <int BITS, int GS, bool ADD>
+template <int BITS, int GS, bool ADD, int XC>
 int launch_persist_t(const QgemvArgs &a, hipStream_t stream) {
   constexpr int BPW = PersistShape<BITS, GS>::BPW;
   constexpr int MAXW = PersistShape<BITS, GS>::MAXW;
@@ -370,18 +413,28 @@ int launch_persist_t(const QgemvArgs &a, hipStream_t stream) {
   // two (an even block count)
   constexpr bool CAN_PAIRK = BPW == 2 && 4 * GS * BITS == 512;
   if (CAN_PAIRK && nblk % 2 == 0) {
-    hipLaunchKernelGGL((qgemv_persist_kernel<BITS, GS, BPW, S, MAXW, ADD, CAN_PAIRK>), dim3(G), dim3(64 * waves),
+    hipLaunchKernelGGL((qgemv_persist_kernel<BITS, GS, BPW, S, MAXW, ADD, CAN_PAIRK, XC>), dim3(G), dim3(64 * waves),
                        0, stream, a.codes, a.scales, a.biases, a.x, a.y, a.res, a.M, a.N, a.K);
     return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
   }
-  hipLaunchKernelGGL((qgemv_persist_kernel<BITS, GS, BPW, S, MAXW, ADD, false>), dim3(G), dim3(64 * waves),
+  hipLaunchKernelGGL((qgemv_persist_kernel<BITS, GS, BPW, S, MAXW, ADD, false, XC>), dim3(G), dim3(64 * waves),
                      0, stream, a.codes, a.scales, a.biases, a.x, a.y, a.res, a.M, a.N, a.K);
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
 }
 
+template <int BITS, int GS, int XC>
+int launch_persist_c(const QgemvArgs &a, hipStream_t stream) {
+  return a.res ? launch_persist_t<BITS, GS, true, XC>(a, stream) : launch_persist_t<BITS, GS, false, XC>(a, stream);
+}
+
+// Activations of up to 4 or 8 rows in compact loads (compact_pick): 4 or 2
+// times fewer activation load instructions in the prologue.  The arithmetic
+// is the same either way.
 template <int BITS, int GS>
 int launch_persist_gs(const QgemvArgs &a, hipStream_t stream) {
-  return a.res ? launch_persist_t<BITS, GS, true>(a, stream) : launch_persist_t<BITS, GS, false>(a, stream);
+  if (a.M <= 4) return launch_persist_c<BITS, GS, 4>(a, stream);
+  if (a.M <= 8) return launch_persist_c<BITS, GS, 8>(a, stream);
+  return launch_persist_c<BITS, GS, 0>(a, stream);
 }
 
 }  // namespace

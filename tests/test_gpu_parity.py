@@ -202,7 +202,7 @@ def test_row_of_m_row_call_equals_single_row_call_bitwise(path, bits, gs, N, K):
         singles.append(y1)
     torch.cuda.synchronize()
     singles = torch.cat(singles).cpu().numpy()
-    for M in (2, 3, 4, 5, 8, 12, 16):
+    for M in (2, 3, 4, 5, 6, 7, 8, 9, 12, 16):
         y = d.run_host(M, path)
         assert np.array_equal(y, singles[:M]), f"M={M}"
 
