@@ -31,7 +31,8 @@ struct GatherArgs {
 // block scale before the MFMA, exactly, so B holds the weights themselves).
 // GATHER: the rows of a (slot, tile group) item are the pairs routed to the
 // slot's expert (slots: the union of e_idx in ascending id order; pairs in
-// ascending order, 16 at a time), gathered from x and scattered to y[pair].
+// ascending order, 16 at a time, or XC with compact rows), gathered from x
+// and scattered to y[pair].
 // With one tile per workgroup the grid walks the items with its stride;
 // with two, workgroup b serves item b and exits if its slot is past the
 // union.  (KS = 1, not PERSIST, affine codes.)
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   // compact activation loads: XG operands per load, NLD loads per batch; a
   // load holds operands of one block, and the operands of a load cover part
   // of one super-chunk (LPU loads each) or whole super-chunks (SPL each)
-  static_assert(XC == 0 || ((XC == 4 || XC == 8) && !GATHER), "compact activation rows");
+  static_assert(XC == 0 || XC == 4 || XC == 8, "compact activation rows");
   constexpr int XG = XC ? 16 / XC : 1;
   constexpr int OPS = XR * HS;        // activation operands per super-chunk
   constexpr int NGR = UNR * OPS;      // activation operands per batch
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   // numbered (u, i, l) -> (u*OPS + i*HS + l); this lane holds operand
   // ld*XG + lane%XG of row (lane%16)/XG at its K-part kb.  Its element
   // offset within the batch is (ld / LPU)*SPL*SCW + xlp[ld % LPU].
-  const uint16_t *xrc = x + (size_t)min((lane & 15) / XG, M - 1) * K;
+  const uint16_t *xrc = x + xrow(min((lane & 15) / XG, M - 1)) * K;
   int xlp[LPU];
   if constexpr (XC != 0) {
 #pragma unroll
@@ -664,9 +665,13 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   for (int o = threadIdx.x + NT * blockDim.x; o < NT * 256; o += blockDim.x) finish(o, false, 0.f);
   };
 
+  // rows per chunk of a gathered expert's pairs: 16, or the compact row
+  // count (the launcher takes it at least the activation rows, so a routing
+  // with at most one pair per expert and row still gives one chunk per expert)
+  constexpr int CH = XC ? XC : 16;
   if constexpr (GSORT) {
     // items (slot, tile group) in slot-major order, walked with the grid
-    // stride; each slot's pairs are taken 16 rows at a time
+    // stride; each slot's pairs are taken CH rows at a time
     const int items = gmeta[0] * ngroups;
     const size_t G_ = (size_t)(K / GS);
     bool first = true;
@@ -678,18 +683,18 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
       biases = biases0 + (size_t)expert * N * G_;
       pbase = gstart[slot];
       const int pairs = gstart[slot + 1] - pbase;
-      for (c0 = 0; c0 < pairs; c0 += 16) {
-        M = min(16, pairs - c0);
+      for (c0 = 0; c0 < pairs; c0 += CH) {
+        M = min(CH, pairs - c0);
         if (!first) __syncthreads();  // reduction buffer drained
         first = false;
         group(w - slot * ngroups);
       }
     }
   } else if constexpr (GATHER) {
-    // the expert's pairs, 16 rows at a time
+    // the expert's pairs, CH rows at a time
     const int pairs = gmeta[1];
-    for (c0 = 0; c0 < pairs; c0 += 16) {
-      M = min(16, pairs - c0);
+    for (c0 = 0; c0 < pairs; c0 += CH) {
+      M = min(CH, pairs - c0);
       if (c0 != 0) __syncthreads();  // reduction buffer drained
       group((int)blockIdx.x % ngroups);
     }

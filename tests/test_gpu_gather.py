@@ -36,14 +36,16 @@ class MoeDevice:
         self.biases = torch.from_numpy(p.biases.view(np.int16)).to(d)
         self.x = torch.from_numpy(p.x.view(np.int16)).to(d)
 
-    def run(self, x_idx, e_idx, fill=float("nan")):
+    def run(self, x_idx, e_idx, fill=float("nan"), X=None):
+        # X: activation rows passed to the call (the first X rows of x)
         import torch
         s = self.p.shape
+        X = self.p.x.shape[0] if X is None else X
         P = len(e_idx)
         xi = torch.from_numpy(np.asarray(x_idx, np.int32)).to("cuda:0")
         ei = torch.from_numpy(np.asarray(e_idx, np.int32)).to("cuda:0")
         y = torch.full((P, s.N), fill, dtype=torch.float32, device="cuda:0")
-        q.qgemv_gather(self.codes, self.scales, self.biases, self.x, xi, ei, y, P, self.p.x.shape[0],
+        q.qgemv_gather(self.codes, self.scales, self.biases, self.x, xi, ei, y, P, X,
                        s.E, s.N, s.K, s.bits, s.group_size)
         torch.cuda.synchronize()
         return y.cpu().numpy()
@@ -85,6 +87,24 @@ def test_many_pairs_on_one_expert():
     e_idx[[5, 17, 33]] = [0, 11, 3]
     say("gather many pairs on one expert")
     check(p, d.run(x_idx, e_idx), x_idx, e_idx, label="one expert")
+
+
+@pytest.mark.parametrize("bits,gs", [(4, 64), (2, 64), (8, 32)])
+def test_few_activation_rows_every_element_and_bitwise(bits, gs):
+    # at most 4 activation rows: compact activation loads, experts' pairs
+    # taken 4 at a time (an expert with more pairs than rows gets several
+    # chunks); each pair's row is the same float as with 16 rows passed
+    p = small(bits=bits, gs=gs, seed=19 + bits)
+    d = MoeDevice(p)
+    rng = np.random.default_rng(7)
+    for X in (1, 3, 4):
+        for P in (1, 9, 40):
+            x_idx = rng.integers(0, X, size=P)
+            e_idx = rng.integers(0, 3 if P == 40 else p.shape.E, size=P)  # P = 40: ~13 pairs per expert
+            say(f"gather few rows bits={bits} gs={gs} X={X} P={P}")
+            y = d.run(x_idx, e_idx, X=X)
+            check(p, y, x_idx, e_idx, label=f"X={X} P={P}")
+            assert np.array_equal(y, d.run(x_idx, e_idx)), f"X={X} P={P} against 16 rows"
 
 
 def test_invalid_pairs_leave_rows_untouched():
