@@ -106,6 +106,7 @@ int launch_gather(const QgemvArgs &a, const int32_t *x_idx, const int32_t *e_idx
     switch (a.group_size) {
       case 32: return launch_gather_t<8, 32>(a, ga, stream);
       case 64: return launch_gather_t<8, 64>(a, ga, stream);
+      case 128: return launch_gather_t<8, 128>(a, ga, stream);
     }
   }
   return QGEMV_EUNSUPPORTED;

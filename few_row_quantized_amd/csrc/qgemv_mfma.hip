@@ -189,9 +189,6 @@ bool mfma_supports_fp(int K, int fmt) {
 
 bool mfma_supports(int K, int bits, int group_size) {
   if (bits == 2 && group_size < 64) return false;
-  // 8-bit gs128: a bias block (4 groups) would be 8 super-chunks per batch,
-  // beyond the register budget
-  if (bits == 8 && group_size > 64) return false;
   const int scw = 512 / bits;  // codes per 64-byte super-chunk
   return K % scw == 0 && K % (4 * group_size) == 0;
 }
@@ -218,6 +215,7 @@ int launch_mfma(const QgemvArgs &a, hipStream_t stream) {
     switch (a.group_size) {
       case 32: return launch_mfma_gs<8, 32>(a, stream);
       case 64: return launch_mfma_gs<8, 64>(a, stream);
+      case 128: return launch_mfma_gs<8, 128>(a, stream);
     }
   } else if (a.bits == 4) {
     switch (a.group_size) {

@@ -154,8 +154,8 @@ int qgemv_select(int M, int N, int K, int bits, int group_size);
  * GGML_METAL_MM_MIN; MLX page, Facts: forced qmv vs qmm sweeps).
  * Returns QGEMV_EUNSUPPORTED if the path cannot run the shape (the MFMA path
  * needs K to be a multiple of 4*group_size and of 256 (2-bit) / 128 (4-bit) /
- * 64 (8-bit), group_size >= 64 for 2-bit codes and group_size <= 64 for 8-bit
- * codes).  Other arguments as qgemv_small.
+ * 64 (8-bit), and group_size >= 64 for 2-bit codes).  Other arguments as
+ * qgemv_small.
  */
 int qgemv_run_path(int path, const uint8_t *codes, const uint16_t *scales,
                    const uint16_t *biases, const uint16_t *x, float *y, int M, int N, int K,

@@ -141,8 +141,8 @@ def test_mfma_path_shape_support():
     assert not sup("mfma", 4, 4096, 640, 4, 128)    # K not a multiple of 4*gs
     assert sup("dot", 4, 4096, 192, 4, 32)
     assert sup("mfma", 4, 4096, 4096, 8, 32) and sup("mfma", 4, 4096, 4096, 8, 64)
-    assert not sup("mfma", 4, 4096, 4096, 8, 128)   # 8-bit gs128: dot path only
-    assert sup("dot", 4, 4096, 4096, 8, 128)
+    assert sup("mfma", 4, 4096, 4096, 8, 128) and sup("dot", 4, 4096, 4096, 8, 128)
+    assert not sup("mfma", 4, 4096, 4352, 8, 128)   # K not a multiple of 4*gs
     # a forced path that cannot run the shape is refused before launch
     assert q.lib().qgemv_run_path(q.PATH_MFMA, A, A, A, A, A, 4, 64, 192, 4, 32, None) == q.EUNSUPPORTED
 
