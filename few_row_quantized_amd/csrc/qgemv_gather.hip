@@ -31,11 +31,11 @@ namespace {
 
 constexpr int kGatherWideTiles = 64;
 
-template <int BITS, int GS, int NT, int XC>
+template <int BITS, int GS, int NT, int XC, bool XDYN>
 int launch_gather_nt(const QgemvArgs &a, const GatherArgs &ga, hipStream_t stream) {
   constexpr int MAXT = MfmaShape<BITS, GS, NT>::MAXT;
   constexpr int SPI = MfmaShape<BITS, GS, NT>::SPI;
-  const auto kern = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, false, false, kAffine, true, XC>;
+  const auto kern = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, false, false, kAffine, true, XC, XDYN>;
   const int nblk = a.K / (4 * GS);
   // at most 4 waves (K-slices) per item: more workgroups resident per CU, so
   // more items' loads in flight (128-expert top-8 1536 x 2048 gate/up: 70.3 ->
@@ -76,13 +76,16 @@ int launch_gather_nt(const QgemvArgs &a, const GatherArgs &ga, hipStream_t strea
 template <int BITS, int GS>
 int launch_gather_t(const QgemvArgs &a, const GatherArgs &ga, hipStream_t stream) {
   if ((a.N + 15) / 16 >= kGatherWideTiles && a.K / (4 * GS) <= 4)
-    return launch_gather_nt<BITS, GS, 2, 0>(a, ga, stream);
+    return launch_gather_nt<BITS, GS, 2, 0, false>(a, ga, stream);
   // activation rows in compact loads (compact_pick) when there are at most 4
   // of them: a valid routing then sends each expert at most 4 pairs, one
   // chunk (128-expert top-8 2048 -> 1536 gate/up: 8.89 -> 8.46 us at M = 1,
-  // 20.98 -> 20.06 at M = 4; with 8 rows at M = 5..8 within 1%)
-  if (ga.X <= 4) return launch_gather_nt<BITS, GS, 1, 4>(a, ga, stream);
-  return launch_gather_nt<BITS, GS, 1, 0>(a, ga, stream);
+  // 20.98 -> 20.06 at M = 4; with 8 rows at M = 5..8 within 1%); with more
+  // rows, each chunk of at most 4 pairs takes them (the same shape: 25.7 ->
+  // 25.1 us at M = 5, 60.3 -> 58.3 at M = 16; with two tiles per workgroup
+  // neither helped: 2048 x 768 +1% at M = 5..16)
+  if (ga.X <= 4) return launch_gather_nt<BITS, GS, 1, 4, false>(a, ga, stream);
+  return launch_gather_nt<BITS, GS, 1, 0, true>(a, ga, stream);
 }
 
 }  // namespace

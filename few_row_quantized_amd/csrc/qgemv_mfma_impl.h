@@ -4,6 +4,8 @@
 // (qgemv_gather.hip).  The design is described in qgemv_mfma.hip.
 #pragma once
 
+#include <type_traits>
+
 #include "qgemv_device.h"
 #include "qgemv_internal.h"
 
@@ -37,7 +39,7 @@ struct GatherArgs {
 // with two, workgroup b serves item b and exits if its slot is past the
 // union.  (KS = 1, not PERSIST, affine codes.)
 template <int BITS, int GS, int NT, int MAXT, int SPI, int KS, bool PERSIST, bool ADD, int FMT,
-          bool GATHER = false, int XC = 0>
+          bool GATHER = false, int XC = 0, bool XDYN = false>
 __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *y,
@@ -65,18 +67,10 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   constexpr int UNR = SPI > BSC ? SPI : BSC;
   constexpr int BPB = UNR / BSC;       // blocks per batch
   static_assert(BSC >= 1 && BLKW % SCW == 0 && UNR % BSC == 0 && CPG >= 1, "block layout");
-  // compact activation loads: XG operands per load, NLD loads per batch; a
-  // load holds operands of one block, and the operands of a load cover part
-  // of one super-chunk (LPU loads each) or whole super-chunks (SPL each)
+  // compact activation rows (XC: 4 or 8; XDYN, gathered verify: 4 for the
+  // chunks of at most 4 rows, none for the others)
   static_assert(XC == 0 || XC == 4 || XC == 8, "compact activation rows");
-  constexpr int XG = XC ? 16 / XC : 1;
-  constexpr int OPS = XR * HS;        // activation operands per super-chunk
-  constexpr int NGR = UNR * OPS;      // activation operands per batch
-  constexpr int NLD = NGR / XG;
-  constexpr int LPU = OPS >= XG ? OPS / XG : 1;
-  constexpr int SPL = OPS >= XG ? 1 : XG / OPS;
-  static_assert(NGR % XG == 0 && (OPS % XG == 0 || XG % OPS == 0) && (BSC * OPS) % XG == 0,
-                "compact activation layout");
+  static_assert(!XDYN || (GATHER && XC == 0), "per-chunk compact rows");
 
   __shared__ float red[MAXT / 64][NT][4][64];
 
@@ -227,14 +221,26 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   auto yrow = [&](const int m) -> size_t { return GATHER ? (size_t)gsorted[pbase + c0 + m] : (size_t)m; };
 
   // One tile group (16*NT output columns over all of K) per call of `group`.
-  auto group = [&](const int tg) {
+  auto group_x = [&](auto xc_tag, const int tg) {
+  // compact activation loads: XG operands per load, NLD loads per batch; a
+  // load holds operands of one block, and the operands of a load cover part
+  // of one super-chunk (LPU loads each) or whole super-chunks (SPL each)
+  constexpr int XCV = decltype(xc_tag)::value;
+  constexpr int XG = XCV ? 16 / XCV : 1;
+  constexpr int OPS = XR * HS;        // activation operands per super-chunk
+  constexpr int NGR = UNR * OPS;      // activation operands per batch
+  constexpr int NLD = NGR / XG;
+  constexpr int LPU = OPS >= XG ? OPS / XG : 1;
+  constexpr int SPL = OPS >= XG ? 1 : XG / OPS;
+  static_assert(NGR % XG == 0 && (OPS % XG == 0 || XG % OPS == 0) && (BSC * OPS) % XG == 0,
+                "compact activation layout");
   // Activation loads in the quad-row layout (lane L: what lane (L/4, L%4)
   // needs) once several rows are distinct; with few rows most lanes read the
   // same row anyway and the move to the operand lanes would only cost (the
   // data each lane ends up with is the same either way, so results do not
   // depend on the choice).  Thresholds measured on the square shapes; M is
   // the rows of this group (a gathered expert's chunk of pairs).
-  const bool xquad = XC == 0 && (FMT != kAffine || M >= (BITS == 8 ? 3 : (LVL == 0 ? 8 : 5)));
+  const bool xquad = XCV == 0 && (FMT != kAffine || M >= (BITS == 8 ? 3 : (LVL == 0 ? 8 : 5)));
   const int xkb = xquad ? (lane & 3) : kb;
   int xoff[4];
 #pragma unroll
@@ -260,14 +266,14 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   // so their lanes read valid clamped addresses instead of branching around
   // the loads (a branch would force a wait on every load).
   const uint16_t *xr = x + xrow(min(xquad ? (lane >> 2) : col, M - 1)) * K;
-  // Compact activation loads (XC = 4 or 8 rows, M <= XC; see compact_pick):
+  // Compact activation loads (XCV = 4 or 8 rows, M <= XCV; see compact_pick):
   // load ld of a batch carries operands ld*XG .. ld*XG + XG-1 of the batch,
   // numbered (u, i, l) -> (u*OPS + i*HS + l); this lane holds operand
   // ld*XG + lane%XG of row (lane%16)/XG at its K-part kb.  Its element
   // offset within the batch is (ld / LPU)*SPL*SCW + xlp[ld % LPU].
   const uint16_t *xrc = x + xrow(min((lane & 15) / XG, M - 1)) * K;
   int xlp[LPU];
-  if constexpr (XC != 0) {
+  if constexpr (XCV != 0) {
 #pragma unroll
     for (int p = 0; p < LPU; ++p) {
       const int f = p * XG + (lane & (XG - 1));  // operand within the load's first super-chunk
@@ -326,10 +332,10 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     const int nb = min(BPB, b_end - blk0);  // blocks in this batch (uniform)
     // ---- issue: activations first (L2), then codes (HBM), then metadata
     u32x4_t xv[UNR][XR][HS];
-    u32x4_t cx[XC ? NLD : 1];
+    u32x4_t cx[XCV ? NLD : 1];
     u32x4_t cv[UNR][NT];
     uint2 s4[BPB][NT], b4[BPB][NT];
-    if constexpr (XC != 0) {
+    if constexpr (XCV != 0) {
       // a load of a block past the batch reads the batch's first operands
       // (never used)
       const uint16_t *xb = xrc + (size_t)blk0 * BSC * SCW;
@@ -392,7 +398,7 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     // code pairing and form the per-group activation sums.  xsum of group
     // g0 + j ends up in row j of this lane's column, i.e. in the A layout of
     // v_mfma_f32_16x16x4_f32 for the bias product.
-    if constexpr (XC != 0) {
+    if constexpr (XCV != 0) {
 #pragma unroll
       for (int u = 0; u < UNR; ++u)
 #pragma unroll
@@ -663,6 +669,14 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     if (o < NT * 256) finish(o, true, ADD ? rpre[j] : 0.f);
   }
   for (int o = threadIdx.x + NT * blockDim.x; o < NT * 256; o += blockDim.x) finish(o, false, 0.f);
+  };
+  auto group = [&](const int tg) {
+    if constexpr (XDYN) {
+      if (M <= 4) group_x(std::integral_constant<int, 4>{}, tg);
+      else group_x(std::integral_constant<int, 0>{}, tg);
+    } else {
+      group_x(std::integral_constant<int, XC>{}, tg);
+    }
   };
 
   // rows per chunk of a gathered expert's pairs: 16, or the compact row
