@@ -23,7 +23,10 @@
 //   come as whole 128-byte lines (8 rows per load) where a bias block holds
 //   an even number of 64-byte super-chunks (pair_to_operand_lanes).
 // * Every S tiles the waves' partial 16x16 tiles are summed through LDS in
-//   block order (deterministic, no atomics) and rows m < M are stored.
+//   block order (deterministic, no atomics) and rows m < M are stored.  Two
+//   LDS buffers alternate between groups of S tiles, so a group needs one
+//   workgroup barrier, not two (27B gate 5120 x 17408: 15.6 -> 14.3 us at
+//   M = 1, 16.1 -> 15.6 at M = 8).
 // * Fused residual sum (ADD, "metal : few-row MMA mat-mul and batched copies
 //   for speculative decoding", Overview: MUL_MAT + ADD writes the residual
 //   sum from the store): the residual of the S tiles' outputs a thread stores
@@ -79,7 +82,7 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   constexpr int OPS = 4 * HS;  // activation operands per super-chunk
   constexpr int LPU = OPS / XG;
 
-  __shared__ float red[S][MAXW][4][64];
+  __shared__ float red[2][S][MAXW][4][64];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -257,6 +260,7 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   // tile (do-while: no guard branch that would let the compiler sink the
   // prologue loads below the activation work)
   int j0 = 0;
+  int rb = 0;  // reduction buffer of this group
   do {
     // residual of the outputs this thread stores for these S tiles (its first
     // S reduction steps: all of them with at least 4 waves); clamped indices
@@ -352,7 +356,7 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
       // a partial whose column held only zero weights is exactly 0
       const uint32_t keep = keep_mask(column_or(nz));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[s][wave][i][lane] = unless_zero(acc[i], keep);
+      for (int i = 0; i < 4; ++i) red[rb][s][wave][i][lane] = unless_zero(acc[i], keep);
     }
 
     // ---- sum the group's partial tiles over the waves in block order
@@ -363,7 +367,7 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
       float v = 0.f;
       for (int w = 0; w < W; ++w) {
         const int pw = w >= rot ? w - rot : w - rot + W;  // wave acting as virtual wave w
-        v += red[s][pw][i][l];
+        v += red[rb][s][pw][i][l];
       }
       // MFMA row a holds activation row a / XG (compact loads: each row XG times)
       const int a = 4 * (l >> 4) + i;
@@ -383,7 +387,9 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
       if (o < nj * 256) finish(o, true, ADD ? rpre[j] : 0.f);
     }
     for (int o = threadIdx.x + S * blockDim.x; o < nj * 256; o += blockDim.x) finish(o, false, 0.f);
-    __syncthreads();  // red is rewritten by the next group
+    // the next group writes the other buffer; the group after it waits at
+    // that group's barrier, by which every thread has finished reading this one
+    rb ^= 1;
     j0 += S;
   } while (j0 < ntile);
 }
