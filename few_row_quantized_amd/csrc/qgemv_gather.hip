@@ -8,9 +8,9 @@
 // qgemv_mfma_impl.h).  The work is the (expert slot, 16-column tile group)
 // items, slots being the union's experts in ascending id order, each with its
 // pairs in ascending order taken 16 rows at a time (4 when there are at most
-// 4 activation rows).  The host does not know
-// the union size (the routing stays on the device), so it plans for
-// min(P, E) slots:
+// 4 activation rows; a chunk of at most 4 pairs loads its activations in the
+// compact form either way).  The host does not know the union size (the
+// routing stays on the device), so it plans for min(P, E) slots:
 // * one tile per workgroup: a grid of the workgroups resident at once, each
 //   sorting the routing once and walking the items with the grid stride
 //   (measured on the 128-expert top-8 1536 x 2048 gate/up shape: 80.7 ->
