@@ -53,7 +53,7 @@ def test_widest_n_every_element(K, bits, gs):
     for path in ("dot", "mfma", "auto"):
         if not q.qgemv_path_supported(path, 1, N, K, bits, gs):
             continue
-        for M in (1, 16):
+        for M in (1, 8, 16):
             say(f"max N {path} K={K} N={N} bits={bits} gs={gs} M={M}")
             y = d.run_host(M, path)
             assert np.all(np.isfinite(y)), "non-finite output"
