@@ -1,0 +1,61 @@
+"""GPU parity on seeded random shapes: every path that runs the shape, at
+random row counts, against the fp64 oracle, every element; and, within a
+forced path, row 0 of every M-row call bitwise equal to the single-row call
+(K <= 4096, where no kernel configuration depends on M).
+
+The shapes are drawn to cross the kernels' choices: N from a few columns (one
+ragged tile) to past 256 tiles (the persistent kernels), K from one bias block
+to 4096, every supported bit width and group size, outlier channels on half of
+them."""
+import numpy as np
+import pytest
+
+from few_row_quantized_amd import qgemv as q
+from few_row_quantized_amd import synth
+
+from gpu_util import DeviceProblem, OracleRows, say
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = [(2, 32), (2, 64), (2, 128), (4, 32), (4, 64), (4, 128), (8, 32), (8, 64), (8, 128)]
+
+
+def draw_cases(n_cases: int, seed: int):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n_cases):
+        bits, gs = FORMATS[rng.integers(len(FORMATS))]
+        step = int(np.lcm(64, 4 * gs))  # K a multiple of a bias block (and of 64)
+        K = step * int(rng.integers(1, 4096 // step + 1))
+        N = int(rng.choice([rng.integers(1, 48), rng.integers(48, 1200), rng.integers(4096, 6000)]))
+        Ms = sorted(set(int(m) for m in rng.integers(1, 17, size=3)))
+        cases.append((i, bits, gs, K, N, Ms, bool(rng.integers(2))))
+    return cases
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu(require_gpu):
+    import torch
+    torch.cuda.init()
+    yield
+
+
+@pytest.mark.parametrize("i,bits,gs,K,N,Ms,outliers", draw_cases(24, seed=20261202))
+def test_random_shape_every_element(i, bits, gs, K, N, Ms, outliers):
+    import torch
+    p = synth.make_problem(synth.custom_shape(K, N, bits, gs, seed=5000 + i, outliers=outliers), m_max=16)
+    d = DeviceProblem(p)
+    orc = OracleRows.affine(p, max(Ms))
+    for path in ("dot", "mfma", "auto"):
+        if not q.qgemv_path_supported(path, 1, N, K, bits, gs):
+            continue
+        y1 = None
+        for M in [1] + Ms:
+            say(f"random case {i}: {path} bits={bits} gs={gs} K={K} N={N} M={M}")
+            y = d.run_host(M, path)
+            orc.check(y, M, label=f"case {i} {path} M={M}")
+            if M == 1:
+                y1 = y
+            elif path != "auto":  # the dispatcher may pick another path at another M
+                assert np.array_equal(y[:1], y1), f"case {i} {path}: row 0 of M={M} differs from M=1"
+        torch.cuda.synchronize()
