@@ -23,17 +23,23 @@
 // * A persistent grid of one workgroup per CU.  Workgroup b takes half
 //   b & 1 of the bias blocks (4 groups) of K and the contiguous range
 //   [g*T/GP, (g+1)*T/GP) of the T 16-column tiles, g = b >> 1, GP = grid/2.
-// * Prologue (and each phase change): the next step's codes and metadata
-//   are requested, then the workgroup copies its share of x (M rows of the
-//   phase's blocks) into LDS, already re-paired to the code pairing of the
-//   MFMA operand (elements (0,2), (1,3), (4,6), (5,7) of each 8 for 4-bit
-//   codes, (e, e+4) of each 8 for 2-bit codes), and forms the
-//   activation sum of every group of that share from the registers: the
-//   lanes holding a group's units reduce their sums by a fixed butterfly
-//   (summing a group from LDS instead, one lane per group, put every lane of
-//   a wave on the same bank: row offsets of GS*2 bytes).
 // * Phase q covers the blocks [q*nb/P, (q+1)*nb/P) of the half; wave w owns
-//   its blocks lo+w, lo+w+W, ...  The workgroup walks (phase, tile) steps in
+//   its blocks lo+w, lo+w+W, ... and reads activations only from their LDS
+//   columns.  So each wave stages its own blocks (prologue and each phase
+//   change, after the next step's codes and metadata are requested): the M
+//   rows of its blocks are copied into LDS, already re-paired to the code
+//   pairing of the MFMA operand (elements (0,2), (1,3), (4,6), (5,7) of each
+//   8 for 4-bit codes, (e, e+4) of each 8 for 2-bit codes), with the
+//   activation sum of every group formed from the registers (the lanes
+//   holding a group's units reduce their sums by a fixed butterfly; summing
+//   a group from LDS instead, one lane per group, put every lane of a wave
+//   on the same bank: row offsets of GS*2 bytes).  No workgroup barrier
+//   orders the staging: a wave starts its first step as soon as its own
+//   blocks are staged and restages its columns when it leaves a phase (27B
+//   down projection, K = 17408: 19.3 -> 17.9 us at M = 1, 25.9 -> 21.6 at
+//   M = 8, 31.2 -> 24.3 at M = 12, against a workgroup-wide staging with a
+//   barrier at each phase change).
+// * The workgroup walks (phase, tile) steps in
 //   phase-major order; each step's codes and metadata come through a
 //   register ring of S slots (the next step's loads are in flight while the
 //   current one is multiplied, also across a phase change; codes as whole
@@ -56,6 +62,8 @@
 //   for speculative decoding", Overview: MUL_MAT + ADD writes the residual
 //   sum from the store): y is prefilled with kSplitSentinel; the first half
 //   to land leaves its partial, the second stores (a + b) + r.
+
+#include <type_traits>
 
 #include "qgemv_device.h"
 #include "qgemv_internal.h"
@@ -94,9 +102,6 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
   constexpr bool MQ = BITS == 4 && GS <= 64;
   constexpr int UE = BITS == 4 ? 8 : 16;  // elements of one re-pairing unit
   constexpr int GU = GS / UE;             // units per group (a power of two <= 16)
-  // staging units per thread per round: their registers are live next to
-  // one ring slot, so at most 32 VGPRs, 16 when the slot holds 8 super-chunks
-  constexpr int XU = (BPW * BSC >= 8 ? 4 : 8) / (UE / 8);
   static_assert(BSC >= 1 && BLKW % SCW == 0 && CPG >= 1 && (BITS == 2 || BITS == 4), "layout");
   // codes of two consecutive super-chunks as whole 128-byte lines (8 rows per
   // load, pair_to_operand_lanes) where a block has an even number of them;
@@ -198,48 +203,84 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
     ++it;
   };
 
-  // ---- stage x of phase q into LDS, re-paired, with the activation sum of
-  // every group, XU units per thread at a time (all loads of a round issued
-  // before any is used; clamped indices read a valid unit and are not
-  // stored).  Units are dealt to consecutive lanes, so the GU lanes holding
-  // a group's units add their sums in a fixed butterfly.
-  auto stage = [&](const int q) {
+  // ---- stage this wave's blocks of phase q into LDS (every row), re-paired,
+  // with the activation sum of every group; the other waves neither read nor
+  // write these columns, so no workgroup barrier is needed.  The wave's units
+  // (block, row, unit) are taken 64 at a time, XB rounds per batch (then
+  // smaller batches for the rest); a group's units are on consecutive lanes.
+  constexpr int UPB = BLKW / UE;                      // units per block row
+  // rounds per batch: their registers are live next to one ring slot (32
+  // VGPRs, 16 with 4-block slots)
+  constexpr int XB = (BPW >= 4 ? 4 : 8) / (UE / 8);
+  auto stage_wave = [&](const int q) {
     const int lo = phase_lo(q);
-    const int upr = (phase_lo(q + 1) - lo) * BLKW / UE;  // units per row
-    const int units = M * upr;
-    const uint16_t *xh = x + (size_t)(p_lo + lo) * BLKW;
-    for (int u0 = 0; u0 < units; u0 += XU * (int)blockDim.x) {
-      u32x4_t v[XU][UE / 8];
+    const int nbq = phase_lo(q + 1) - lo;
+    int kown = 0;  // blocks of this wave in the phase (a prefix of its slots)
 #pragma unroll
-      for (int j = 0; j < XU; ++j) {
-        const int u = min(u0 + j * (int)blockDim.x + (int)threadIdx.x, units - 1);
-        const int m = u / upr;
-        const int c = u - m * upr;
+    for (int k = 0; k < BPW; ++k) kown += wave + k * W < nbq ? 1 : 0;
+    const int per_blk = M * UPB;
+    const int units = kown * per_blk;
+    const int rounds = (units + 63) >> 6;
+    const uint16_t *xh = x + (size_t)(p_lo + lo) * BLKW;
+    // unit t -> LDS unit column c of row m (slot k's block is lq = wave + k*W)
+    auto locate = [&](const int t, int &m, int &c) {
+      int rem = t, k = 0;
+#pragma unroll
+      for (int kk = 1; kk < BPW; ++kk) {
+        if (rem >= per_blk) {
+          rem -= per_blk;
+          ++k;
+        }
+      }
+      m = rem / UPB;
+      c = (wave + k * W) * UPB + (rem - m * UPB);
+    };
+    auto batch = [&](auto nb_tag, const int r0) {
+      constexpr int NB = decltype(nb_tag)::value;
+      u32x4_t v[NB][UE / 8];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        int m, c;
+        locate(min((r0 + j) * 64 + lane, units - 1), m, c);
 #pragma unroll
         for (int h = 0; h < UE / 8; ++h)
           v[j][h] = *reinterpret_cast<const u32x4_t *>(xh + (size_t)m * K + (size_t)c * UE + 8 * h);
       }
 #pragma unroll
-      for (int j = 0; j < XU; ++j) {
-        const int u = u0 + j * (int)blockDim.x + (int)threadIdx.x;
-        float p = 0.f;
+      for (int j = 0; j < NB; ++j) {
+        const int t = (r0 + j) * 64 + lane;
+        float pp = 0.f;
 #pragma unroll
         for (int h = 0; h < UE / 8; ++h)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) p = dot2_bf16(v[j][h][e], 0x3F803F80u, p);
+          for (int e = 0; e < 4; ++e) pp = dot2_bf16(v[j][h][e], 0x3F803F80u, pp);
 #pragma unroll
-        for (int off = 1; off < GU; off <<= 1) p += __shfl_xor(p, off);
-        if (u < units) {
-          const int m = u / upr;
-          const int c = u - m * upr;
-          if ((threadIdx.x & (GU - 1)) == 0) xs[m * gpr + c / GU] = p;
+        for (int off = 1; off < GU; off <<= 1) pp += __shfl_xor(pp, off);
+        if (t < units) {
+          int m, c;
+          locate(t, m, c);
+          if ((lane & (GU - 1)) == 0) xs[m * gpr + c / GU] = pp;
           u32x4_t *dst = reinterpret_cast<u32x4_t *>(xl + (size_t)m * pitch + (size_t)c * UE * 2);
 #pragma unroll
           for (int h = 0; h < UE / 8; ++h) dst[h] = pair_activations<BITS>(v[j][h]);
         }
       }
+    };
+    int r = 0;
+    for (; r + XB <= rounds; r += XB) batch(std::integral_constant<int, XB>{}, r);
+    if constexpr (XB > 4) {
+      if (r + 4 <= rounds) {
+        batch(std::integral_constant<int, 4>{}, r);
+        r += 4;
+      }
     }
-    __syncthreads();
+    if constexpr (XB > 2) {
+      if (r + 2 <= rounds) {
+        batch(std::integral_constant<int, 2>{}, r);
+        r += 2;
+      }
+    }
+    if (r < rounds) batch(std::integral_constant<int, 1>{}, r);
   };
 
   // this lane's activation row in LDS (rows m >= M read row M-1)
@@ -260,10 +301,7 @@ __global__ __launch_bounds__(64 * kXMaxWaves) void qgemv_persist_x_kernel(
       if (step >= steps) break;
       const int q = step / ntile;
       const int tt = step - q * ntile;
-      if (tt == 0) {
-        if (q != 0) __syncthreads();  // every wave is done with the previous phase
-        stage(q);
-      }
+      if (tt == 0) stage_wave(q);
       issue((s + S - 1) % S);
       __builtin_amdgcn_sched_barrier(0);
 
