@@ -32,6 +32,21 @@
 //   sum from the store): the residual of the S tiles' outputs a thread stores
 //   is loaded when their first tile starts and added in the store, so
 //   y = fl(product + r), bit for bit the plain call and a separate fp32 add.
+// * 8-bit codes (groups of 32 or 64; MLX page, Facts: the int8 M = 8
+//   speedup) take two code registers per MFMA step in natural order, as in
+//   the single-pass kernel.  With more than 16 bias blocks (K > 4096 at
+//   groups of 64) two blocks per wave spill registers, so K is split in two
+//   halves over two workgroups instead (KS = 2: workgroup b takes half b & 1
+//   of the blocks for tile range b >> 1; each half is added into y, zeroed
+//   before the launch, which receives exactly two addends, so the result does
+//   not depend on which lands first; with the residual sum y is prefilled
+//   with kSplitSentinel and the second half stores (a + b) + r).  Measured in
+//   graph chains against the single-pass kernel: 8-bit 15360 x 3840 19.4 ->
+//   15.0 us at M = 1, 20.0 -> 15.8 at M = 8; 8-bit 17408 x 5120 (split)
+//   33.5 -> 22.3 us at M = 1, 35.2 -> 23.8 at M = 8.  The split is slower
+//   for every other format here (27B gate 5120 x 17408 4-bit gs128 15.5 ->
+//   19.3 us at M = 8, FFN-up gs64 10.4 -> 12.7, 2-bit gate/up 15.7 -> 16.1,
+//   the 8-bit 15360 x 3840 shape 15.9 -> 18.7), so only those rows take it.
 // The inner MFMA step (code layout, partial lane transpose, unpack to exact
 // bf16 q, per-group scale fold, bias product by v_mfma_f32_16x16x4_f32,
 // zero-weight flags) is the one of the single-pass kernel.
@@ -46,7 +61,7 @@ namespace {
 // y and res may be the same buffer (in-place residual sum): neither is
 // declared restrict; every element is read before it is written, by the same
 // thread.
-template <int BITS, int GS, int BPW, int S, int MAXW, bool ADD, bool PAIRK, int XC>
+template <int BITS, int GS, int BPW, int S, int MAXW, bool ADD, bool PAIRK, int XC, int KS>
 __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *y,
@@ -54,7 +69,10 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   constexpr int CW = 128 / BITS;         // codes per 16-byte chunk
   constexpr int SCW = 4 * CW;            // codes per 64-byte super-chunk
   constexpr int DW = CW / 4;             // codes per dword
-  constexpr int HS = BITS == 4 ? 1 : 2;  // MFMA steps per code dword
+  constexpr int HS = BITS == 2 ? 2 : 1;  // MFMA steps per code dword (8-bit: one per two dwords)
+  // activation operands per super-chunk and HS: one per code register
+  // (2/4-bit) or per pair of code registers (8-bit)
+  constexpr int XR = BITS == 8 ? 2 : 4;
   constexpr int BLKW = 4 * GS;           // codes per bias block
   constexpr int BSC = BLKW / SCW;        // super-chunks per block
   constexpr int CPG = GS / CW;           // chunks per group
@@ -74,13 +92,17 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   // 11.3 -> 10.6 us at M = 8), slower by 1-5% with groups of 128 and for
   // 2-bit codes, where metadata loads are few
   constexpr bool MQ = BITS == 4 && GS <= 64;
-  static_assert(BSC >= 1 && BLKW % SCW == 0 && CPG >= 1, "block layout");
+  static_assert(BSC >= 1 && BLKW % SCW == 0 && CPG >= 1 && GPS >= 1, "block layout");
   // compact activation loads (XC = 4 or 8 rows, M <= XC; see compact_pick):
-  // XG operands per load, LPU loads per super-chunk
+  // XG operands per load; a load covers part of one super-chunk (LPU loads
+  // each) or whole super-chunks (SPL each), NLB loads per block
   static_assert(XC == 0 || XC == 4 || XC == 8, "compact activation rows");
   constexpr int XG = XC ? 16 / XC : 1;
-  constexpr int OPS = 4 * HS;  // activation operands per super-chunk
-  constexpr int LPU = OPS / XG;
+  constexpr int OPS = XR * HS;  // activation operands per super-chunk
+  constexpr int LPU = OPS >= XG ? OPS / XG : 1;
+  constexpr int SPL = OPS >= XG ? 1 : XG / OPS;
+  constexpr int NLB = BSC * OPS / XG;
+  static_assert((OPS % XG == 0 || XG % OPS == 0) && (BSC * OPS) % XG == 0, "compact activation layout");
 
   __shared__ float red[2][S][MAXW][4][64];
 
@@ -110,48 +132,56 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   for (int i = 0; i < 4; ++i) xoff[i] = lvl_chunk<LVL>(i, xkb) * CW + lvl_dword<LVL>(i, xkb) * DW;
 
   // tile range of this workgroup (the products stay below 2^31: the grid is
-  // at most the CU count and T <= 2^18)
+  // at most the CU count and T <= 2^18); with K split in two (KS = 2),
+  // workgroup b takes half b & 1 of the bias blocks for tile range b >> 1
   const int T = (N + 15) >> 4;
-  const int t_first = (int)(blockIdx.x * (unsigned)T / gridDim.x);
-  const int ntile = (int)((blockIdx.x + 1) * (unsigned)T / gridDim.x) - t_first;
+  const int part = KS == 2 ? (int)(blockIdx.x & 1u) : 0;
+  const unsigned gi = KS == 2 ? blockIdx.x >> 1 : blockIdx.x;
+  const unsigned GPn = KS == 2 ? gridDim.x >> 1 : gridDim.x;
+  const int t_first = (int)(gi * (unsigned)T / GPn);
+  const int ntile = (int)((gi + 1) * (unsigned)T / GPn) - t_first;
+  const int p_lo = part ? nblk >> 1 : 0;                                  // first block of the part
+  const int nbp = KS == 1 ? nblk : (part ? nblk - (nblk >> 1) : nblk >> 1);  // its blocks
 
-  // owned blocks (vw, vw + W, ...; PAIRK: vw*BPW, vw*BPW + 1, adjacent); a
-  // wave past the last block loads a valid block and skips the arithmetic
+  // owned blocks of the part (vw, vw + W, ...; PAIRK: vw*BPW, vw*BPW + 1,
+  // adjacent); a wave past the last block loads a valid block and skips the
+  // arithmetic
   int blk[BPW];
   bool own[BPW];
 #pragma unroll
   for (int k = 0; k < BPW; ++k) {
     const int b = PAIRK ? vw * BPW + k : vw + k * W;
-    own[k] = b < nblk;
-    blk[k] = own[k] ? b : nblk - 1;
+    own[k] = b < nbp;
+    blk[k] = p_lo + (own[k] ? b : nbp - 1);
   }
 
   // ---- activations of the owned blocks (rows m >= M read row M-1: their
   // outputs are never stored), later re-paired to the code pairing and
   // summed per group into the A layout of the bias MFMA
   const uint16_t *xr = x + (size_t)min(xquad ? (lane >> 2) : col, M - 1) * K;
-  u32x4_t xv[BPW][BSC][4][HS];
+  u32x4_t xv[BPW][BSC][XR][HS];
   float xsum[BPW];
-  // compact loads: load p of a super-chunk carries its operands p*XG ..
-  // p*XG + XG-1 (operand (i, l) -> i*HS + l); this lane holds operand
-  // p*XG + lane%XG of row (lane%16)/XG at its K-part kb
-  u32x4_t cx[XC ? BPW : 1][XC ? BSC : 1][LPU];
+  // compact loads: load ld of a block carries its operands ld*XG ..
+  // ld*XG + XG-1 (operand (u, i, l) -> (u*XR + i)*HS + l); this lane holds
+  // operand ld*XG + lane%XG of row (lane%16)/XG at its K-part kb, at element
+  // (ld / LPU)*SPL*SCW + xlp[ld % LPU] of the block
+  u32x4_t cx[XC ? BPW : 1][XC ? NLB : 1];
   if constexpr (XC != 0) {
     const uint16_t *xrc = x + (size_t)min((lane & 15) / XG, M - 1) * K;
     int xlp[LPU];
 #pragma unroll
     for (int p = 0; p < LPU; ++p) {
       const int f = p * XG + (lane & (XG - 1));
-      const int i = f / HS, l = f % HS;
-      xlp[p] = lvl_chunk<LVL>(i, kb) * CW + lvl_dword<LVL>(i, kb) * DW + 8 * l;
+      const int u = f / OPS, i = (f % OPS) / HS, l = f % HS;
+      const int ii = BITS == 8 ? 2 * i : i;
+      xlp[p] = u * SCW + lvl_chunk<LVL>(ii, kb) * CW + lvl_dword<LVL>(ii, kb) * DW + 8 * l;
     }
 #pragma unroll
     for (int k = 0; k < BPW; ++k)
 #pragma unroll
-      for (int u = 0; u < BSC; ++u)
-#pragma unroll
-        for (int p = 0; p < LPU; ++p)
-          cx[k][u][p] = *reinterpret_cast<const u32x4_t *>(xrc + (blk[k] * BSC + u) * SCW + xlp[p]);
+      for (int ld = 0; ld < NLB; ++ld)
+        cx[k][ld] = *reinterpret_cast<const u32x4_t *>(xrc + blk[k] * BSC * SCW + (ld / LPU) * SPL * SCW +
+                                                        xlp[ld % LPU]);
   } else {
 #pragma unroll
     for (int k = 0; k < BPW; ++k)
@@ -159,10 +189,11 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
       for (int u = 0; u < BSC; ++u) {
         const int k0 = (blk[k] * BSC + u) * SCW;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < XR; ++i)
 #pragma unroll
           for (int l = 0; l < HS; ++l)
-            xv[k][u][i][l] = *reinterpret_cast<const u32x4_t *>(xr + k0 + xoff[i] + 8 * l);
+            xv[k][u][i][l] =
+                *reinterpret_cast<const u32x4_t *>(xr + k0 + (BITS == 8 ? xoff[2 * i] : xoff[i]) + 8 * l);
       }
   }
 
@@ -220,11 +251,11 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
 #pragma unroll
       for (int u = 0; u < BSC; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < XR; ++i)
 #pragma unroll
           for (int l = 0; l < HS; ++l) {
-            const int f = i * HS + l;
-            xv[k][u][i][l] = compact_pick<XG>(cx[k][u][f / XG], f % XG);
+            const int f = (u * XR + i) * HS + l;
+            xv[k][u][i][l] = compact_pick<XG>(cx[k][f / XG], f % XG);
           }
   } else if (xquad) {
 #pragma unroll
@@ -232,7 +263,7 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
 #pragma unroll
       for (int u = 0; u < BSC; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < XR; ++i)
 #pragma unroll
           for (int l = 0; l < HS; ++l) xv[k][u][i][l] = to_operand_lanes(xv[k][u][i][l]);
   }
@@ -242,6 +273,17 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
     float P[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < BSC; ++u) {
+      if constexpr (BITS == 8) {
+        // natural order: only the group sums; step e of the super-chunk
+        // holds 8 codes of group (u*SCW + 32e)/GS of the block
+#pragma unroll
+        for (int e = 0; e < XR; ++e) {
+          const int j = (u * SCW + 32 * e) / GS;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) P[j] = dot2_bf16(xv[k][u][e][0][c], 0x3F803F80u, P[j]);
+        }
+        continue;
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = u * GPS + i / REGS_G;
@@ -311,6 +353,44 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
             to_operand_lanes(cv[s][k][u], cur);
           }
           transpose_rows_lvl<LVL>(cur);
+          if constexpr (BITS == 8) {
+            // MFMA step e takes code registers 2e, 2e+1 (8 consecutive codes
+            // of this lane's row; the activations at xoff[2e]..+7)
+#pragma unroll
+            for (int e = 0; e < XR; ++e) {
+              const int kk = u * SCW + 32 * e;  // first code of the step within the block
+              const int jg = kk / GS;           // its group within the block
+              const bool gfirst = kk % GS == 0;
+              const bool glast = (kk + 32) % GS == 0;
+              // zero-weight traces: code words against the group's first,
+              // then the group's weight s*c + b at its last step
+              if (gfirst) {
+                zc0 = cur[2 * e];
+                nz |= fields_spread<BITS>(cur[2 * e]);
+              } else {
+                nz |= cur[2 * e] ^ zc0;
+              }
+              nz |= cur[2 * e + 1] ^ zc0;
+              pin(nz);
+              if (glast) {
+                const uint2 sw_v = s4[s][k];
+                const uint2 bw16_v = b4[s][k];
+                nz |= weight_trace(half_bits_to_float(field16(sw_v, jg)), low_field<BITS>(zc0),
+                                   half_bits_to_float(field16(bw16_v, jg)));
+              }
+              const u32x4_t bw = unpack8_quad(cur[2 * e], cur[2 * e + 1]);
+              accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8_t, xv[k][u][e][0]), __builtin_bit_cast(bf16x8_t, bw),
+                  gfirst ? zero4 : accg, 0, 0, 0);
+              if (glast) {
+                const uint2 sw_v = s4[s][k];
+                const float scl = half_bits_to_float(field16(sw_v, jg));
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[q] = fmaf(scl, accg[q], acc[q]);
+              }
+            }
+            continue;
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int jg = u * GPS + i / REGS_G;  // group within the block
@@ -374,11 +454,22 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
       const int m = a % XG == 0 ? a / XG : M;
       const int n = 16 * (t_first + j0 + s) + (l & 15);
       if (m < M && n < N) {
+        float *dst = y + (size_t)m * N + n;
         if constexpr (ADD) {
           if (!pre) rv = res[(size_t)m * N + n];
-          v += rv;
         }
-        y[(size_t)m * N + n] = v;
+        if constexpr (KS == 1) {
+          *dst = ADD ? v + rv : v;
+        } else if constexpr (!ADD) {
+          // y was zeroed before the launch and receives exactly two addends:
+          // 0 + a + b equals 0 + b + a bit for bit, whichever half lands first
+          unsafeAtomicAdd(dst, v);
+        } else {
+          // y held kSplitSentinel: the first half leaves its partial there,
+          // the second finds it and stores (a + b) + r
+          const float old = atomicExch(dst, v);
+          if (__builtin_bit_cast(uint32_t, old) != kSplitSentinel) *dst = (old + v) + rv;
+        }
       }
     };
 #pragma unroll
@@ -399,33 +490,50 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
 // the depth S of the prefetch ring.
 template <int BITS, int GS>
 struct PersistShape {
-  static constexpr int BPW = (BITS == 4 && GS == 32) || (BITS == 2 && GS == 64) ? 2 : 1;
-  static constexpr int MAXW = (BITS == 4 && GS <= 64) ? 16 : 12;
+  static constexpr int BPW = (BITS != 2 && GS == 32) || (BITS == 2 && GS == 64) ? 2 : 1;
+  static constexpr int MAXW = (BITS != 2 && GS <= 64) ? 16 : 12;
   static constexpr int S = 2;
 };
 
-template <int BITS, int GS, bool ADD, int XC>
-int launch_persist_t(const QgemvArgs &a, hipStream_t stream) {
-  constexpr int BPW = PersistShape<BITS, GS>::BPW;
-  constexpr int MAXW = PersistShape<BITS, GS>::MAXW;
+template <int BITS, int GS, int BPW, int MAXW, int KS, bool ADD, int XC>
+int launch_persist_k(const QgemvArgs &a, hipStream_t stream) {
   constexpr int S = PersistShape<BITS, GS>::S;
   const int nblk = a.K / (4 * GS);
-  if (nblk > MAXW * BPW) return QGEMV_EUNSUPPORTED;  // activations would not fit the registers
-  const int waves = (nblk + BPW - 1) / BPW;
+  const int nbh = nblk - (KS == 2 ? nblk >> 1 : 0);  // blocks of the longer part
+  if (nbh > MAXW * BPW) return QGEMV_EUNSUPPORTED;   // activations would not fit the registers
+  const int waves = (nbh + BPW - 1) / BPW;
   const int tiles = (a.N + 15) / 16;
   const int cus = device_cu_count();
-  const int G = tiles < cus ? tiles : cus;
+  const int G = KS * (tiles < cus / KS ? tiles : cus / KS);
+  if constexpr (KS == 2) {
+    // the halves are added into y, prefilled here; not for an in-place
+    // residual sum, whose residual the prefill would erase
+    if (ADD && static_cast<const void *>(a.res) == static_cast<const void *>(a.y)) return QGEMV_EUNSUPPORTED;
+    const int st = launch_fill(a.y, (size_t)a.M * a.N, ADD ? kSplitSentinel : 0u, stream);
+    if (st != QGEMV_OK) return st;
+  }
   // the wave's two one-super-chunk blocks as whole lines where every wave has
   // two (an even block count)
-  constexpr bool CAN_PAIRK = BPW == 2 && 4 * GS * BITS == 512;
+  constexpr bool CAN_PAIRK = KS == 1 && BPW == 2 && 4 * GS * BITS == 512;
   if (CAN_PAIRK && nblk % 2 == 0) {
-    hipLaunchKernelGGL((qgemv_persist_kernel<BITS, GS, BPW, S, MAXW, ADD, CAN_PAIRK, XC>), dim3(G), dim3(64 * waves),
-                       0, stream, a.codes, a.scales, a.biases, a.x, a.y, a.res, a.M, a.N, a.K);
+    hipLaunchKernelGGL((qgemv_persist_kernel<BITS, GS, BPW, S, MAXW, ADD, CAN_PAIRK, XC, KS>), dim3(G),
+                       dim3(64 * waves), 0, stream, a.codes, a.scales, a.biases, a.x, a.y, a.res, a.M, a.N, a.K);
     return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
   }
-  hipLaunchKernelGGL((qgemv_persist_kernel<BITS, GS, BPW, S, MAXW, ADD, false, XC>), dim3(G), dim3(64 * waves),
-                     0, stream, a.codes, a.scales, a.biases, a.x, a.y, a.res, a.M, a.N, a.K);
+  hipLaunchKernelGGL((qgemv_persist_kernel<BITS, GS, BPW, S, MAXW, ADD, false, XC, KS>), dim3(G),
+                     dim3(64 * waves), 0, stream, a.codes, a.scales, a.biases, a.x, a.y, a.res, a.M, a.N, a.K);
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}
+
+template <int BITS, int GS, bool ADD, int XC>
+int launch_persist_t(const QgemvArgs &a, hipStream_t stream) {
+  using Sh = PersistShape<BITS, GS>;
+  // 8-bit codes in groups of 64 with more than 16 bias blocks: K split in two
+  // halves over two workgroups (two blocks per wave spill registers)
+  if constexpr (BITS == 8 && GS == 64) {
+    if (a.K / (4 * GS) > Sh::MAXW * Sh::BPW) return launch_persist_k<BITS, GS, 1, 16, 2, ADD, XC>(a, stream);
+  }
+  return launch_persist_k<BITS, GS, Sh::BPW, Sh::MAXW, 1, ADD, XC>(a, stream);
 }
 
 template <int BITS, int GS, int XC>
@@ -447,10 +555,14 @@ int launch_persist_gs(const QgemvArgs &a, hipStream_t stream) {
 
 int launch_persist(const QgemvArgs &a, hipStream_t stream) {
   if (!mfma_supports(a.K, a.bits, a.group_size)) return QGEMV_EUNSUPPORTED;
-  // 8-bit codes take the single-pass kernel: a persistent variant (one block
-  // per wave) measured slower than it on the 15360 x 3840 shape, 31.5 vs
-  // 18.7 us at M = 1
-  if (a.bits == 8) return QGEMV_EUNSUPPORTED;
+  if (a.bits == 8) {
+    // groups of 128 span two super-chunks: the single-pass kernel
+    switch (a.group_size) {
+      case 32: return launch_persist_gs<8, 32>(a, stream);
+      case 64: return launch_persist_gs<8, 64>(a, stream);
+    }
+    return QGEMV_EUNSUPPORTED;
+  }
   if (a.bits == 4) {
     switch (a.group_size) {
       case 32: return launch_persist_gs<4, 32>(a, stream);

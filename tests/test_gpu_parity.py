@@ -143,7 +143,7 @@ def test_ragged_shapes_every_element(path, K, N, bits, gs):
 PERSIST = [
     (1024, 4113, 4, 32), (2048, 4500, 4, 64), (3072, 5000, 4, 128), (6144, 4200, 4, 128),
     (1280, 4700, 2, 64), (2048, 9000, 2, 128), (8192, 4500, 4, 128),
-    (1024, 4113, 8, 32), (2048, 4500, 8, 64),
+    (1024, 4113, 8, 32), (2048, 4500, 8, 64), (3840, 4200, 8, 64), (5120, 4150, 8, 64),
     (6656, 4200, 4, 128), (8192, 4130, 2, 64), (10240, 4500, 2, 128),
 ]
 
@@ -186,7 +186,7 @@ def test_zero_codes(path):
                                          (4, 64, 4500, 2048), (2, 128, 4500, 2048),
                                          (4, 128, 300, 8192), (2, 64, 150, 10240),
                                          (4, 128, 4200, 6656), (2, 64, 4130, 8192),
-                                         (8, 64, 200, 2048), (8, 32, 4500, 1024), (8, 64, 150, 10240),
+                                         (8, 64, 200, 2048), (8, 32, 4500, 1024), (8, 64, 150, 10240), (8, 64, 4150, 5120),
                                          (4, 64, 4096, 8192)])
 @pytest.mark.parametrize("path", ["dot", "mfma"])
 def test_row_of_m_row_call_equals_single_row_call_bitwise(path, bits, gs, N, K):

@@ -67,6 +67,7 @@ SHAPES = [
     (8192, 33, 4, 64), (512, 72, 2, 32), (1280, 300, 2, 64), (17408, 23, 2, 64),
     (64, 5, 2, 64), (2048, 4500, 4, 64), (1280, 4700, 2, 64), (5120, 1024, 4, 128),
     (1024, 300, 8, 64), (2048, 4500, 8, 32), (5120, 1024, 8, 64), (2048, 97, 8, 128),
+    (3840, 4200, 8, 64), (5120, 4150, 8, 64),
     # long K, many tiles: halves of K with their activations in LDS
     (6656, 4200, 4, 128), (8192, 4130, 2, 64),
 ]
@@ -91,16 +92,22 @@ def test_add_every_element_and_bitwise_plain_plus_add(path, K, N, bits, gs):
 
 
 def _mfma_splits_k(p, M) -> bool:
-    # the MFMA single-pass kernel splits K over two workgroups when its
-    # 16-column tile groups are few for the CUs; these shapes are chosen on
-    # either side of that rule (256 CUs)
+    # the MFMA kernels that split K over two workgroups add the halves into a
+    # prefilled y, which an in-place call cannot have: it takes the unsplit
+    # single-pass kernel, whose sums are ordered otherwise.  The single-pass
+    # kernel splits K when its 16-column tile groups are few for the CUs; the
+    # register-resident persistent kernel (more tiles than CUs) for 8-bit
+    # codes in groups of 64 with more than 16 bias blocks.  The shapes are
+    # chosen on either side of these rules (256 CUs).
     tiles = (p.N + 15) // 16
-    return (tiles < 512 and p.K >= 8192) or (4 * tiles <= 256 and p.K >= 2048)
+    single = (tiles < 512 and p.K >= 8192) or (4 * tiles <= 256 and p.K >= 2048)
+    persist = tiles > 256 and p.bits == 8 and p.group_size == 64 and p.K > 16 * 256
+    return single or persist
 
 
 @pytest.mark.parametrize("K,N,bits,gs", [(2048, 97, 4, 128), (1024, 300, 4, 64),
                                          (2048, 4500, 4, 64), (17408, 23, 2, 64),
-                                         (5120, 1024, 4, 128)])
+                                         (5120, 1024, 4, 128), (5120, 4150, 8, 64)])
 @pytest.mark.parametrize("path", ["dot", "mfma"])
 def test_add_in_place(path, K, N, bits, gs):
     import torch

@@ -26,7 +26,7 @@ from gpu_util import DeviceProblem, OracleRows, say
 pytestmark = pytest.mark.gpu
 
 # K, N, bits, gs: N = 300 runs the single-pass MFMA kernel (K split over two
-# workgroups), N = 4200 / 4128 the persistent kernels (registers for K 4096 and
+# workgroups), N = 4200 / 4128 the persistent kernels (registers for K 3840 to
 # 5120, half of K in LDS for 17408)
 SHAPES = [
     (4096, 300, 4, 32), (4096, 300, 4, 64), (4096, 300, 4, 128),
@@ -35,6 +35,7 @@ SHAPES = [
     (17408, 300, 2, 64), (17408, 300, 2, 128),
     (4096, 4200, 4, 64), (5120, 4200, 2, 64), (17408, 4200, 4, 128), (17408, 4128, 2, 64),
     (4096, 300, 8, 32), (4096, 300, 8, 64), (4096, 300, 8, 128),
+    (4096, 4200, 8, 32), (3840, 4200, 8, 64), (5120, 4200, 8, 64),
 ]
 MS = (1, 2, 8, 16)
 
