@@ -112,6 +112,9 @@ __global__ __launch_bounds__(64) void unpack_probe_mfma(const uint8_t *__restric
   probe_load_operands<false>(codes, RB, tile, sc, N, r);
   bool differ = false;
   if constexpr (LINES) {
+    // no line-load check for 8-bit codes: every byte is a code, so no value
+    // is left to flag a mismatch (their line loads in the persistent kernel
+    // are covered by the parity tests)
     static_assert(BITS != 8, "8-bit codes take the single-pass kernel only");
     uint32_t r2[4];
     probe_load_operands<true>(codes, RB, tile, sc, N, r2);
