@@ -4,8 +4,12 @@
 // verify row is named as unstudied).
 //
 // Every expert in the union of e_idx is read from HBM once per call, for all
-// the pairs routed to it, by the single-pass MFMA kernel (GATHER variant in
-// qgemv_mfma_impl.h).  The work is the (expert slot, 16-column tile group)
+// the pairs routed to it.  With 3 or more activation rows (X) and a shape the
+// persistent MFMA kernel takes, that kernel does it (GATHER variant in
+// qgemv_persist.hip: contiguous ranges of the (chunk, tile) items per
+// workgroup, streamed through its code prefetch ring).  Otherwise the
+// single-pass MFMA kernel (GATHER variant in qgemv_mfma_impl.h) does, as
+// follows.  The work is the (expert slot, 16-column tile group)
 // items, slots being the union's experts in ascending id order, each with its
 // pairs in ascending order taken 16 rows at a time (4 when there are at most
 // 4 activation rows; a chunk of at most 4 pairs loads its activations in the
@@ -77,6 +81,15 @@ template <int BITS, int GS>
 int launch_gather_t(const QgemvArgs &a, const GatherArgs &ga, hipStream_t stream) {
   if ((a.N + 15) / 16 >= kGatherWideTiles && a.K / (4 * GS) <= 4)
     return launch_gather_nt<BITS, GS, 2, 0, false>(a, ga, stream);
+  // from 3 activation rows, the persistent kernel over (chunk, tile) ranges,
+  // where a shape fits it (the 128-expert top-8 2048 -> 1536 gate/up: 17.4
+  // -> 16.6 us at M = 3, 33.3 -> 28.7 at M = 8, 58.2 -> 48.5 at M = 16, one
+  // run; at M = 1 and 2 it measured 8.35 -> 8.88 and 12.00 -> 12.75, its
+  // few items per workgroup not paying for the routing prologue)
+  if (ga.X >= 3) {
+    const int st = launch_persist_gather(a, ga, stream);
+    if (st != QGEMV_EUNSUPPORTED) return st;
+  }
   // activation rows in compact loads (compact_pick) when there are at most 4
   // of them: a valid routing then sends each expert at most 4 pairs, one
   // chunk (128-expert top-8 2048 -> 1536 gate/up: 8.89 -> 8.46 us at M = 1,

@@ -31,6 +31,16 @@ struct QgemvArgs {
 constexpr int kMaxExperts = QGEMV_MAX_EXPERTS;
 constexpr int kMaxPairs = QGEMV_MAX_PAIRS;
 
+// Gathered (MoE) verify: pair p takes activation row x_idx[p] and expert
+// e_idx[p]; the experts are E matrices [N][K] stored one after another.
+struct GatherArgs {
+  const int32_t *x_idx;
+  const int32_t *e_idx;
+  int P;  // pairs
+  int X;  // activation rows
+  int E;  // experts
+};
+
 // LDS of one workgroup: hardware limit on gfx950, and the dot path's
 // preferred x-staging budget (two workgroups per CU).
 constexpr size_t kLdsMax = 160 * 1024;
@@ -74,6 +84,9 @@ bool mfma_supports_fp(int K, int fmt);
 // Probes.
 int launch_unpack_probe(int path, const uint8_t *codes, uint8_t *q_out, int N, int K, int bits,
                         int group_size, hipStream_t stream);
+// Gathered (MoE) verify on the persistent MFMA kernel (QGEMV_EUNSUPPORTED
+// for shapes it does not take).
+int launch_persist_gather(const QgemvArgs &a, const GatherArgs &ga, hipStream_t stream);
 // Gathered (MoE) verify on the MFMA kernel: y[p] = x[x_idx[p]] . W[e_idx[p]]^T.
 int launch_gather(const QgemvArgs &a, const int32_t *x_idx, const int32_t *e_idx, int P, int X,
                   int E, hipStream_t stream);

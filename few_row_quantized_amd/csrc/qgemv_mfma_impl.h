@@ -7,21 +7,12 @@
 #include <type_traits>
 
 #include "qgemv_device.h"
+#include "qgemv_gather_route.h"
 #include "qgemv_internal.h"
 
 namespace qgemv {
 
 namespace {
-
-// Gathered (MoE) verify: pair p takes activation row x_idx[p] and expert
-// e_idx[p]; the experts are E matrices [N][K] stored one after another.
-struct GatherArgs {
-  const int32_t *x_idx;
-  const int32_t *e_idx;
-  int P;  // pairs
-  int X;  // activation rows
-  int E;  // experts
-};
 
 // y and res may be the same buffer (in-place residual sum): neither is
 // declared restrict; every element is read before it is written, by the same
@@ -117,68 +108,20 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   const uint16_t *const biases0 = biases;
   if constexpr (GATHER) {
     static_assert(KS == 1 && !PERSIST && !ADD && FMT == kAffine, "gather variant");
-    const int words = (ga.E + 31) >> 5;
-    if constexpr (!GSORT) {
+    if constexpr (GSORT) {
+      gather_route(ga, gexp, gxr, gsorted, gstart, gslot_exp, gmeta);
+    } else {
+      const int words = (ga.E + 31) >> 5;
       for (int i = threadIdx.x; i < words; i += blockDim.x) gbits[i] = 0u;
       __syncthreads();
-    }
-    for (int p = threadIdx.x; p < ga.P; p += blockDim.x) {
-      const int e = ga.e_idx[p], xi = ga.x_idx[p];
-      const bool valid = e >= 0 && e < ga.E && xi >= 0 && xi < ga.X;
-      gexp[p] = valid ? e : -1;
-      gxr[p] = xi;
-      if constexpr (!GSORT) {
+      for (int p = threadIdx.x; p < ga.P; p += blockDim.x) {
+        const int e = ga.e_idx[p], xi = ga.x_idx[p];
+        const bool valid = e >= 0 && e < ga.E && xi >= 0 && xi < ga.X;
+        gexp[p] = valid ? e : -1;
+        gxr[p] = xi;
         if (valid) atomicOr(&gbits[e >> 5], 1u << (e & 31));
       }
-    }
-    __syncthreads();
-    if constexpr (GSORT) {
-      // position of a valid pair: valid pairs with a smaller expert, or the
-      // same expert and a smaller index, come before it
-      for (int p = threadIdx.x; p < ga.P; p += blockDim.x) {
-        const int e = gexp[p];
-        if (e < 0) continue;
-        int rank = 0;
-        for (int q = 0; q < ga.P; ++q) {
-          const int f = gexp[q];
-          rank += (f >= 0 && (f < e || (f == e && q < p))) ? 1 : 0;
-        }
-        gsorted[rank] = p;
-      }
-      int nvalid = 0;
-      if (wave == 0) {
-        for (int p0 = 0; p0 < ga.P; p0 += 64) {
-          const int p = p0 + lane;
-          nvalid += __popcll(__ballot(p < ga.P && gexp[p] >= 0));
-        }
-      }
       __syncthreads();
-      if (wave == 0) {
-        // slot boundaries: a position whose expert differs from the one before
-        int base = 0;
-        for (int i0 = 0; i0 < nvalid; i0 += 64) {
-          const int i = i0 + lane;
-          int e = -1;
-          bool first = false;
-          if (i < nvalid) {
-            e = gexp[gsorted[i]];
-            first = i == 0 || gexp[gsorted[i - 1]] != e;
-          }
-          const uint64_t bal = __ballot(first);
-          if (first) {
-            const int sl = base + __popcll(bal & ((1ull << lane) - 1ull));
-            gstart[sl] = i;
-            gslot_exp[sl] = e;
-          }
-          base += __popcll(bal);
-        }
-        if (lane == 0) {
-          gmeta[0] = base;
-          gstart[base] = nvalid;
-        }
-      }
-      __syncthreads();
-    } else {
       if (threadIdx.x == 0) {
         // the slot-th set bit of the union bitmap
         const int slot = (int)blockIdx.x / ngroups;
@@ -226,7 +169,7 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   // load holds operands of one block, and the operands of a load cover part
   // of one super-chunk (LPU loads each) or whole super-chunks (SPL each)
   constexpr int XCV = decltype(xc_tag)::value;
-  constexpr int XG = XCV ? 16 / XCV : 1;
+  constexpr int XG = XCV ? 16 / (XCV ? XCV : 1) : 1;
   constexpr int OPS = XR * HS;        // activation operands per super-chunk
   constexpr int NGR = UNR * OPS;      // activation operands per batch
   constexpr int NLD = NGR / XG;

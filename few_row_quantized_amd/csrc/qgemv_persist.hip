@@ -51,7 +51,10 @@
 // bf16 q, per-group scale fold, bias product by v_mfma_f32_16x16x4_f32,
 // zero-weight flags) is the one of the single-pass kernel.
 
+#include <atomic>
+
 #include "qgemv_device.h"
+#include "qgemv_gather_route.h"
 #include "qgemv_internal.h"
 
 namespace qgemv {
@@ -61,11 +64,11 @@ namespace {
 // y and res may be the same buffer (in-place residual sum): neither is
 // declared restrict; every element is read before it is written, by the same
 // thread.
-template <int BITS, int GS, int BPW, int S, int MAXW, bool ADD, bool PAIRK, int XC, int KS>
+template <int BITS, int GS, int BPW, int S, int MAXW, bool ADD, bool PAIRK, int XC, int KS, bool GATHER = false>
 __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *y,
-    const float *res, int M, int N, int K) {
+    const float *res, int M, int N, int K, GatherArgs ga) {
   constexpr int CW = 128 / BITS;         // codes per 16-byte chunk
   constexpr int SCW = 4 * CW;            // codes per 64-byte super-chunk
   constexpr int DW = CW / 4;             // codes per dword
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   // XG operands per load; a load covers part of one super-chunk (LPU loads
   // each) or whole super-chunks (SPL each), NLB loads per block
   static_assert(XC == 0 || XC == 4 || XC == 8, "compact activation rows");
-  constexpr int XG = XC ? 16 / XC : 1;
+  constexpr int XG = XC ? 16 / (XC ? XC : 1) : 1;
   constexpr int OPS = XR * HS;  // activation operands per super-chunk
   constexpr int LPU = OPS >= XG ? OPS / XG : 1;
   constexpr int SPL = OPS >= XG ? 1 : XG / OPS;
@@ -105,6 +108,16 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   static_assert((OPS % XG == 0 || XG % OPS == 0) && (BSC * OPS) % XG == 0, "compact activation layout");
 
   __shared__ float red[2][S][MAXW][4][64];
+  // gathered verify (GATHER): the routing (gather_route), and its slots cut
+  // into chunks of at most CH pairs (16, or XC with compact activation
+  // loads), each one activation set
+  static_assert(!GATHER || (!ADD && KS == 1), "gathered variant");
+  constexpr int CH = XC ? XC : 16;
+  __shared__ int gexp[GATHER ? kMaxPairs : 1], gxr[GATHER ? kMaxPairs : 1], gsorted[GATHER ? kMaxPairs : 1];
+  __shared__ int gstart[GATHER ? kMaxPairs + 1 : 1], gslot_exp[GATHER ? kMaxPairs : 1];
+  __shared__ int gcs[GATHER ? kMaxPairs + 1 : 1];  // first sorted position of each chunk
+  __shared__ int gce[GATHER ? kMaxPairs : 1];      // expert of each chunk
+  __shared__ int gmeta[2];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -124,22 +137,67 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   // activation loads in the quad-row layout once several rows are distinct
   // (results do not depend on the choice; from M = 5 for every group size
-  // here: 27B q at M = 7, 9.44 -> 8.91 us)
-  const bool xquad = XC == 0 && M >= 5;
-  const int xkb = xquad ? (lane & 3) : kb;
+  // here: 27B q at M = 7, 9.44 -> 8.91 us); set with each activation set
+  bool xquad = false;
   int xoff[4];
+
+  // Gathered verify: resolve the routing, then cut each slot's pairs into
+  // chunks of at most CH (wave 0: a scan of the chunk counts over the slots)
+  if constexpr (GATHER) {
+    gather_route(ga, gexp, gxr, gsorted, gstart, gslot_exp, gmeta);
+    const int nslots = gmeta[0];
+    if (wave == 0) {
+      int base = 0;
+      for (int s0 = 0; s0 < nslots; s0 += 64) {
+        const int sl = s0 + lane;
+        const int cnt = sl < nslots ? gstart[sl + 1] - gstart[sl] : 0;
+        const int nch = (cnt + CH - 1) / CH;
+        int inc = nch;  // inclusive scan over the lanes
 #pragma unroll
-  for (int i = 0; i < 4; ++i) xoff[i] = lvl_chunk<LVL>(i, xkb) * CW + lvl_dword<LVL>(i, xkb) * DW;
+        for (int d = 1; d < 64; d <<= 1) {
+          const int v = __shfl_up(inc, d);
+          if (lane >= d) inc += v;
+        }
+        const int first = base + inc - nch;
+        for (int j = 0; j < nch; ++j) {
+          gcs[first + j] = gstart[sl] + CH * j;
+          gce[first + j] = gslot_exp[sl];
+        }
+        base += __shfl(inc, 63);
+      }
+      if (lane == 0) {
+        gmeta[1] = base;
+        gcs[base] = gstart[nslots];
+      }
+    }
+    __syncthreads();
+  }
 
   // tile range of this workgroup (the products stay below 2^31: the grid is
   // at most the CU count and T <= 2^18); with K split in two (KS = 2),
-  // workgroup b takes half b & 1 of the bias blocks for tile range b >> 1
+  // workgroup b takes half b & 1 of the bias blocks for tile range b >> 1.
+  // Gathered: a range of the items (chunk, tile) in chunk-major order
+  // (T tiles per chunk); a workgroup without items has nothing to do.
   const int T = (N + 15) >> 4;
   const int part = KS == 2 ? (int)(blockIdx.x & 1u) : 0;
   const unsigned gi = KS == 2 ? blockIdx.x >> 1 : blockIdx.x;
   const unsigned GPn = KS == 2 ? gridDim.x >> 1 : gridDim.x;
-  const int t_first = (int)(gi * (unsigned)T / GPn);
-  const int ntile = (int)((gi + 1) * (unsigned)T / GPn) - t_first;
+  const uint64_t items = GATHER ? (uint64_t)gmeta[1] * (uint64_t)T : (uint64_t)T;
+  const int t_first = (int)((uint64_t)gi * items / GPn);
+  const int ntile = (int)((uint64_t)(gi + 1) * items / GPn) - t_first;
+  if constexpr (GATHER) {
+    if (ntile <= 0) return;  // uniform for the workgroup
+  }
+  // chunk and tile of item step j of this workgroup
+  auto item_chunk = [&](const int j) -> int { return GATHER ? (t_first + j) / T : 0; };
+  // activation set in registers: its first sorted position and pair count
+  // (gathered); rows a >= the count read the last row, never stored
+  int cur_ch = -1, gcs0 = 0, gcnt = M;
+  auto xrow_at = [&](const int a) -> size_t {
+    const int m = min(a, gcnt - 1);
+    if constexpr (GATHER) return (size_t)gxr[gsorted[gcs0 + m]];
+    return (size_t)m;
+  };
   const int p_lo = part ? nblk >> 1 : 0;                                  // first block of the part
   const int nbp = KS == 1 ? nblk : (part ? nblk - (nblk >> 1) : nblk >> 1);  // its blocks
 
@@ -158,7 +216,6 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   // ---- activations of the owned blocks (rows m >= M read row M-1: their
   // outputs are never stored), later re-paired to the code pairing and
   // summed per group into the A layout of the bias MFMA
-  const uint16_t *xr = x + (size_t)min(xquad ? (lane >> 2) : col, M - 1) * K;
   u32x4_t xv[BPW][BSC][XR][HS];
   float xsum[BPW];
   // compact loads: load ld of a block carries its operands ld*XG ..
@@ -166,8 +223,14 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   // operand ld*XG + lane%XG of row (lane%16)/XG at its K-part kb, at element
   // (ld / LPU)*SPL*SCW + xlp[ld % LPU] of the block
   u32x4_t cx[XC ? BPW : 1][XC ? NLB : 1];
+  auto acts_load = [&]() {
+  xquad = XC == 0 && gcnt >= 5;
+  const int xkb = xquad ? (lane & 3) : kb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xoff[i] = lvl_chunk<LVL>(i, xkb) * CW + lvl_dword<LVL>(i, xkb) * DW;
+  const uint16_t *xr = x + xrow_at(xquad ? (lane >> 2) : col) * K;
   if constexpr (XC != 0) {
-    const uint16_t *xrc = x + (size_t)min((lane & 15) / XG, M - 1) * K;
+    const uint16_t *xrc = x + xrow_at((lane & 15) / XG) * K;
     int xlp[LPU];
 #pragma unroll
     for (int p = 0; p < LPU; ++p) {
@@ -196,6 +259,13 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
                 *reinterpret_cast<const u32x4_t *>(xr + k0 + (BITS == 8 ? xoff[2 * i] : xoff[i]) + 8 * l);
       }
   }
+  };
+  if constexpr (GATHER) {
+    cur_ch = item_chunk(0);
+    gcs0 = gcs[cur_ch];
+    gcnt = gcs[cur_ch + 1] - gcs0;
+  }
+  acts_load();
 
   // ---- prefetch ring of codes and metadata.  Issues past the last tile are
   // still made (a branch around loads would make the compiler wait for every
@@ -204,23 +274,34 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   // different line for every wave of the device.
   u32x4_t cv[S][BPW][BSC];
   uint2 s4[S][BPW], b4[S][BPW];
-  const uint64_t crow_dead = (uint64_t)(16 * t_first) * RB;
-  const uint64_t mrow_dead = (uint64_t)(16 * t_first) * NG;
+  // item step j's tile: its first column, and the first row of its matrix
+  // among the rows of all experts (gathered: the chunk's expert, N rows each)
+  auto item_col0 = [&](const int j) -> int { return 16 * (t_first + j - item_chunk(j) * T); };
+  auto item_mat = [&](const int j) -> uint64_t {
+    if constexpr (GATHER) return (uint64_t)gce[item_chunk(j)] * (uint64_t)N;
+    return 0ull;
+  };
+  const uint64_t crow_dead = (item_mat(0) + (uint64_t)item_col0(0)) * RB;
+  const uint64_t mrow_dead = (item_mat(0) + (uint64_t)item_col0(0)) * NG;
   int it = 0;  // tile step of the next issue
   auto issue = [&](const int slot) {
     const uint64_t m64 = 0ull - (uint64_t)(it < ntile);  // all-ones while live
     // codes: whole 128-byte lines (LINES: lane L on piece L%8 of row L/8,
     // rows 8-15 in a second load) or lane quads (piece L%4 of row L/4, see
     // quad_row_lane); metadata in lane quads where groups are small (MQ),
-    // else per column
-    const int nq = min(16 * (t_first + it) + (lane >> 2), N - 1);
-    const int nl = min(16 * (t_first + it) + (lane >> 3), N - 1);      // LINES: rows 0-7
-    const int nl8 = min(16 * (t_first + it) + 8 + (lane >> 3), N - 1);  // rows 8-15
-    const uint64_t crow = LINES ? (((uint64_t)nl * RB + (lane & 7) * 16) & m64) | (crow_dead & ~m64)
-                                : (((uint64_t)nq * RB + (lane & 3) * 16) & m64) | (crow_dead & ~m64);
-    const uint64_t crow8 = (((uint64_t)nl8 * RB + (lane & 7) * 16) & m64) | (crow_dead & ~m64);
-    const int nm = MQ ? nq : min(16 * (t_first + it) + col, N - 1);
-    const uint64_t mrow = (((uint64_t)nm * NG) & m64) | (mrow_dead & ~m64);
+    // else per column.  Rows past N (a ragged last tile) read row N-1 of the
+    // same matrix.
+    const int jl = GATHER ? min(it, ntile - 1) : it;  // gathered: a live item (chunk table bounds)
+    const int c0 = item_col0(jl);
+    const uint64_t rb = item_mat(jl);
+    const uint64_t nq = rb + (uint64_t)min(c0 + (lane >> 2), N - 1);
+    const uint64_t nl = rb + (uint64_t)min(c0 + (lane >> 3), N - 1);      // LINES: rows 0-7
+    const uint64_t nl8 = rb + (uint64_t)min(c0 + 8 + (lane >> 3), N - 1);  // rows 8-15
+    const uint64_t crow = LINES ? ((nl * RB + (lane & 7) * 16) & m64) | (crow_dead & ~m64)
+                                : ((nq * RB + (lane & 3) * 16) & m64) | (crow_dead & ~m64);
+    const uint64_t crow8 = ((nl8 * RB + (lane & 7) * 16) & m64) | (crow_dead & ~m64);
+    const uint64_t nm = MQ ? nq : rb + (uint64_t)min(c0 + col, N - 1);
+    const uint64_t mrow = ((nm * NG) & m64) | (mrow_dead & ~m64);
 #pragma unroll
     for (int k = 0; k < BPW; ++k) {
 #pragma unroll
@@ -245,6 +326,7 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
   // keep the code loads ahead of the activation work that waits for x
   __builtin_amdgcn_sched_barrier(0);
 
+  auto acts_finish = [&]() {
   if constexpr (XC != 0) {
 #pragma unroll
     for (int k = 0; k < BPW; ++k)
@@ -297,6 +379,8 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
     }
     xsum[k] = rows_transpose_reduce4(P);
   }
+  };
+  acts_finish();
 
   // ---- groups of S tile steps (the unrolled ring); a range always has a
   // tile (do-while: no guard branch that would let the compiler sink the
@@ -321,8 +405,25 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       if (j0 + s >= ntile) break;
+      // gathered: a step that enters a new chunk loads its activation set
+      // first (ahead of the next step's codes, so that waiting for it does
+      // not wait for them)
+      bool fresh = false;
+      if constexpr (GATHER) {
+        const int ch = item_chunk(j0 + s);
+        if (ch != cur_ch) {
+          cur_ch = ch;
+          gcs0 = gcs[ch];
+          gcnt = gcs[ch + 1] - gcs0;
+          acts_load();
+          fresh = true;
+        }
+      }
       issue((s + S - 1) % S);
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (GATHER) {
+        if (fresh) acts_finish();
+      }
 
       f32x4_t acc = zero4;
       // traces of nonzero weights in this lane's quarter of the column (see
@@ -449,12 +550,20 @@ __global__ __launch_bounds__(64 * MAXW) void qgemv_persist_kernel(
         const int pw = w >= rot ? w - rot : w - rot + W;  // wave acting as virtual wave w
         v += red[rb][s][pw][i][l];
       }
-      // MFMA row a holds activation row a / XG (compact loads: each row XG times)
+      // MFMA row a holds activation row a / XG (compact loads: each row XG
+      // times); gathered: pair a of the item's chunk, output row that pair
       const int a = 4 * (l >> 4) + i;
-      const int m = a % XG == 0 ? a / XG : M;
-      const int n = 16 * (t_first + j0 + s) + (l & 15);
-      if (m < M && n < N) {
-        float *dst = y + (size_t)m * N + n;
+      int m = a % XG == 0 ? a / XG : M;
+      int rows = M;
+      size_t yr = (size_t)m;
+      if constexpr (GATHER) {
+        const int ch = item_chunk(j0 + s);
+        rows = gcs[ch + 1] - gcs[ch];
+        yr = (size_t)gsorted[gcs[ch] + min(m, rows - 1)];
+      }
+      const int n = item_col0(j0 + s) + (l & 15);
+      if (m < rows && n < N) {
+        float *dst = y + yr * N + n;
         if constexpr (ADD) {
           if (!pre) rv = res[(size_t)m * N + n];
         }
@@ -517,11 +626,13 @@ int launch_persist_k(const QgemvArgs &a, hipStream_t stream) {
   constexpr bool CAN_PAIRK = KS == 1 && BPW == 2 && 4 * GS * BITS == 512;
   if (CAN_PAIRK && nblk % 2 == 0) {
     hipLaunchKernelGGL((qgemv_persist_kernel<BITS, GS, BPW, S, MAXW, ADD, CAN_PAIRK, XC, KS>), dim3(G),
-                       dim3(64 * waves), 0, stream, a.codes, a.scales, a.biases, a.x, a.y, a.res, a.M, a.N, a.K);
+                       dim3(64 * waves), 0, stream, a.codes, a.scales, a.biases, a.x, a.y, a.res, a.M, a.N, a.K,
+                       GatherArgs{});
     return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
   }
   hipLaunchKernelGGL((qgemv_persist_kernel<BITS, GS, BPW, S, MAXW, ADD, false, XC, KS>), dim3(G),
-                     dim3(64 * waves), 0, stream, a.codes, a.scales, a.biases, a.x, a.y, a.res, a.M, a.N, a.K);
+                     dim3(64 * waves), 0, stream, a.codes, a.scales, a.biases, a.x, a.y, a.res, a.M, a.N, a.K,
+                       GatherArgs{});
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
 }
 
@@ -551,7 +662,82 @@ int launch_persist_gs(const QgemvArgs &a, hipStream_t stream) {
   return launch_persist_c<BITS, GS, 0>(a, stream);
 }
 
+// Gathered verify on the persistent kernel (called for 3 or more activation
+// rows): as many workgroups as are resident at once, each taking a
+// contiguous range of the (chunk, tile) items, where the chunks are the
+// union's experts' pairs 16 at a time (4 or 8 with compact activation loads).
+// The grid decides only which workgroup takes which item; the wave split
+// follows the shape only (as in the dense kernel), so a pair's row does not
+// depend on the other pairs of the call.  Resident workgroups rather than
+// one per CU: 128-expert top-8 2048 -> 1536 gate/up 12.99 -> 12.59 us at
+// M = 2, 19.27 -> 17.94 at M = 4.
+// At most 8 waves (the activation reload inside the tile loop needs the
+// register budget of 512-thread workgroups: at 16 waves the 4-bit gs64
+// variant spilled).
+template <int BITS, int GS, int XC>
+int launch_persist_gather_t(const QgemvArgs &a, const GatherArgs &ga, hipStream_t stream) {
+  using Sh = PersistShape<BITS, GS>;
+  constexpr int BPW = Sh::BPW, MAXW = 8, S = Sh::S;
+  const int nblk = a.K / (4 * GS);
+  if (nblk > MAXW * BPW) return QGEMV_EUNSUPPORTED;  // activations would not fit the registers
+  const int waves = (nblk + BPW - 1) / BPW;
+  constexpr bool CAN_PAIRK = BPW == 2 && 4 * GS * BITS == 512;
+  const bool pairk = CAN_PAIRK && nblk % 2 == 0;
+  static std::atomic<int> occ_cache[2][MAXW + 1];  // per kernel and wave count
+  int occ = occ_cache[pairk][waves].load(std::memory_order_relaxed);
+  if (occ == 0) {
+    const void *k =
+        pairk ? reinterpret_cast<const void *>(qgemv_persist_kernel<BITS, GS, BPW, S, MAXW, false, CAN_PAIRK, XC, 1, true>)
+              : reinterpret_cast<const void *>(qgemv_persist_kernel<BITS, GS, BPW, S, MAXW, false, false, XC, 1, true>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k, 64 * waves, 0) != hipSuccess || occ < 1) occ = 1;
+    occ_cache[pairk][waves].store(occ, std::memory_order_relaxed);
+  }
+  const int G = device_cu_count() * occ;
+  if (pairk) {
+    hipLaunchKernelGGL((qgemv_persist_kernel<BITS, GS, BPW, S, MAXW, false, CAN_PAIRK, XC, 1, true>), dim3(G),
+                       dim3(64 * waves), 0, stream, a.codes, a.scales, a.biases, a.x, a.y,
+                       static_cast<const float *>(nullptr), 16, a.N, a.K, ga);
+    return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+  }
+  hipLaunchKernelGGL((qgemv_persist_kernel<BITS, GS, BPW, S, MAXW, false, false, XC, 1, true>), dim3(G),
+                     dim3(64 * waves), 0, stream, a.codes, a.scales, a.biases, a.x, a.y,
+                     static_cast<const float *>(nullptr), 16, a.N, a.K, ga);
+  return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
+}
+
+// Activation rows in compact loads (compact_pick) when there are at most 4
+// or 8 of them, with chunks of as many pairs (an expert with more pairs gets
+// several chunks); the arithmetic of a pair's row is the same either way.
+template <int BITS, int GS>
+int launch_persist_gather_x(const QgemvArgs &a, const GatherArgs &ga, hipStream_t stream) {
+  if (ga.X <= 4) return launch_persist_gather_t<BITS, GS, 4>(a, ga, stream);
+  if (ga.X <= 8) return launch_persist_gather_t<BITS, GS, 8>(a, ga, stream);
+  return launch_persist_gather_t<BITS, GS, 0>(a, ga, stream);
+}
+
 }  // namespace
+
+int launch_persist_gather(const QgemvArgs &a, const GatherArgs &ga, hipStream_t stream) {
+  if (a.fmt != 0 || !mfma_supports(a.K, a.bits, a.group_size)) return QGEMV_EUNSUPPORTED;
+  if (a.bits == 4) {
+    switch (a.group_size) {
+      case 32: return launch_persist_gather_x<4, 32>(a, ga, stream);
+      case 64: return launch_persist_gather_x<4, 64>(a, ga, stream);
+      case 128: return launch_persist_gather_x<4, 128>(a, ga, stream);
+    }
+  } else if (a.bits == 2) {
+    switch (a.group_size) {
+      case 64: return launch_persist_gather_x<2, 64>(a, ga, stream);
+      case 128: return launch_persist_gather_x<2, 128>(a, ga, stream);
+    }
+  } else {
+    switch (a.group_size) {
+      case 32: return launch_persist_gather_x<8, 32>(a, ga, stream);
+      case 64: return launch_persist_gather_x<8, 64>(a, ga, stream);
+    }
+  }
+  return QGEMV_EUNSUPPORTED;
+}
 
 int launch_persist(const QgemvArgs &a, hipStream_t stream) {
   if (!mfma_supports(a.K, a.bits, a.group_size)) return QGEMV_EUNSUPPORTED;

@@ -279,12 +279,14 @@ int qgemv_unpack_probe_fp(int path, const uint8_t *codes, uint16_t *out, int N, 
  * K, and the MFMA path's K requirements); 1 <= P <= QGEMV_MAX_PAIRS;
  * 1 <= E <= QGEMV_MAX_EXPERTS; X >= 1; pointers non-NULL, codes, scales,
  * biases, x and y 16-byte aligned, x_idx and e_idx 4-byte aligned.
- * Runs on the MFMA kernel (any number of pairs per expert, 16 rows at a
- * time); each pair's row has the numerics of the MFMA path (within the
- * tolerance of qgemv_small; its K is split over at most 4 waves, so it may
- * differ from a dense call in the last bits), is deterministic, and does not
- * depend on the other pairs of the call (bitwise the same as a call with
- * that pair alone).
+ * Runs on an MFMA kernel (any number of pairs per expert, 16 rows at a
+ * time): the single-pass one for X <= 2, the persistent one for X >= 3 where
+ * the shape fits it.  Each pair's row has the numerics of the MFMA path
+ * (within the tolerance of qgemv_small; its K split over waves is the
+ * kernel's own, so it may differ from a dense call, and between the two
+ * kernels, in the last bits), is deterministic, and does not depend on the
+ * other pairs of the call (bitwise the same as a call with the same x and X
+ * and that pair alone).
  */
 int qgemv_gather(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
                  const uint16_t *x, const int32_t *x_idx, const int32_t *e_idx, float *y, int P,

@@ -2,10 +2,11 @@
 against the fp64 oracle.
 
 Bars: every element within 1e-3 * sum|x w| + 1e-6 of the oracle, full
-sizes included; each pair's row bitwise equal to a call with that pair alone
-(the kernel configuration depends on the shape only, not on the other
-pairs); repeated calls bitwise identical; pairs with invalid indices leave
-their row of y untouched.
+sizes included; each pair's row bitwise equal to a call with the same
+activation rows X and that pair alone (the kernel and its configuration depend
+on the shape and X only, not on the other pairs: the single-pass kernel for
+X <= 2, the persistent one from X = 3); repeated calls bitwise identical;
+pairs with invalid indices leave their row of y untouched.
 """
 import numpy as np
 import pytest
@@ -91,20 +92,22 @@ def test_many_pairs_on_one_expert():
 
 @pytest.mark.parametrize("bits,gs", [(4, 64), (2, 64), (8, 32)])
 def test_few_activation_rows_every_element_and_bitwise(bits, gs):
-    # at most 4 activation rows: compact activation loads, experts' pairs
-    # taken 4 at a time (an expert with more pairs than rows gets several
-    # chunks); each pair's row is the same float as with 16 rows passed
+    # at most 4 or 8 activation rows: compact activation loads, experts' pairs
+    # taken 4 or 8 at a time (an expert with more pairs than rows gets several
+    # chunks); each pair's row is the same float as with the most rows passed
+    # to the same kernel (2 rows: the single-pass kernel; 16: the persistent)
     p = small(bits=bits, gs=gs, seed=19 + bits)
     d = MoeDevice(p)
     rng = np.random.default_rng(7)
-    for X in (1, 3, 4):
+    for X in (1, 2, 3, 4, 5, 8):
         for P in (1, 9, 40):
             x_idx = rng.integers(0, X, size=P)
             e_idx = rng.integers(0, 3 if P == 40 else p.shape.E, size=P)  # P = 40: ~13 pairs per expert
             say(f"gather few rows bits={bits} gs={gs} X={X} P={P}")
             y = d.run(x_idx, e_idx, X=X)
             check(p, y, x_idx, e_idx, label=f"X={X} P={P}")
-            assert np.array_equal(y, d.run(x_idx, e_idx)), f"X={X} P={P} against 16 rows"
+            Xr = 2 if X <= 2 else 16
+            assert np.array_equal(y, d.run(x_idx, e_idx, X=Xr)), f"X={X} P={P} against {Xr} rows"
 
 
 def test_invalid_pairs_leave_rows_untouched():
@@ -120,17 +123,19 @@ def test_invalid_pairs_leave_rows_untouched():
     check(p, y[good], x_idx[good], e_idx[good], label="valid pairs")
 
 
-def test_pair_rows_do_not_depend_on_the_other_pairs_and_repeat():
+@pytest.mark.parametrize("X", [2, 16])
+def test_pair_rows_do_not_depend_on_the_other_pairs_and_repeat(X):
     p = small(E=6, K=2048, N=1536, seed=17)  # 96 tiles, K=2048
     d = MoeDevice(p)
     rng = np.random.default_rng(3)
-    x_idx = rng.integers(0, 16, size=24)
+    x_idx = rng.integers(0, X, size=24)
     e_idx = rng.integers(0, 6, size=24)
-    say("gather pair rows vs single-pair calls, bitwise")
-    y = d.run(x_idx, e_idx)
-    assert np.array_equal(y, d.run(x_idx, e_idx))
+    say(f"gather pair rows vs single-pair calls, bitwise, X={X}")
+    y = d.run(x_idx, e_idx, X=X)
+    check(p, y, x_idx, e_idx, label=f"X={X}")
+    assert np.array_equal(y, d.run(x_idx, e_idx, X=X))
     for i in range(len(e_idx)):
-        y1 = d.run(x_idx[i:i + 1], e_idx[i:i + 1])
+        y1 = d.run(x_idx[i:i + 1], e_idx[i:i + 1], X=X)
         assert np.array_equal(y1[0], y[i]), f"pair {i}"
 
 
