@@ -147,13 +147,17 @@ def test_full_size_every_element(name):
     d = MoeDevice(p)
     xa, ea = p.pairs(16)
     orc = OracleRows.gather(p, xa, ea)
-    for M in (1, 2, 4, 8, 16):
+    # X = M activation rows, as a verify step passes them (M <= 2: the
+    # single-pass kernel, M >= 3: the persistent one where the shape fits it),
+    # and X = 16 rows passed for every M
+    for M in (1, 2, 3, 4, 8, 16):
         x_idx, e_idx = p.pairs(M)
         assert np.array_equal(x_idx, xa[:len(x_idx)]) and np.array_equal(e_idx, ea[:len(e_idx)])
-        say(f"gather full {name} M={M} pairs={len(e_idx)} union={len(set(e_idx.tolist()))}")
-        y = d.run(x_idx, e_idx)
-        assert np.all(np.isfinite(y))
-        orc.check(y, len(e_idx), label=f"{name} M={M}")
+        for X in sorted({M, 16}):
+            say(f"gather full {name} M={M} X={X} pairs={len(e_idx)} union={len(set(e_idx.tolist()))}")
+            y = d.run(x_idx, e_idx, X=X)
+            assert np.all(np.isfinite(y))
+            orc.check(y, len(e_idx), label=f"{name} M={M} X={X}")
 
 
 def test_full_size_pair_rows_do_not_depend_on_the_other_pairs():
