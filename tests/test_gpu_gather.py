@@ -174,3 +174,37 @@ def test_full_size_pair_rows_do_not_depend_on_the_other_pairs():
     for i in sorted(rng.choice(len(e_idx), size=24, replace=False).tolist()):
         y1 = d.run(x_idx[i:i + 1], e_idx[i:i + 1])
         assert np.array_equal(y1[0], y[i]), f"pair {i} (expert {int(e_idx[i])}, row {int(x_idx[i])})"
+
+
+@pytest.mark.parametrize("X", [2, 3, 16])
+def test_max_pairs_on_few_experts(X):
+    # QGEMV_MAX_PAIRS pairs on 3 experts of a ragged N: ~85 pairs per expert,
+    # so every expert takes several chunks (16 pairs each with 16 rows, 4 with
+    # 3 rows) and a workgroup's item range crosses chunk and expert borders;
+    # sampled pairs computed alone give the same bits
+    p = small(E=5, K=1024, N=200, X=16, seed=23)
+    d = MoeDevice(p)
+    rng = np.random.default_rng(29)
+    P = q.MAX_PAIRS
+    x_idx = rng.integers(0, X, size=P)
+    e_idx = rng.choice([0, 2, 4], size=P)
+    say(f"gather max pairs X={X} P={P}")
+    y = d.run(x_idx, e_idx, X=X)
+    check(p, y, x_idx, e_idx, label=f"X={X} P={P}")
+    for i in sorted(rng.choice(P, size=6, replace=False).tolist()):
+        y1 = d.run(x_idx[i:i + 1], e_idx[i:i + 1], X=X)
+        assert np.array_equal(y1[0], y[i]), f"pair {i}"
+
+
+@pytest.mark.parametrize("X", [2, 8])
+def test_many_experts(X):
+    # QGEMV_MAX_EXPERTS experts stored, 64 pairs on random ones (the union
+    # bitmap and the rank sort over ids up to 4095); small N and K
+    p = small(E=q.MAX_EXPERTS, K=256, N=48, X=16, seed=31)
+    d = MoeDevice(p)
+    rng = np.random.default_rng(37)
+    x_idx = rng.integers(0, X, size=64)
+    e_idx = rng.integers(0, q.MAX_EXPERTS, size=64)
+    e_idx[:4] = [0, q.MAX_EXPERTS - 1, q.MAX_EXPERTS - 1, 2048]
+    say(f"gather many experts X={X}")
+    check(p, d.run(x_idx, e_idx, X=X), x_idx, e_idx, label=f"X={X}")
