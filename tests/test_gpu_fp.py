@@ -7,8 +7,8 @@ Bars:
   E4M3 values are bf16 values); through the real kernels, unit scales and
   one-hot x give y equal to the element exactly;
 * y: |y - y_ref| <= 1e-3 * sum_k |x_k w_k| + 1e-6 per element (plus the
-  residual term for the fused residual sum), every element on small and ragged
-  shapes, sampled columns at full size;
+  residual term for the fused residual sum), every element on small, ragged
+  and full-size shapes;
 * row m of an M-row call equals the M=1 call on x[m] bitwise; the fused
   residual sum equals the plain product plus r rounded once, bit for bit.
 """
