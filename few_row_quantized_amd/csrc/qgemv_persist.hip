@@ -47,6 +47,13 @@
 //   for every other format here (27B gate 5120 x 17408 4-bit gs128 15.5 ->
 //   19.3 us at M = 8, FFN-up gs64 10.4 -> 12.7, 2-bit gate/up 15.7 -> 16.1,
 //   the 8-bit 15360 x 3840 shape 15.9 -> 18.7), so only those rows take it.
+// * Gathered verify (GATHER; MLX page, Facts: MoE gather_qmm verify): every
+//   workgroup resolves the device routing (gather_route), cuts each expert's
+//   pairs into chunks of at most 16 (4 or 8 with compact activation loads)
+//   and takes a contiguous range of the (chunk, tile) items in chunk-major
+//   order, so consecutive items are adjacent tiles of one expert and stream
+//   through the same prefetch ring; a step entering a new chunk reloads the
+//   activation set (its pairs' rows) and stores to its pairs' rows of y.
 // The inner MFMA step (code layout, partial lane transpose, unpack to exact
 // bf16 q, per-group scale fold, bias product by v_mfma_f32_16x16x4_f32,
 // zero-weight flags) is the one of the single-pass kernel.
