@@ -86,6 +86,12 @@ bool path_supported(int path, int K, int bits, int group_size) {
 // take the nearest group size of the same bit width.
 int select_path(int M, int N, int K, int bits, int group_size) {
   if (!qgemv::mfma_supports(K, bits, group_size)) return QGEMV_PATH_DOT;
+  // A partial last bias block runs the single-pass MFMA kernel only (the
+  // table's entries were measured with whole blocks, the persistent kernels
+  // included): the dot path up to M = 3 (measured crossovers M = 3 to 5:
+  // 4-bit gs128 11008 x 4096 13.9 / 13.6 us at M = 3, 8960 x 1536 and
+  // 4864 x 896 at M = 5, 2-bit gs128 11008 x 2048 at M = 4)
+  if (!qgemv::mfma_whole_blocks(K, group_size) && M < 4) return QGEMV_PATH_DOT;
   const int nc = qgemv::select_n_class(N), kc = qgemv::select_k_class(K);
   const qgemv::SelectEntry *best = nullptr;
   int best_d = 1 << 30;

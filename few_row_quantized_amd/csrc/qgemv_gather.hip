@@ -35,12 +35,12 @@ namespace {
 
 constexpr int kGatherWideTiles = 64;
 
-template <int BITS, int GS, int NT, int XC, bool XDYN>
+template <int BITS, int GS, int NT, int XC, bool XDYN, bool PB = false>
 int launch_gather_nt(const QgemvArgs &a, const GatherArgs &ga, hipStream_t stream) {
   constexpr int MAXT = MfmaShape<BITS, GS, NT>::MAXT;
   constexpr int SPI = MfmaShape<BITS, GS, NT>::SPI;
-  const auto kern = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, false, false, kAffine, true, XC, XDYN>;
-  const int nblk = a.K / (4 * GS);
+  const auto kern = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, false, false, kAffine, true, XC, XDYN, PB>;
+  const int nblk = (a.K + 4 * GS - 1) / (4 * GS);  // the last block may be partial
   // at most 4 waves (K-slices) per item: more workgroups resident per CU, so
   // more items' loads in flight (128-expert top-8 1536 x 2048 gate/up: 70.3 ->
   // 60.2 us at M = 16, 40.0 -> 33.8 at M = 8, 8.74 -> 8.75 at M = 1; 2 waves:
@@ -79,6 +79,16 @@ int launch_gather_nt(const QgemvArgs &a, const GatherArgs &ga, hipStream_t strea
 // 37.5 -> 29.0 us; 1536 x 2048 (8 blocks) 84.2 -> 87.0 us, so it stays at one.
 template <int BITS, int GS>
 int launch_gather_t(const QgemvArgs &a, const GatherArgs &ga, hipStream_t stream) {
+  // experts with a partial last bias block: the single-pass kernel's variant
+  // for them, one tile per workgroup
+  constexpr bool CAN_PB = BITS != 8 && 4 * GS > 512 / BITS;
+  if (a.K % (4 * GS) != 0) {
+    if constexpr (CAN_PB) {
+      if (ga.X <= 4) return launch_gather_nt<BITS, GS, 1, 4, false, true>(a, ga, stream);
+      return launch_gather_nt<BITS, GS, 1, 0, true, true>(a, ga, stream);
+    }
+    return QGEMV_EUNSUPPORTED;
+  }
   if ((a.N + 15) / 16 >= kGatherWideTiles && a.K / (4 * GS) <= 4)
     return launch_gather_nt<BITS, GS, 2, 0, false>(a, ga, stream);
   // from 3 activation rows, the persistent kernel over (chunk, tile) ranges,

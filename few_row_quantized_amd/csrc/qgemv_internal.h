@@ -80,6 +80,7 @@ int launch_persist_x(const QgemvArgs &a, hipStream_t stream);
 // Shape support of the MFMA path (host check): affine codes, FP formats.
 bool mfma_supports(int K, int bits, int group_size);
 bool mfma_supports_fp(int K, int fmt);
+bool mfma_whole_blocks(int K, int group_size);
 
 // Probes.
 int launch_unpack_probe(int path, const uint8_t *codes, uint8_t *q_out, int N, int K, int bits,

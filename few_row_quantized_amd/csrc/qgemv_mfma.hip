@@ -77,36 +77,36 @@ int resident_per_cu(int waves, std::atomic<int> (&cache)[17]) {
   return occ;
 }
 
-template <int BITS, int GS, int NT, bool ADD, int FMT, int XC, int KS, bool PERSIST>
+template <int BITS, int GS, int NT, bool ADD, int FMT, int XC, int KS, bool PERSIST, bool PB>
 const void *mfma_kernel_ptr() {
   constexpr int MAXT = MfmaShape<BITS, GS, NT>::MAXT;
   constexpr int SPI = MfmaShape<BITS, GS, NT>::SPI;
   return reinterpret_cast<const void *>(
-      qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, KS, PERSIST, ADD, FMT, false, XC>);
+      qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, KS, PERSIST, ADD, FMT, false, XC, false, PB>);
 }
 
 // Launch with XC compact activation rows (0: none).  The persistent grid
 // takes no compact variant.
-template <int BITS, int GS, int NT, bool ADD, int FMT, int XC>
+template <int BITS, int GS, int NT, bool ADD, int FMT, int XC, bool PB>
 int launch_mfma_k(const QgemvArgs &a, int ksplit, bool single, int waves, int grid, int groups,
                   hipStream_t stream) {
   constexpr int MAXT = MfmaShape<BITS, GS, NT>::MAXT;
   constexpr int SPI = MfmaShape<BITS, GS, NT>::SPI;
-  const auto kern = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, XC == 0, ADD, FMT, false, XC>;
-  const auto kern1 = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, false, ADD, FMT, false, XC>;
-  const auto kern_s = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 2, XC == 0, ADD, FMT, false, XC>;
-  const auto kern1_s = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 2, false, ADD, FMT, false, XC>;
+  const auto kern = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, XC == 0, ADD, FMT, false, XC, false, PB>;
+  const auto kern1 = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 1, false, ADD, FMT, false, XC, false, PB>;
+  const auto kern_s = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 2, XC == 0, ADD, FMT, false, XC, false, PB>;
+  const auto kern1_s = qgemv_mfma_kernel<BITS, GS, NT, MAXT, SPI, 2, false, ADD, FMT, false, XC, false, PB>;
   const auto k = ksplit == 1 ? (single ? kern1 : kern) : (single ? kern1_s : kern_s);
   hipLaunchKernelGGL(k, dim3(grid), dim3(64 * waves), 0, stream, a.codes, a.scales, a.biases, a.x,
                      a.y, a.res, a.M, a.N, a.K, groups, GatherArgs{});
   return hipGetLastError() == hipSuccess ? QGEMV_OK : QGEMV_EHIP;
 }
 
-template <int BITS, int GS, int NT, bool ADD, int FMT>
+template <int BITS, int GS, int NT, bool ADD, int FMT, bool PB>
 int launch_mfma_t(const QgemvArgs &a, hipStream_t stream) {
   constexpr int MAXT = MfmaShape<BITS, GS, NT>::MAXT;
   static_assert(MAXT / 64 <= 16, "wave cap");
-  const int nblk = a.K / (4 * GS);
+  const int nblk = (a.K + 4 * GS - 1) / (4 * GS);  // the last block may be partial
   const int tiles = (a.N + 15) / 16;
   const int cus = device_cu_count();
   // Few tile groups for the CUs: split K in two halves across workgroups
@@ -124,7 +124,7 @@ int launch_mfma_t(const QgemvArgs &a, hipStream_t stream) {
   // one tile group per workgroup when all are resident at once, else the
   // persistent grid (one per resident workgroup, walking the groups)
   static std::atomic<int> occ0[17], occ4[2][17], occ8[2][17];
-  const int slots = resident_per_cu<mfma_kernel_ptr<BITS, GS, NT, ADD, FMT, 0, 1, true>>(waves, occ0) * cus;
+  const int slots = resident_per_cu<mfma_kernel_ptr<BITS, GS, NT, ADD, FMT, 0, 1, true, PB>>(waves, occ0) * cus;
   const bool single = groups <= slots;
   if (ksplit == 2) {
     const int st = launch_fill(a.y, (size_t)a.M * a.N, ADD ? kSplitSentinel : 0u, stream);
@@ -142,15 +142,17 @@ int launch_mfma_t(const QgemvArgs &a, hipStream_t stream) {
   if constexpr (NT == 1) {
     auto fits = [&](const int occ) { return groups <= occ * cus; };
     if (single && a.M <= 4 &&
-        fits(ksplit == 1 ? resident_per_cu<mfma_kernel_ptr<BITS, GS, NT, ADD, FMT, 4, 1, false>>(waves, occ4[0])
-                         : resident_per_cu<mfma_kernel_ptr<BITS, GS, NT, ADD, FMT, 4, 2, false>>(waves, occ4[1])))
-      return launch_mfma_k<BITS, GS, NT, ADD, FMT, 4>(a, ksplit, single, waves, grid, groups, stream);
-    if (single && a.M <= 8 &&
-        fits(ksplit == 1 ? resident_per_cu<mfma_kernel_ptr<BITS, GS, NT, ADD, FMT, 8, 1, false>>(waves, occ8[0])
-                         : resident_per_cu<mfma_kernel_ptr<BITS, GS, NT, ADD, FMT, 8, 2, false>>(waves, occ8[1])))
-      return launch_mfma_k<BITS, GS, NT, ADD, FMT, 8>(a, ksplit, single, waves, grid, groups, stream);
+        fits(ksplit == 1 ? resident_per_cu<mfma_kernel_ptr<BITS, GS, NT, ADD, FMT, 4, 1, false, PB>>(waves, occ4[0])
+                         : resident_per_cu<mfma_kernel_ptr<BITS, GS, NT, ADD, FMT, 4, 2, false, PB>>(waves, occ4[1])))
+      return launch_mfma_k<BITS, GS, NT, ADD, FMT, 4, PB>(a, ksplit, single, waves, grid, groups, stream);
+    // (not with a partial last block: there the 8-row form measured slower
+    // than the full one, 11008 x 4096 at M = 8: 18.7 against 14.6 us)
+    if (!PB && single && a.M <= 8 &&
+        fits(ksplit == 1 ? resident_per_cu<mfma_kernel_ptr<BITS, GS, NT, ADD, FMT, 8, 1, false, PB>>(waves, occ8[0])
+                         : resident_per_cu<mfma_kernel_ptr<BITS, GS, NT, ADD, FMT, 8, 2, false, PB>>(waves, occ8[1])))
+      return launch_mfma_k<BITS, GS, NT, ADD, FMT, 8, PB>(a, ksplit, single, waves, grid, groups, stream);
   }
-  return launch_mfma_k<BITS, GS, NT, ADD, FMT, 0>(a, ksplit, single, waves, grid, groups, stream);
+  return launch_mfma_k<BITS, GS, NT, ADD, FMT, 0, PB>(a, ksplit, single, waves, grid, groups, stream);
 }
 
 template <int BITS, int GS, int FMT = kAffine>
@@ -166,12 +168,26 @@ int launch_mfma_gs(const QgemvArgs &a, hipStream_t stream) {
   const int tiles = (a.N + 15) / 16;
   const int cus = device_cu_count();
   const bool wide = tiles >= 2 * cus;
-  if (a.res) {
-    if (wide) return launch_mfma_t<BITS, GS, 2, true, FMT>(a, stream);
-    return launch_mfma_t<BITS, GS, 1, true, FMT>(a, stream);
+  // a partial last bias block: its own variant (affine 2/4-bit codes whose
+  // blocks span more than one super-chunk)
+  constexpr bool CAN_PB = FMT == kAffine && BITS != 8 && 4 * GS > 512 / BITS;
+  if constexpr (CAN_PB) {
+    if (a.K % (4 * GS) != 0) {
+      if (a.res) {
+        if (wide) return launch_mfma_t<BITS, GS, 2, true, FMT, true>(a, stream);
+        return launch_mfma_t<BITS, GS, 1, true, FMT, true>(a, stream);
+      }
+      if (wide) return launch_mfma_t<BITS, GS, 2, false, FMT, true>(a, stream);
+      return launch_mfma_t<BITS, GS, 1, false, FMT, true>(a, stream);
+    }
   }
-  if (wide) return launch_mfma_t<BITS, GS, 2, false, FMT>(a, stream);
-  return launch_mfma_t<BITS, GS, 1, false, FMT>(a, stream);
+  if (a.K % (4 * GS) != 0) return QGEMV_EUNSUPPORTED;
+  if (a.res) {
+    if (wide) return launch_mfma_t<BITS, GS, 2, true, FMT, false>(a, stream);
+    return launch_mfma_t<BITS, GS, 1, true, FMT, false>(a, stream);
+  }
+  if (wide) return launch_mfma_t<BITS, GS, 2, false, FMT, false>(a, stream);
+  return launch_mfma_t<BITS, GS, 1, false, FMT, false>(a, stream);
 }
 
 }  // namespace
@@ -187,11 +203,18 @@ bool mfma_supports_fp(int K, int fmt) {
   return K % 128 == 0;  // one 128-element block of bias blocks per super-chunk
 }
 
+// Whole 64-byte super-chunks and whole groups; bias blocks of 4 groups, of
+// which the single-pass kernel also takes a partial last one (2- and 4-bit
+// codes, at least 4 groups in K); the persistent kernels need whole blocks
+// (mfma_whole_blocks).
 bool mfma_supports(int K, int bits, int group_size) {
   if (bits == 2 && group_size < 64) return false;
   const int scw = 512 / bits;  // codes per 64-byte super-chunk
-  return K % scw == 0 && K % (4 * group_size) == 0;
+  if (K % scw != 0 || K % group_size != 0) return false;
+  return K % (4 * group_size) == 0 || (bits != 8 && K / group_size >= 4);
 }
+
+bool mfma_whole_blocks(int K, int group_size) { return K % (4 * group_size) == 0; }
 
 int launch_mfma(const QgemvArgs &a, hipStream_t stream) {
   if (a.fmt != kAffine) {
@@ -205,7 +228,7 @@ int launch_mfma(const QgemvArgs &a, hipStream_t stream) {
   // with the activations in registers, or, for K too long for them, in LDS
   // (one half of K per workgroup); otherwise one tile group per workgroup in
   // a single pass
-  if ((a.N + 15) / 16 > device_cu_count()) {
+  if ((a.N + 15) / 16 > device_cu_count() && mfma_whole_blocks(a.K, a.group_size)) {
     int st = launch_persist(a, stream);
     if (st != QGEMV_EUNSUPPORTED) return st;
     st = launch_persist_x(a, stream);

@@ -30,7 +30,7 @@ namespace {
 // with two, workgroup b serves item b and exits if its slot is past the
 // union.  (KS = 1, not PERSIST, affine codes.)
 template <int BITS, int GS, int NT, int MAXT, int SPI, int KS, bool PERSIST, bool ADD, int FMT,
-          bool GATHER = false, int XC = 0, bool XDYN = false>
+          bool GATHER = false, int XC = 0, bool XDYN = false, bool PB = false>
 __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ biases, const uint16_t *__restrict__ x, float *y,
@@ -79,7 +79,16 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
   const int waves = blockDim.x >> 6;
   const int col = lane & 15;
   const int kb = lane >> 4;
-  const int NBLK = K / BLKW;
+  // Bias blocks of 4 groups; with PB the last one is partial (affine 2/4-bit
+  // codes: K a whole number of super-chunks and of groups, at least 4
+  // groups).  Its missing super-chunks load the row's last real one (valid
+  // addresses) with their activations set to zero, and its metadata load is
+  // moved back inside the row and shifted, so the missing groups carry scale
+  // and bias 0: they add exactly nothing.  (A compile-time variant: the
+  // clamps cost whole-block shapes 5-20% in the single-pass kernel.)
+  static_assert(!PB || (FMT == kAffine && BITS != 8), "partial blocks: affine 2/4-bit codes");
+  const int NBLK = PB ? (K + BLKW - 1) / BLKW : K / BLKW;
+  const int NSC = K / SCW;  // real super-chunks per row
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   // element offset, within a super-chunk, of the codes register i holds in
   // this lane's row after the partial transpose
@@ -285,14 +294,14 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
 #pragma unroll
       for (int ld = 0; ld < NLD; ++ld) {
         const int blk = ld * XG / (BSC * OPS);
-        cx[ld] = *reinterpret_cast<const u32x4_t *>(
-            xb + (blk < nb ? (ld / LPU) * SPL * SCW + xlp[ld % LPU] : xlp[0]));
+        const bool in = blk < nb && (!PB || blk0 * BSC + (ld / LPU) * SPL < NSC);
+        cx[ld] = *reinterpret_cast<const u32x4_t *>(xb + (in ? (ld / LPU) * SPL * SCW + xlp[ld % LPU] : xlp[0]));
       }
     } else {
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         if (u / BSC < nb) {
-          const int k0 = (blk0 * BSC + u) * SCW;
+          const int k0 = (PB ? min(blk0 * BSC + u, NSC - 1) : blk0 * BSC + u) * SCW;
 #pragma unroll
           for (int i = 0; i < XR; ++i)
 #pragma unroll
@@ -305,7 +314,7 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       if (u / BSC < nb) {
-        const int gsc = blk0 * BSC + u;
+        const int gsc = PB ? min(blk0 * BSC + u, NSC - 1) : blk0 * BSC + u;
 #pragma unroll
         for (int t = 0; t < NT; ++t) cv[u][t] = load_stream_u32x4(crow[t] + (size_t)gsc * 64);
       }
@@ -316,8 +325,9 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           if constexpr (HAS_BIAS) {
-            s4[bb][t] = *reinterpret_cast<const uint2 *>(srow[t] + (size_t)(blk0 + bb) * 4);
-            b4[bb][t] = *reinterpret_cast<const uint2 *>(brow[t] + (size_t)(blk0 + bb) * 4);
+            const int gm = PB ? min((blk0 + bb) * 4, G - 4) : (blk0 + bb) * 4;  // inside the row (G >= 4)
+            s4[bb][t] = *reinterpret_cast<const uint2 *>(srow[t] + (size_t)gm);
+            b4[bb][t] = *reinterpret_cast<const uint2 *>(brow[t] + (size_t)gm);
           } else if constexpr (FMT == kNvfp4) {
             // the 8 scale bytes of the block's 128 elements
             s4[bb][t] = *reinterpret_cast<const uint2 *>(srow8[t] + (size_t)(blk0 + bb) * 8);
@@ -336,6 +346,27 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
     // keep the whole batch of loads ahead of the compute: without this the
     // scheduler may sink later loads below the first waits and serialize them
     __builtin_amdgcn_sched_barrier(0);
+
+    // ---- a partial last block (uniform): activations of its missing
+    // super-chunks are zero (their metadata fields are moved below, where
+    // the metadata is first used: the metadata loads are the batch's last)
+    if constexpr (PB) {
+      if ((blk0 + nb) * BSC > NSC) {
+        if constexpr (XCV != 0) {
+#pragma unroll
+          for (int ld = 0; ld < NLD; ++ld)
+            if (blk0 * BSC + (ld / LPU) * SPL >= NSC) cx[ld] = u32x4_t{0u, 0u, 0u, 0u};
+        } else {
+#pragma unroll
+          for (int u = 0; u < UNR; ++u)
+            if (blk0 * BSC + u >= NSC)
+#pragma unroll
+              for (int i = 0; i < XR; ++i)
+#pragma unroll
+                for (int l = 0; l < HS; ++l) xv[u][i][l] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+      }
+    }
 
     // ---- activation work, overlapping the code loads: re-pair x to the
     // code pairing and form the per-group activation sums.  xsum of group
@@ -392,6 +423,25 @@ __global__ __launch_bounds__(MAXT) void qgemv_mfma_kernel(
       if constexpr (HAS_BIAS) xsum[bb] = rows_transpose_reduce4(P);
     }
 
+    // a partial last block's metadata fields move down to their groups (its
+    // missing groups get scale and bias 0)
+    if constexpr (PB) {
+      if ((blk0 + nb) * BSC > NSC) {
+#pragma unroll
+        for (int bb = 0; bb < BPB; ++bb) {
+          const int sh = (blk0 + bb) * 4 - min((blk0 + bb) * 4, G - 4);  // 0..3 inside K
+          if (bb < nb && sh > 0) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              const uint64_t sv = ((uint64_t)s4[bb][t].y << 32 | s4[bb][t].x) >> (16 * sh);
+              const uint64_t bv = ((uint64_t)b4[bb][t].y << 32 | b4[bb][t].x) >> (16 * sh);
+              s4[bb][t] = make_uint2((uint32_t)sv, (uint32_t)(sv >> 32));
+              b4[bb][t] = make_uint2((uint32_t)bv, (uint32_t)(bv >> 32));
+            }
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int bb = 0; bb < BPB; ++bb)
 #pragma unroll

@@ -725,7 +725,8 @@ int launch_persist_gather_x(const QgemvArgs &a, const GatherArgs &ga, hipStream_
 }  // namespace
 
 int launch_persist_gather(const QgemvArgs &a, const GatherArgs &ga, hipStream_t stream) {
-  if (a.fmt != 0 || !mfma_supports(a.K, a.bits, a.group_size)) return QGEMV_EUNSUPPORTED;
+  if (a.fmt != 0 || !mfma_supports(a.K, a.bits, a.group_size) || !mfma_whole_blocks(a.K, a.group_size))
+    return QGEMV_EUNSUPPORTED;
   if (a.bits == 4) {
     switch (a.group_size) {
       case 32: return launch_persist_gather_x<4, 32>(a, ga, stream);
@@ -747,7 +748,7 @@ int launch_persist_gather(const QgemvArgs &a, const GatherArgs &ga, hipStream_t 
 }
 
 int launch_persist(const QgemvArgs &a, hipStream_t stream) {
-  if (!mfma_supports(a.K, a.bits, a.group_size)) return QGEMV_EUNSUPPORTED;
+  if (!mfma_supports(a.K, a.bits, a.group_size) || !mfma_whole_blocks(a.K, a.group_size)) return QGEMV_EUNSUPPORTED;
   if (a.bits == 8) {
     // groups of 128 span two super-chunks: the single-pass kernel
     switch (a.group_size) {

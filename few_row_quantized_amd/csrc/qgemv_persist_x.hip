@@ -488,7 +488,8 @@ int launch_persist_x_gs(const QgemvArgs &a, hipStream_t stream) {
 }  // namespace
 
 int launch_persist_x(const QgemvArgs &a, hipStream_t stream) {
-  if (a.fmt != kAffine || !mfma_supports(a.K, a.bits, a.group_size)) return QGEMV_EUNSUPPORTED;
+  if (a.fmt != kAffine || !mfma_supports(a.K, a.bits, a.group_size) || !mfma_whole_blocks(a.K, a.group_size))
+    return QGEMV_EUNSUPPORTED;
   // an in-place residual sum cannot be prefilled
   if (a.res && static_cast<const void *>(a.res) == static_cast<const void *>(a.y)) return QGEMV_EUNSUPPORTED;
   if (a.bits == 4) {

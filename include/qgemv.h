@@ -153,8 +153,10 @@ int qgemv_select(int M, int N, int K, int bits, int group_size);
  * pages' A/B knobs: the specgate-metal README's GGML_METAL_NO_MV_EXT /
  * GGML_METAL_MM_MIN; MLX page, Facts: forced qmv vs qmm sweeps).
  * Returns QGEMV_EUNSUPPORTED if the path cannot run the shape (the MFMA path
- * needs K to be a multiple of 4*group_size and of 256 (2-bit) / 128 (4-bit) /
- * 64 (8-bit), and group_size >= 64 for 2-bit codes).  Other arguments as
+ * needs K to be a multiple of 256 (2-bit) / 128 (4-bit) / 64 (8-bit), and
+ * group_size >= 64 for 2-bit codes; K a multiple of 4*group_size, or for 2-
+ * and 4-bit codes at least 4 groups, the remainder then running as a partial
+ * last block of the single-pass MFMA kernel).  Other arguments as
  * qgemv_small.
  */
 int qgemv_run_path(int path, const uint8_t *codes, const uint16_t *scales,

@@ -58,6 +58,8 @@ def mfma_configuration(M: int, N: int, K: int, bits: int, gs: int, cus: int):
     register-resident persistent kernel): ("long_k", phases, bpw, waves) or
     ("single_pass",)."""
     tiles = (N + 15) // 16
+    if K % (4 * gs) != 0:  # a partial last bias block: the single-pass kernel only
+        return ("single_pass",)
     if tiles > cus and not register_persistent_fits(K, bits, gs):
         c = long_k_config(M, N, K, bits, gs, cus)
         if c is not None:

@@ -4,16 +4,15 @@ Every code of row n equals a zero point z_n (rows cycle through all code
 values) and its bias is -z_n * s exactly, so y = 0 and the tolerance is the
 absolute floor 1e-6 alone: the case where a decode that carries an offset, or a
 scale term and a bias term that cancel in fp32, loses to rounding.  The kernels
-decode codes without an offset and apply each group as
-s * (P_codes - P_z) + b' * sum x with the group's integer zero point
-z = round(-b/s), b' = b + z*s, and P_z formed by the same arithmetic as P_codes
-with z in every code slot; on a zero row the two products see identical
-operands and b' is exactly 0, so:
+decode codes without an offset, and each lane keeps traces of nonzero weights
+in the groups it folds (codes that differ within a group, or a group weight
+s*c + b that is not exactly zero) and contributes exactly 0 when there are
+none, so:
 * every element is exactly 0, and with a residual exactly the residual;
 * hence within the tolerance (the worst |dy|/tol is printed).
 Both paths and the dispatcher, 2-, 4- and 8-bit codes, every group size, short
-and long K, single-pass and persistent MFMA kernels, plain and fused sums,
-activations with x20 outlier channels.
+and long K (a partial last bias block included), single-pass and persistent
+MFMA kernels, plain and fused sums, activations with x20 outlier channels.
 """
 import numpy as np
 import pytest
@@ -36,6 +35,8 @@ SHAPES = [
     (4096, 4200, 4, 64), (5120, 4200, 2, 64), (17408, 4200, 4, 128), (17408, 4128, 2, 64),
     (4096, 300, 8, 32), (4096, 300, 8, 64), (4096, 300, 8, 128),
     (4096, 4200, 8, 32), (3840, 4200, 8, 64), (5120, 4200, 8, 64),
+    # a partial last bias block (single-pass MFMA kernel)
+    (640, 300, 4, 128), (11008, 300, 4, 128), (768, 300, 2, 128), (4864, 4200, 4, 128),
 ]
 MS = (1, 2, 8, 16)
 

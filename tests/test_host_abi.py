@@ -138,7 +138,8 @@ def test_mfma_path_shape_support():
     assert sup("mfma", 4, 4096, 4096, 2, 64)
     assert not sup("mfma", 4, 4096, 4096, 2, 32)   # 2-bit gs32: dot path only
     assert not sup("mfma", 4, 4096, 192, 4, 32)     # K not a multiple of 128
-    assert not sup("mfma", 4, 4096, 640, 4, 128)    # K not a multiple of 4*gs
+    assert sup("mfma", 4, 4096, 640, 4, 128)        # a partial last bias block (5 groups)
+    assert not sup("mfma", 4, 4096, 384, 4, 128)    # fewer than 4 groups
     assert sup("dot", 4, 4096, 192, 4, 32)
     assert sup("mfma", 4, 4096, 4096, 8, 32) and sup("mfma", 4, 4096, 4096, 8, 64)
     assert sup("mfma", 4, 4096, 4096, 8, 128) and sup("dot", 4, 4096, 4096, 8, 128)
