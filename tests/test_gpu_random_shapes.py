@@ -63,6 +63,42 @@ def test_random_shape_every_element(i, bits, gs, K, N, Ms, outliers):
         torch.cuda.synchronize()
 
 
+def draw_partial_cases(n_cases: int, seed: int):
+    # K a whole number of super-chunks (128 codes at 4 bits, 256 at 2) with
+    # at least 4 groups but not a whole number of 4-group bias blocks: the
+    # single-pass MFMA kernel's partial-block variant
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n_cases:
+        bits, gs = [(4, 64), (4, 128), (2, 128)][rng.integers(3)]
+        scw = 512 // bits
+        K = scw * int(rng.integers(1, 12288 // scw + 1))
+        if K % gs or K // gs < 4 or K % (4 * gs) == 0:
+            continue
+        N = int(rng.choice([rng.integers(1, 48), rng.integers(48, 1200), rng.integers(4096, 6000)]))
+        Ms = sorted(set(int(m) for m in rng.integers(1, 17, size=3)))
+        cases.append((len(cases), bits, gs, K, N, Ms, bool(rng.integers(2))))
+    return cases
+
+
+@pytest.mark.parametrize("i,bits,gs,K,N,Ms,outliers", draw_partial_cases(12, seed=20261204))
+def test_random_partial_block_shape_every_element(i, bits, gs, K, N, Ms, outliers):
+    p = synth.make_problem(synth.custom_shape(K, N, bits, gs, seed=7000 + i, outliers=outliers), m_max=16)
+    d = DeviceProblem(p)
+    orc = OracleRows.affine(p, max(Ms))
+    for path in ("dot", "mfma", "auto"):
+        assert q.qgemv_path_supported(path, 1, N, K, bits, gs)
+        y1 = None
+        for M in [1] + Ms:
+            say(f"random partial-block case {i}: {path} bits={bits} gs={gs} K={K} N={N} M={M}")
+            y = d.run_host(M, path)
+            orc.check(y, M, label=f"case {i} {path} M={M}")
+            if M == 1:
+                y1 = y
+            elif path != "auto":
+                assert np.array_equal(y[:1], y1), f"case {i} {path}: row 0 of M={M} differs from M=1"
+
+
 def draw_fp_cases(n_cases: int, seed: int):
     rng = np.random.default_rng(seed)
     cases = []

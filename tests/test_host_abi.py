@@ -160,6 +160,19 @@ def test_select_returns_a_supported_path_everywhere():
                     assert q.qgemv_path_supported(p, M, 4096, K, bits, gs)
 
 
+def test_select_keeps_the_dot_path_below_four_rows_on_partial_blocks():
+    # K with a partial last bias block (11008 = 86 groups of 128): only the
+    # single-pass MFMA kernel takes it, so the dot path up to M = 3; whole
+    # blocks (11264 = 88 groups) follow the measured table
+    for K, bits in ((11008, 4), (8960, 4), (11008, 2)):
+        for M in range(1, 17):
+            p = q.qgemv_select(M, 4096, K, bits, 128)
+            if M < 4:
+                assert p == q.PATH_DOT, (K, bits, M)
+            assert q.qgemv_path_supported(p, M, 4096, K, bits, 128)
+    assert any(q.qgemv_select(M, 4096, 11264, 4, 128) == q.PATH_MFMA for M in (2, 3))
+
+
 def test_stream_probe_validation():
     L = q.lib()
     assert L.qgemv_stream_probe(None, 1024, A, 4, 0, None) == q.EINVAL
